@@ -1,0 +1,221 @@
+"""CPU oracle for the routed-expert FP8 MoE prefill layer (ctypes binding).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``; never by the product package.
+The C source (``oracle.c``) states what each step computes and which passage
+of the pages it follows; the pins that tie it to something other than itself
+are in ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+FAULTS = {
+    "none": 0,
+    "weight_scale_index": 1,
+    "drop_last_kblock": 2,
+    "unstable_plan": 3,
+    "silu_clamp": 4,
+    "pad_garbage": 5,
+    "nan_code_is_nan": 6,
+    "group_64": 7,
+    "down_scale_transposed": 8,
+    "encode_truncate": 9,
+    "drop_rho": 10,
+    "silu_sign": 11,
+    "gate_up_swap": 12,
+}
+
+OUT_BF16 = 0
+OUT_F32 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c: gcc -O2, OpenMP, no fast-math, no FP contraction."""
+    src = os.path.join(_HERE, "oracle.c")
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fno-fast-math", "-ffp-contract=off",
+                               "-fPIC", "-shared", "-std=c11", src, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+                ("gate_scale", ctypes.c_void_p), ("up_scale", ctypes.c_void_p),
+                ("down_scale", ctypes.c_void_p)]
+
+
+class _Debug(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("xq", "sx", "gu", "hq", "sh", "y", "counts", "offsets", "perm", "inv")]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        lib.orc_e4m3_decode.argtypes = [ctypes.c_uint32]
+        lib.orc_e4m3_decode.restype = ctypes.c_float
+        lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.orc_e4m3_encode.restype = ctypes.c_uint32
+        for name in ("orc_decode_array", "orc_encode_array", "orc_bf16_to_f32_array",
+                     "orc_f32_to_bf16_array"):
+            getattr(lib, name).argtypes = [P, ctypes.c_int64, P]
+            getattr(lib, name).restype = None
+        lib.orc_quantize_rows.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P]
+        lib.orc_quantize_rows.restype = None
+        lib.orc_plan.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
+        lib.orc_plan.restype = ctypes.c_int64
+        lib.orc_forward.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int32, P, P, P, ctypes.c_int64,
+                                    ctypes.c_float, ctypes.c_int32, P, ctypes.POINTER(_Debug)]
+        lib.orc_forward.restype = ctypes.c_int64
+        lib.orc_bruteforce_fp64.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int32, P, P, P,
+                                            ctypes.c_int64, ctypes.c_double, ctypes.c_int32, P]
+        lib.orc_bruteforce_fp64.restype = ctypes.c_int32
+        lib.orc_set_fault.argtypes = [ctypes.c_int32]
+        lib.orc_set_fault.restype = None
+        lib.orc_max_threads.argtypes = []
+        lib.orc_max_threads.restype = ctypes.c_int32
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "need a C-contiguous array"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def set_fault(name: str) -> None:
+    """Plant a deliberate mistake in the oracle (for testing the pins only)."""
+    _load().orc_set_fault(FAULTS[name])
+
+
+def max_threads() -> int:
+    return int(_load().orc_max_threads())
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float32)
+    _load().orc_decode_array(_p(c), c.size, _p(out))
+    return out
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    f = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(f.shape, np.uint8)
+    _load().orc_encode_array(_p(f), f.size, _p(out))
+    return out
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    u = np.ascontiguousarray(b, dtype=np.uint16)
+    out = np.empty(u.shape, np.float32)
+    _load().orc_bf16_to_f32_array(_p(u), u.size, _p(out))
+    return out
+
+
+def f32_to_bf16(f: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(v.shape, np.uint16)
+    _load().orc_f32_to_bf16_array(_p(v), v.size, _p(out))
+    return out
+
+
+def quantize_rows(x: np.ndarray):
+    """(codes u8[rows][cols], scales f32[rows][cols/128]) for f32 x[rows][cols]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    if cols % 128:
+        raise ValueError("cols must be a multiple of 128")
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, cols // 128), np.float32)
+    _load().orc_quantize_rows(_p(x), rows, cols, _p(q), _p(s))
+    return q, s
+
+
+def plan(ids: np.ndarray, E: int):
+    """Stable counting sort of the slots by expert: (counts, offsets, perm, inv, n_bad)."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    perm = np.empty(max(T * k, 1), np.int32)
+    inv = np.empty(max(T * k, 1), np.int32)
+    bad = _load().orc_plan(_p(ids), T, k, E, _p(counts), _p(offsets), _p(perm), _p(inv))
+    return counts, offsets, perm[: offsets[E]], inv[: T * k], int(bad)
+
+
+def _layer_struct(layer):
+    arrs = [np.ascontiguousarray(a) for a in (layer.gate, layer.up, layer.down)]
+    sc = [np.ascontiguousarray(a, dtype=np.float32) for a in
+          (layer.gate_scale, layer.up_scale, layer.down_scale)]
+    st = _Layer(layer.E, layer.H, layer.I, *(a.ctypes.data for a in arrs),
+                *(a.ctypes.data for a in sc))
+    return st, arrs + sc  # keep the arrays alive
+
+
+def forward(layer, x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, rho: float,
+            out_dtype: int = OUT_BF16, debug: bool = False):
+    """The layer on T tokens.  Returns out (u16 bf16 bits or f32 [T][H]) and,
+    with debug=True, a dict of the intermediate arrays (sorted-order rows)."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    T, k = ids.shape
+    H, I, E = layer.H, layer.I, layer.E
+    Ip = 128 * ((I + 127) // 128)
+    out = np.empty((T, H), np.uint16 if out_dtype == OUT_BF16 else np.float32)
+    st, keep = _layer_struct(layer)
+    dbg = None
+    d = None
+    if debug:
+        routed = int(((ids >= 0) & (ids < E)).sum())
+        d = dict(xq=np.empty((T, H), np.uint8), sx=np.empty((T, H // 128), np.float32),
+                 gu=np.empty((routed, 2 * Ip), np.float32), hq=np.empty((routed, Ip), np.uint8),
+                 sh=np.empty((routed, Ip // 128), np.float32), y=np.empty((routed, H), np.float32),
+                 counts=np.empty(E, np.int32), offsets=np.empty(E + 1, np.int32),
+                 perm=np.empty(max(routed, 1), np.int32), inv=np.empty(max(T * k, 1), np.int32))
+        dbg = _Debug(*(d[n].ctypes.data for n in
+                       ("xq", "sx", "gu", "hq", "sh", "y", "counts", "offsets", "perm", "inv")))
+    bad = _load().orc_forward(ctypes.byref(st), k, _p(x_bits), _p(ids), _p(w), T, float(rho),
+                              out_dtype, _p(out), ctypes.byref(dbg) if dbg is not None else None)
+    del keep
+    if bad < 0:
+        raise ValueError("bad arguments")
+    if debug:
+        d["perm"] = d["perm"][: d["offsets"][E]]
+        d["inv"] = d["inv"][: T * k]
+        d["n_bad"] = int(bad)
+        return out, d
+    return out
+
+
+def bruteforce_fp64(layer, x_bits, ids, w, rho, quantize_activations=True) -> np.ndarray:
+    """Dense FP64 evaluation (tiny inputs only).  out f64[T][H]."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    T, k = ids.shape
+    out = np.empty((T, layer.H), np.float64)
+    st, keep = _layer_struct(layer)
+    _load().orc_bruteforce_fp64(ctypes.byref(st), k, _p(x_bits), _p(ids), _p(w), T, float(rho),
+                                1 if quantize_activations else 0, _p(out))
+    del keep
+    return out
