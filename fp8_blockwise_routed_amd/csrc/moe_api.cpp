@@ -1,0 +1,647 @@
+// C-ABI entry points of the routed-expert FP8 MoE prefill library.  Host code
+// only: argument checks, device memory, weight upload, the per-pass launch
+// sequence and the handle's fail-closed state.  Kernels are in
+// moe_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/moe_fp8_prefill.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+struct Dims {
+  int64_t E, k, H, I, Ip, nH, nI, max_rows, P;  // P = max_rows * k
+};
+
+Dims dims_of(const moe_fp8_prefill_desc* d) {
+  Dims m;
+  m.E = d->num_experts;
+  m.k = d->top_k;
+  m.H = d->hidden;
+  m.I = d->inter;
+  m.Ip = kBlock * ((m.I + kBlock - 1) / kBlock);
+  m.nH = m.H / kBlock;
+  m.nI = m.Ip / kBlock;
+  m.max_rows = d->max_rows;
+  m.P = m.max_rows * m.k;
+  return m;
+}
+
+int64_t align256(int64_t n) { return (n + 255) & ~int64_t(255); }
+
+// Workspace pieces, in allocation order.
+struct WsSizes {
+  int64_t xq, sx, hq, sh, y, counts, offsets, perm, inv, small_tiles, big_tiles, n_tiles, err;
+  int64_t total() const {
+    return align256(xq) + align256(sx) + align256(hq) + align256(sh) + align256(y) +
+           align256(counts) + align256(offsets) + align256(perm) + align256(inv) +
+           align256(small_tiles) + align256(big_tiles) + align256(n_tiles) + align256(err);
+  }
+};
+
+WsSizes ws_sizes(const Dims& m) {
+  WsSizes w;
+  w.xq = m.max_rows * m.H;
+  w.sx = m.max_rows * m.nH * 4;
+  w.hq = m.P * m.Ip;
+  w.sh = m.P * m.nI * 4;
+  w.y = m.P * m.H * 4;
+  w.counts = m.E * 4;
+  w.offsets = (m.E + 1) * 4;
+  w.perm = m.P * 4;
+  w.inv = m.P * 4;
+  w.small_tiles = m.E * (int64_t)sizeof(Tile);
+  w.big_tiles = (m.P / kSmallRows + m.E + 1) * (int64_t)sizeof(Tile);
+  w.n_tiles = 2 * 4;
+  w.err = 4;
+  return w;
+}
+
+int64_t weight_bytes_of(const Dims& m) {
+  const int64_t codes = m.E * (2 * m.Ip * m.H + m.H * m.Ip);
+  const int64_t scales = m.E * (2 * m.nI * m.nH + m.nH * m.nI) * 4;
+  return align256(codes) + align256(scales);
+}
+
+struct StageEvents {
+  hipEvent_t ev[MOE_NUM_STAGES + 1];
+};
+
+}  // namespace
+
+struct moe_fp8_prefill {
+  moe_fp8_prefill_desc desc;
+  Dims m;
+  int device = 0;
+  int num_cus = 256;
+  // weights
+  uint8_t* w13 = nullptr;
+  float* s13 = nullptr;
+  uint8_t* w2 = nullptr;
+  float* s2 = nullptr;
+  // workspace
+  uint8_t* xq = nullptr;
+  float* sx = nullptr;
+  uint8_t* hq = nullptr;
+  float* sh = nullptr;
+  float* y = nullptr;
+  int32_t* counts = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* perm = nullptr;
+  int32_t* inv = nullptr;
+  Tile* small_tiles = nullptr;
+  Tile* big_tiles = nullptr;
+  int32_t* n_tiles = nullptr;
+  int32_t* err = nullptr;
+  std::vector<void*> allocations;
+  // state
+  std::atomic<int> busy{0};
+  bool failed = false;
+  bool inject_failure = false;
+  hipEvent_t done = nullptr;
+  hipStream_t last_stream = nullptr;
+  bool has_last = false;
+  int64_t last_T = 0;  // rows of the last pass
+  // timing
+  bool timing = false;
+  std::vector<StageEvents> pending;
+  std::vector<StageEvents> free_events;
+};
+
+namespace {
+
+int fail(moe_fp8_prefill* h, int code = MOE_ERR_DEVICE) {
+  if (h) h->failed = true;
+  return code;
+}
+
+hipError_t dalloc(moe_fp8_prefill* h, void** p, int64_t bytes) {
+  *p = nullptr;
+  hipError_t e = hipMalloc(p, (size_t)(bytes > 0 ? bytes : 1));
+  if (e == hipSuccess) h->allocations.push_back(*p);
+  return e;
+}
+
+void free_all(moe_fp8_prefill* h) {
+  for (void* p : h->allocations) (void)hipFree(p);
+  h->allocations.clear();
+  if (h->done) (void)hipEventDestroy(h->done);
+  for (auto& s : h->pending)
+    for (auto ev : s.ev) (void)hipEventDestroy(ev);
+  for (auto& s : h->free_events)
+    for (auto ev : s.ev) (void)hipEventDestroy(ev);
+  h->pending.clear();
+  h->free_events.clear();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Upload experts [e0, e0+n) from canonical buffers (host or device) and
+// re-lay them out into the handle's weight arrays.
+int upload_weights(moe_fp8_prefill* h, hipStream_t s) {
+  const moe_fp8_prefill_desc* d = &h->desc;
+  const Dims& m = h->m;
+  const int64_t wcode = m.I * m.H;              // one gate (or up, or down) matrix
+  const int64_t wscale = ((m.I + 127) / 128) * m.nH;  // scales per matrix
+  if (d->weights_on_device) {
+    LayoutArgs a{d->gate, d->up, d->down, d->gate_scale, d->up_scale, d->down_scale,
+                 0, (int32_t)m.E, (int32_t)m.H, (int32_t)m.I, (int32_t)m.Ip,
+                 h->w13, h->s13, h->w2, h->s2};
+    // process in groups of experts so the launch grids stay moderate
+    for (int64_t e0 = 0; e0 < m.E; e0 += 8) {
+      const int64_t n = (m.E - e0) < 8 ? (m.E - e0) : 8;
+      a.gate = d->gate + e0 * wcode;
+      a.up = d->up + e0 * wcode;
+      a.down = d->down + e0 * wcode;
+      a.gate_scale = d->gate_scale + e0 * wscale;
+      a.up_scale = d->up_scale + e0 * wscale;
+      a.down_scale = d->down_scale + e0 * wscale;
+      a.e0 = (int32_t)e0;
+      a.n = (int32_t)n;
+      if (launch_layout(a, s) != hipSuccess) return MOE_ERR_DEVICE;
+    }
+    return hipStreamSynchronize(s) == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+  }
+  // host source: stage a group of experts at a time through device memory
+  const int64_t group = 8;
+  const int64_t n_g = m.E < group ? m.E : group;
+  uint8_t* stage = nullptr;
+  float* sstage = nullptr;
+  const int64_t code_bytes = 3 * wcode * n_g;
+  const int64_t scale_bytes = 3 * wscale * n_g * 4;
+  if (hipMalloc((void**)&stage, (size_t)code_bytes) != hipSuccess) return MOE_ERR_OUT_OF_MEMORY;
+  if (hipMalloc((void**)&sstage, (size_t)scale_bytes) != hipSuccess) {
+    (void)hipFree(stage);
+    return MOE_ERR_OUT_OF_MEMORY;
+  }
+  int rc = MOE_OK;
+  for (int64_t e0 = 0; e0 < m.E && rc == MOE_OK; e0 += group) {
+    const int64_t n = (m.E - e0) < group ? (m.E - e0) : group;
+    uint8_t* g = stage;
+    uint8_t* u = stage + wcode * n;
+    uint8_t* dn = stage + 2 * wcode * n;
+    float* gs = sstage;
+    float* us = sstage + wscale * n;
+    float* ds = sstage + 2 * wscale * n;
+    bool ok = hipMemcpyAsync(g, d->gate + e0 * wcode, (size_t)(wcode * n), hipMemcpyHostToDevice, s) == hipSuccess &&
+              hipMemcpyAsync(u, d->up + e0 * wcode, (size_t)(wcode * n), hipMemcpyHostToDevice, s) == hipSuccess &&
+              hipMemcpyAsync(dn, d->down + e0 * wcode, (size_t)(wcode * n), hipMemcpyHostToDevice, s) == hipSuccess &&
+              hipMemcpyAsync(gs, d->gate_scale + e0 * wscale, (size_t)(wscale * n * 4), hipMemcpyHostToDevice, s) == hipSuccess &&
+              hipMemcpyAsync(us, d->up_scale + e0 * wscale, (size_t)(wscale * n * 4), hipMemcpyHostToDevice, s) == hipSuccess &&
+              hipMemcpyAsync(ds, d->down_scale + e0 * wscale, (size_t)(wscale * n * 4), hipMemcpyHostToDevice, s) == hipSuccess;
+    if (!ok) {
+      rc = MOE_ERR_DEVICE;
+      break;
+    }
+    LayoutArgs a{g, u, dn, gs, us, ds, (int32_t)e0, (int32_t)n, (int32_t)m.H, (int32_t)m.I, (int32_t)m.Ip,
+                 h->w13, h->s13, h->w2, h->s2};
+    if (launch_layout(a, s) != hipSuccess) rc = MOE_ERR_DEVICE;
+    // the staging buffer is reused by the next group
+    if (rc == MOE_OK && hipStreamSynchronize(s) != hipSuccess) rc = MOE_ERR_DEVICE;
+  }
+  (void)hipStreamSynchronize(s);
+  (void)hipFree(stage);
+  (void)hipFree(sstage);
+  return rc;
+}
+
+// Grid of a persistent GEMM launch: enough resident workgroups to fill the
+// chip, never more than the largest possible number of work items.
+int gemm_grid(const moe_fp8_prefill* h, int64_t max_items, bool big) {
+  const int64_t per_cu = big ? 2 : 16;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(max_items, h->num_cus * per_cu));
+}
+
+// The two gate_up launches (1-subtile tiles, then multi-subtile tiles) of a
+// pass over t rows / P slots whose plan and activations are in the workspace.
+hipError_t launch_gate_up_pair(moe_fp8_prefill* h, int64_t t, int64_t P, float* gu_dbg, hipStream_t s) {
+  const Dims& m = h->m;
+  const int64_t nb = m.Ip / kBlock;
+  GateUpArgs ga{h->xq, h->sx, t * m.H, t * m.nH * 4, h->perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip,
+                h->w13, h->s13, h->small_tiles, h->n_tiles, h->hq, h->sh, gu_dbg};
+  hipError_t e = launch_gate_up(ga, false, gemm_grid(h, m.E * nb, false), s);
+  if (e != hipSuccess) return e;
+  ga.tiles = h->big_tiles;
+  ga.n_tiles = h->n_tiles + 1;
+  return launch_gate_up(ga, true, gemm_grid(h, (P / kSmallRows + m.E) * nb, true), s);
+}
+
+int get_stage_events(moe_fp8_prefill* h, StageEvents* out) {
+  if (!h->free_events.empty()) {
+    *out = h->free_events.back();
+    h->free_events.pop_back();
+    return MOE_OK;
+  }
+  for (int i = 0; i <= MOE_NUM_STAGES; ++i)
+    if (hipEventCreate(&out->ev[i]) != hipSuccess) return MOE_ERR_DEVICE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_fp8_prefill_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_OUT_OF_MEMORY: return "device out of memory";
+    case MOE_ERR_DEVICE: return "device (HIP) error; handle failed";
+    case MOE_ERR_FAILED_STATE: return "handle failed earlier and refuses work";
+    case MOE_ERR_BUSY: return "handle is in use by another call";
+    case MOE_ERR_BAD_EXPERT_ID: return "expert id >= number of experts (slot skipped)";
+    default: return "unknown error code";
+  }
+}
+
+int moe_fp8_prefill_validate(const moe_fp8_prefill_desc* d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->struct_size != (int32_t)sizeof(moe_fp8_prefill_desc)) return MOE_ERR_INVALID_ARG;
+  if (!d->gate || !d->up || !d->down || !d->gate_scale || !d->up_scale || !d->down_scale)
+    return MOE_ERR_INVALID_ARG;
+  if (d->num_experts < 1 || d->top_k < 1 || d->hidden < 1 || d->inter < 1 || d->max_rows < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (d->block != kBlock) return MOE_ERR_UNSUPPORTED;
+  if (d->activation != MOE_ACT_SILU_UNCLAMPED) return MOE_ERR_UNSUPPORTED;
+  if (d->out_dtype != MOE_DTYPE_BF16 && d->out_dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
+  if (d->hidden % kBlock != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->hidden > kMaxKBlocks * kBlock || d->inter > kMaxKBlocks * kBlock) return MOE_ERR_UNSUPPORTED;
+  if (d->num_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (d->top_k > d->num_experts || d->top_k > 256) return MOE_ERR_UNSUPPORTED;
+  if (!std::isfinite(d->routed_scale)) return MOE_ERR_INVALID_ARG;
+  const Dims m = dims_of(d);
+  // 32-bit buffer offsets inside one pass: activations, h, and one expert's
+  // weight block row
+  if (m.P >= (int64_t(1) << 31) || m.max_rows * m.H >= (int64_t(1) << 31) ||
+      m.P * m.Ip >= (int64_t(1) << 31) || m.Ip * m.H >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t moe_fp8_prefill_workspace_bytes(const moe_fp8_prefill_desc* d) {
+  const int rc = moe_fp8_prefill_validate(d);
+  if (rc != MOE_OK) return -rc;
+  return ws_sizes(dims_of(d)).total();
+}
+
+int64_t moe_fp8_prefill_weight_bytes(const moe_fp8_prefill_desc* d) {
+  const int rc = moe_fp8_prefill_validate(d);
+  if (rc != MOE_OK) return -rc;
+  return weight_bytes_of(dims_of(d));
+}
+
+int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  const int rc = moe_fp8_prefill_validate(d);
+  if (rc != MOE_OK) return rc;
+  moe_fp8_prefill* h = new (std::nothrow) moe_fp8_prefill();
+  if (!h) return MOE_ERR_OUT_OF_MEMORY;
+  h->desc = *d;
+  h->m = dims_of(d);
+  const Dims& m = h->m;
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return MOE_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, h->device) == hipSuccess && prop.multiProcessorCount > 0)
+    h->num_cus = prop.multiProcessorCount;
+
+  const WsSizes w = ws_sizes(m);
+  void* p;
+  bool ok = true;
+  auto get = [&](int64_t bytes) -> void* {
+    if (!ok) return nullptr;
+    if (dalloc(h, &p, bytes) != hipSuccess) {
+      ok = false;
+      return nullptr;
+    }
+    return p;
+  };
+  h->w13 = (uint8_t*)get(m.E * 2 * m.Ip * m.H);
+  h->s13 = (float*)get(m.E * m.nI * m.nH * 2 * 4);
+  h->w2 = (uint8_t*)get(m.E * m.H * m.Ip);
+  h->s2 = (float*)get(m.E * m.nH * m.nI * 4);
+  h->xq = (uint8_t*)get(w.xq);
+  h->sx = (float*)get(w.sx);
+  h->hq = (uint8_t*)get(w.hq);
+  h->sh = (float*)get(w.sh);
+  h->y = (float*)get(w.y);
+  h->counts = (int32_t*)get(w.counts);
+  h->offsets = (int32_t*)get(w.offsets);
+  h->perm = (int32_t*)get(w.perm);
+  h->inv = (int32_t*)get(w.inv);
+  h->small_tiles = (Tile*)get(w.small_tiles);
+  h->big_tiles = (Tile*)get(w.big_tiles);
+  h->n_tiles = (int32_t*)get(w.n_tiles);
+  h->err = (int32_t*)get(w.err);
+  if (!ok) {
+    free_all(h);
+    delete h;
+    return MOE_ERR_OUT_OF_MEMORY;
+  }
+  hipStream_t s = (hipStream_t)d->stream;
+  if (hipEventCreateWithFlags(&h->done, hipEventDisableTiming) != hipSuccess ||
+      hipMemsetAsync(h->err, 0, 4, s) != hipSuccess) {
+    free_all(h);
+    delete h;
+    return MOE_ERR_DEVICE;
+  }
+  const int up = upload_weights(h, s);
+  if (up != MOE_OK || hipStreamSynchronize(s) != hipSuccess) {
+    free_all(h);
+    delete h;
+    return up != MOE_OK ? up : MOE_ERR_DEVICE;
+  }
+  // the caller's weight pointers are not kept
+  h->desc.gate = h->desc.up = h->desc.down = nullptr;
+  h->desc.gate_scale = h->desc.up_scale = h->desc.down_scale = nullptr;
+  *out = h;
+  return MOE_OK;
+}
+
+int moe_fp8_prefill_run(moe_fp8_prefill* h, const void* x, const int32_t* ids, const float* w,
+                        int64_t T, void* out, void* stream_) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  if (h->failed) return MOE_ERR_FAILED_STATE;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !ids || !w || !out || !aligned16(x) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  int expected = 0;
+  if (!h->busy.compare_exchange_strong(expected, 1)) return MOE_ERR_BUSY;
+  struct Release {
+    std::atomic<int>& b;
+    ~Release() { b.store(0); }
+  } release{h->busy};
+
+  hipStream_t s = (hipStream_t)stream_;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return fail(h);
+  if (cap != hipStreamCaptureStatusNone) return MOE_ERR_UNSUPPORTED;
+  if (h->inject_failure) {
+    h->inject_failure = false;
+    return fail(h);
+  }
+  if (h->has_last && h->last_stream != s && hipStreamWaitEvent(s, h->done, 0) != hipSuccess)
+    return fail(h);
+
+  const Dims& m = h->m;
+  const int64_t out_elem = h->desc.out_dtype == MOE_DTYPE_F32 ? 4 : 2;
+  // Upper bounds of the tile lists; the kernels read the real counts.
+  const int nb_dn = (int)(m.H / kBlock);
+
+  for (int64_t r0 = 0; r0 < T; r0 += m.max_rows) {
+    const int64_t t = (T - r0) < m.max_rows ? (T - r0) : m.max_rows;
+    const int64_t P = t * m.k;
+    StageEvents ev{};
+    if (h->timing) {
+      if (get_stage_events(h, &ev) != MOE_OK) return fail(h);
+      if (hipEventRecord(ev.ev[0], s) != hipSuccess) return fail(h);
+    }
+    PlanArgs pa{ids + r0 * m.k, (int32_t)t, (int32_t)m.k, (int32_t)m.E, h->counts, h->offsets,
+                h->perm, h->inv, h->small_tiles, h->big_tiles, h->n_tiles, h->err};
+    if (launch_plan(pa, s) != hipSuccess) return fail(h);
+    if (h->timing && hipEventRecord(ev.ev[1], s) != hipSuccess) return fail(h);
+
+    QuantArgs qa{(const uint16_t*)x + r0 * m.H, (int32_t)t, (int32_t)m.H, h->xq, h->sx};
+    if (launch_quant(qa, s) != hipSuccess) return fail(h);
+    if (h->timing && hipEventRecord(ev.ev[2], s) != hipSuccess) return fail(h);
+
+    int g_small, g_big;
+    if (launch_gate_up_pair(h, t, P, nullptr, s) != hipSuccess) return fail(h);
+    if (h->timing && hipEventRecord(ev.ev[3], s) != hipSuccess) return fail(h);
+
+    g_small = gemm_grid(h, m.E * nb_dn, false);
+    g_big = gemm_grid(h, (P / kSmallRows + m.E) * nb_dn, true);
+    DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2, h->small_tiles, h->n_tiles, h->y};
+    if (launch_down(da, false, g_small, s) != hipSuccess) return fail(h);
+    da.tiles = h->big_tiles;
+    da.n_tiles = h->n_tiles + 1;
+    if (launch_down(da, true, g_big, s) != hipSuccess) return fail(h);
+    if (h->timing && hipEventRecord(ev.ev[4], s) != hipSuccess) return fail(h);
+
+    CombineArgs ca{h->y, h->inv, w + r0 * m.k, (int32_t)t, (int32_t)m.k, (int32_t)m.H,
+                   h->desc.routed_scale, h->desc.out_dtype == MOE_DTYPE_F32 ? 1 : 0,
+                   (uint8_t*)out + r0 * m.H * out_elem};
+    if (launch_combine(ca, s) != hipSuccess) return fail(h);
+    if (h->timing) {
+      if (hipEventRecord(ev.ev[5], s) != hipSuccess) return fail(h);
+      h->pending.push_back(ev);
+    }
+    h->last_T = t;
+  }
+  if (hipEventRecord(h->done, s) != hipSuccess) return fail(h);
+  h->last_stream = s;
+  h->has_last = true;
+  return MOE_OK;
+}
+
+int moe_fp8_prefill_status(moe_fp8_prefill* h) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  if (h->failed) return MOE_ERR_FAILED_STATE;
+  if (h->has_last && hipEventSynchronize(h->done) != hipSuccess) return fail(h);
+  int32_t e = 0;
+  if (hipMemcpy(&e, h->err, 4, hipMemcpyDeviceToHost) != hipSuccess) return fail(h);
+  if (e) {
+    if (hipMemset(h->err, 0, 4) != hipSuccess) return fail(h);
+    return MOE_ERR_BAD_EXPERT_ID;
+  }
+  return MOE_OK;
+}
+
+void moe_fp8_prefill_destroy(moe_fp8_prefill* h) {
+  if (!h) return;
+  if (h->has_last) (void)hipEventSynchronize(h->done);
+  (void)hipDeviceSynchronize();
+  free_all(h);
+  delete h;
+}
+
+int moe_fp8_prefill_debug_plan(moe_fp8_prefill* h, int32_t* counts, int32_t* offsets, int32_t* perm,
+                               int32_t* inv, int64_t cap) {
+  if (!h || !counts || !offsets || !perm || !inv) return MOE_ERR_INVALID_ARG;
+  if (h->failed) return MOE_ERR_FAILED_STATE;
+  const int64_t P = h->last_T * h->m.k;
+  if (cap < P) return MOE_ERR_INVALID_ARG;
+  if (hipDeviceSynchronize() != hipSuccess) return fail(h);
+  const int64_t E = h->m.E;
+  if (hipMemcpy(counts, h->counts, E * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(offsets, h->offsets, (E + 1) * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(h);
+  const int64_t routed = offsets[E];
+  if (routed > P) return fail(h);
+  if ((routed > 0 && hipMemcpy(perm, h->perm, routed * 4, hipMemcpyDeviceToHost) != hipSuccess) ||
+      (P > 0 && hipMemcpy(inv, h->inv, P * 4, hipMemcpyDeviceToHost) != hipSuccess))
+    return fail(h);
+  return MOE_OK;
+}
+
+int moe_fp8_prefill_debug_activations(moe_fp8_prefill* h, uint8_t* xq, float* sx, int64_t rows) {
+  if (!h || !xq || !sx || rows < 0 || rows > h->last_T) return MOE_ERR_INVALID_ARG;
+  if (h->failed) return MOE_ERR_FAILED_STATE;
+  if (hipDeviceSynchronize() != hipSuccess) return fail(h);
+  if (rows == 0) return MOE_OK;
+  if (hipMemcpy(xq, h->xq, rows * h->m.H, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(sx, h->sx, rows * h->m.nH * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(h);
+  return MOE_OK;
+}
+
+int moe_fp8_prefill_debug_intermediates(moe_fp8_prefill* h, uint8_t* hq, float* sh, float* y,
+                                        int64_t cap_rows, int64_t* n_rows) {
+  if (!h || !n_rows) return MOE_ERR_INVALID_ARG;
+  if (h->failed) return MOE_ERR_FAILED_STATE;
+  if (hipDeviceSynchronize() != hipSuccess) return fail(h);
+  int32_t routed = 0;
+  if (hipMemcpy(&routed, h->offsets + h->m.E, 4, hipMemcpyDeviceToHost) != hipSuccess) return fail(h);
+  *n_rows = routed;
+  if (routed > cap_rows) return MOE_ERR_INVALID_ARG;
+  if (routed == 0) return MOE_OK;
+  const Dims& m = h->m;
+  if ((hq && hipMemcpy(hq, h->hq, routed * m.Ip, hipMemcpyDeviceToHost) != hipSuccess) ||
+      (sh && hipMemcpy(sh, h->sh, routed * m.nI * 4, hipMemcpyDeviceToHost) != hipSuccess) ||
+      (y && hipMemcpy(y, h->y, routed * m.H * 4, hipMemcpyDeviceToHost) != hipSuccess))
+    return fail(h);
+  return MOE_OK;
+}
+
+int moe_fp8_prefill_debug_gate_up(moe_fp8_prefill* h, float* gu, int64_t cap_rows, int64_t* n_rows) {
+  if (!h || !gu || !n_rows) return MOE_ERR_INVALID_ARG;
+  if (h->failed) return MOE_ERR_FAILED_STATE;
+  if (hipDeviceSynchronize() != hipSuccess) return fail(h);
+  int32_t routed = 0;
+  if (hipMemcpy(&routed, h->offsets + h->m.E, 4, hipMemcpyDeviceToHost) != hipSuccess) return fail(h);
+  *n_rows = routed;
+  if (routed > cap_rows) return MOE_ERR_INVALID_ARG;
+  if (routed == 0) return MOE_OK;
+  const int64_t bytes = (int64_t)routed * 2 * h->m.Ip * 4;
+  float* dbg = nullptr;
+  if (hipMalloc((void**)&dbg, (size_t)bytes) != hipSuccess) return MOE_ERR_OUT_OF_MEMORY;
+  // re-run the last pass's gate_up (deterministic: rewrites identical h)
+  int rc = MOE_OK;
+  if (launch_gate_up_pair(h, h->last_T, h->last_T * h->m.k, dbg, nullptr) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(gu, dbg, (size_t)bytes, hipMemcpyDeviceToHost) != hipSuccess)
+    rc = fail(h);
+  (void)hipFree(dbg);
+  return rc;
+}
+
+int moe_fp8_prefill_debug_unpack(moe_fp8_prefill* h, int32_t e, uint8_t* gate, uint8_t* up,
+                                 uint8_t* down, float* gate_scale, float* up_scale, float* down_scale) {
+  if (!h || !gate || !up || !down || !gate_scale || !up_scale || !down_scale) return MOE_ERR_INVALID_ARG;
+  const Dims& m = h->m;
+  if (e < 0 || e >= m.E) return MOE_ERR_INVALID_ARG;
+  if (h->failed) return MOE_ERR_FAILED_STATE;
+  if (hipDeviceSynchronize() != hipSuccess) return fail(h);
+  const int64_t n13 = 2 * m.Ip * m.H, n2 = m.H * m.Ip;
+  std::vector<uint8_t> b13((size_t)n13), b2((size_t)n2);
+  std::vector<float> s13((size_t)(m.nI * m.nH * 2)), s2((size_t)(m.nH * m.nI));
+  if (hipMemcpy(b13.data(), h->w13 + e * n13, n13, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(b2.data(), h->w2 + e * n2, n2, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(s13.data(), h->s13 + e * m.nI * m.nH * 2, s13.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(s2.data(), h->s2 + e * m.nH * m.nI, s2.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(h);
+  // inverse of the layout kernels' index map
+  const int64_t nH = m.nH, nI = m.nI, NB13 = m.nI, NB2 = m.nH;
+  for (int64_t nb = 0; nb < NB13; ++nb)
+    for (int64_t kb = 0; kb < nH; ++kb)
+      for (int w = 0; w < 4; ++w)
+        for (int t = 0; t < 4; ++t)
+          for (int half = 0; half < 2; ++half)
+            for (int lane = 0; lane < 64; ++lane) {
+              const int64_t row = nb * 128 + w * 32 + (t & 1) * 16 + (lane & 15);
+              if (row >= m.I) continue;
+              const int64_t k0 = kb * 128 + (lane >> 4) * 32 + half * 16;
+              const int64_t src = ((((nb * nH + kb) * 4 + w) * 4 + t) * 2 + half) * 1024 + lane * 16;
+              uint8_t* dst = (t < 2 ? gate : up) + row * m.H + k0;
+              std::memcpy(dst, &b13[(size_t)src], 16);
+            }
+  for (int64_t nb = 0; nb < NB2; ++nb)
+    for (int64_t kb = 0; kb < nI; ++kb)
+      for (int w = 0; w < 4; ++w)
+        for (int t = 0; t < 2; ++t)
+          for (int half = 0; half < 2; ++half)
+            for (int lane = 0; lane < 64; ++lane) {
+              const int64_t row = nb * 128 + w * 32 + t * 16 + (lane & 15);
+              const int64_t k0 = kb * 128 + (lane >> 4) * 32 + half * 16;
+              const int64_t src = ((((nb * nI + kb) * 4 + w) * 2 + t) * 2 + half) * 1024 + lane * 16;
+              for (int i = 0; i < 16; ++i)
+                if (k0 + i < m.I) down[row * m.I + k0 + i] = b2[(size_t)src + i];
+            }
+  const int64_t nIr = (m.I + 127) / 128;  // == nI
+  for (int64_t i = 0; i < nIr * nH; ++i) {
+    gate_scale[i] = s13[(size_t)i * 2];
+    up_scale[i] = s13[(size_t)i * 2 + 1];
+  }
+  for (int64_t i = 0; i < nH * nI; ++i) down_scale[i] = s2[(size_t)i];
+  return MOE_OK;
+}
+
+int moe_fp8_prefill_debug_mfma(const uint8_t* a, const uint8_t* b, float* d) {
+  if (!a || !b || !d) return MOE_ERR_INVALID_ARG;
+  uint8_t *da = nullptr, *db = nullptr;
+  float* dd = nullptr;
+  int rc = MOE_OK;
+  if (hipMalloc((void**)&da, 2048) != hipSuccess || hipMalloc((void**)&db, 2048) != hipSuccess ||
+      hipMalloc((void**)&dd, 3072) != hipSuccess) {
+    rc = MOE_ERR_OUT_OF_MEMORY;
+  } else if (hipMemcpy(da, a, 2048, hipMemcpyHostToDevice) != hipSuccess ||
+             hipMemcpy(db, b, 2048, hipMemcpyHostToDevice) != hipSuccess ||
+             launch_mfma_probe(da, db, dd, nullptr) != hipSuccess ||
+             hipMemcpy(d, dd, 3072, hipMemcpyDeviceToHost) != hipSuccess) {
+    rc = MOE_ERR_DEVICE;
+  }
+  if (da) (void)hipFree(da);
+  if (db) (void)hipFree(db);
+  if (dd) (void)hipFree(dd);
+  return rc;
+}
+
+int moe_fp8_prefill_set_timing(moe_fp8_prefill* h, int32_t enable) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  h->timing = enable != 0;
+  return MOE_OK;
+}
+
+int moe_fp8_prefill_read_timing(moe_fp8_prefill* h, float* stage_ms, int32_t max_records,
+                                int32_t* n_records) {
+  if (!h || !n_records || (max_records > 0 && !stage_ms)) return MOE_ERR_INVALID_ARG;
+  if (h->failed) return MOE_ERR_FAILED_STATE;
+  int32_t n = 0;
+  for (auto& s : h->pending) {
+    if (hipEventSynchronize(s.ev[MOE_NUM_STAGES]) != hipSuccess) return fail(h);
+    if (n < max_records) {
+      for (int i = 0; i < MOE_NUM_STAGES; ++i) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, s.ev[i], s.ev[i + 1]) != hipSuccess) return fail(h);
+        stage_ms[n * MOE_NUM_STAGES + i] = ms;
+      }
+      ++n;
+    }
+    h->free_events.push_back(s);
+  }
+  h->pending.clear();
+  *n_records = n;
+  return MOE_OK;
+}
+
+int moe_fp8_prefill_debug_inject_failure(moe_fp8_prefill* h) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  h->inject_failure = true;
+  return MOE_OK;
+}
+
+}  // extern "C"

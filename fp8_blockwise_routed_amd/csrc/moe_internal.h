@@ -1,0 +1,108 @@
+// Internal interface between the C-ABI host code (moe_api.cpp) and the HIP
+// kernels (moe_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kBlock = 128;          // weight block edge and activation group
+constexpr int kWaves = 4;            // waves per GEMM workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSmallRows = 16;       // experts with <= this many rows use the 1-subtile GEMM
+constexpr int kBigRows = 64;         // rows per tile of the multi-subtile GEMM
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxKBlocks = 128;     // H/128 and Ip/128 limit (LDS-staged weight scales)
+
+// Bytes of swizzled weights per (expert, 128-row output block, 128-wide K block).
+constexpr int kGateUpChunk = kWaves * 4 * 2048;  // gate 128 rows + up 128 rows
+constexpr int kDownChunk = kWaves * 2 * 2048;    // 128 rows of down
+
+// A GEMM work tile: rows [p0, p0+rows) of the sorted slot order, all of expert e.
+struct Tile {
+  int32_t e, p0, rows, pad;
+};
+
+struct PlanArgs {
+  const int32_t* ids;  // [T*k]
+  int32_t T, k, E;
+  int32_t* counts;     // [E]
+  int32_t* offsets;    // [E+1]
+  int32_t* perm;       // [T*k]
+  int32_t* inv;        // [T*k]
+  Tile* small_tiles;   // [E]
+  Tile* big_tiles;     // [T*k/16 + E]
+  int32_t* n_tiles;    // [2]: small, big
+  int32_t* err;        // sticky bad-id flag
+};
+
+struct QuantArgs {
+  const uint16_t* x;   // bf16 [T][H]
+  int32_t T, H;
+  uint8_t* xq;         // [T][H]
+  float* sx;           // [T][H/128]
+};
+
+struct GateUpArgs {
+  const uint8_t* xq;   // [T][H]
+  const float* sx;     // [T][H/128]
+  int64_t xq_bytes, sx_bytes;  // extents of xq and sx (buffer bounds)
+  const int32_t* perm;
+  int32_t k, H, Ip;
+  const uint8_t* w13;  // swizzled
+  const float* s13;    // [E][Ip/128][H/128][2]
+  const Tile* tiles;
+  const int32_t* n_tiles;
+  uint8_t* hq;         // [P][Ip]
+  float* sh;           // [P][Ip/128]
+  float* gu_dbg;       // optional [P][2*Ip] FP32 gate|up before the epilogue
+};
+
+struct DownArgs {
+  const uint8_t* hq;   // [P][Ip]
+  const float* sh;     // [P][Ip/128]
+  int64_t hq_bytes, sh_bytes;  // extents of hq and sh (buffer bounds)
+  int32_t H, Ip;
+  const uint8_t* w2;   // swizzled
+  const float* s2;     // [E][H/128][Ip/128]
+  const Tile* tiles;
+  const int32_t* n_tiles;
+  float* y;            // [P][H]
+};
+
+struct CombineArgs {
+  const float* y;      // [P][H]
+  const int32_t* inv;  // [T*k]
+  const float* w;      // [T][k]
+  int32_t T, k, H;
+  float rho;
+  int32_t out_f32;
+  void* out;
+};
+
+struct LayoutArgs {
+  // canonical codes of experts [e0, e0 + n) on the device
+  const uint8_t* gate;  // [n][I][H]
+  const uint8_t* up;    // [n][I][H]
+  const uint8_t* down;  // [n][H][I]
+  const float* gate_scale;  // [n][nI][nH]
+  const float* up_scale;
+  const float* down_scale;  // [n][nH][nI]
+  int32_t e0, n, H, I, Ip;
+  uint8_t* w13;
+  float* s13;
+  uint8_t* w2;
+  float* s2;
+};
+
+// Launchers (return the launch status).
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_quant(const QuantArgs& a, hipStream_t s);
+hipError_t launch_gate_up(const GateUpArgs& a, bool big, int grid, hipStream_t s);
+hipError_t launch_down(const DownArgs& a, bool big, int grid, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
+hipError_t launch_mfma_probe(const uint8_t* a, const uint8_t* b, float* d, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,778 @@
+// HIP kernels of the routed-expert FP8 MoE prefill pass, written for gfx950
+// (CDNA4: wave64, FP8 MFMA 16x16x128, 160 KiB LDS per CU).
+//
+// Launch order per pass (after "TensorFold #2852", description: plan, grouped
+// gate+up, gate-up epilogue, grouped down, combine):
+//   plan      one workgroup: stable counting sort of the (token, slot) pairs by
+//             expert, inverse map, and two tile lists (small / big experts)
+//   quant     BF16 rows -> E4M3 codes + FP32 scale per 128-column group
+//   gate_up   grouped FP8 GEMM against [gate; up] of each expert, FP32
+//             accumulation with per-K-block scale promotion, fused epilogue
+//             h = silu(g) * u and per-128-group E4M3 quantisation of h
+//   down      grouped FP8 GEMM of h against down, FP32 rows y (sorted order)
+//   combine   out[t] = rho * sum_j w[t,j] * y[t,j], ascending j, one rounding
+//
+// Exactness: every GEMM variant issues the same MFMA per 16x16 output tile
+// and K block, applies the block scales in the same order and never splits K,
+// so an output row depends only on its own input row ("TensorFold #2852",
+// exactness paragraph).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- helpers --
+
+__device__ __forceinline__ i32x4 ld16(const void* p) {
+  return *reinterpret_cast<const i32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, i32x4 v) { *reinterpret_cast<i32x4*>(p) = v; }
+
+__device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// D = A(16x128 E4M3) * B(128x16 E4M3), FP32, zero accumulator in.  Lane l
+// holds row/column l%16 and 32 K bytes for lane group l/16 in both operands;
+// D lane l, element i is row 4*(l/16)+i, column l%16.
+__device__ __forceinline__ f32x4 mfma_e4m3(i32x8 a, i32x8 b) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+// |v| as an ordered integer: NaN > Inf > finite, so an unsigned max over these
+// is a NaN-propagating max|v|.
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Max over the 16 lanes that share l/16.
+__device__ __forceinline__ uint32_t max16(uint32_t v) {
+  v = umax(v, (uint32_t)__shfl_xor((int)v, 1));
+  v = umax(v, (uint32_t)__shfl_xor((int)v, 2));
+  v = umax(v, (uint32_t)__shfl_xor((int)v, 4));
+  v = umax(v, (uint32_t)__shfl_xor((int)v, 8));
+  return v;
+}
+
+// FP32 -> OCP E4M3 byte: round to nearest, ties to even; saturate at 448;
+// zero results keep the sign; NaN gives +0.
+__device__ __forceinline__ uint32_t to_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0u;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;            // >= 448
+  if (a < 0x3C800000u) {                                 // < 2^-6: multiples of 2^-9
+    const float q = __uint_as_float(a) * 512.0f;
+    return sign | (uint32_t)__builtin_rintf(q);
+  }
+  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);  // keep 3 mantissa bits, RNE
+  return sign | ((r >> 20) - (120u << 3));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
+  return ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16) & 0xFFFFu;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return __fdiv_rn(g, 1.0f + expf(-g)) * u;
+}
+
+// -------------------------------------------------------------------- plan --
+// One workgroup of 1024 threads.  Counting sort that keeps slot order within
+// an expert: histogram with LDS atomics, exclusive scan, then chunks of 1024
+// slots ranked inside each wave by a ballot match on the expert id and across
+// waves by per-wave counts.
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  // scratch: kPlanWaves ints
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int base = 0, all = 0;
+  for (int w = 0; w < kPlanWaves; ++w) {
+    int s = scratch[w];
+    if (w < wave) base += s;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int cursor[kMaxExperts];
+  __shared__ int wcnt[kPlanWaves][kMaxExperts];
+  __shared__ int scan_scratch[kPlanWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, P = a.T * a.k;
+
+  for (int e = tid; e < kMaxExperts; e += kPlanThreads) cnt[e] = 0;
+  for (int i = tid; i < kPlanWaves * kMaxExperts; i += kPlanThreads) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  int bad = 0;
+  for (int f = tid; f < P; f += kPlanThreads) {
+    const int e = a.ids[f];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    else if (e >= E) bad = 1;
+  }
+  if (bad) *a.err = 1;
+  __syncthreads();
+
+  // offsets and tile lists; thread e owns expert e (E <= 1024)
+  const int n = tid < E ? cnt[tid] : 0;
+  int total;
+  const int off = block_exclusive_scan(n, scan_scratch, &total);
+  const int is_small = (n >= 1 && n <= kSmallRows) ? 1 : 0;
+  const int n_big = n > kSmallRows ? (n + kBigRows - 1) / kBigRows : 0;
+  int n_small_all, n_big_all;
+  const int small_at = block_exclusive_scan(is_small, scan_scratch, &n_small_all);
+  const int big_at = block_exclusive_scan(n_big, scan_scratch, &n_big_all);
+  if (tid < E) {
+    a.counts[tid] = n;
+    a.offsets[tid] = off;
+    cursor[tid] = off;
+    if (is_small) a.small_tiles[small_at] = Tile{tid, off, n, 0};
+    if (n_big) {
+      // split n rows into n_big tiles of near-equal size, multiples of 16 rows
+      const int per = ((n + n_big - 1) / n_big + 15) & ~15;
+      for (int i = 0; i < n_big; ++i) {
+        const int r0 = i * per;
+        const int r = (n - r0) < per ? (n - r0) : per;
+        a.big_tiles[big_at + i] = Tile{tid, off + r0, r, 0};
+      }
+    }
+  }
+  if (tid == 0) {
+    a.offsets[E] = total;
+    a.n_tiles[0] = n_small_all;
+    a.n_tiles[1] = n_big_all;
+  }
+  __syncthreads();
+
+  // stable scatter
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < P; c0 += kPlanThreads) {
+    const int f = c0 + tid;
+    const int e = f < P ? a.ids[f] : -1;
+    const bool valid = e >= 0 && e < E;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t bm = __ballot(bit);
+      same &= bit ? bm : ~bm;
+    }
+    const int rank = __popcll(same & lt_mask);
+    const int group = __popcll(same);
+    if (valid && rank == 0) wcnt[wave][e] = group;
+    __syncthreads();
+    if (valid) {
+      int before = 0;
+      for (int w = 0; w < wave; ++w) before += wcnt[w][e];
+      const int pos = cursor[e] + before + rank;
+      a.perm[pos] = f;
+      a.inv[f] = pos;
+    } else if (f < P) {
+      a.inv[f] = -1;
+    }
+    __syncthreads();
+    if (valid && rank == 0) {
+      atomicAdd(&cursor[e], group);
+      wcnt[wave][e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------- quant --
+// 16 lanes per 128-column group, 8 BF16 values (16 bytes) per lane.
+
+__global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
+  const int nH = a.H / kBlock;
+  const int64_t groups = (int64_t)a.T * nH;
+  const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  if (g >= groups) return;  // whole 16-lane groups leave together
+  const int64_t t = g / nH;
+  const int kg = (int)(g - t * nH);
+  const uint16_t* src = a.x + t * a.H + kg * kBlock + sub * 8;
+  const i32x4 raw = ld16(src);
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32((uint32_t)raw[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32((uint32_t)raw[i] >> 16);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = umax(m, abs_bits(v[i]));
+  m = max16(m);
+  const float amax = __uint_as_float(m);
+  const float s = __fdiv_rn(amax, 448.0f);
+  uint32_t lo = 0, hi = 0;
+  if (amax != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= to_e4m3(__fdiv_rn(v[i], s)) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= to_e4m3(__fdiv_rn(v[4 + i], s)) << (8 * i);
+  }
+  uint32_t* dst = reinterpret_cast<uint32_t*>(a.xq + t * a.H + kg * kBlock + sub * 8);
+  dst[0] = lo;
+  dst[1] = hi;
+  if (sub == 0) a.sx[g] = s;
+}
+
+hipError_t launch_quant(const QuantArgs& a, hipStream_t s) {
+  const int64_t groups = (int64_t)a.T * (a.H / kBlock);
+  const int64_t blocks = (groups + 15) / 16;
+  hipLaunchKernelGGL(quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- GEMM common --
+// Buffer resources (SGPR base + VGPR offset + SGPR/immediate offset) keep the
+// per-lane address state of the streaming loads at one VGPR each.
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ i32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ float bloadf(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+// Activation tile in LDS: BM rows x 128 bytes per K block, 16-byte chunks
+// XOR-swizzled by row so the MFMA fragment reads (16 rows, same chunk) hit
+// distinct banks.
+__device__ __forceinline__ int a_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ i32x8 a_frag(const uint8_t* lds, int m, int lane) {
+  const int row = m * 16 + (lane & 15);
+  const int g = lane >> 4;
+  return cat(ld16(lds + a_off(row, 2 * g)), ld16(lds + a_off(row, 2 * g + 1)));
+}
+
+// ----------------------------------------------------------------- gate_up --
+// Workgroup tile: up to 16*MT rows of one expert x (128 gate + 128 up)
+// columns of one 128-row block nb, so the epilogue sees one whole 128-wide
+// group of h.  Wave w owns gate columns 32w..32w+31 and the same up columns
+// (tiles 0,1 = gate, 2,3 = up).  Weights stream straight from HBM into MFMA
+// operand registers (pre-swizzled at create time: 2 KB per 16x128 tile, lane
+// l's 32 bytes split into two 1 KB halves); activation rows are gathered
+// through the plan's permutation into LDS.
+
+template <int MT>
+__global__ __launch_bounds__(kThreads, (MT == 1 ? 4 : 2)) void gate_up_kernel(GateUpArgs a) {
+  constexpr int BM = 16 * MT;
+  constexpr int APASS = (BM + 31) / 32;  // 16-byte activation loads per thread
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][BM * 128];
+  __shared__ float sx_lds[2][BM];
+  __shared__ int tok_lds[BM];
+  __shared__ uint32_t red_lds[kWaves][BM];
+  __shared__ __attribute__((aligned(16))) uint8_t h_lds[BM * 128];
+  __shared__ float sh_lds[BM];
+  __shared__ float ws_lds[2 * kMaxKBlocks];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int H = a.H, Ip = a.Ip, nH = H / kBlock, NB = Ip / kBlock;
+  const int n_items = a.n_tiles[0] * NB;
+  const int arow = tid >> 3, achunk = tid & 7;
+  const rsrc_t xr = make_rsrc(a.xq, (uint32_t)a.xq_bytes);
+  const rsrc_t sr = make_rsrc(a.sx, (uint32_t)a.sx_bytes);
+  const uint32_t bvoff = (uint32_t)(wave * 8192 + lane * 16);
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int tile = item / NB, nb = item - tile * NB;
+    const Tile td = a.tiles[tile];
+    const int e = td.e, p0 = td.p0, rows = td.rows;
+    const int mt = (rows + 15) >> 4;
+    const int mrows = mt * 16;
+
+    __syncthreads();  // LDS of the previous item is no longer read
+    if (tid < BM) tok_lds[tid] = a.perm[p0 + (tid < rows ? tid : 0)] / a.k;
+    {
+      const float* ws = a.s13 + (size_t)(e * NB + nb) * nH * 2;
+      for (int i = tid; i < 2 * nH; i += kThreads) ws_lds[i] = ws[i];
+    }
+    __syncthreads();
+
+    const rsrc_t wr = make_rsrc(a.w13 + (size_t)(e * NB + nb) * nH * kGateUpChunk, (uint32_t)(nH * kGateUpChunk));
+    uint32_t avoff[APASS];
+#pragma unroll
+    for (int p = 0; p < APASS; ++p) {
+      const int r = arow + 32 * p;
+      avoff[p] = r < mrows ? (uint32_t)(tok_lds[r] * H + achunk * 16) : 0u;
+    }
+    const uint32_t svoff = tid < mrows ? (uint32_t)(tok_lds[tid] * nH * 4) : 0u;
+
+    i32x4 areg[APASS];
+    float sreg = 0.f;
+    i32x8 b0[4], b1[4];
+    f32x4 acc[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto load_a = [&](int kb) {
+#pragma unroll
+      for (int p = 0; p < APASS; ++p)
+        if (arow + 32 * p < mrows) areg[p] = bload16(xr, avoff[p], (uint32_t)(kb * kBlock));
+      if (tid < mrows) sreg = bloadf(sr, svoff, (uint32_t)(kb * 4));
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+      for (int p = 0; p < APASS; ++p) {
+        const int r = arow + 32 * p;
+        if (r < mrows) st16(&a_lds[buf][a_off(r, achunk)], areg[p]);
+      }
+      if (tid < mrows) sx_lds[buf][tid] = sreg;
+    };
+    // kb == nH is the prefetch past the last block: a lane offset of 2^31 is
+    // beyond the buffer range whichever offsets the range check includes, so
+    // the loads return zeros without touching memory.
+    auto load_b = [&](int kb, i32x8* b) {
+      const bool in = kb < nH;
+      const uint32_t vo = bvoff + (in ? 0u : 0x80000000u);
+      const uint32_t so = in ? (uint32_t)(kb * kGateUpChunk) : 0u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        b[t] = cat(bload16(wr, vo, so + t * 2048), bload16(wr, vo, so + t * 2048 + 1024));
+    };
+    // one K block: prefetch block kb+1 (activations to registers, weights to
+    // `nxt`), multiply block kb from LDS and `cur`, then publish kb+1.  The
+    // prefetch is unconditional so the wait counts stay static: past the last
+    // block the weight read is out of range (zeros, no memory access) and the
+    // activation read repeats the last block.
+    auto step = [&](int kb, i32x8(&cur)[4], i32x8(&nxt)[4]) {
+      const int buf = kb & 1;
+      load_a(kb + 1 < nH ? kb + 1 : kb);
+      load_b(kb + 1, nxt);
+      const float wsg = ws_lds[2 * kb], wsu = ws_lds[2 * kb + 1];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < mt) {
+          const i32x8 af = a_frag(a_lds[buf], m, lane);
+          f32x4 p[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) p[t] = mfma_e4m3(af, cur[t]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float rs = sx_lds[buf][m * 16 + grp * 4 + i];
+            const float sg = rs * wsg, su = rs * wsu;
+            acc[m][0][i] = __builtin_fmaf(p[0][i], sg, acc[m][0][i]);
+            acc[m][1][i] = __builtin_fmaf(p[1][i], sg, acc[m][1][i]);
+            acc[m][2][i] = __builtin_fmaf(p[2][i], su, acc[m][2][i]);
+            acc[m][3][i] = __builtin_fmaf(p[3][i], su, acc[m][3][i]);
+          }
+        }
+      }
+      store_a(buf ^ 1);
+      __syncthreads();
+    };
+
+    load_a(0);
+    load_b(0, b0);
+    store_a(0);
+    __syncthreads();
+    for (int kb = 0; kb < nH; kb += 2) {
+      step(kb, b0, b1);
+      if (kb + 1 < nH) step(kb + 1, b1, b0);
+    }
+
+    // inspection hook: FP32 gate and up before the epilogue (null in normal use)
+    if (a.gu_dbg) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < mt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = m * 16 + grp * 4 + i;
+            if (r < rows) {
+              float* g = a.gu_dbg + (size_t)(p0 + r) * 2 * Ip + nb * kBlock + wave * 32 + col;
+              g[0] = acc[m][0][i];
+              g[16] = acc[m][1][i];
+              g[Ip] = acc[m][2][i];
+              g[Ip + 16] = acc[m][3][i];
+            }
+          }
+        }
+      }
+    }
+
+    // epilogue: h = silu(gate) * up; amax per row over the 128 columns
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[m][0][i] = silu_mul(acc[m][0][i], acc[m][2][i]);
+          acc[m][1][i] = silu_mul(acc[m][1][i], acc[m][3][i]);
+          const uint32_t mb = max16(umax(abs_bits(acc[m][0][i]), abs_bits(acc[m][1][i])));
+          if (col == 0) red_lds[wave][m * 16 + grp * 4 + i] = mb;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = m * 16 + grp * 4 + i;
+          const uint32_t mb = umax(umax(red_lds[0][r], red_lds[1][r]), umax(red_lds[2][r], red_lds[3][r]));
+          const float amax = __uint_as_float(mb);
+          const float s = __fdiv_rn(amax, 448.0f);
+          uint32_t c0 = 0, c1 = 0;
+          if (amax != 0.0f) {
+            c0 = to_e4m3(__fdiv_rn(acc[m][0][i], s));
+            c1 = to_e4m3(__fdiv_rn(acc[m][1][i], s));
+          }
+          h_lds[r * 128 + wave * 32 + col] = (uint8_t)c0;
+          h_lds[r * 128 + wave * 32 + 16 + col] = (uint8_t)c1;
+          if (wave == 0 && col == 0) sh_lds[r] = s;
+        }
+      }
+    }
+    __syncthreads();
+    for (int r = arow; r < rows; r += 32)
+      st16(a.hq + (size_t)(p0 + r) * Ip + nb * kBlock + achunk * 16, ld16(&h_lds[r * 128 + achunk * 16]));
+    if (tid < rows) a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
+  }
+}
+
+hipError_t launch_gate_up(const GateUpArgs& a, bool big, int grid, hipStream_t s) {
+  if (big)
+    hipLaunchKernelGGL(gate_up_kernel<kBigRows / 16>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(gate_up_kernel<1>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------------- down --
+// Workgroup tile: up to 16*MT rows of one expert x 128 hidden columns (one
+// weight block row); wave w owns columns 32w..32w+31 (two 16-column tiles).
+
+template <int MT>
+__global__ __launch_bounds__(kThreads, (MT == 1 ? 4 : 2)) void down_kernel(DownArgs a) {
+  constexpr int BM = 16 * MT;
+  constexpr int APASS = (BM + 31) / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][BM * 128];
+  __shared__ float s_lds[2][BM];
+  __shared__ float ws_lds[kMaxKBlocks];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int H = a.H, Ip = a.Ip, nI = Ip / kBlock, NB = H / kBlock;
+  const int n_items = a.n_tiles[0] * NB;
+  const int arow = tid >> 3, achunk = tid & 7;
+  const rsrc_t hr = make_rsrc(a.hq, (uint32_t)a.hq_bytes);
+  const rsrc_t sr = make_rsrc(a.sh, (uint32_t)a.sh_bytes);
+  const uint32_t bvoff = (uint32_t)(wave * 4096 + lane * 16);
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int tile = item / NB, nb = item - tile * NB;
+    const Tile td = a.tiles[tile];
+    const int e = td.e, p0 = td.p0, rows = td.rows;
+    const int mt = (rows + 15) >> 4;
+    const int mrows = mt * 16;
+
+    const rsrc_t wr = make_rsrc(a.w2 + (size_t)(e * NB + nb) * nI * kDownChunk, (uint32_t)(nI * kDownChunk));
+    uint32_t avoff[APASS];
+#pragma unroll
+    for (int p = 0; p < APASS; ++p) {
+      const int r = arow + 32 * p;
+      avoff[p] = (uint32_t)((p0 + (r < rows ? r : 0)) * Ip + achunk * 16);
+    }
+    const uint32_t svoff = (uint32_t)((p0 + (tid < rows ? tid : 0)) * nI * 4);
+
+    i32x4 areg[APASS];
+    float sreg = 0.f;
+    i32x8 b0[2], b1[2];
+    f32x4 acc[MT][2];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto load_a = [&](int kb) {
+#pragma unroll
+      for (int p = 0; p < APASS; ++p)
+        if (arow + 32 * p < mrows) areg[p] = bload16(hr, avoff[p], (uint32_t)(kb * kBlock));
+      if (tid < mrows) sreg = bloadf(sr, svoff, (uint32_t)(kb * 4));
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+      for (int p = 0; p < APASS; ++p) {
+        const int r = arow + 32 * p;
+        if (r < mrows) st16(&a_lds[buf][a_off(r, achunk)], areg[p]);
+      }
+      if (tid < mrows) s_lds[buf][tid] = sreg;
+    };
+    auto load_b = [&](int kb, i32x8* b) {  // kb == nI: out of range, zeros
+      const bool in = kb < nI;
+      const uint32_t vo = bvoff + (in ? 0u : 0x80000000u);
+      const uint32_t so = in ? (uint32_t)(kb * kDownChunk) : 0u;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        b[t] = cat(bload16(wr, vo, so + t * 2048), bload16(wr, vo, so + t * 2048 + 1024));
+    };
+    auto step = [&](int kb, i32x8(&cur)[2], i32x8(&nxt)[2]) {
+      const int buf = kb & 1;
+      load_a(kb + 1 < nI ? kb + 1 : kb);
+      load_b(kb + 1, nxt);
+      const float wsc = ws_lds[kb];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < mt) {
+          const i32x8 af = a_frag(a_lds[buf], m, lane);
+          const f32x4 q0 = mfma_e4m3(af, cur[0]);
+          const f32x4 q1 = mfma_e4m3(af, cur[1]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float sc = s_lds[buf][m * 16 + grp * 4 + i] * wsc;
+            acc[m][0][i] = __builtin_fmaf(q0[i], sc, acc[m][0][i]);
+            acc[m][1][i] = __builtin_fmaf(q1[i], sc, acc[m][1][i]);
+          }
+        }
+      }
+      store_a(buf ^ 1);
+      __syncthreads();
+    };
+
+    __syncthreads();  // LDS of the previous item is no longer read
+    {
+      const float* ws = a.s2 + (size_t)(e * NB + nb) * nI;
+      for (int i = tid; i < nI; i += kThreads) ws_lds[i] = ws[i];
+    }
+    load_a(0);
+    load_b(0, b0);
+    store_a(0);
+    __syncthreads();
+    for (int kb = 0; kb < nI; kb += 2) {
+      step(kb, b0, b1);
+      if (kb + 1 < nI) step(kb + 1, b1, b0);
+    }
+
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = m * 16 + grp * 4 + i;
+          if (r < rows) {
+            float* dst = a.y + (size_t)(p0 + r) * H + nb * kBlock + wave * 32 + col;
+            dst[0] = acc[m][0][i];
+            dst[16] = acc[m][1][i];
+          }
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_down(const DownArgs& a, bool big, int grid, hipStream_t s) {
+  if (big)
+    hipLaunchKernelGGL(down_kernel<kBigRows / 16>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(down_kernel<1>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- combine --
+// One workgroup per token; 4 consecutive columns per thread.
+
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int t = blockIdx.x;
+  const int k = a.k, H = a.H;
+  __shared__ int pos[256];
+  __shared__ float wt[256];
+  for (int j = threadIdx.x; j < k; j += 256) {
+    pos[j] = a.inv[(size_t)t * k + j];
+    wt[j] = a.w[(size_t)t * k + j];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int p = pos[j];
+      if (p >= 0) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(a.y + (size_t)p * H + c);
+        const float wj = wt[j];
+        acc[0] = acc[0] + wj * v[0];
+        acc[1] = acc[1] + wj * v[1];
+        acc[2] = acc[2] + wj * v[2];
+        acc[3] = acc[3] + wj * v[3];
+      }
+    }
+    const f32x4 o = {a.rho * acc[0], a.rho * acc[1], a.rho * acc[2], a.rho * acc[3]};
+    if (a.out_f32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + (size_t)t * H + c) = o;
+    } else {
+      const uint32_t lo = f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16);
+      const uint32_t hi = f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + (size_t)t * H + c);
+      dst[0] = lo;
+      dst[1] = hi;
+    }
+  }
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ layout --
+// Canonical codes -> MFMA-operand order, one 16-byte output chunk per thread.
+//   w13: [e][nb][kb][wave 4][tile 4: g0 g1 u0 u1][half 2][lane 64][16 B]
+//   w2 : [e][nb][kb][wave 4][tile 2][half 2][lane 64][16 B]
+// Lane l of tile t covers output row 16*(t&1) + l%16 of the wave's 32 rows
+// and K bytes 32*(l/16) + 16*half + [0, 16) of the 128-wide block.  Rows or
+// columns at or beyond I are zero; NaN codes 0x7F / 0xFF become 0x00 / 0x80.
+
+__device__ __forceinline__ uint8_t clean(uint8_t b) { return (b & 0x7F) == 0x7F ? (uint8_t)(b & 0x80) : b; }
+
+__global__ void layout_w13_kernel(LayoutArgs a) {
+  const int nH = a.H / kBlock, NB = a.Ip / kBlock;
+  const int64_t per_e = (int64_t)NB * nH * (kGateUpChunk / 16);
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= per_e * a.n) return;
+  const int le = (int)(q / per_e);
+  int64_t r = q - le * per_e;
+  const int lane = (int)(r & 63); r >>= 6;
+  const int half = (int)(r & 1); r >>= 1;
+  const int t = (int)(r & 3); r >>= 2;
+  const int w = (int)(r & 3); r >>= 2;
+  const int kb = (int)(r % nH);
+  const int nb = (int)(r / nH);
+  const int row = nb * kBlock + w * 32 + (t & 1) * 16 + (lane & 15);
+  const int k0 = kb * kBlock + (lane >> 4) * 32 + half * 16;
+  const uint8_t* src = (t < 2 ? a.gate : a.up) + ((size_t)le * a.I + row) * a.H + k0;
+  uint8_t v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = row < a.I ? clean(src[i]) : (uint8_t)0;
+  uint8_t* dst = a.w13 + ((size_t)(a.e0 + le) * per_e + (q - le * per_e)) * 16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dst[i] = v[i];
+}
+
+__global__ void layout_w2_kernel(LayoutArgs a) {
+  const int nI = a.Ip / kBlock, NB = a.H / kBlock;
+  const int64_t per_e = (int64_t)NB * nI * (kDownChunk / 16);
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= per_e * a.n) return;
+  const int le = (int)(q / per_e);
+  int64_t r = q - le * per_e;
+  const int lane = (int)(r & 63); r >>= 6;
+  const int half = (int)(r & 1); r >>= 1;
+  const int t = (int)(r & 1); r >>= 1;
+  const int w = (int)(r & 3); r >>= 2;
+  const int kb = (int)(r % nI);
+  const int nb = (int)(r / nI);
+  const int row = nb * kBlock + w * 32 + t * 16 + (lane & 15);
+  const int k0 = kb * kBlock + (lane >> 4) * 32 + half * 16;
+  const uint8_t* src = a.down + ((size_t)le * a.H + row) * a.I;
+  uint8_t v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = (k0 + i) < a.I ? clean(src[k0 + i]) : (uint8_t)0;
+  uint8_t* dst = a.w2 + ((size_t)(a.e0 + le) * per_e + (q - le * per_e)) * 16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dst[i] = v[i];
+}
+
+__global__ void layout_scales_kernel(LayoutArgs a) {
+  const int nH = a.H / kBlock, nI = a.Ip / kBlock;
+  const int64_t n13 = (int64_t)a.n * nI * nH;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n13) {
+    const size_t base = (size_t)a.e0 * nI * nH;
+    a.s13[(base + i) * 2] = a.gate_scale[i];
+    a.s13[(base + i) * 2 + 1] = a.up_scale[i];
+    a.s2[base + i] = a.down_scale[i];  // same element count, [nH][nI] order kept
+  }
+}
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
+  const int nH = a.H / kBlock, NB = a.Ip / kBlock;
+  const int64_t c13 = (int64_t)a.n * NB * nH * (kGateUpChunk / 16);
+  const int64_t c2 = (int64_t)a.n * nH * NB * (kDownChunk / 16);
+  const int64_t cs = (int64_t)a.n * NB * nH;
+  hipLaunchKernelGGL(layout_w13_kernel, dim3((unsigned)((c13 + 255) / 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(layout_w2_kernel, dim3((unsigned)((c2 + 255) / 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(layout_scales_kernel, dim3((unsigned)((cs + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------- probe --
+
+__global__ __launch_bounds__(64) void mfma_probe_kernel(const uint8_t* a, const uint8_t* b, float* d) {
+  const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
+  const i32x8 af = cat(ld16(a + c * 128 + g * 32), ld16(a + c * 128 + g * 32 + 16));
+  const i32x8 bf = cat(ld16(b + c * 128 + g * 32), ld16(b + c * 128 + g * 32 + 16));
+  const f32x4 r = mfma_e4m3(af, bf);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[(g * 4 + i) * 16 + c] = r[i];
+  // second result: the same product as four K=32 FP8 MFMAs chained through
+  // the accumulator (lane l holds 8 K bytes 8*(l/16).. of each 32-wide slice)
+  f32x4 r2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const long av = *reinterpret_cast<const long*>(a + c * 128 + s * 32 + g * 8);
+    const long bv = *reinterpret_cast<const long*>(b + c * 128 + s * 32 + g * 8);
+    r2 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(av, bv, r2, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[256 + (g * 4 + i) * 16 + c] = r2[i];
+  // third result: four independent K=32 MFMAs, each promoted to FP32
+  f32x4 r3 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const long av = *reinterpret_cast<const long*>(a + c * 128 + s * 32 + g * 8);
+    const long bv = *reinterpret_cast<const long*>(b + c * 128 + s * 32 + g * 8);
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(av, bv, z, 0, 0, 0);
+    r3 = r3 + part;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[512 + (g * 4 + i) * 16 + c] = r3[i];
+}
+
+hipError_t launch_mfma_probe(const uint8_t* a, const uint8_t* b, float* d, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(1), dim3(64), 0, s, a, b, d);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,196 @@
+/*
+ * moe_fp8_prefill: the routed-expert FFN of a top-k mixture-of-experts layer
+ * during prompt prefill, on one MI355X (gfx950), as a C-ABI library.
+ *
+ * The method (sources are the pages' titles and sections):
+ *   - "ktransformers #2244" (Full GLM-5.3 streamed FP8 GPU prefill), Design:
+ *     prefill runs W8A8 on the GPU: E4M3 expert weights with block scales and
+ *     FP8 activations; full GLM uses unclamped SiLU; routed scaling is kept;
+ *     all weights and scales are reserved up front in one per-layer slot;
+ *     stream-ordered reuse; fail closed after a staging failure; unsupported
+ *     dimensions / activation / quantisation and CUDA-graph capture are
+ *     rejected; expert arithmetic is tiled without repeating weight transfer.
+ *   - "hpc-ops #80" (GLM-4.6-FP8 on H20), gap table row 6: blockwise FP8 MoE
+ *     (per-128x128 weight blocks) instead of per-tensor scales, which saturate
+ *     on outlier tokens; a non-128-multiple intermediate size is zero-padded.
+ *   - "ktransformers #2245" (Exact AVX2 FP8 arithmetic conversion), Semantics
+ *     and scope: E4M3 decode; NaN codes act as signed zeros.
+ *   - "TensorFold #2852" (a whole prompt pass routes its experts in one call),
+ *     description and exactness paragraph: plan, grouped gate+up, gate-up
+ *     epilogue, grouped down, combine; a skip id that is never loaded; the
+ *     whole K accumulated in one pass (no split-K) and a deterministic member
+ *     order, so a row's bits do not depend on how many rows share a call.
+ *
+ * What run() computes, for token t (rho = routed scale):
+ *   out[t] = cast( rho * sum_{j<k} w[t,j] * y[t,j] )            (FP32 sum, ascending j)
+ *   y[t,j] = D_e . Q( silu(G_e . Q(x[t])) * (U_e . Q(x[t])) ),  e = ids[t,j]
+ * Q = dynamic E4M3 quantisation per row and per 128-column group
+ *     (s = max|v| / 448, q = round-to-nearest-even(v / s), saturating at 448);
+ * G_e, U_e, D_e = the expert's E4M3 matrices with FP32 128x128 block scales;
+ * each product is accumulated in FP32, K block by K block, each block's dot
+ * multiplied by (activation scale * weight scale).  silu(z) = z / (1 + e^-z).
+ *
+ * Error behaviour: every call returns an MOE_* code.  A HIP failure inside
+ * create or run leaves the handle FAILED: every later run returns
+ * MOE_ERR_FAILED_STATE (fail closed).  Expert ids >= E are skipped and
+ * reported by moe_fp8_prefill_status() as MOE_ERR_BAD_EXPERT_ID.
+ */
+#ifndef MOE_FP8_PREFILL_H_
+#define MOE_FP8_PREFILL_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null / misaligned pointer, negative size, bad struct_size */
+  MOE_ERR_UNSUPPORTED = 2,   /* dimensions, activation, block or dtype outside the method */
+  MOE_ERR_OUT_OF_MEMORY = 3, /* device allocation failed in create */
+  MOE_ERR_DEVICE = 4,        /* a HIP call failed; the handle is now FAILED */
+  MOE_ERR_FAILED_STATE = 5,  /* the handle failed earlier and refuses work */
+  MOE_ERR_BUSY = 6,          /* another thread is inside run() on this handle */
+  MOE_ERR_BAD_EXPERT_ID = 7  /* a routed id was >= E; those slots were skipped */
+};
+
+enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 };
+enum { MOE_ACT_SILU_UNCLAMPED = 0 };
+
+/*
+ * Layer description for create().  Weight layout is the checkpoint's:
+ *   gate, up   : u8 [E][I][H]   E4M3 codes, row = intermediate feature
+ *   down       : u8 [E][H][I]   E4M3 codes, row = hidden feature
+ *   gate_scale, up_scale : f32 [E][ceil(I/128)][H/128]   block (row blk, col blk)
+ *   down_scale           : f32 [E][H/128][ceil(I/128)]
+ * A block (nb, kb) covers rows 128*nb.. and columns 128*kb..; edge blocks of a
+ * non-128-multiple I are partial.  Pointers are host memory unless
+ * weights_on_device != 0 (then device memory on the current device).  The
+ * library copies and re-lays out the weights; the caller may free its copies
+ * once create() returns.
+ */
+typedef struct moe_fp8_prefill_desc {
+  int32_t struct_size;      /* sizeof(moe_fp8_prefill_desc) */
+  int32_t num_experts;      /* E, 1..1024 */
+  int32_t top_k;            /* k, 1..min(E, 256) */
+  int32_t hidden;           /* H, multiple of 128 */
+  int32_t inter;            /* I >= 1; padded to Ip = 128*ceil(I/128) with zero codes */
+  int32_t max_rows;         /* rows per internal pass; run() chunks larger T */
+  int32_t out_dtype;        /* MOE_DTYPE_BF16 or MOE_DTYPE_F32 */
+  int32_t activation;       /* MOE_ACT_SILU_UNCLAMPED */
+  int32_t block;            /* 128 */
+  float routed_scale;       /* rho, finite */
+  int32_t weights_on_device;
+  const uint8_t* gate;
+  const uint8_t* up;
+  const uint8_t* down;
+  const float* gate_scale;
+  const float* up_scale;
+  const float* down_scale;
+  void* stream;             /* hipStream_t used for the upload; NULL = null stream */
+} moe_fp8_prefill_desc;
+
+typedef struct moe_fp8_prefill moe_fp8_prefill;
+
+/* Checks a description on the host: no GPU call, no allocation.
+ * Returns MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED. */
+int moe_fp8_prefill_validate(const moe_fp8_prefill_desc* d);
+
+/* Device bytes create() will allocate for workspace (all of it is reserved up
+ * front; run() allocates nothing), and for the re-laid-out weights.  Negative
+ * (minus an MOE_* code) for an invalid description. */
+int64_t moe_fp8_prefill_workspace_bytes(const moe_fp8_prefill_desc* d);
+int64_t moe_fp8_prefill_weight_bytes(const moe_fp8_prefill_desc* d);
+
+/* Validates, allocates weights + workspace on the current device, uploads
+ * and re-lays out the weights (NaN codes 0x7F/0xFF become 0x00/0x80, the I
+ * edge is zero-padded), then synchronises.  *out stays NULL on error. */
+int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out);
+
+/*
+ * One prefill pass over T tokens, asynchronous on `stream` (hipStream_t; NULL
+ * = null stream).  All pointers are device memory owned by the caller and must
+ * stay valid until the stream passes this call:
+ *   x     : bf16 [T][H], 16-byte aligned
+ *   ids   : i32 [T][k]; id < 0 is a skip slot (never loaded); id >= E is
+ *           skipped and flagged (see status)
+ *   w     : f32 [T][k] routing weights (used as given)
+ *   out   : [T][H] of out_dtype, 16-byte aligned
+ * T = 0 is a no-op.  T > max_rows is processed in passes of max_rows rows; a
+ * row's result does not depend on T, on the chunking or on the other rows.
+ * No allocation, no host synchronisation.  A different stream from the last
+ * call waits on that call first.  Returns MOE_ERR_UNSUPPORTED while the stream
+ * is capturing, MOE_ERR_BUSY on concurrent use of one handle.
+ */
+int moe_fp8_prefill_run(moe_fp8_prefill* h, const void* x, const int32_t* ids,
+                        const float* w, int64_t T, void* out, void* stream);
+
+/* Synchronises the handle's last stream; returns and clears device-detected
+ * errors (MOE_ERR_BAD_EXPERT_ID), or MOE_ERR_FAILED_STATE, else MOE_OK. */
+int moe_fp8_prefill_status(moe_fp8_prefill* h);
+
+/* NULL-safe.  Synchronises, then frees everything. */
+void moe_fp8_prefill_destroy(moe_fp8_prefill* h);
+
+/* Static string for an MOE_* code. */
+const char* moe_fp8_prefill_strerror(int code);
+
+/* ---- inspection (synchronous; for tests and tooling) ------------------ */
+
+/* The last pass's plan, copied to host buffers: counts i32[E], offsets
+ * i32[E+1], perm i32[cap] (sorted position -> slot t*k+j), inv i32[cap]
+ * (slot -> sorted position or -1).  cap must be >= that pass's T*k. */
+int moe_fp8_prefill_debug_plan(moe_fp8_prefill* h, int32_t* counts, int32_t* offsets,
+                               int32_t* perm, int32_t* inv, int64_t cap);
+
+/* The last pass's quantised activations: xq u8[rows][H], sx f32[rows][H/128]
+ * (token order), rows = that pass's T. */
+int moe_fp8_prefill_debug_activations(moe_fp8_prefill* h, uint8_t* xq, float* sx,
+                                      int64_t rows);
+
+/* The last pass's per-slot intermediates in sorted order: hq u8[n][Ip],
+ * sh f32[n][Ip/128], y f32[n][H]; n = number of routed slots (<= cap_rows).
+ * Any pointer may be NULL. */
+int moe_fp8_prefill_debug_intermediates(moe_fp8_prefill* h, uint8_t* hq, float* sh,
+                                        float* y, int64_t cap_rows, int64_t* n_rows);
+
+/* The last pass's FP32 gate and up outputs before the SiLU / quantisation
+ * epilogue, gu f32[n][2*Ip] (gate columns then up columns, sorted order),
+ * recomputed by re-running that pass's gate_up stage into a temporary device
+ * buffer (this call allocates; it is an inspection tool). */
+int moe_fp8_prefill_debug_gate_up(moe_fp8_prefill* h, float* gu, int64_t cap_rows,
+                                  int64_t* n_rows);
+
+/* Expert e's weights back in the canonical layout above (I rows / columns,
+ * after NaN-code sanitising): gate, up u8[I][H]; down u8[H][I]; scales as in
+ * the description.  Host buffers. */
+int moe_fp8_prefill_debug_unpack(moe_fp8_prefill* h, int32_t e, uint8_t* gate, uint8_t* up,
+                                 uint8_t* down, float* gate_scale, float* up_scale,
+                                 float* down_scale);
+
+/* One 16x16x128 FP8 MFMA through the library's operand convention, on the
+ * current device: d[0][i][n] = sum_c dec(a[i][c]) * dec(b[n][c]); d[1] is the
+ * same product as four 16x16x32 FP8 MFMAs chained through the accumulator,
+ * d[2] as four independent 16x16x32 MFMAs summed in FP32.  Host buffers
+ * a u8[16][128], b u8[16][128], d f32[3][16][16]. */
+int moe_fp8_prefill_debug_mfma(const uint8_t* a, const uint8_t* b, float* d);
+
+/* Per-stage GPU timing with HIP events on the run stream.  When enabled,
+ * every pass records events around its stages; read_timing() synchronises and
+ * returns up to max_records rows of MOE_NUM_STAGES milliseconds
+ * (plan, quantise, gate_up, down, combine), then clears the record. */
+#define MOE_NUM_STAGES 5
+int moe_fp8_prefill_set_timing(moe_fp8_prefill* h, int32_t enable);
+int moe_fp8_prefill_read_timing(moe_fp8_prefill* h, float* stage_ms, int32_t max_records,
+                                int32_t* n_records);
+
+/* Test hook: force the next run to behave as if a HIP call failed (host-side
+ * flag only; no GPU fault is produced). */
+int moe_fp8_prefill_debug_inject_failure(moe_fp8_prefill* h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP8_PREFILL_H_ */

@@ -83,6 +83,9 @@ def _load():
         lib.orc_forward.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int32, P, P, P, ctypes.c_int64,
                                     ctypes.c_float, ctypes.c_int32, P, ctypes.POINTER(_Debug)]
         lib.orc_forward.restype = ctypes.c_int64
+        lib.orc_down_combine.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int32, P, P, P, P,
+                                         ctypes.c_int64, ctypes.c_float, ctypes.c_int32, P, P]
+        lib.orc_down_combine.restype = ctypes.c_int64
         lib.orc_bruteforce_fp64.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int32, P, P, P,
                                             ctypes.c_int64, ctypes.c_double, ctypes.c_int32, P]
         lib.orc_bruteforce_fp64.restype = ctypes.c_int32
@@ -205,6 +208,26 @@ def forward(layer, x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, rho: floa
         d["n_bad"] = int(bad)
         return out, d
     return out
+
+
+def down_combine(layer, hq: np.ndarray, sh: np.ndarray, ids: np.ndarray, w: np.ndarray, rho: float,
+                 out_dtype: int = OUT_BF16):
+    """Continue the layer from given h codes (sorted order of the plan of ids).
+    Returns (out, y)."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    hq = np.ascontiguousarray(hq, dtype=np.uint8)
+    sh = np.ascontiguousarray(sh, dtype=np.float32)
+    T, k = ids.shape
+    out = np.empty((T, layer.H), np.uint16 if out_dtype == OUT_BF16 else np.float32)
+    y = np.empty((max(hq.shape[0], 1), layer.H), np.float32)
+    st, keep = _layer_struct(layer)
+    P = _load().orc_down_combine(ctypes.byref(st), k, _p(hq), _p(sh), _p(ids), _p(w), T, float(rho),
+                                 out_dtype, _p(out), _p(y))
+    del keep
+    if P < 0 or P != hq.shape[0]:
+        raise ValueError("bad arguments or h rows do not match the plan")
+    return out, y[:P]
 
 
 def bruteforce_fp64(layer, x_bits, ids, w, rho, quantize_activations=True) -> np.ndarray:

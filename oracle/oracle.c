@@ -281,6 +281,56 @@ static float silu_mul(float g, float u) {
   return (g / (1.0f + expf(-g))) * u;
 }
 
+/* Down projection of the decoded h rows (sorted order) and the weighted
+ * combine: y[p] = D_e . h[p] blockwise as above; out[t] = cast(rho * sum_j
+ * w[t,j] * y[inv[t*k+j]]), FP32, ascending j, one rounding at the end. */
+static void down_and_combine(const orc_layer* L, int64_t k, const float* hd, const float* sh,
+                             const int32_t* counts, const int32_t* offsets, const int32_t* inv,
+                             const float* w, int64_t T, float rho, int32_t out_dtype, void* out,
+                             float* y) {
+  const int64_t E = L->E, H = L->H, I = L->I;
+  const int64_t Ip = 128 * ((I + 127) / 128), nH = H / 128, nI = Ip / 128;
+#pragma omp parallel
+  {
+    float* wrow = (float*)malloc(sizeof(float) * (size_t)Ip);
+    float* wsc = (float*)malloc(sizeof(float) * (size_t)nI);
+#pragma omp for collapse(2) schedule(dynamic, 8)
+    for (int64_t e = 0; e < E; ++e) {
+      for (int64_t n = 0; n < H; ++n) {
+        if (counts[e] == 0) continue;
+        const uint8_t* src = L->down + (e * H + n) * I;
+        for (int64_t c = 0; c < Ip; ++c) wrow[c] = c < I ? orc_e4m3_decode(src[c]) : 0.0f;
+        const float* ds = L->down_scale + e * nH * nI;
+        for (int64_t kb = 0; kb < nI; ++kb)
+          wsc[kb] = (g_fault == FAULT_DOWN_SCALE_TRANSPOSED)
+                        ? ds[(kb % nH) * nI + ((n / 128) % nI)]
+                        : ds[(n / 128) * nI + kb];
+        for (int64_t p = offsets[e]; p < offsets[e + 1]; ++p)
+          y[p * H + n] = blocked_dot(hd + p * Ip, sh + p * nI, wrow, wsc, Ip);
+      }
+    }
+    free(wrow);
+    free(wsc);
+  }
+
+  /* weighted combine: ascending slot order, FP32, rho once, one rounding */
+  float r = (g_fault == FAULT_DROP_RHO) ? 1.0f : rho;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t n = 0; n < H; ++n) {
+      float acc = 0.0f;
+      for (int64_t j = 0; j < k; ++j) {
+        int32_t p = inv[t * k + j];
+        if (p >= 0) acc = acc + w[t * k + j] * y[(int64_t)p * H + n];
+      }
+      float v = r * acc;
+      if (out_dtype == 0)
+        ((uint16_t*)out)[t * H + n] = (uint16_t)orc_f32_to_bf16(v);
+      else
+        ((float*)out)[t * H + n] = v;
+    }
+  }
+}
+
 /*
  * The routed-expert layer on T tokens.
  * x: bf16 bits u16[T][H]; ids: i32[T][k]; w: f32[T][k].
@@ -345,47 +395,8 @@ int64_t orc_forward(const orc_layer* L, int32_t k, const uint16_t* x, const int3
   float* hd = h; /* reuse: decoded codes of hq */
   for (int64_t i = 0; i < P * Ip; ++i) hd[i] = orc_e4m3_decode(hq[i]);
 
-  /* down */
   float* y = (float*)malloc(sizeof(float) * (size_t)(P * H + 1));
-#pragma omp parallel
-  {
-    float* wrow = (float*)malloc(sizeof(float) * (size_t)Ip);
-    float* wsc = (float*)malloc(sizeof(float) * (size_t)nI);
-#pragma omp for collapse(2) schedule(dynamic, 8)
-    for (int64_t e = 0; e < E; ++e) {
-      for (int64_t n = 0; n < H; ++n) {
-        if (counts[e] == 0) continue;
-        const uint8_t* src = L->down + (e * H + n) * I;
-        for (int64_t c = 0; c < Ip; ++c) wrow[c] = c < I ? orc_e4m3_decode(src[c]) : 0.0f;
-        const float* ds = L->down_scale + e * nH * nI;
-        for (int64_t kb = 0; kb < nI; ++kb)
-          wsc[kb] = (g_fault == FAULT_DOWN_SCALE_TRANSPOSED)
-                        ? ds[(kb % nH) * nI + ((n / 128) % nI)]
-                        : ds[(n / 128) * nI + kb];
-        for (int64_t p = offsets[e]; p < offsets[e + 1]; ++p)
-          y[p * H + n] = blocked_dot(hd + p * Ip, sh + p * nI, wrow, wsc, Ip);
-      }
-    }
-    free(wrow);
-    free(wsc);
-  }
-
-  /* weighted combine: ascending slot order, FP32, rho once, one rounding */
-  float r = (g_fault == FAULT_DROP_RHO) ? 1.0f : rho;
-  for (int64_t t = 0; t < T; ++t) {
-    for (int64_t n = 0; n < H; ++n) {
-      float acc = 0.0f;
-      for (int64_t j = 0; j < k; ++j) {
-        int32_t p = inv[t * k + j];
-        if (p >= 0) acc = acc + w[t * k + j] * y[(int64_t)p * H + n];
-      }
-      float v = r * acc;
-      if (out_dtype == 0)
-        ((uint16_t*)out)[t * H + n] = (uint16_t)orc_f32_to_bf16(v);
-      else
-        ((float*)out)[t * H + n] = v;
-    }
-  }
+  down_and_combine(L, k, hd, sh, counts, offsets, inv, w, T, rho, out_dtype, out, y);
 
   if (dbg) {
     if (dbg->xq) memcpy(dbg->xq, xq, (size_t)(T * H));
@@ -526,4 +537,37 @@ int32_t orc_bruteforce_fp64(const orc_layer* L, int32_t k, const uint16_t* x,
   free(hv);
   free(ha);
   return 0;
+}
+
+/*
+ * The second half of the layer from given h codes: hq u8[P][Ip] and
+ * sh f32[P][Ip/128] in the sorted order of the plan of ids (P = routed
+ * slots).  Used to continue the oracle from another implementation's h
+ * codes where an FP32 value decided a code near a rounding boundary.
+ * out as in orc_forward; y (optional) f32[P][H].  Returns P, or -1.
+ */
+int64_t orc_down_combine(const orc_layer* L, int32_t k, const uint8_t* hq, const float* sh,
+                         const int32_t* ids, const float* w, int64_t T, float rho,
+                         int32_t out_dtype, void* out, float* y_out) {
+  const int64_t E = L->E, H = L->H, I = L->I;
+  if (E < 1 || k < 1 || H % 128 != 0 || I < 1 || T < 0) return -1;
+  const int64_t Ip = 128 * ((I + 127) / 128), S = T * k;
+  int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+  int32_t* perm = (int32_t*)malloc(sizeof(int32_t) * (size_t)(S + 1));
+  int32_t* inv = (int32_t*)malloc(sizeof(int32_t) * (size_t)(S + 1));
+  orc_plan(ids, T, k, (int32_t)E, counts, offsets, perm, inv);
+  const int64_t P = offsets[E];
+  float* hd = (float*)malloc(sizeof(float) * (size_t)(P * Ip + 1));
+  for (int64_t i = 0; i < P * Ip; ++i) hd[i] = orc_e4m3_decode(hq[i]);
+  float* y = (float*)malloc(sizeof(float) * (size_t)(P * H + 1));
+  down_and_combine(L, k, hd, sh, counts, offsets, inv, w, T, rho, out_dtype, out, y);
+  if (y_out) memcpy(y_out, y, sizeof(float) * (size_t)(P * H));
+  free(counts);
+  free(offsets);
+  free(perm);
+  free(inv);
+  free(hd);
+  free(y);
+  return P;
 }
