@@ -29,8 +29,8 @@ MOE_ERR_BAD_EXPERT_ID = 7
 MOE_DTYPE_BF16 = 0
 MOE_DTYPE_F32 = 1
 MOE_ACT_SILU_UNCLAMPED = 0
-MOE_NUM_STAGES = 5
-STAGES = ("plan", "quant", "gate_up", "down", "combine")
+MOE_NUM_STAGES = 7
+STAGES = ("plan", "quant", "gate_up_small", "gate_up_big", "down_small", "down_big", "combine")
 
 EXPORTED = (
     "moe_fp8_prefill_validate", "moe_fp8_prefill_workspace_bytes", "moe_fp8_prefill_weight_bytes",
@@ -261,7 +261,7 @@ def moe_fp8_prefill_set_timing(handle: int, enable: bool) -> None:
 
 
 def moe_fp8_prefill_read_timing(handle: int, max_records: int = 4096) -> np.ndarray:
-    """[records][5] milliseconds: plan, quant, gate_up, down, combine."""
+    """[records][7] milliseconds, one row per pass, in the order of STAGES."""
     buf = np.zeros((max_records, MOE_NUM_STAGES), np.float32)
     n = ctypes.c_int32()
     _check(load_library().moe_fp8_prefill_read_timing(ctypes.c_void_p(handle), _np_ptr(buf),

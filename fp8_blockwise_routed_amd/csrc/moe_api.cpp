@@ -224,13 +224,15 @@ int gemm_grid(const moe_fp8_prefill* h, int64_t max_items, bool big) {
 
 // The two gate_up launches (1-subtile tiles, then multi-subtile tiles) of a
 // pass over t rows / P slots whose plan and activations are in the workspace.
-hipError_t launch_gate_up_pair(moe_fp8_prefill* h, int64_t t, int64_t P, float* gu_dbg, hipStream_t s) {
+hipError_t launch_gate_up_pair(moe_fp8_prefill* h, int64_t t, int64_t P, float* gu_dbg, hipStream_t s,
+                               hipEvent_t between = nullptr) {
   const Dims& m = h->m;
   const int64_t nb = m.Ip / kBlock;
   GateUpArgs ga{h->xq, h->sx, t * m.H, t * m.nH * 4, h->perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip,
                 h->w13, h->s13, h->small_tiles, h->n_tiles, h->hq, h->sh, gu_dbg};
   hipError_t e = launch_gate_up(ga, false, gemm_grid(h, m.E * nb, false), s);
   if (e != hipSuccess) return e;
+  if (between && (e = hipEventRecord(between, s)) != hipSuccess) return e;
   ga.tiles = h->big_tiles;
   ga.n_tiles = h->n_tiles + 1;
   return launch_gate_up(ga, true, gemm_grid(h, (P / kSmallRows + m.E) * nb, true), s);
@@ -420,24 +422,26 @@ int moe_fp8_prefill_run(moe_fp8_prefill* h, const void* x, const int32_t* ids, c
     if (h->timing && hipEventRecord(ev.ev[2], s) != hipSuccess) return fail(h);
 
     int g_small, g_big;
-    if (launch_gate_up_pair(h, t, P, nullptr, s) != hipSuccess) return fail(h);
-    if (h->timing && hipEventRecord(ev.ev[3], s) != hipSuccess) return fail(h);
+    if (launch_gate_up_pair(h, t, P, nullptr, s, h->timing ? ev.ev[3] : nullptr) != hipSuccess)
+      return fail(h);
+    if (h->timing && hipEventRecord(ev.ev[4], s) != hipSuccess) return fail(h);
 
     g_small = gemm_grid(h, m.E * nb_dn, false);
     g_big = gemm_grid(h, (P / kSmallRows + m.E) * nb_dn, true);
     DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2, h->small_tiles, h->n_tiles, h->y};
     if (launch_down(da, false, g_small, s) != hipSuccess) return fail(h);
+    if (h->timing && hipEventRecord(ev.ev[5], s) != hipSuccess) return fail(h);
     da.tiles = h->big_tiles;
     da.n_tiles = h->n_tiles + 1;
     if (launch_down(da, true, g_big, s) != hipSuccess) return fail(h);
-    if (h->timing && hipEventRecord(ev.ev[4], s) != hipSuccess) return fail(h);
+    if (h->timing && hipEventRecord(ev.ev[6], s) != hipSuccess) return fail(h);
 
     CombineArgs ca{h->y, h->inv, w + r0 * m.k, (int32_t)t, (int32_t)m.k, (int32_t)m.H,
                    h->desc.routed_scale, h->desc.out_dtype == MOE_DTYPE_F32 ? 1 : 0,
                    (uint8_t*)out + r0 * m.H * out_elem};
     if (launch_combine(ca, s) != hipSuccess) return fail(h);
     if (h->timing) {
-      if (hipEventRecord(ev.ev[5], s) != hipSuccess) return fail(h);
+      if (hipEventRecord(ev.ev[7], s) != hipSuccess) return fail(h);
       h->pending.push_back(ev);
     }
     h->last_T = t;

@@ -176,11 +176,13 @@ int moe_fp8_prefill_debug_unpack(moe_fp8_prefill* h, int32_t e, uint8_t* gate, u
  * a u8[16][128], b u8[16][128], d f32[3][16][16]. */
 int moe_fp8_prefill_debug_mfma(const uint8_t* a, const uint8_t* b, float* d);
 
-/* Per-stage GPU timing with HIP events on the run stream.  When enabled,
- * every pass records events around its stages; read_timing() synchronises and
- * returns up to max_records rows of MOE_NUM_STAGES milliseconds
- * (plan, quantise, gate_up, down, combine), then clears the record. */
-#define MOE_NUM_STAGES 5
+/* Per-launch GPU timing with HIP events on the run stream.  When enabled,
+ * every pass records events between its kernel launches; read_timing()
+ * synchronises and returns up to max_records rows (one per pass) of
+ * MOE_NUM_STAGES milliseconds: plan, quantise, gate_up (1-subtile tiles),
+ * gate_up (multi-subtile tiles), down (1-subtile), down (multi-subtile),
+ * combine; then clears the record. */
+#define MOE_NUM_STAGES 7
 int moe_fp8_prefill_set_timing(moe_fp8_prefill* h, int32_t enable);
 int moe_fp8_prefill_read_timing(moe_fp8_prefill* h, float* stage_ms, int32_t max_records,
                                 int32_t* n_records);
