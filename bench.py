@@ -25,8 +25,25 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 METRIC = "input tokens/sec per MoE layer (1 MI355X) + % FP8 MFMA peak / % HBM peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_small_glm_t256_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
+COUNTERS_MD = os.path.join(PROFILES, "gate_up_stream_glm_e256_t256_counters.md")
+STATS_MD = os.path.join(PROFILES, "kernel_stats_glm_e256_t256.md")
 KERNEL_SOURCE = os.path.join(ROOT, "fp8_blockwise_routed_amd", "csrc", "moe_kernels.hip")
+DOMINANT = "gate_up_stream_kernel"   # the 1-subtile gate_up launch (experts with 1..16 rows)
+
+# The commands whose output --summarize-profiles reads (run from the repository root).
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_kt -o kt -- "
+             "python3 bench.py --steps 10 --warmup 3 --cpu-tokens 0",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o fetch -- "
+             "python3 bench.py --steps 3 --warmup 1 --cpu-tokens 0",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -o write -- "
+             "python3 bench.py --steps 3 --warmup 1 --cpu-tokens 0",
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_copy_fetch -o cf -- "
+                  "python3 bench.py --copy-calibration",
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_copy_write -o cw -- "
+                  "python3 bench.py --copy-calibration",
+}
 
 
 def log(msg: str) -> None:
@@ -66,28 +83,112 @@ def algorithmic_work(wl, counts):
                 slots=P, per_expert_gate_up_bytes=2 * Ip * H + 8 * nI * nH)
 
 
-def read_traffic(n_launch_bytes):
+def read_traffic():
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     counter summary, or None if absent or taken on different kernel source."""
+    fields = {}
     try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+        with open(COUNTERS_MD) as f:
+            for line in f:
+                if line.startswith("- ") and ": " in line:
+                    key, val = line[2:].split(": ", 1)
+                    fields[key.strip()] = val.strip().strip("`")
+    except OSError:
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
-def cpu_baseline(layer, wl, x, ids, w, n_tokens):
-    """The oracle, as it stands, on the first n_tokens rows of the same batch."""
+def _csv_rows(pattern):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(pattern, recursive=True)):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _mean_counter(rows, name_part, counter):
+    vals = [float(r["Counter_Value"]) for r in rows
+            if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def summarize_profiles(out_dir: str) -> int:
+    """Write the committed profile summaries from rocprofv3 CSV output under
+    out_dir (the PROFILE_COMMANDS runs)."""
+    stats = _csv_rows(os.path.join(out_dir, "prof_kt", "**", "*kernel_stats.csv"))
+    if not stats:
+        log("no kernel_stats.csv found")
+        return 1
+    src = kernel_source_hash()
+    lines = ["# Kernel time, GLM-class layer E=256 top-8 H=6144 I=2048, T=256 rows", "",
+             "Command (repository root, one MI355X):", "", f"    {PROFILE_COMMANDS['trace']}", "",
+             f"- kernel_source_sha256_16: `{src}`", "",
+             "| kernel | calls | average us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    lines += ["", "The layout kernels run once, inside create() (weight upload), outside the timed steps."]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(STATS_MD, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    fetch = _csv_rows(os.path.join(out_dir, "prof_fetch", "**", "*counter_collection.csv"))
+    write = _csv_rows(os.path.join(out_dir, "prof_write", "**", "*counter_collection.csv"))
+    cfetch = _csv_rows(os.path.join(out_dir, "prof_copy_fetch", "**", "*counter_collection.csv"))
+    cwrite = _csv_rows(os.path.join(out_dir, "prof_copy_write", "**", "*counter_collection.csv"))
+    f_kib, nf = _mean_counter(fetch, DOMINANT, "FETCH_SIZE")
+    w_kib, nw = _mean_counter(write, DOMINANT, "WRITE_SIZE")
+    cf_kib, _ = _mean_counter(cfetch, "copyBuffer", "FETCH_SIZE")
+    cw_kib, _ = _mean_counter(cwrite, "copyBuffer", "WRITE_SIZE")
+    if None in (f_kib, w_kib, cf_kib, cw_kib):
+        log("counter CSVs incomplete")
+        return 1
+    copy_kib = (1 << 30) / 1024
+    f_scale, w_scale = copy_kib / cf_kib, copy_kib / cw_kib
+    hbm = int(round((f_kib * f_scale + w_kib * w_scale) * 1024))
+    lines = [f"# HBM traffic of {DOMINANT}<3> (gate_up, experts with 1..16 rows), "
+             "GLM-class layer E=256 T=256", "",
+             "Commands (repository root, one MI355X), one counter per run:", ""]
+    lines += [f"    {PROFILE_COMMANDS[k]}" for k in ("fetch", "write", "copy_fetch", "copy_write")]
+    lines += ["", "Counters are KiB per dispatch, averaged over the kernel's dispatches "
+                  f"({nf} FETCH, {nw} WRITE).  The copy runs move 1 GiB (1048576 KiB) each way "
+                  "with torch's device copy; its readings give the scale factors.", "",
+              f"- FETCH_SIZE_kib_per_dispatch: {f_kib:.1f}",
+              f"- WRITE_SIZE_kib_per_dispatch: {w_kib:.1f}",
+              f"- copy_FETCH_SIZE_kib: {cf_kib:.1f}",
+              f"- copy_WRITE_SIZE_kib: {cw_kib:.1f}",
+              f"- fetch_scale: {f_scale:.4f}",
+              f"- write_scale: {w_scale:.4f}",
+              f"- hbm_bytes_per_launch: {hbm}",
+              f"- kernel_source_sha256_16: `{src}`", ""]
+    with open(COUNTERS_MD, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"hbm_bytes_per_launch": hbm, "fetch_scale": f_scale, "write_scale": w_scale}))
+    return 0
+
+
+def cpu_baseline(layer, wl, x, ids, w, n_tokens, repeats):
+    """The oracle, as it stands, on the first n_tokens rows of the same batch:
+    median wall clock of `repeats` runs."""
     import oracle
-    t0 = time.perf_counter()
-    oracle.forward(layer, x[:n_tokens], ids[:n_tokens], w[:n_tokens], wl.rho, oracle.OUT_BF16)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.forward(layer, x[:n_tokens], ids[:n_tokens], w[:n_tokens], wl.rho, oracle.OUT_BF16)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     return dict(value=n_tokens / dt, unit="tokens/s", cores=oracle.max_threads(), kind="oracle",
-                sample=f"first {n_tokens} of the {wl.T} rows of the timed batch "
-                       f"(all their routed experts), wall clock {dt:.2f} s")
+                sample=f"first {n_tokens} of the {wl.T} rows of the timed batch with all their "
+                       f"routed experts; median of {repeats} runs, {dt:.2f} s each")
 
 
 def main() -> int:
@@ -100,7 +201,25 @@ def main() -> int:
                     help="rows of the batch the CPU oracle is timed on (0 skips it)")
     ap.add_argument("--no-timing-events", action="store_true",
                     help="skip the per-launch HIP events (roofline needs them)")
+    ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries from rocprofv3 CSV output under DIR")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        return summarize_profiles(args.summarize_profiles)
+    if args.copy_calibration:
+        import torch
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n}))
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this path runs on one GPU; multi-GPU sharding is design only "
                                    "(expert-parallel all-to-all), so --gpus must be 1"}))
@@ -177,9 +296,9 @@ def main() -> int:
         res["stages_ms"] = {name: float(v) for name, v in zip(pkg.STAGES, mean)}
         gu_ms = float(mean[pkg.STAGES.index("gate_up_small")])
         achieved = work["gu_small_bytes"] / (gu_ms * 1e-3) / 1e9
-        traffic = read_traffic(work["gu_small_bytes"])
+        traffic = read_traffic()
         res["roofline"] = {
-            "kernel": "gate_up_kernel<1> (experts with 1..16 rows)",
+            "kernel": "gate_up_stream_kernel (experts with 1..16 rows)",
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
             "algorithmic_bytes_per_launch": work["gu_small_bytes"],
@@ -188,7 +307,8 @@ def main() -> int:
         }
     if args.cpu_tokens > 0:
         log(f"[bench] CPU oracle on {args.cpu_tokens} rows")
-        res["cpu_baseline"] = cpu_baseline(layer, wl, x, ids, w, min(args.cpu_tokens, wl.T))
+        res["cpu_baseline"] = cpu_baseline(layer, wl, x, ids, w, min(args.cpu_tokens, wl.T),
+                                           max(1, args.cpu_repeats))
     moe.close()
     print(json.dumps(res), flush=True)
     return 0

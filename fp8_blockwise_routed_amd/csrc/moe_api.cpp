@@ -217,8 +217,8 @@ int upload_weights(moe_fp8_prefill* h, hipStream_t s) {
 
 // Grid of a persistent GEMM launch: enough resident workgroups to fill the
 // chip, never more than the largest possible number of work items.
-int gemm_grid(const moe_fp8_prefill* h, int64_t max_items, bool big) {
-  const int64_t per_cu = big ? 2 : 16;
+int gemm_grid(const moe_fp8_prefill* h, int64_t max_items, bool big, bool gate_up) {
+  const int64_t per_cu = big ? 2 : (gate_up ? kGateUpWgPerCu : kDownWgPerCu);
   return (int)std::max<int64_t>(1, std::min<int64_t>(max_items, h->num_cus * per_cu));
 }
 
@@ -230,12 +230,12 @@ hipError_t launch_gate_up_pair(moe_fp8_prefill* h, int64_t t, int64_t P, float* 
   const int64_t nb = m.Ip / kBlock;
   GateUpArgs ga{h->xq, h->sx, t * m.H, t * m.nH * 4, h->perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip,
                 h->w13, h->s13, h->small_tiles, h->n_tiles, h->hq, h->sh, gu_dbg};
-  hipError_t e = launch_gate_up(ga, false, gemm_grid(h, m.E * nb, false), s);
+  hipError_t e = launch_gate_up(ga, false, gemm_grid(h, m.E * nb, false, true), s);
   if (e != hipSuccess) return e;
   if (between && (e = hipEventRecord(between, s)) != hipSuccess) return e;
   ga.tiles = h->big_tiles;
   ga.n_tiles = h->n_tiles + 1;
-  return launch_gate_up(ga, true, gemm_grid(h, (P / kSmallRows + m.E) * nb, true), s);
+  return launch_gate_up(ga, true, gemm_grid(h, (P / kSmallRows + m.E) * nb, true, true), s);
 }
 
 int get_stage_events(moe_fp8_prefill* h, StageEvents* out) {
@@ -426,8 +426,8 @@ int moe_fp8_prefill_run(moe_fp8_prefill* h, const void* x, const int32_t* ids, c
       return fail(h);
     if (h->timing && hipEventRecord(ev.ev[4], s) != hipSuccess) return fail(h);
 
-    g_small = gemm_grid(h, m.E * nb_dn, false);
-    g_big = gemm_grid(h, (P / kSmallRows + m.E) * nb_dn, true);
+    g_small = gemm_grid(h, m.E * nb_dn, false, false);
+    g_big = gemm_grid(h, (P / kSmallRows + m.E) * nb_dn, true, false);
     DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2, h->small_tiles, h->n_tiles, h->y};
     if (launch_down(da, false, g_small, s) != hipSuccess) return fail(h);
     if (h->timing && hipEventRecord(ev.ev[5], s) != hipSuccess) return fail(h);

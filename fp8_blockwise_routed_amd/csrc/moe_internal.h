@@ -12,6 +12,26 @@ constexpr int kWaves = 4;            // waves per GEMM workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSmallRows = 16;       // experts with <= this many rows use the 1-subtile GEMM
 constexpr int kBigRows = 64;         // rows per tile of the multi-subtile GEMM
+#ifndef MOE_STREAM_DEPTH
+#define MOE_STREAM_DEPTH 3
+#endif
+#ifndef MOE_STREAM_DEPTH_DOWN
+#define MOE_STREAM_DEPTH_DOWN 4
+#endif
+#ifndef MOE_WEIGHT_AUX
+#define MOE_WEIGHT_AUX 2
+#endif
+#ifndef MOE_GU_WG_PER_CU
+#define MOE_GU_WG_PER_CU 3
+#endif
+#ifndef MOE_DN_WG_PER_CU
+#define MOE_DN_WG_PER_CU 4
+#endif
+constexpr int kWeightAux = MOE_WEIGHT_AUX;          // cache-policy bits of the weight loads
+constexpr int kGateUpWgPerCu = MOE_GU_WG_PER_CU;  // persistent grid of the streaming gate_up
+constexpr int kDownWgPerCu = MOE_DN_WG_PER_CU;    // persistent grid of the streaming down
+constexpr int kStreamDepth = MOE_STREAM_DEPTH;           // K blocks in flight per wave, streaming gate_up
+constexpr int kStreamDepthDown = MOE_STREAM_DEPTH_DOWN;  // K blocks in flight per wave, streaming down
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxKBlocks = 128;     // H/128 and Ip/128 limit (LDS-staged weight scales)
 

@@ -268,6 +268,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ i32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
+// Weight stream loads: read once per pass, cache policy kWeightAux.
+__device__ __forceinline__ i32x4 wload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kWeightAux);
+}
 __device__ __forceinline__ float bloadf(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
@@ -473,11 +477,143 @@ __global__ __launch_bounds__(kThreads, (MT == 1 ? 4 : 2)) void gate_up_kernel(Ga
   }
 }
 
+// Streaming gate_up for experts with at most 16 rows (the HBM-bound regime):
+// one 16-row subtile, so every weight byte feeds one MFMA.  No LDS activation
+// tile and no barrier inside the K loop: each wave loads its own activation
+// fragment (L2 resident) and weight fragments straight into registers, D K
+// blocks deep, so the four waves stream independently.  Row scales for all K
+// blocks are staged in LDS once per tile.  Same MFMA, promotion order and
+// epilogue arithmetic as gate_up_kernel, so a row's bits do not depend on
+// which variant ran it.
+template <int D>
+__global__ __launch_bounds__(kThreads, D <= 2 ? 4 : 3) void gate_up_stream_kernel(GateUpArgs a) {
+  constexpr int BM = kSmallRows;
+  __shared__ float sxt[BM][kMaxKBlocks];
+  __shared__ float ws_lds[2 * kMaxKBlocks];
+  __shared__ int tok_lds[BM];
+  __shared__ uint32_t red_lds[kWaves][BM];
+  __shared__ __attribute__((aligned(16))) uint8_t h_lds[BM * 128];
+  __shared__ float sh_lds[BM];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int H = a.H, Ip = a.Ip, nH = H / kBlock, NB = Ip / kBlock;
+  const int n_items = a.n_tiles[0] * NB;
+  const rsrc_t xr = make_rsrc(a.xq, (uint32_t)a.xq_bytes);
+  const uint32_t bvoff = (uint32_t)(wave * 8192 + lane * 16);
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int tile = item / NB, nb = item - tile * NB;
+    const Tile td = a.tiles[tile];
+    const int e = td.e, p0 = td.p0, rows = td.rows;
+
+    __syncthreads();  // LDS of the previous item is no longer read
+    if (tid < BM) tok_lds[tid] = a.perm[p0 + (tid < rows ? tid : 0)] / a.k;
+    {
+      const float* ws = a.s13 + (size_t)(e * NB + nb) * nH * 2;
+      for (int i = tid; i < 2 * nH; i += kThreads) ws_lds[i] = ws[i];
+    }
+    __syncthreads();
+    for (int i = tid; i < BM * nH; i += kThreads) {
+      const int r = i / nH, kb = i - r * nH;
+      sxt[r][kb] = a.sx[(size_t)tok_lds[r] * nH + kb];
+    }
+    __syncthreads();
+
+    const rsrc_t wr = make_rsrc(a.w13 + (size_t)(e * NB + nb) * nH * kGateUpChunk, (uint32_t)(nH * kGateUpChunk));
+    const uint32_t avo = (uint32_t)(tok_lds[col] * H + grp * 32);
+    i32x8 A[D], B[D][4];
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Block kb's operands; kb >= nH reads out of range (zeros, no memory access).
+    auto load = [&](int kb, i32x8& af, i32x8(&bf)[4]) {
+      const bool in = kb < nH;
+      const uint32_t oob = in ? 0u : 0x80000000u;
+      const uint32_t so = in ? (uint32_t)(kb * kGateUpChunk) : 0u;
+      const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
+      af = cat(bload16(xr, avo + oob, sa), bload16(xr, avo + oob, sa + 16));
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        bf[t] = cat(wload16(wr, bvoff + oob, so + t * 2048), wload16(wr, bvoff + oob, so + t * 2048 + 1024));
+    };
+    auto compute = [&](int kb, const i32x8& af, const i32x8(&bf)[4]) {
+      f32x4 p[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) p[t] = mfma_e4m3(af, bf[t]);
+      const float wsg = ws_lds[2 * kb], wsu = ws_lds[2 * kb + 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float rs = sxt[grp * 4 + i][kb];
+        const float sg = rs * wsg, su = rs * wsu;
+        acc[0][i] = __builtin_fmaf(p[0][i], sg, acc[0][i]);
+        acc[1][i] = __builtin_fmaf(p[1][i], sg, acc[1][i]);
+        acc[2][i] = __builtin_fmaf(p[2][i], su, acc[2][i]);
+        acc[3][i] = __builtin_fmaf(p[3][i], su, acc[3][i]);
+      }
+    };
+
+#pragma unroll
+    for (int s = 0; s < D - 1; ++s) load(s, A[s], B[s]);
+    for (int kb0 = 0; kb0 < nH; kb0 += D) {
+#pragma unroll
+      for (int s = 0; s < D; ++s) {
+        load(kb0 + s + D - 1, A[(s + D - 1) % D], B[(s + D - 1) % D]);
+        if (kb0 + s < nH) compute(kb0 + s, A[s], B[s]);
+      }
+    }
+
+    // epilogue: h = silu(gate) * up, per-row amax over the 128 columns, E4M3
+    if (a.gu_dbg) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = grp * 4 + i;
+        if (r < rows) {
+          float* g = a.gu_dbg + (size_t)(p0 + r) * 2 * Ip + nb * kBlock + wave * 32 + col;
+          g[0] = acc[0][i];
+          g[16] = acc[1][i];
+          g[Ip] = acc[2][i];
+          g[Ip + 16] = acc[3][i];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[0][i] = silu_mul(acc[0][i], acc[2][i]);
+      acc[1][i] = silu_mul(acc[1][i], acc[3][i]);
+      const uint32_t mb = max16(umax(abs_bits(acc[0][i]), abs_bits(acc[1][i])));
+      if (col == 0) red_lds[wave][grp * 4 + i] = mb;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = grp * 4 + i;
+      const uint32_t mb = umax(umax(red_lds[0][r], red_lds[1][r]), umax(red_lds[2][r], red_lds[3][r]));
+      const float amax = __uint_as_float(mb);
+      const float sc = __fdiv_rn(amax, 448.0f);
+      uint32_t c0 = 0, c1 = 0;
+      if (amax != 0.0f) {
+        c0 = to_e4m3(__fdiv_rn(acc[0][i], sc));
+        c1 = to_e4m3(__fdiv_rn(acc[1][i], sc));
+      }
+      h_lds[r * 128 + wave * 32 + col] = (uint8_t)c0;
+      h_lds[r * 128 + wave * 32 + 16 + col] = (uint8_t)c1;
+      if (wave == 0 && col == 0) sh_lds[r] = sc;
+    }
+    __syncthreads();
+    if ((tid >> 3) < rows)
+      st16(a.hq + (size_t)(p0 + (tid >> 3)) * Ip + nb * kBlock + (tid & 7) * 16,
+           ld16(&h_lds[(tid >> 3) * 128 + (tid & 7) * 16]));
+    if (tid < rows) a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
+  }
+}
+
 hipError_t launch_gate_up(const GateUpArgs& a, bool big, int grid, hipStream_t s) {
   if (big)
     hipLaunchKernelGGL(gate_up_kernel<kBigRows / 16>, dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(gate_up_kernel<1>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(gate_up_stream_kernel<kStreamDepth>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -603,11 +739,93 @@ __global__ __launch_bounds__(kThreads, (MT == 1 ? 4 : 2)) void down_kernel(DownA
   }
 }
 
+// Streaming down for experts with at most 16 rows; structure as
+// gate_up_stream_kernel (no LDS tile, no barrier in the K loop, D blocks of
+// prefetch), arithmetic as down_kernel.
+template <int D>
+__global__ __launch_bounds__(kThreads, 4) void down_stream_kernel(DownArgs a) {
+  constexpr int BM = kSmallRows;
+  __shared__ float sht[BM][kMaxKBlocks];
+  __shared__ float ws_lds[kMaxKBlocks];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int H = a.H, Ip = a.Ip, nI = Ip / kBlock, NB = H / kBlock;
+  const int n_items = a.n_tiles[0] * NB;
+  const rsrc_t hr = make_rsrc(a.hq, (uint32_t)a.hq_bytes);
+  const uint32_t bvoff = (uint32_t)(wave * 4096 + lane * 16);
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int tile = item / NB, nb = item - tile * NB;
+    const Tile td = a.tiles[tile];
+    const int e = td.e, p0 = td.p0, rows = td.rows;
+
+    __syncthreads();  // LDS of the previous item is no longer read
+    {
+      const float* ws = a.s2 + (size_t)(e * NB + nb) * nI;
+      for (int i = tid; i < nI; i += kThreads) ws_lds[i] = ws[i];
+      for (int i = tid; i < BM * nI; i += kThreads) {
+        const int r = i / nI, kb = i - r * nI;
+        sht[r][kb] = a.sh[(size_t)(p0 + (r < rows ? r : 0)) * nI + kb];
+      }
+    }
+    __syncthreads();
+
+    const rsrc_t wr = make_rsrc(a.w2 + (size_t)(e * NB + nb) * nI * kDownChunk, (uint32_t)(nI * kDownChunk));
+    const uint32_t avo = (uint32_t)((p0 + (col < rows ? col : 0)) * Ip + grp * 32);
+    i32x8 A[D], B[D][2];
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+
+    // block kb's operands; kb >= nI reads out of range (zeros, no memory access)
+    auto load = [&](int kb, i32x8& af, i32x8(&bf)[2]) {
+      const bool in = kb < nI;
+      const uint32_t oob = in ? 0u : 0x80000000u;
+      const uint32_t so = in ? (uint32_t)(kb * kDownChunk) : 0u;
+      const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
+      af = cat(bload16(hr, avo + oob, sa), bload16(hr, avo + oob, sa + 16));
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        bf[t] = cat(wload16(wr, bvoff + oob, so + t * 2048), wload16(wr, bvoff + oob, so + t * 2048 + 1024));
+    };
+    auto compute = [&](int kb, const i32x8& af, const i32x8(&bf)[2]) {
+      const f32x4 q0 = mfma_e4m3(af, bf[0]);
+      const f32x4 q1 = mfma_e4m3(af, bf[1]);
+      const float wsc = ws_lds[kb];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = sht[grp * 4 + i][kb] * wsc;
+        acc[0][i] = __builtin_fmaf(q0[i], sc, acc[0][i]);
+        acc[1][i] = __builtin_fmaf(q1[i], sc, acc[1][i]);
+      }
+    };
+
+#pragma unroll
+    for (int s = 0; s < D - 1; ++s) load(s, A[s], B[s]);
+    for (int kb0 = 0; kb0 < nI; kb0 += D) {
+#pragma unroll
+      for (int s = 0; s < D; ++s) {
+        load(kb0 + s + D - 1, A[(s + D - 1) % D], B[(s + D - 1) % D]);
+        if (kb0 + s < nI) compute(kb0 + s, A[s], B[s]);
+      }
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = grp * 4 + i;
+      if (r < rows) {
+        float* dst = a.y + (size_t)(p0 + r) * H + nb * kBlock + wave * 32 + col;
+        dst[0] = acc[0][i];
+        dst[16] = acc[1][i];
+      }
+    }
+  }
+}
+
 hipError_t launch_down(const DownArgs& a, bool big, int grid, hipStream_t s) {
   if (big)
     hipLaunchKernelGGL(down_kernel<kBigRows / 16>, dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(down_kernel<1>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(down_stream_kernel<kStreamDepthDown>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -624,7 +842,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     wt[j] = a.w[(size_t)t * k + j];
   }
   __syncthreads();
-  for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
+  for (int c = (blockIdx.y * 256 + threadIdx.x) * 4; c < H; c += gridDim.y * 256 * 4) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       const int p = pos[j];
@@ -651,7 +869,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(a.T, (a.H + 1023) / 1024), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
