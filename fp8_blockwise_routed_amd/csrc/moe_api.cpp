@@ -218,7 +218,7 @@ int upload_weights(moe_fp8_prefill* h, hipStream_t s) {
 // Grid of a persistent GEMM launch: enough resident workgroups to fill the
 // chip, never more than the largest possible number of work items.
 int gemm_grid(const moe_fp8_prefill* h, int64_t max_items, bool big, bool gate_up) {
-  const int64_t per_cu = big ? 2 : (gate_up ? kGateUpWgPerCu : kDownWgPerCu);
+  const int64_t per_cu = big ? 1 : (gate_up ? kGateUpWgPerCu : kDownWgPerCu);
   return (int)std::max<int64_t>(1, std::min<int64_t>(max_items, h->num_cus * per_cu));
 }
 
@@ -427,7 +427,7 @@ int moe_fp8_prefill_run(moe_fp8_prefill* h, const void* x, const int32_t* ids, c
     if (h->timing && hipEventRecord(ev.ev[4], s) != hipSuccess) return fail(h);
 
     g_small = gemm_grid(h, m.E * nb_dn, false, false);
-    g_big = gemm_grid(h, (P / kSmallRows + m.E) * nb_dn, true, false);
+    g_big = gemm_grid(h, (P / kSmallRows + m.E) * ((nb_dn + 1) / 2), true, false);
     DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2, h->small_tiles, h->n_tiles, h->y};
     if (launch_down(da, false, g_small, s) != hipSuccess) return fail(h);
     if (h->timing && hipEventRecord(ev.ev[5], s) != hipSuccess) return fail(h);

@@ -11,7 +11,7 @@ constexpr int kBlock = 128;          // weight block edge and activation group
 constexpr int kWaves = 4;            // waves per GEMM workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSmallRows = 16;       // experts with <= this many rows use the 1-subtile GEMM
-constexpr int kBigRows = 64;         // rows per tile of the multi-subtile GEMM
+constexpr int kBigRows = 256;        // rows per tile of the large-expert GEMMs
 #ifndef MOE_STREAM_DEPTH
 #define MOE_STREAM_DEPTH 3
 #endif
@@ -39,9 +39,10 @@ constexpr int kMaxKBlocks = 128;     // H/128 and Ip/128 limit (LDS-staged weigh
 constexpr int kGateUpChunk = kWaves * 4 * 2048;  // gate 128 rows + up 128 rows
 constexpr int kDownChunk = kWaves * 2 * 2048;    // 128 rows of down
 
-// A GEMM work tile: rows [p0, p0+rows) of the sorted slot order, all of expert e.
+// A GEMM work tile: rows [p0, p0+rows) of the sorted slot order, all of
+// expert e, whose large-expert tiles are first .. first+count-1.
 struct Tile {
-  int32_t e, p0, rows, pad;
+  int32_t e, p0, rows, first, count, pad0, pad1, pad2;
 };
 
 struct PlanArgs {

@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -153,14 +155,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.counts[tid] = n;
     a.offsets[tid] = off;
     cursor[tid] = off;
-    if (is_small) a.small_tiles[small_at] = Tile{tid, off, n, 0};
+    if (is_small) a.small_tiles[small_at] = Tile{tid, off, n, small_at, 1, 0, 0, 0};
     if (n_big) {
       // split n rows into n_big tiles of near-equal size, multiples of 16 rows
       const int per = ((n + n_big - 1) / n_big + 15) & ~15;
       for (int i = 0; i < n_big; ++i) {
         const int r0 = i * per;
         const int r = (n - r0) < per ? (n - r0) : per;
-        a.big_tiles[big_at + i] = Tile{tid, off + r0, r, 0};
+        a.big_tiles[big_at + i] = Tile{tid, off + r0, r, big_at, n_big, 0, 0, 0};
       }
     }
   }
@@ -288,191 +290,271 @@ __device__ __forceinline__ i32x8 a_frag(const uint8_t* lds, int m, int lane) {
 }
 
 // ----------------------------------------------------------------- gate_up --
-// Workgroup tile: up to 16*MT rows of one expert x (128 gate + 128 up)
-// columns of one 128-row block nb, so the epilogue sees one whole 128-wide
-// group of h.  Wave w owns gate columns 32w..32w+31 and the same up columns
-// (tiles 0,1 = gate, 2,3 = up).  Weights stream straight from HBM into MFMA
-// operand registers (pre-swizzled at create time: 2 KB per 16x128 tile, lane
-// l's 32 bytes split into two 1 KB halves); activation rows are gathered
-// through the plan's permutation into LDS.
+// Large-expert gate_up: a 512-thread workgroup computes a tile of up to 256
+// rows of one expert x (128 gate + 128 up) columns of one 128-row block nb,
+// so the epilogue sees one whole 128-wide group of h.  Eight waves in 4 (rows)
+// x 2 (columns): wave (wm, wn) owns rows 64wm..64wm+63 and gate / up columns
+// 64wn..64wn+63 (4 gate + 4 up n-tiles), 32 accumulator tiles.  Operands go
+// to LDS by buffer-load-to-LDS (no staging registers), double-buffered per K
+// block: the activation rows gathered through the plan's permutation (each
+// lane fetches the 16-byte chunk that lands in its XOR-swizzled slot) and the
+// 32 KiB weight chunk, already in fragment order, copied linearly.
 
-template <int MT>
-__global__ __launch_bounds__(kThreads, (MT == 1 ? 4 : 2)) void gate_up_kernel(GateUpArgs a) {
-  constexpr int BM = 16 * MT;
-  constexpr int APASS = (BM + 31) / 32;  // 16-byte activation loads per thread
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][BM * 128];
-  __shared__ float sx_lds[2][BM];
-  __shared__ int tok_lds[BM];
-  __shared__ uint32_t red_lds[kWaves][BM];
-  __shared__ __attribute__((aligned(16))) uint8_t h_lds[BM * 128];
-  __shared__ float sh_lds[BM];
+constexpr int kTileThreads = 512;
+constexpr int kTileRows = kBigRows;  // 256
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One wave instruction: each lane loads `bytes` (4 or 16) from r at
+// voff + soff and the wave writes them contiguously at lds_base.
+template <int AUX>
+__device__ __forceinline__ void dma16(rsrc_t r, uint8_t* lds_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, soff, 0, AUX);
+}
+__device__ __forceinline__ void dma4(rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 4, voff, soff, 0, 0);
+}
+
+// K-loop barrier of the LDS-DMA ring.  The compiler lowers __syncthreads()
+// after waiting for every LDS-DMA load the wave has in flight, which would
+// drain the ring each K step; this barrier leaves them in flight.  Callers
+// first wait (vmcnt) for the loads of the stage the other waves read next,
+// and for their own LDS reads (lgkmcnt) of the stage the next DMA reuses.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Work-item order of the large-expert GEMMs.  The items (tile, weight block)
+// of one expert are visited in blocks of kItemTiles row tiles x kItemBlocks
+// weight blocks, and each run of 32 consecutive items goes to the 32 CUs of
+// one XCD, so the workgroups running side by side on an XCD share each weight
+// chunk ~4 ways and each activation tile ~8 ways in that XCD's L2.
+// Item i: the tile at position i / NB in tile-major order has the same
+// expert, whose items start at first * NB.
+constexpr int kItemTiles = 4, kItemBlocks = 8, kXcds = 8;
+
+struct Item {
+  int e, p0, rows, nb;
+};
+
+// All fields are workgroup-uniform; readfirstlane keeps them in SGPRs so the
+// buffer descriptors built from them stay scalar.
+__device__ __forceinline__ Item item_of(int i, int NB, const Tile* tiles) {
+  const int tg = i / NB;
+  const int first = __builtin_amdgcn_readfirstlane(tiles[tg].first);
+  const int me = __builtin_amdgcn_readfirstlane(tiles[tg].count);
+  const int li = i - first * NB;
+  const int full = NB / kItemBlocks;
+  int nbb = li / (me * kItemBlocks), rem, nbs;
+  if (nbb < full) {
+    rem = li - nbb * me * kItemBlocks;
+    nbs = kItemBlocks;
+  } else {
+    nbb = full;
+    rem = li - full * me * kItemBlocks;
+    nbs = NB - full * kItemBlocks;
+  }
+  const int per_mb = kItemTiles * nbs;
+  const int mb = rem / per_mb;
+  const int r2 = rem - mb * per_mb;
+  const int m_in = r2 / nbs;
+  const Tile* t = tiles + first + mb * kItemTiles + m_in;
+  Item it;
+  it.e = __builtin_amdgcn_readfirstlane(t->e);
+  it.p0 = __builtin_amdgcn_readfirstlane(t->p0);
+  it.rows = __builtin_amdgcn_readfirstlane(t->rows);
+  it.nb = __builtin_amdgcn_readfirstlane(nbb * kItemBlocks + (r2 - m_in * nbs));
+  return it;
+}
+
+// r-th item of this workgroup: consecutive 32-item runs per XCD when the grid
+// is a multiple of the XCD count (workgroups are dealt to XCDs round-robin)
+__device__ __forceinline__ int item_index(int r) {
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  if (G % kXcds) return b + r * G;
+  const int slots = G / kXcds;
+  return (r * kXcds + b % kXcds) * slots + b / kXcds;
+}
+
+__global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArgs a) {
+  constexpr int BM = kTileRows;
+  constexpr int NS = 3;  // activation stages in LDS (2 K blocks ahead)
+  constexpr int DB = 3;  // weight register stages (2 K blocks ahead)
+  // one LDS object per stage, indexed only by compile-time stage numbers, so
+  // the compiler can tell a DMA into one stage from reads of another and does
+  // not make the MFMA reads wait for the DMAs just issued
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds2[BM * 128];
+  __shared__ __attribute__((aligned(256))) float sx_lds0[BM];
+  __shared__ __attribute__((aligned(256))) float sx_lds1[BM];
+  __shared__ __attribute__((aligned(256))) float sx_lds2[BM];
   __shared__ float ws_lds[2 * kMaxKBlocks];
+  __shared__ int tok_lds[BM];
+  __shared__ uint32_t red_lds[kTileThreads / 64][BM];
+  __shared__ float sh_lds[BM];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: keep it (and all that derives from it) scalar
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int H = a.H, Ip = a.Ip, nH = H / kBlock, NB = Ip / kBlock;
   const int n_items = a.n_tiles[0] * NB;
-  const int arow = tid >> 3, achunk = tid & 7;
   const rsrc_t xr = make_rsrc(a.xq, (uint32_t)a.xq_bytes);
   const rsrc_t sr = make_rsrc(a.sx, (uint32_t)a.sx_bytes);
-  const uint32_t bvoff = (uint32_t)(wave * 8192 + lane * 16);
+  // wave w owns gate and up columns 16w..16w+15 of the block: 32-column
+  // group w/2, tiles (w&1) and 2 + (w&1) of the swizzled chunk
+  const uint32_t bg_off = (uint32_t)((((wave >> 1) * 4 + (wave & 1)) * 2) * 1024 + lane * 16);
+  const uint32_t bu_off = bg_off + 4 * 1024;
+  const int afr = (lane & 15) * 128;
+  const int afc0 = ((2 * grp) ^ (lane & 7)) << 4, afc1 = ((2 * grp + 1) ^ (lane & 7)) << 4;
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int tile = item / NB, nb = item - tile * NB;
-    const Tile td = a.tiles[tile];
-    const int e = td.e, p0 = td.p0, rows = td.rows;
-    const int mt = (rows + 15) >> 4;
-    const int mrows = mt * 16;
+  for (int r = 0;; ++r) {
+    const int item = item_index(r);
+    if (item >= n_items) break;
+    const Item it = item_of(item, NB, a.tiles);
+    const int e = it.e, p0 = it.p0, rows = it.rows, nb = it.nb;
+    const int mt = (rows + 15) >> 4;  // 16-row subtiles holding rows (uniform)
 
     __syncthreads();  // LDS of the previous item is no longer read
     if (tid < BM) tok_lds[tid] = a.perm[p0 + (tid < rows ? tid : 0)] / a.k;
     {
       const float* ws = a.s13 + (size_t)(e * NB + nb) * nH * 2;
-      for (int i = tid; i < 2 * nH; i += kThreads) ws_lds[i] = ws[i];
+      for (int i = tid; i < 2 * nH; i += kTileThreads) ws_lds[i] = ws[i];
     }
     __syncthreads();
 
     const rsrc_t wr = make_rsrc(a.w13 + (size_t)(e * NB + nb) * nH * kGateUpChunk, (uint32_t)(nH * kGateUpChunk));
-    uint32_t avoff[APASS];
+    // activation DMA: instruction q of wave w fills LDS bytes [(8q + w) * 1024,
+    // +1024) = rows 8(8q + w) .. +8; rows past the tile read out of range
+    uint32_t avo[4];
 #pragma unroll
-    for (int p = 0; p < APASS; ++p) {
-      const int r = arow + 32 * p;
-      avoff[p] = r < mrows ? (uint32_t)(tok_lds[r] * H + achunk * 16) : 0u;
+    for (int q = 0; q < 4; ++q) {
+      const int row = (q * 8 + wave) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ (row & 7);
+      avo[q] = (uint32_t)(tok_lds[row] * H + c * 16) + ((q * 8 + wave) * 8 < mt * 16 ? 0u : 0x80000000u);
     }
-    const uint32_t svoff = tid < mrows ? (uint32_t)(tok_lds[tid] * nH * 4) : 0u;
+    const uint32_t svo = wave < 4 ? (uint32_t)(tok_lds[wave * 64 + lane] * nH * 4) : 0u;
 
-    i32x4 areg[APASS];
-    float sreg = 0.f;
-    i32x8 b0[4], b1[4];
-    f32x4 acc[MT][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto load_a = [&](int kb) {
-#pragma unroll
-      for (int p = 0; p < APASS; ++p)
-        if (arow + 32 * p < mrows) areg[p] = bload16(xr, avoff[p], (uint32_t)(kb * kBlock));
-      if (tid < mrows) sreg = bloadf(sr, svoff, (uint32_t)(kb * 4));
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-      for (int p = 0; p < APASS; ++p) {
-        const int r = arow + 32 * p;
-        if (r < mrows) st16(&a_lds[buf][a_off(r, achunk)], areg[p]);
-      }
-      if (tid < mrows) sx_lds[buf][tid] = sreg;
-    };
-    // kb == nH is the prefetch past the last block: a lane offset of 2^31 is
-    // beyond the buffer range whichever offsets the range check includes, so
-    // the loads return zeros without touching memory.
-    auto load_b = [&](int kb, i32x8* b) {
+    // every stage issues the same loads (out of range past the end), so the
+    // wait count below is exact: 4 activation DMAs (+1 scale DMA on waves
+    // 0-3), then 4 weight loads
+    // K block kb goes to stage kb % NS; every stage issues the same loads (out
+    // of range past the end), so the wait count below is exact: 4 activation
+    // DMAs (+1 scale DMA on waves 0-3), then 4 weight loads
+    auto issue = [&](auto ST, int kb, i32x8& bg, i32x8& bu) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value;
+      uint8_t* al = st == 0 ? a_lds0 : st == 1 ? a_lds1 : a_lds2;
+      float* sl = st == 0 ? sx_lds0 : st == 1 ? sx_lds1 : sx_lds2;
       const bool in = kb < nH;
-      const uint32_t vo = bvoff + (in ? 0u : 0x80000000u);
+      const uint32_t oob = in ? 0u : 0x80000000u;
+      const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dma16<0>(xr, al + (q * 8 + wave) * 1024, avo[q] + oob, sa);
+      if (wave < 4) dma4(sr, sl + wave * 64, svo + oob, in ? (uint32_t)(kb * 4) : 0u);
       const uint32_t so = in ? (uint32_t)(kb * kGateUpChunk) : 0u;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        b[t] = cat(bload16(wr, vo, so + t * 2048), bload16(wr, vo, so + t * 2048 + 1024));
-    };
-    // one K block: prefetch block kb+1 (activations to registers, weights to
-    // `nxt`), multiply block kb from LDS and `cur`, then publish kb+1.  The
-    // prefetch is unconditional so the wait counts stay static: past the last
-    // block the weight read is out of range (zeros, no memory access) and the
-    // activation read repeats the last block.
-    auto step = [&](int kb, i32x8(&cur)[4], i32x8(&nxt)[4]) {
-      const int buf = kb & 1;
-      load_a(kb + 1 < nH ? kb + 1 : kb);
-      load_b(kb + 1, nxt);
-      const float wsg = ws_lds[2 * kb], wsu = ws_lds[2 * kb + 1];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < mt) {
-          const i32x8 af = a_frag(a_lds[buf], m, lane);
-          f32x4 p[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) p[t] = mfma_e4m3(af, cur[t]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float rs = sx_lds[buf][m * 16 + grp * 4 + i];
-            const float sg = rs * wsg, su = rs * wsu;
-            acc[m][0][i] = __builtin_fmaf(p[0][i], sg, acc[m][0][i]);
-            acc[m][1][i] = __builtin_fmaf(p[1][i], sg, acc[m][1][i]);
-            acc[m][2][i] = __builtin_fmaf(p[2][i], su, acc[m][2][i]);
-            acc[m][3][i] = __builtin_fmaf(p[3][i], su, acc[m][3][i]);
-          }
-        }
-      }
-      store_a(buf ^ 1);
-      __syncthreads();
+      bg = cat(wload16(wr, bg_off + oob, so), wload16(wr, bg_off + oob, so + 1024));
+      bu = cat(wload16(wr, bu_off + oob, so), wload16(wr, bu_off + oob, so + 1024));
     };
 
-    load_a(0);
-    load_b(0, b0);
-    store_a(0);
-    __syncthreads();
-    for (int kb = 0; kb < nH; kb += 2) {
-      step(kb, b0, b1);
-      if (kb + 1 < nH) step(kb + 1, b1, b0);
-    }
+    f32x4 acc[16][2];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    i32x8 BG[DB], BU[DB];
 
-    // inspection hook: FP32 gate and up before the epilogue (null in normal use)
-    if (a.gu_dbg) {
+    // one K block: issue block kb + 2 into the stage freed last step, multiply
+    // block kb out of stage s, then wait for block kb + 1
+    auto step = [&](auto S, int kb0) __attribute__((always_inline)) {
+      constexpr int s = decltype(S)::value;
+      const int kb = kb0 + s;
+      issue(std::integral_constant<int, (s + 2) % NS>{}, kb + 2, BG[(s + 2) % DB], BU[(s + 2) % DB]);
+      if (kb < nH) {
+        const float wsg = ws_lds[2 * kb], wsu = ws_lds[2 * kb + 1];
+        const uint8_t* abuf = (s == 0 ? a_lds0 : s == 1 ? a_lds1 : a_lds2) + afr;
+        const float* srow = (s == 0 ? sx_lds0 : s == 1 ? sx_lds1 : sx_lds2) + grp * 4;
+        // A fragments one subtile ahead; the scheduling barriers keep the
+        // compiler from hoisting all sixteen (128 VGPRs) over the MFMAs
+        i32x8 an = cat(ld16(abuf + afc0), ld16(abuf + afc1));
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < mt) {
+        for (int m = 0; m < 16; ++m) {
+          if (m < mt) {
+            const i32x8 af = an;
+            if (m + 1 < mt) an = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
+            const f32x4 pg = mfma_e4m3(af, BG[s]);
+            const f32x4 pu = mfma_e4m3(af, BU[s]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = m * 16 + grp * 4 + i;
-            if (r < rows) {
-              float* g = a.gu_dbg + (size_t)(p0 + r) * 2 * Ip + nb * kBlock + wave * 32 + col;
-              g[0] = acc[m][0][i];
-              g[16] = acc[m][1][i];
-              g[Ip] = acc[m][2][i];
-              g[Ip + 16] = acc[m][3][i];
+            for (int i = 0; i < 4; ++i) {
+              const float rs = srow[m * 16 + i];
+              acc[m][0][i] = __builtin_fmaf(pg[i], rs * wsg, acc[m][0][i]);
+              acc[m][1][i] = __builtin_fmaf(pu[i], rs * wsu, acc[m][1][i]);
             }
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-    }
+      __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): block kb + 1 has landed
+      ring_barrier();
+    };
 
-    // epilogue: h = silu(gate) * up; amax per row over the 128 columns
+    issue(std::integral_constant<int, 0>{}, 0, BG[0], BU[0]);
+    issue(std::integral_constant<int, 1>{}, 1, BG[1], BU[1]);
+    __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): block 0 has landed
+    ring_barrier();
+    static_assert(NS == 3 && DB == 3, "the K loop is unrolled by the stage count");
+    for (int kb0 = 0; kb0 < nH; kb0 += NS) {
+      step(std::integral_constant<int, 0>{}, kb0);
+      step(std::integral_constant<int, 1>{}, kb0);
+      step(std::integral_constant<int, 2>{}, kb0);
+    }
+    // the out-of-range loads issued past the last block still write zeros
+    // to their stages: let them land before the LDS is reused
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+
+    // epilogue (activation stage 0 is free now: it becomes the h staging tile)
+    uint8_t* h_lds = a_lds0;
+    if (a.gu_dbg) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
+      for (int m = 0; m < 16; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = m * 16 + grp * 4 + i;
+          if (m < mt && row < rows) {
+            float* g = a.gu_dbg + (size_t)(p0 + row) * 2 * Ip + nb * kBlock + wave * 16 + col;
+            g[0] = acc[m][0][i];
+            g[Ip] = acc[m][1][i];
+          }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
       if (m < mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[m][0][i] = silu_mul(acc[m][0][i], acc[m][2][i]);
-          acc[m][1][i] = silu_mul(acc[m][1][i], acc[m][3][i]);
-          const uint32_t mb = max16(umax(abs_bits(acc[m][0][i]), abs_bits(acc[m][1][i])));
+          acc[m][0][i] = silu_mul(acc[m][0][i], acc[m][1][i]);
+          const uint32_t mb = max16(abs_bits(acc[m][0][i]));
           if (col == 0) red_lds[wave][m * 16 + grp * 4 + i] = mb;
         }
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
+    for (int m = 0; m < 16; ++m) {
       if (m < mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = m * 16 + grp * 4 + i;
-          const uint32_t mb = umax(umax(red_lds[0][r], red_lds[1][r]), umax(red_lds[2][r], red_lds[3][r]));
+          const int row = m * 16 + grp * 4 + i;
+          uint32_t mb = 0;
+#pragma unroll
+          for (int w = 0; w < kTileThreads / 64; ++w) mb = umax(mb, red_lds[w][row]);
           const float amax = __uint_as_float(mb);
-          const float s = __fdiv_rn(amax, 448.0f);
-          uint32_t c0 = 0, c1 = 0;
-          if (amax != 0.0f) {
-            c0 = to_e4m3(__fdiv_rn(acc[m][0][i], s));
-            c1 = to_e4m3(__fdiv_rn(acc[m][1][i], s));
-          }
-          h_lds[r * 128 + wave * 32 + col] = (uint8_t)c0;
-          h_lds[r * 128 + wave * 32 + 16 + col] = (uint8_t)c1;
-          if (wave == 0 && col == 0) sh_lds[r] = s;
+          const float sc = __fdiv_rn(amax, 448.0f);
+          const uint32_t c = amax != 0.0f ? to_e4m3(__fdiv_rn(acc[m][0][i], sc)) : 0u;
+          h_lds[row * 128 + wave * 16 + col] = (uint8_t)c;
+          if (wave == 0 && col == 0) sh_lds[row] = sc;
         }
       }
     }
     __syncthreads();
-    for (int r = arow; r < rows; r += 32)
-      st16(a.hq + (size_t)(p0 + r) * Ip + nb * kBlock + achunk * 16, ld16(&h_lds[r * 128 + achunk * 16]));
+    for (int row = tid >> 3; row < rows; row += kTileThreads / 8)
+      st16(a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + (tid & 7) * 16, ld16(&h_lds[row * 128 + (tid & 7) * 16]));
     if (tid < rows) a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
   }
 }
@@ -611,125 +693,152 @@ __global__ __launch_bounds__(kThreads, D <= 2 ? 4 : 3) void gate_up_stream_kerne
 
 hipError_t launch_gate_up(const GateUpArgs& a, bool big, int grid, hipStream_t s) {
   if (big)
-    hipLaunchKernelGGL(gate_up_kernel<kBigRows / 16>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(gate_up_tile_kernel, dim3(grid), dim3(kTileThreads), 0, s, a);
   else
     hipLaunchKernelGGL(gate_up_stream_kernel<kStreamDepth>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 // -------------------------------------------------------------------- down --
-// Workgroup tile: up to 16*MT rows of one expert x 128 hidden columns (one
-// weight block row); wave w owns columns 32w..32w+31 (two 16-column tiles).
+// Large-expert down: a 512-thread workgroup computes up to 256 rows x 256
+// hidden columns (weight blocks nb2, nb2+1).  As in gate_up_tile_kernel, each
+// wave owns 32 columns for all rows (block nb2 + w/4, 32-column group w%4):
+// its weight fragments stream into registers 2 K blocks ahead and the shared
+// h rows arrive in a 3-stage LDS ring by buffer-load-to-LDS.
 
-template <int MT>
-__global__ __launch_bounds__(kThreads, (MT == 1 ? 4 : 2)) void down_kernel(DownArgs a) {
-  constexpr int BM = 16 * MT;
-  constexpr int APASS = (BM + 31) / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][BM * 128];
-  __shared__ float s_lds[2][BM];
-  __shared__ float ws_lds[kMaxKBlocks];
+__global__ __launch_bounds__(kTileThreads, 1) void down_tile_kernel(DownArgs a) {
+  constexpr int BM = kTileRows;
+  constexpr int NS = 3, DB = 3;
+  // one LDS object per stage (see gate_up_tile_kernel)
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds2[BM * 128];
+  __shared__ __attribute__((aligned(256))) float s_lds0[BM];
+  __shared__ __attribute__((aligned(256))) float s_lds1[BM];
+  __shared__ __attribute__((aligned(256))) float s_lds2[BM];
+  __shared__ float ws_lds[2][kMaxKBlocks];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int H = a.H, Ip = a.Ip, nI = Ip / kBlock, NB = H / kBlock;
-  const int n_items = a.n_tiles[0] * NB;
-  const int arow = tid >> 3, achunk = tid & 7;
+  const int NB2 = (NB + 1) >> 1;
+  const int n_items = a.n_tiles[0] * NB2;
   const rsrc_t hr = make_rsrc(a.hq, (uint32_t)a.hq_bytes);
   const rsrc_t sr = make_rsrc(a.sh, (uint32_t)a.sh_bytes);
-  const uint32_t bvoff = (uint32_t)(wave * 4096 + lane * 16);
+  const int half = wave >> 2;  // which of the two weight blocks
+  const uint32_t b0_off = (uint32_t)((((wave & 3) * 2) * 2) * 1024 + lane * 16);
+  const uint32_t b1_off = b0_off + 2 * 1024;
+  const int afr = (lane & 15) * 128;
+  const int afc0 = ((2 * grp) ^ (lane & 7)) << 4, afc1 = ((2 * grp + 1) ^ (lane & 7)) << 4;
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int tile = item / NB, nb = item - tile * NB;
-    const Tile td = a.tiles[tile];
-    const int e = td.e, p0 = td.p0, rows = td.rows;
-    const int mt = (rows + 15) >> 4;
-    const int mrows = mt * 16;
-
-    const rsrc_t wr = make_rsrc(a.w2 + (size_t)(e * NB + nb) * nI * kDownChunk, (uint32_t)(nI * kDownChunk));
-    uint32_t avoff[APASS];
-#pragma unroll
-    for (int p = 0; p < APASS; ++p) {
-      const int r = arow + 32 * p;
-      avoff[p] = (uint32_t)((p0 + (r < rows ? r : 0)) * Ip + achunk * 16);
-    }
-    const uint32_t svoff = (uint32_t)((p0 + (tid < rows ? tid : 0)) * nI * 4);
-
-    i32x4 areg[APASS];
-    float sreg = 0.f;
-    i32x8 b0[2], b1[2];
-    f32x4 acc[MT][2];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto load_a = [&](int kb) {
-#pragma unroll
-      for (int p = 0; p < APASS; ++p)
-        if (arow + 32 * p < mrows) areg[p] = bload16(hr, avoff[p], (uint32_t)(kb * kBlock));
-      if (tid < mrows) sreg = bloadf(sr, svoff, (uint32_t)(kb * 4));
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-      for (int p = 0; p < APASS; ++p) {
-        const int r = arow + 32 * p;
-        if (r < mrows) st16(&a_lds[buf][a_off(r, achunk)], areg[p]);
-      }
-      if (tid < mrows) s_lds[buf][tid] = sreg;
-    };
-    auto load_b = [&](int kb, i32x8* b) {  // kb == nI: out of range, zeros
-      const bool in = kb < nI;
-      const uint32_t vo = bvoff + (in ? 0u : 0x80000000u);
-      const uint32_t so = in ? (uint32_t)(kb * kDownChunk) : 0u;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        b[t] = cat(bload16(wr, vo, so + t * 2048), bload16(wr, vo, so + t * 2048 + 1024));
-    };
-    auto step = [&](int kb, i32x8(&cur)[2], i32x8(&nxt)[2]) {
-      const int buf = kb & 1;
-      load_a(kb + 1 < nI ? kb + 1 : kb);
-      load_b(kb + 1, nxt);
-      const float wsc = ws_lds[kb];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < mt) {
-          const i32x8 af = a_frag(a_lds[buf], m, lane);
-          const f32x4 q0 = mfma_e4m3(af, cur[0]);
-          const f32x4 q1 = mfma_e4m3(af, cur[1]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float sc = s_lds[buf][m * 16 + grp * 4 + i] * wsc;
-            acc[m][0][i] = __builtin_fmaf(q0[i], sc, acc[m][0][i]);
-            acc[m][1][i] = __builtin_fmaf(q1[i], sc, acc[m][1][i]);
-          }
-        }
-      }
-      store_a(buf ^ 1);
-      __syncthreads();
-    };
+  for (int r = 0;; ++r) {
+    const int item = item_index(r);
+    if (item >= n_items) break;
+    const Item it = item_of(item, NB2, a.tiles);
+    const int nb2 = it.nb * 2;
+    const bool two = nb2 + 1 < NB;  // second weight block present
+    const int e = it.e, p0 = it.p0, rows = it.rows;
+    const int mt = (half == 1 && !two) ? 0 : (rows + 15) >> 4;
 
     __syncthreads();  // LDS of the previous item is no longer read
     {
-      const float* ws = a.s2 + (size_t)(e * NB + nb) * nI;
-      for (int i = tid; i < nI; i += kThreads) ws_lds[i] = ws[i];
+      const float* ws = a.s2 + (size_t)(e * NB + nb2) * nI;
+      for (int i = tid; i < nI; i += kTileThreads) {
+        ws_lds[0][i] = ws[i];
+        ws_lds[1][i] = two ? ws[nI + i] : 0.f;
+      }
     }
-    load_a(0);
-    load_b(0, b0);
-    store_a(0);
     __syncthreads();
-    for (int kb = 0; kb < nI; kb += 2) {
-      step(kb, b0, b1);
-      if (kb + 1 < nI) step(kb + 1, b1, b0);
+
+    // this wave's weight block: nb2 + half (absent -> out of range)
+    const rsrc_t wr = make_rsrc(a.w2 + (size_t)(e * NB + nb2 + (two ? half : 0)) * nI * kDownChunk,
+                                (uint32_t)(nI * kDownChunk));
+    const uint32_t wmask = (half == 1 && !two) ? 0x80000000u : 0u;
+    const int mrows16 = ((rows + 15) >> 4) * 16;
+    uint32_t avo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = (q * 8 + wave) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ (row & 7);
+      avo[q] = (uint32_t)((p0 + (row < rows ? row : 0)) * Ip + c * 16) +
+               ((q * 8 + wave) * 8 < mrows16 ? 0u : 0x80000000u);
     }
+    const int srow = wave * 64 + lane;
+    const uint32_t svo = (uint32_t)((p0 + (srow < rows ? srow : 0)) * nI * 4);
+
+    auto issue = [&](auto ST, int kb, i32x8& b0, i32x8& b1) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value;
+      uint8_t* al = st == 0 ? a_lds0 : st == 1 ? a_lds1 : a_lds2;
+      float* sl = st == 0 ? s_lds0 : st == 1 ? s_lds1 : s_lds2;
+      const bool in = kb < nI;
+      const uint32_t oob = in ? 0u : 0x80000000u;
+      const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dma16<0>(hr, al + (q * 8 + wave) * 1024, avo[q] + oob, sa);
+      if (wave < 4) dma4(sr, sl + wave * 64, svo + oob, in ? (uint32_t)(kb * 4) : 0u);
+      const uint32_t so = in ? (uint32_t)(kb * kDownChunk) : 0u;
+      b0 = cat(wload16(wr, b0_off + (oob | wmask), so), wload16(wr, b0_off + (oob | wmask), so + 1024));
+      b1 = cat(wload16(wr, b1_off + (oob | wmask), so), wload16(wr, b1_off + (oob | wmask), so + 1024));
+    };
+
+    f32x4 acc[16][2];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    i32x8 B0[DB], B1[DB];
+
+    auto step = [&](auto S, int kb0) __attribute__((always_inline)) {
+      constexpr int s = decltype(S)::value;
+      const int kb = kb0 + s;
+      issue(std::integral_constant<int, (s + 2) % NS>{}, kb + 2, B0[(s + 2) % DB], B1[(s + 2) % DB]);
+      if (kb < nI) {
+        const float wsc = ws_lds[half][kb];
+        const uint8_t* abuf = (s == 0 ? a_lds0 : s == 1 ? a_lds1 : a_lds2) + afr;
+        const float* srw = (s == 0 ? s_lds0 : s == 1 ? s_lds1 : s_lds2) + grp * 4;
+        i32x8 an = cat(ld16(abuf + afc0), ld16(abuf + afc1));
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          if (m < mt) {
+            const i32x8 af = an;
+            if (m + 1 < mt) an = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
+            const f32x4 q0 = mfma_e4m3(af, B0[s]);
+            const f32x4 q1 = mfma_e4m3(af, B1[s]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float sc = srw[m * 16 + i] * wsc;
+              acc[m][0][i] = __builtin_fmaf(q0[i], sc, acc[m][0][i]);
+              acc[m][1][i] = __builtin_fmaf(q1[i], sc, acc[m][1][i]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): block kb + 1 has landed
+      ring_barrier();
+    };
+
+    issue(std::integral_constant<int, 0>{}, 0, B0[0], B1[0]);
+    issue(std::integral_constant<int, 1>{}, 1, B0[1], B1[1]);
+    __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): block 0 has landed
+    ring_barrier();
+    static_assert(NS == 3 && DB == 3, "the K loop is unrolled by the stage count");
+    for (int kb0 = 0; kb0 < nI; kb0 += NS) {
+      step(std::integral_constant<int, 0>{}, kb0);
+      step(std::integral_constant<int, 1>{}, kb0);
+      step(std::integral_constant<int, 2>{}, kb0);
+    }
+    // the out-of-range loads issued past the last block still write zeros
+    // to their stages: let them land before the next item's loads
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
 
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
+    for (int m = 0; m < 16; ++m) {
       if (m < mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = m * 16 + grp * 4 + i;
-          if (r < rows) {
-            float* dst = a.y + (size_t)(p0 + r) * H + nb * kBlock + wave * 32 + col;
+          const int row = m * 16 + grp * 4 + i;
+          if (row < rows) {
+            float* dst = a.y + (size_t)(p0 + row) * H + (nb2 + half) * kBlock + (wave & 3) * 32 + col;
             dst[0] = acc[m][0][i];
             dst[16] = acc[m][1][i];
           }
@@ -823,7 +932,7 @@ __global__ __launch_bounds__(kThreads, 4) void down_stream_kernel(DownArgs a) {
 
 hipError_t launch_down(const DownArgs& a, bool big, int grid, hipStream_t s) {
   if (big)
-    hipLaunchKernelGGL(down_kernel<kBigRows / 16>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(down_tile_kernel, dim3(grid), dim3(kTileThreads), 0, s, a);
   else
     hipLaunchKernelGGL(down_stream_kernel<kStreamDepthDown>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
