@@ -19,6 +19,9 @@ FLAGS = [
     "-ffp-contract=off",
     # never emit packed FP32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the GEMMs promote every MFMA result with VALU
+    # FMAs, which cannot read the accumulation registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

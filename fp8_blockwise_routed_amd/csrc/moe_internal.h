@@ -11,7 +11,7 @@ constexpr int kBlock = 128;          // weight block edge and activation group
 constexpr int kWaves = 4;            // waves per GEMM workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSmallRows = 16;       // experts with <= this many rows use the 1-subtile GEMM
-constexpr int kBigRows = 256;        // rows per tile of the large-expert GEMMs
+constexpr int kBigRows = 128;        // rows per tile of the large-expert GEMMs
 #ifndef MOE_STREAM_DEPTH
 #define MOE_STREAM_DEPTH 3
 #endif

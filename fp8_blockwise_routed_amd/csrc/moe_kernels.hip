@@ -35,6 +35,7 @@ __device__ __forceinline__ i32x4 ld16(const void* p) {
   return *reinterpret_cast<const i32x4*>(p);
 }
 __device__ __forceinline__ void st16(void* p, i32x4 v) { *reinterpret_cast<i32x4*>(p) = v; }
+__device__ __forceinline__ f32x4 ld16f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 __device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -290,18 +291,25 @@ __device__ __forceinline__ i32x8 a_frag(const uint8_t* lds, int m, int lane) {
 }
 
 // ----------------------------------------------------------------- gate_up --
-// Large-expert gate_up: a 512-thread workgroup computes a tile of up to 256
+// Large-expert gate_up: a 256-thread workgroup computes a tile of up to 128
 // rows of one expert x (128 gate + 128 up) columns of one 128-row block nb,
-// so the epilogue sees one whole 128-wide group of h.  Eight waves in 4 (rows)
-// x 2 (columns): wave (wm, wn) owns rows 64wm..64wm+63 and gate / up columns
-// 64wn..64wn+63 (4 gate + 4 up n-tiles), 32 accumulator tiles.  Operands go
-// to LDS by buffer-load-to-LDS (no staging registers), double-buffered per K
-// block: the activation rows gathered through the plan's permutation (each
-// lane fetches the 16-byte chunk that lands in its XOR-swizzled slot) and the
-// 32 KiB weight chunk, already in fragment order, copied linearly.
+// so the epilogue sees one whole 128-wide group of h.  Wave w owns gate and
+// up columns 32w..32w+31 (4 n-tiles) for all rows: each activation fragment
+// it reads from LDS feeds four MFMAs, and its weight fragments (8 KiB per K
+// block) stream into registers one K block ahead.  The activation rows,
+// gathered through the plan's permutation, arrive in a double-buffered LDS
+// tile by buffer-load-to-LDS (each lane fetches the 16-byte chunk that lands
+// in its XOR-swizzled slot).  One wave per SIMD, up to 512 registers each.
+//
+// Block kb + 1 is loaded while block kb is multiplied, and each K step ends
+// by waiting for every load of the wave (vmcnt 0) before the barrier: the
+// completion of buffer-load-to-LDS and of loads into registers is not
+// ordered between the two kinds, so a partial count could pass with some of
+// block kb + 1's DMA still in flight.
 
-constexpr int kTileThreads = 512;
-constexpr int kTileRows = kBigRows;  // 256
+constexpr int kTileThreads = 256;
+constexpr int kTileRows = kBigRows;  // 128
+static_assert(kTileRows == 128, "the big-tile kernels cover 128 rows");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -313,6 +321,36 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint8_t* lds_base, uint32_t voff
 }
 __device__ __forceinline__ void dma4(rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 4, voff, soff, 0, 0);
+}
+
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), in order.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(static_cast<F&&>(f));
+  }
+}
+
+// Scheduling hint for the current basic block: the LDS reads first, then
+// NM times (one MFMA, NV VALU instructions), so the promotion FMAs issue
+// while the MFMAs execute.
+template <int NM, int NV>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+  }
+}
+
+// Empty asm that takes the four accumulator tiles of a subtile as read-write
+// VGPR operands: it emits nothing, but the FMAs that produce them cannot be
+// moved past it, so a subtile's promotion stays beside the next subtile's
+// MFMAs instead of drifting to the end of the K step.
+__device__ __forceinline__ void pin_in_place(f32x4 (&a)[4]) {
+  asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
 }
 
 // K-loop barrier of the LDS-DMA ring.  The compiler lowers __syncthreads()
@@ -376,17 +414,16 @@ __device__ __forceinline__ int item_index(int r) {
 
 __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArgs a) {
   constexpr int BM = kTileRows;
-  constexpr int NS = 3;  // activation stages in LDS (2 K blocks ahead)
-  constexpr int DB = 3;  // weight register stages (2 K blocks ahead)
+  constexpr int NS = 2;  // activation stages in LDS (1 K block ahead)
+  constexpr int DB = 2;  // weight register stages (1 K block ahead)
+  constexpr int MT = BM / 16;
   // one LDS object per stage, indexed only by compile-time stage numbers, so
   // the compiler can tell a DMA into one stage from reads of another and does
   // not make the MFMA reads wait for the DMAs just issued
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[BM * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds1[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t a_lds2[BM * 128];
-  __shared__ __attribute__((aligned(256))) float sx_lds0[BM];
-  __shared__ __attribute__((aligned(256))) float sx_lds1[BM];
-  __shared__ __attribute__((aligned(256))) float sx_lds2[BM];
+  __shared__ __attribute__((aligned(256))) float sx_lds0[2 * BM];
+  __shared__ __attribute__((aligned(256))) float sx_lds1[2 * BM];
   __shared__ float ws_lds[2 * kMaxKBlocks];
   __shared__ int tok_lds[BM];
   __shared__ uint32_t red_lds[kTileThreads / 64][BM];
@@ -400,10 +437,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
   const int n_items = a.n_tiles[0] * NB;
   const rsrc_t xr = make_rsrc(a.xq, (uint32_t)a.xq_bytes);
   const rsrc_t sr = make_rsrc(a.sx, (uint32_t)a.sx_bytes);
-  // wave w owns gate and up columns 16w..16w+15 of the block: 32-column
-  // group w/2, tiles (w&1) and 2 + (w&1) of the swizzled chunk
-  const uint32_t bg_off = (uint32_t)((((wave >> 1) * 4 + (wave & 1)) * 2) * 1024 + lane * 16);
-  const uint32_t bu_off = bg_off + 4 * 1024;
+  // wave w reads n-tiles g0, g1, u0, u1 of 32-column group w of the chunk
+  const uint32_t b_off = (uint32_t)(wave * 4 * 2 * 1024 + lane * 16);
   const int afr = (lane & 15) * 128;
   const int afc0 = ((2 * grp) ^ (lane & 7)) << 4, afc1 = ((2 * grp + 1) ^ (lane & 7)) << 4;
 
@@ -423,86 +458,119 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
     __syncthreads();
 
     const rsrc_t wr = make_rsrc(a.w13 + (size_t)(e * NB + nb) * nH * kGateUpChunk, (uint32_t)(nH * kGateUpChunk));
-    // activation DMA: instruction q of wave w fills LDS bytes [(8q + w) * 1024,
-    // +1024) = rows 8(8q + w) .. +8; rows past the tile read out of range
+    // activation DMA: instruction q of wave w fills LDS bytes [(4q + w) * 1024,
+    // +1024) = rows 8(4q + w) .. +8; rows past the last subtile read out of range
     uint32_t avo[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int row = (q * 8 + wave) * 8 + (lane >> 3);
+      const int row = (q * 4 + wave) * 8 + (lane >> 3);
       const int c = (lane & 7) ^ (row & 7);
-      avo[q] = (uint32_t)(tok_lds[row] * H + c * 16) + ((q * 8 + wave) * 8 < mt * 16 ? 0u : 0x80000000u);
+      avo[q] = (uint32_t)(tok_lds[row] * H + c * 16) + ((q * 4 + wave) * 8 < mt * 16 ? 0u : 0x80000000u);
     }
-    const uint32_t svo = wave < 4 ? (uint32_t)(tok_lds[wave * 64 + lane] * nH * 4) : 0u;
+    const uint32_t svo = wave < 2 ? (uint32_t)(tok_lds[wave * 64 + lane] * nH * 4) : 0x80000000u;
 
-    // every stage issues the same loads (out of range past the end), so the
-    // wait count below is exact: 4 activation DMAs (+1 scale DMA on waves
-    // 0-3), then 4 weight loads
-    // K block kb goes to stage kb % NS; every stage issues the same loads (out
-    // of range past the end), so the wait count below is exact: 4 activation
-    // DMAs (+1 scale DMA on waves 0-3), then 4 weight loads
-    auto issue = [&](auto ST, int kb, i32x8& bg, i32x8& bu) __attribute__((always_inline)) {
-      constexpr int st = decltype(ST)::value;
-      uint8_t* al = st == 0 ? a_lds0 : st == 1 ? a_lds1 : a_lds2;
-      float* sl = st == 0 ? sx_lds0 : st == 1 ? sx_lds1 : sx_lds2;
+    // K block kb goes to stage kb % NS.  Its 13 loads come in 7 parts: the
+    // weight n-tiles (parts 0-3, two loads each), the activation DMAs (parts
+    // 4-5, two each) and the row-scale DMA (part 6; waves 2-3 load out of
+    // range into the unused half of the stage).  Every stage issues all of
+    // them, out of range past the last block, so the wait count is exact.
+    auto issue_part = [&](auto ST, auto PT, int kb, i32x8(&b)[4]) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value, p = decltype(PT)::value;
       const bool in = kb < nH;
       const uint32_t oob = in ? 0u : 0x80000000u;
-      const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
+      if constexpr (p < 4) {
+        const uint32_t so = in ? (uint32_t)(kb * kGateUpChunk) : 0u;
+        b[p] = cat(wload16(wr, b_off | oob, so + p * 2048), wload16(wr, b_off | oob, so + p * 2048 + 1024));
+      } else if constexpr (p < 6) {
+        uint8_t* al = st == 0 ? a_lds0 : a_lds1;
+        const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dma16<0>(xr, al + (q * 8 + wave) * 1024, avo[q] + oob, sa);
-      if (wave < 4) dma4(sr, sl + wave * 64, svo + oob, in ? (uint32_t)(kb * 4) : 0u);
-      const uint32_t so = in ? (uint32_t)(kb * kGateUpChunk) : 0u;
-      bg = cat(wload16(wr, bg_off + oob, so), wload16(wr, bg_off + oob, so + 1024));
-      bu = cat(wload16(wr, bu_off + oob, so), wload16(wr, bu_off + oob, so + 1024));
+        for (int q = 2 * (p - 4); q < 2 * (p - 4) + 2; ++q)
+          dma16<0>(xr, al + (q * 4 + wave) * 1024, avo[q] | oob, sa);
+      } else {
+        float* sl = st == 0 ? sx_lds0 : sx_lds1;
+        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * 4) : 0u);
+      }
+    };
+    auto issue = [&](auto ST, int kb, i32x8(&b)[4]) __attribute__((always_inline)) {
+      static_for<7>([&](auto PT) __attribute__((always_inline)) { issue_part(ST, PT, kb, b); });
     };
 
-    f32x4 acc[16][2];
+    // acc[m][t]: rows 16m + 4grp + i, n-tile t (gate 0-1, up 2-3)
+    f32x4 acc[MT][4];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    i32x8 BG[DB], BU[DB];
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    i32x8 B[DB][4];
 
-    // one K block: issue block kb + 2 into the stage freed last step, multiply
-    // block kb out of stage s, then wait for block kb + 1
+    // one K block: issue block kb + 1 into the other stage (read last step),
+    // multiply block kb out of stage s, then wait for block kb + 1
     auto step = [&](auto S, int kb0) __attribute__((always_inline)) {
       constexpr int s = decltype(S)::value;
       const int kb = kb0 + s;
-      issue(std::integral_constant<int, (s + 2) % NS>{}, kb + 2, BG[(s + 2) % DB], BU[(s + 2) % DB]);
+      issue(std::integral_constant<int, 1 - s>{}, kb + 1, B[1 - s]);
       if (kb < nH) {
         const float wsg = ws_lds[2 * kb], wsu = ws_lds[2 * kb + 1];
-        const uint8_t* abuf = (s == 0 ? a_lds0 : s == 1 ? a_lds1 : a_lds2) + afr;
-        const float* srow = (s == 0 ? sx_lds0 : s == 1 ? sx_lds1 : sx_lds2) + grp * 4;
-        // A fragments one subtile ahead; the scheduling barriers keep the
-        // compiler from hoisting all sixteen (128 VGPRs) over the MFMAs
-        i32x8 an = cat(ld16(abuf + afc0), ld16(abuf + afc1));
+        const uint8_t* abuf = (s == 0 ? a_lds0 : a_lds1) + afr;
+        const float* srow = (s == 0 ? sx_lds0 : sx_lds1) + grp * 4;
+        // Software pipeline over the 16-row subtiles: while the four MFMAs
+        // of subtile m run, the VALU promotes subtile m - 1's products into
+        // the FP32 accumulators (one wave per SIMD: nothing else would fill
+        // the MFMA pipe during the promotion).  A fragments are read one
+        // subtile ahead, row scales kept for three subtiles, in rotating
+        // register sets.
+        i32x8 A2[2];
+        f32x4 R3[3], P[2][4];
+        A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
+        R3[0] = ld16f(srow);
+        auto promote = [&](auto J) __attribute__((always_inline)) {
+          constexpr int j = decltype(J)::value;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          if (m < mt) {
-            const i32x8 af = an;
-            if (m + 1 < mt) an = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
-            const f32x4 pg = mfma_e4m3(af, BG[s]);
-            const f32x4 pu = mfma_e4m3(af, BU[s]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float rs = srow[m * 16 + i];
-              acc[m][0][i] = __builtin_fmaf(pg[i], rs * wsg, acc[m][0][i]);
-              acc[m][1][i] = __builtin_fmaf(pu[i], rs * wsu, acc[m][1][i]);
-            }
+          for (int i = 0; i < 4; ++i) {
+            const float rs = R3[j % 3][i];
+            const float cg = rs * wsg, cu = rs * wsu;
+            acc[j][0][i] = __builtin_fmaf(P[j & 1][0][i], cg, acc[j][0][i]);
+            acc[j][1][i] = __builtin_fmaf(P[j & 1][1][i], cg, acc[j][1][i]);
+            acc[j][2][i] = __builtin_fmaf(P[j & 1][2][i], cu, acc[j][2][i]);
+            acc[j][3][i] = __builtin_fmaf(P[j & 1][3][i], cu, acc[j][3][i]);
           }
+          pin_in_place(acc[j]);
+        };
+        auto next = [&](auto M) __attribute__((always_inline)) {
+          constexpr int m = decltype(M)::value;
+          if constexpr (m + 1 < MT) {
+            A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
+            R3[(m + 1) % 3] = ld16f(srow + (m + 1) * 16);
+          }
+        };
+        // All MT subtiles are multiplied even when the tile holds fewer rows
+        // (the last tile of an expert): the rows past the end are zeros, the
+        // surplus MFMAs hide under the weight stream such tiles wait for, and
+        // a branch-free body lets subtile m's MFMAs run while the VALU
+        // promotes subtile m - 1 (one basic block per subtile).
+        static_for<MT>([&](auto M) __attribute__((always_inline)) {
+          constexpr int m = decltype(M)::value;
+          next(M);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) P[m & 1][t] = mfma_e4m3(A2[m & 1], B[s][t]);
+          if constexpr (m > 0) promote(std::integral_constant<int, m - 1>{});
+          interleave_mfma_valu<4, 6>();
           __builtin_amdgcn_sched_barrier(0);
-        }
+        });
+        promote(std::integral_constant<int, MT - 1>{});
       }
-      __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): block kb + 1 has landed
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block kb + 1 has landed
       ring_barrier();
     };
 
-    issue(std::integral_constant<int, 0>{}, 0, BG[0], BU[0]);
-    issue(std::integral_constant<int, 1>{}, 1, BG[1], BU[1]);
-    __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): block 0 has landed
+    issue(std::integral_constant<int, 0>{}, 0, B[0]);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block 0 has landed
     ring_barrier();
-    static_assert(NS == 3 && DB == 3, "the K loop is unrolled by the stage count");
+    static_assert(NS == 2 && DB == 2, "the K loop is unrolled by the stage count");
     for (int kb0 = 0; kb0 < nH; kb0 += NS) {
       step(std::integral_constant<int, 0>{}, kb0);
       step(std::integral_constant<int, 1>{}, kb0);
-      step(std::integral_constant<int, 2>{}, kb0);
     }
     // the out-of-range loads issued past the last block still write zeros
     // to their stages: let them land before the LDS is reused
@@ -512,31 +580,34 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
     uint8_t* h_lds = a_lds0;
     if (a.gu_dbg) {
 #pragma unroll
-      for (int m = 0; m < 16; ++m)
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = m * 16 + grp * 4 + i;
           if (m < mt && row < rows) {
-            float* g = a.gu_dbg + (size_t)(p0 + row) * 2 * Ip + nb * kBlock + wave * 16 + col;
+            float* g = a.gu_dbg + (size_t)(p0 + row) * 2 * Ip + nb * kBlock + wave * 32 + col;
             g[0] = acc[m][0][i];
-            g[Ip] = acc[m][1][i];
+            g[16] = acc[m][1][i];
+            g[Ip] = acc[m][2][i];
+            g[Ip + 16] = acc[m][3][i];
           }
         }
     }
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < MT; ++m) {
       if (m < mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[m][0][i] = silu_mul(acc[m][0][i], acc[m][1][i]);
-          const uint32_t mb = max16(abs_bits(acc[m][0][i]));
+          acc[m][0][i] = silu_mul(acc[m][0][i], acc[m][2][i]);
+          acc[m][1][i] = silu_mul(acc[m][1][i], acc[m][3][i]);
+          const uint32_t mb = max16(umax(abs_bits(acc[m][0][i]), abs_bits(acc[m][1][i])));
           if (col == 0) red_lds[wave][m * 16 + grp * 4 + i] = mb;
         }
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < MT; ++m) {
       if (m < mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -546,8 +617,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
           for (int w = 0; w < kTileThreads / 64; ++w) mb = umax(mb, red_lds[w][row]);
           const float amax = __uint_as_float(mb);
           const float sc = __fdiv_rn(amax, 448.0f);
-          const uint32_t c = amax != 0.0f ? to_e4m3(__fdiv_rn(acc[m][0][i], sc)) : 0u;
-          h_lds[row * 128 + wave * 16 + col] = (uint8_t)c;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const uint32_t c = amax != 0.0f ? to_e4m3(__fdiv_rn(acc[m][t][i], sc)) : 0u;
+            h_lds[row * 128 + wave * 32 + t * 16 + col] = (uint8_t)c;
+          }
           if (wave == 0 && col == 0) sh_lds[row] = sc;
         }
       }
@@ -700,22 +774,22 @@ hipError_t launch_gate_up(const GateUpArgs& a, bool big, int grid, hipStream_t s
 }
 
 // -------------------------------------------------------------------- down --
-// Large-expert down: a 512-thread workgroup computes up to 256 rows x 256
-// hidden columns (weight blocks nb2, nb2+1).  As in gate_up_tile_kernel, each
-// wave owns 32 columns for all rows (block nb2 + w/4, 32-column group w%4):
-// its weight fragments stream into registers 2 K blocks ahead and the shared
-// h rows arrive in a 3-stage LDS ring by buffer-load-to-LDS.
+// Large-expert down: a 256-thread workgroup computes up to 128 rows x 256
+// hidden columns (weight blocks nb2, nb2+1).  As in gate_up_tile_kernel, wave
+// w owns 64 columns for all rows (block nb2 + w/2, columns 64(w%2)..+63, 4
+// n-tiles): its weight fragments stream into registers one K block ahead and
+// the shared h rows arrive in a double-buffered LDS tile by
+// buffer-load-to-LDS, with the same exact waits.
 
 __global__ __launch_bounds__(kTileThreads, 1) void down_tile_kernel(DownArgs a) {
   constexpr int BM = kTileRows;
-  constexpr int NS = 3, DB = 3;
+  constexpr int NS = 2, DB = 2;
+  constexpr int MT = BM / 16;
   // one LDS object per stage (see gate_up_tile_kernel)
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[BM * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds1[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t a_lds2[BM * 128];
-  __shared__ __attribute__((aligned(256))) float s_lds0[BM];
-  __shared__ __attribute__((aligned(256))) float s_lds1[BM];
-  __shared__ __attribute__((aligned(256))) float s_lds2[BM];
+  __shared__ __attribute__((aligned(256))) float s_lds0[2 * BM];
+  __shared__ __attribute__((aligned(256))) float s_lds1[2 * BM];
   __shared__ float ws_lds[2][kMaxKBlocks];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -726,9 +800,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void down_tile_kernel(DownArgs a) 
   const int n_items = a.n_tiles[0] * NB2;
   const rsrc_t hr = make_rsrc(a.hq, (uint32_t)a.hq_bytes);
   const rsrc_t sr = make_rsrc(a.sh, (uint32_t)a.sh_bytes);
-  const int half = wave >> 2;  // which of the two weight blocks
-  const uint32_t b0_off = (uint32_t)((((wave & 3) * 2) * 2) * 1024 + lane * 16);
-  const uint32_t b1_off = b0_off + 2 * 1024;
+  const int half = wave >> 1;  // which of the two weight blocks
+  // n-tiles 0-3 of the wave are 32-column groups 2(w%2), 2(w%2)+1 of its block
+  const uint32_t b_off = (uint32_t)((wave & 1) * 4 * 2 * 1024 + lane * 16);
   const int afr = (lane & 15) * 128;
   const int afc0 = ((2 * grp) ^ (lane & 7)) << 4, afc1 = ((2 * grp + 1) ^ (lane & 7)) << 4;
 
@@ -739,7 +813,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void down_tile_kernel(DownArgs a) 
     const int nb2 = it.nb * 2;
     const bool two = nb2 + 1 < NB;  // second weight block present
     const int e = it.e, p0 = it.p0, rows = it.rows;
-    const int mt = (half == 1 && !two) ? 0 : (rows + 15) >> 4;
+    const int mt_all = (rows + 15) >> 4;
+    const int mt = (half == 1 && !two) ? 0 : mt_all;
 
     __syncthreads();  // LDS of the previous item is no longer read
     {
@@ -755,92 +830,122 @@ __global__ __launch_bounds__(kTileThreads, 1) void down_tile_kernel(DownArgs a) 
     const rsrc_t wr = make_rsrc(a.w2 + (size_t)(e * NB + nb2 + (two ? half : 0)) * nI * kDownChunk,
                                 (uint32_t)(nI * kDownChunk));
     const uint32_t wmask = (half == 1 && !two) ? 0x80000000u : 0u;
-    const int mrows16 = ((rows + 15) >> 4) * 16;
     uint32_t avo[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int row = (q * 8 + wave) * 8 + (lane >> 3);
+      const int row = (q * 4 + wave) * 8 + (lane >> 3);
       const int c = (lane & 7) ^ (row & 7);
       avo[q] = (uint32_t)((p0 + (row < rows ? row : 0)) * Ip + c * 16) +
-               ((q * 8 + wave) * 8 < mrows16 ? 0u : 0x80000000u);
+               ((q * 4 + wave) * 8 < mt_all * 16 ? 0u : 0x80000000u);
     }
+    // row scales: waves 0-1 load rows 64w + lane, waves 2-3 load out of
+    // range into the unused half of the stage
     const int srow = wave * 64 + lane;
-    const uint32_t svo = (uint32_t)((p0 + (srow < rows ? srow : 0)) * nI * 4);
+    const uint32_t svo = wave < 2 ? (uint32_t)((p0 + (srow < rows ? srow : 0)) * nI * 4) : 0x80000000u;
 
-    auto issue = [&](auto ST, int kb, i32x8& b0, i32x8& b1) __attribute__((always_inline)) {
-      constexpr int st = decltype(ST)::value;
-      uint8_t* al = st == 0 ? a_lds0 : st == 1 ? a_lds1 : a_lds2;
-      float* sl = st == 0 ? s_lds0 : st == 1 ? s_lds1 : s_lds2;
+    // block kb's 13 loads in 7 parts, as in gate_up_tile_kernel
+    auto issue_part = [&](auto ST, auto PT, int kb, i32x8(&b)[4]) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value, p = decltype(PT)::value;
       const bool in = kb < nI;
       const uint32_t oob = in ? 0u : 0x80000000u;
-      const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
+      if constexpr (p < 4) {
+        const uint32_t so = in ? (uint32_t)(kb * kDownChunk) : 0u;
+        b[p] = cat(wload16(wr, b_off | oob | wmask, so + p * 2048),
+                   wload16(wr, b_off | oob | wmask, so + p * 2048 + 1024));
+      } else if constexpr (p < 6) {
+        uint8_t* al = st == 0 ? a_lds0 : a_lds1;
+        const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dma16<0>(hr, al + (q * 8 + wave) * 1024, avo[q] + oob, sa);
-      if (wave < 4) dma4(sr, sl + wave * 64, svo + oob, in ? (uint32_t)(kb * 4) : 0u);
-      const uint32_t so = in ? (uint32_t)(kb * kDownChunk) : 0u;
-      b0 = cat(wload16(wr, b0_off + (oob | wmask), so), wload16(wr, b0_off + (oob | wmask), so + 1024));
-      b1 = cat(wload16(wr, b1_off + (oob | wmask), so), wload16(wr, b1_off + (oob | wmask), so + 1024));
+        for (int q = 2 * (p - 4); q < 2 * (p - 4) + 2; ++q)
+          dma16<0>(hr, al + (q * 4 + wave) * 1024, avo[q] | oob, sa);
+      } else {
+        float* sl = st == 0 ? s_lds0 : s_lds1;
+        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * 4) : 0u);
+      }
+    };
+    auto issue = [&](auto ST, int kb, i32x8(&b)[4]) __attribute__((always_inline)) {
+      static_for<7>([&](auto PT) __attribute__((always_inline)) { issue_part(ST, PT, kb, b); });
     };
 
-    f32x4 acc[16][2];
+    f32x4 acc[MT][4];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    i32x8 B0[DB], B1[DB];
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    i32x8 B[DB][4];
 
     auto step = [&](auto S, int kb0) __attribute__((always_inline)) {
       constexpr int s = decltype(S)::value;
       const int kb = kb0 + s;
-      issue(std::integral_constant<int, (s + 2) % NS>{}, kb + 2, B0[(s + 2) % DB], B1[(s + 2) % DB]);
+      issue(std::integral_constant<int, 1 - s>{}, kb + 1, B[1 - s]);
       if (kb < nI) {
         const float wsc = ws_lds[half][kb];
-        const uint8_t* abuf = (s == 0 ? a_lds0 : s == 1 ? a_lds1 : a_lds2) + afr;
-        const float* srw = (s == 0 ? s_lds0 : s == 1 ? s_lds1 : s_lds2) + grp * 4;
-        i32x8 an = cat(ld16(abuf + afc0), ld16(abuf + afc1));
+        const uint8_t* abuf = (s == 0 ? a_lds0 : a_lds1) + afr;
+        const float* srw = (s == 0 ? s_lds0 : s_lds1) + grp * 4;
+        // software pipeline as in gate_up_tile_kernel
+        i32x8 A2[2];
+        f32x4 R3[3], Q[2][4];
+        A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
+        R3[0] = ld16f(srw);
+        auto promote = [&](auto J) __attribute__((always_inline)) {
+          constexpr int j = decltype(J)::value;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          if (m < mt) {
-            const i32x8 af = an;
-            if (m + 1 < mt) an = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
-            const f32x4 q0 = mfma_e4m3(af, B0[s]);
-            const f32x4 q1 = mfma_e4m3(af, B1[s]);
+          for (int i = 0; i < 4; ++i) {
+            const float sc = R3[j % 3][i] * wsc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float sc = srw[m * 16 + i] * wsc;
-              acc[m][0][i] = __builtin_fmaf(q0[i], sc, acc[m][0][i]);
-              acc[m][1][i] = __builtin_fmaf(q1[i], sc, acc[m][1][i]);
-            }
+            for (int t = 0; t < 4; ++t) acc[j][t][i] = __builtin_fmaf(Q[j & 1][t][i], sc, acc[j][t][i]);
           }
+          pin_in_place(acc[j]);
+        };
+        auto next = [&](auto M) __attribute__((always_inline)) {
+          constexpr int m = decltype(M)::value;
+          if constexpr (m + 1 < MT) {
+            A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
+            R3[(m + 1) % 3] = ld16f(srw + (m + 1) * 16);
+          }
+        };
+        // All MT subtiles are multiplied even when the tile holds fewer rows
+        // (the last tile of an expert): the rows past the end are zeros, the
+        // surplus MFMAs hide under the weight stream such tiles wait for, and
+        // a branch-free body lets subtile m's MFMAs run while the VALU
+        // promotes subtile m - 1 (one basic block per subtile).
+        static_for<MT>([&](auto M) __attribute__((always_inline)) {
+          constexpr int m = decltype(M)::value;
+          next(M);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) Q[m & 1][t] = mfma_e4m3(A2[m & 1], B[s][t]);
+          if constexpr (m > 0) promote(std::integral_constant<int, m - 1>{});
+          interleave_mfma_valu<4, 5>();
           __builtin_amdgcn_sched_barrier(0);
-        }
+        });
+        promote(std::integral_constant<int, MT - 1>{});
       }
-      __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): block kb + 1 has landed
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block kb + 1 has landed
       ring_barrier();
     };
 
-    issue(std::integral_constant<int, 0>{}, 0, B0[0], B1[0]);
-    issue(std::integral_constant<int, 1>{}, 1, B0[1], B1[1]);
-    __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): block 0 has landed
+    issue(std::integral_constant<int, 0>{}, 0, B[0]);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block 0 has landed
     ring_barrier();
-    static_assert(NS == 3 && DB == 3, "the K loop is unrolled by the stage count");
+    static_assert(NS == 2 && DB == 2, "the K loop is unrolled by the stage count");
     for (int kb0 = 0; kb0 < nI; kb0 += NS) {
       step(std::integral_constant<int, 0>{}, kb0);
       step(std::integral_constant<int, 1>{}, kb0);
-      step(std::integral_constant<int, 2>{}, kb0);
     }
     // the out-of-range loads issued past the last block still write zeros
     // to their stages: let them land before the next item's loads
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
 
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < MT; ++m) {
       if (m < mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = m * 16 + grp * 4 + i;
           if (row < rows) {
-            float* dst = a.y + (size_t)(p0 + row) * H + (nb2 + half) * kBlock + (wave & 3) * 32 + col;
-            dst[0] = acc[m][0][i];
-            dst[16] = acc[m][1][i];
+            float* dst = a.y + (size_t)(p0 + row) * H + (nb2 + half) * kBlock + (wave & 1) * 64 + col;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dst[t * 16] = acc[m][t][i];
           }
         }
       }

@@ -168,8 +168,14 @@ SLICE_T16 = Workload("slice_e160_k8_h5120_i192_t16", 160, 8, 5120, 192, 16,
 SLICE_T64 = dataclasses.replace(SLICE_T16, name="slice_e160_k8_h5120_i192_t64", T=64)
 SLICE_T1024 = dataclasses.replace(SLICE_T16, name="slice_e160_k8_h5120_i192_t1024", T=1024)
 
+# Compute-bound probe (not one of the pages' configurations): every token
+# routes to all 8 experts of a GLM-shaped layer, so each expert gets T rows
+# and the grouped GEMMs run at ~6,100 FLOP per weight byte.
+PROBE_T4096 = Workload("probe_e8_k8_h6144_i2048_t4096", 8, 8, 6144, 2048, 4096,
+                       ROUTE_SIGMOID_UNIFORM, 1.0, 0.0)
+
 WORKLOADS = {w.name: w for w in (TINY, GLM_T256, GLM_T4096, GLM_T8192_ZIPF,
-                                 SLICE_T16, SLICE_T64, SLICE_T1024)}
+                                 SLICE_T16, SLICE_T64, SLICE_T1024, PROBE_T4096)}
 
 
 def make_inputs(wl: Workload):
