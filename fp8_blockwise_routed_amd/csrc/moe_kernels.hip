@@ -479,8 +479,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
       const bool in = kb < nH;
       const uint32_t oob = in ? 0u : 0x80000000u;
       if constexpr (p < 4) {
+        // default cache policy: the other row tiles of this expert read the
+        // same weight chunk soon after, from L2
         const uint32_t so = in ? (uint32_t)(kb * kGateUpChunk) : 0u;
-        b[p] = cat(wload16(wr, b_off | oob, so + p * 2048), wload16(wr, b_off | oob, so + p * 2048 + 1024));
+        b[p] = cat(bload16(wr, b_off | oob, so + p * 2048), bload16(wr, b_off | oob, so + p * 2048 + 1024));
       } else if constexpr (p < 6) {
         uint8_t* al = st == 0 ? a_lds0 : a_lds1;
         const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
@@ -850,8 +852,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void down_tile_kernel(DownArgs a) 
       const uint32_t oob = in ? 0u : 0x80000000u;
       if constexpr (p < 4) {
         const uint32_t so = in ? (uint32_t)(kb * kDownChunk) : 0u;
-        b[p] = cat(wload16(wr, b_off | oob | wmask, so + p * 2048),
-                   wload16(wr, b_off | oob | wmask, so + p * 2048 + 1024));
+        b[p] = cat(bload16(wr, b_off | oob | wmask, so + p * 2048),
+                   bload16(wr, b_off | oob | wmask, so + p * 2048 + 1024));
       } else if constexpr (p < 6) {
         uint8_t* al = st == 0 ? a_lds0 : a_lds1;
         const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
