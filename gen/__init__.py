@@ -57,6 +57,9 @@ def _load():
         lib.gen_routing.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_double, P, P]
         lib.gen_routing.restype = None
+        lib.gen_logits.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_double, P]
+        lib.gen_logits.restype = None
         _lib = lib
     return _lib
 
@@ -131,6 +134,16 @@ def make_routing(T: int, E: int, k: int, kind: int, seed: int = 0, n_masked: int
     w = np.empty((T, k), np.float32)
     _load().gen_routing(seed, T, E, k, kind, n_masked, zipf_s, _ptr(ids), _ptr(w))
     return ids, w
+
+
+def make_logits(T: int, E: int, kind: int, seed: int = 0, n_masked: int = 0,
+                zipf_s: float = 1.2) -> np.ndarray:
+    """Router logits float32[T][E], the same draws ``make_routing`` selects
+    from (N(0,1), U(0,1), or Zipf log-popularity + Gumbel with -inf for the
+    masked experts), rounded to FP32."""
+    logits = np.empty((T, E), np.float32)
+    _load().gen_logits(seed, T, E, kind, n_masked, zipf_s, _ptr(logits))
+    return logits
 
 
 def bf16_bits_to_f32(x: np.ndarray) -> np.ndarray:

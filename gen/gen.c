@@ -248,24 +248,60 @@ enum { ROUTE_SOFTMAX = 0, ROUTE_SIGMOID_NORMAL = 1, ROUTE_SIGMOID_UNIFORM = 2, R
  * Slots are ordered by descending score, ties to the lower expert id.
  * ids: i32[T][k]; w: f32[T][k].
  */
+/* Zipf log-popularity per expert (n_masked lowest ranks get -inf). */
+static double* zipf_logp(uint64_t seed, int32_t E, int32_t n_masked, double zipf_s) {
+  double* logp = (double*)malloc(sizeof(double) * (size_t)E);
+  keyed* order = (keyed*)malloc(sizeof(keyed) * (size_t)E);
+  uint64_t pkey = stream_key(seed, TAG_EXPERT_PERM);
+  for (int32_t e = 0; e < E; ++e) {
+    order[e].key = draw(pkey, (uint64_t)e);
+    order[e].idx = e;
+  }
+  qsort(order, (size_t)E, sizeof(keyed), cmp_keyed);
+  for (int32_t r = 0; r < E; ++r) {
+    int64_t e = order[r].idx;
+    logp[e] = (r < E - n_masked) ? -zipf_s * log((double)(r + 1)) : -INFINITY;
+  }
+  free(order);
+  return logp;
+}
+
+/* The routing logit of (token t, expert e) for a routing kind. */
+static double logit_at(int32_t kind, uint64_t lkey, uint64_t gkey, const double* logp,
+                       int64_t t, int32_t E, int32_t e) {
+  uint64_t idx = (uint64_t)(t * E + e);
+  switch (kind) {
+    case ROUTE_SOFTMAX:
+    case ROUTE_SIGMOID_NORMAL:
+      return (double)normal_at(lkey, idx);
+    case ROUTE_SIGMOID_UNIFORM:
+      return unit_open_d(draw(lkey, idx));
+    default: {
+      double u = unit_open_d(draw(gkey, idx));
+      return logp[e] - log(-log(u));
+    }
+  }
+}
+
+/*
+ * Router logits as FP32 [T][E], drawn exactly as gen_routing draws them
+ * (the input of an on-device router).
+ */
+void gen_logits(uint64_t seed, int64_t T, int32_t E, int32_t kind, int32_t n_masked,
+                double zipf_s, float* logits) {
+  double* logp = kind == ROUTE_ZIPF ? zipf_logp(seed, E, n_masked, zipf_s) : NULL;
+  uint64_t lkey = stream_key(seed, TAG_LOGIT);
+  uint64_t gkey = stream_key(seed, TAG_GUMBEL);
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t e = 0; e < E; ++e)
+      logits[t * E + e] = (float)logit_at(kind, lkey, gkey, logp, t, E, e);
+  free(logp);
+}
+
 void gen_routing(uint64_t seed, int64_t T, int32_t E, int32_t k, int32_t kind,
                  int32_t n_masked, double zipf_s, int32_t* ids, float* w) {
-  double* logp = NULL;
-  if (kind == ROUTE_ZIPF) {
-    logp = (double*)malloc(sizeof(double) * (size_t)E);
-    keyed* order = (keyed*)malloc(sizeof(keyed) * (size_t)E);
-    uint64_t pkey = stream_key(seed, TAG_EXPERT_PERM);
-    for (int32_t e = 0; e < E; ++e) {
-      order[e].key = draw(pkey, (uint64_t)e);
-      order[e].idx = e;
-    }
-    qsort(order, (size_t)E, sizeof(keyed), cmp_keyed);
-    for (int32_t r = 0; r < E; ++r) {
-      int64_t e = order[r].idx;
-      logp[e] = (r < E - n_masked) ? -zipf_s * log((double)(r + 1)) : -INFINITY;
-    }
-    free(order);
-  }
+  double* logp = kind == ROUTE_ZIPF ? zipf_logp(seed, E, n_masked, zipf_s) : NULL;
   uint64_t lkey = stream_key(seed, TAG_LOGIT);
   uint64_t gkey = stream_key(seed, TAG_GUMBEL);
 #pragma omp parallel
@@ -275,21 +311,7 @@ void gen_routing(uint64_t seed, int64_t T, int32_t E, int32_t k, int32_t kind,
 #pragma omp for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
       for (int32_t e = 0; e < E; ++e) {
-        uint64_t idx = (uint64_t)(t * E + e);
-        double l;
-        switch (kind) {
-          case ROUTE_SOFTMAX:
-          case ROUTE_SIGMOID_NORMAL:
-            l = (double)normal_at(lkey, idx);
-            break;
-          case ROUTE_SIGMOID_UNIFORM:
-            l = unit_open_d(draw(lkey, idx));
-            break;
-          default: {
-            double u = unit_open_d(draw(gkey, idx));
-            l = logp[e] - log(-log(u));
-          }
-        }
+        double l = logit_at(kind, lkey, gkey, logp, t, E, e);
         score[e] = l;
         taken[e] = 0;
       }

@@ -32,7 +32,12 @@ FAULTS = {
     "drop_rho": 10,
     "silu_sign": 11,
     "gate_up_swap": 12,
+    "route_tie_high": 13,
+    "route_all_experts": 14,
 }
+
+ROUTE_SOFTMAX = 0
+ROUTE_SIGMOID = 1
 
 OUT_BF16 = 0
 OUT_F32 = 1
@@ -93,6 +98,8 @@ def _load():
         lib.orc_set_fault.restype = None
         lib.orc_max_threads.argtypes = []
         lib.orc_max_threads.restype = ctypes.c_int32
+        lib.orc_route.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P]
+        lib.orc_route.restype = ctypes.c_int32
         _lib = lib
     return _lib
 
@@ -163,6 +170,19 @@ def plan(ids: np.ndarray, E: int):
     inv = np.empty(max(T * k, 1), np.int32)
     bad = _load().orc_plan(_p(ids), T, k, E, _p(counts), _p(offsets), _p(perm), _p(inv))
     return counts, offsets, perm[: offsets[E]], inv[: T * k], int(bad)
+
+
+def route(logits: np.ndarray, k: int, kind: int):
+    """Top-k router on FP32 logits [T][E]: (ids int32[T][k] in descending
+    logit order, ties to the lower id, NaN last; weights float64[T][k],
+    softmax (kind 0) or sigmoid (kind 1) scores normalised over the chosen)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    if _load().orc_route(_p(logits), T, E, k, kind, _p(ids), _p(w)) != 0:
+        raise ValueError("bad router arguments")
+    return ids, w
 
 
 def _layer_struct(layer):

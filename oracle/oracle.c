@@ -51,6 +51,8 @@ enum {
   FAULT_DROP_RHO = 10,
   FAULT_SILU_SIGN = 11,         /* silu(-g)                                  */
   FAULT_GATE_UP_SWAP = 12,      /* silu(u) * g                               */
+  FAULT_ROUTE_TIE_HIGH = 13,    /* router ties go to the higher expert id    */
+  FAULT_ROUTE_ALL_EXPERTS = 14, /* softmax weights normalised over all E     */
 };
 static int g_fault = FAULT_NONE;
 void orc_set_fault(int32_t f) { g_fault = f; }
@@ -570,4 +572,64 @@ int64_t orc_down_combine(const orc_layer* L, int32_t k, const uint8_t* hq, const
   free(hd);
   free(y);
   return P;
+}
+
+/* ---- the router (upstream of the layer, fused on the device) ------------ */
+
+/* Orders two experts for top-k: larger logit first; a NaN logit ranks below
+ * every number; equal logits go to the lower expert id. */
+static int route_before(float la, int32_t a, float lb, int32_t b) {
+  int na = la != la, nb = lb != lb;
+  if (na != nb) return nb;           /* the non-NaN one first */
+  if (!na && la != lb) return la > lb;
+  if (g_fault == FAULT_ROUTE_TIE_HIGH) return a > b;
+  return a < b;
+}
+
+/*
+ * Top-k routing of one token's router logits ("hpc-ops #80", gap table: the
+ * router's top-k is part of the fused MoE step; "TensorFold #2852": top-k
+ * slots in descending score).  The k experts with the largest logits, in
+ * descending order, ties to the lower id (sigmoid and exp are increasing, so
+ * this is also the order of the scores).  Weights, in FP64:
+ *   kind 0 (softmax): s_j = exp(l_j - l_0), w_j = s_j / sum of the chosen s
+ *                     (softmax over all experts, renormalised over the chosen);
+ *   kind 1 (sigmoid): s_j = 1 / (1 + exp(-l_j)), w_j = s_j / sum of chosen s.
+ * A chosen set with no mass (sum 0, or a softmax whose largest chosen logit
+ * is -inf) gets all-zero weights.
+ * logits f32[T][E]; ids i32[T][k]; w f64[T][k].  Returns 0, or -1.
+ */
+int32_t orc_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t kind,
+                  int32_t* ids, double* w) {
+  if (T < 0 || E < 1 || k < 1 || k > E || (kind != 0 && kind != 1)) return -1;
+  unsigned char* taken = (unsigned char*)malloc((size_t)E);
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * E;
+    memset(taken, 0, (size_t)E);
+    for (int32_t j = 0; j < k; ++j) {      /* selection, one slot at a time */
+      int32_t best = -1;
+      for (int32_t e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || route_before(l[e], e, l[best], best))) best = e;
+      taken[best] = 1;
+      ids[t * k + j] = best;
+    }
+    double sum = 0.0;
+    const double l0 = (double)l[ids[t * k]];
+    double* wt = w + t * k;
+    if (kind == 0 && g_fault == FAULT_ROUTE_ALL_EXPERTS) {
+      double all = 0.0;
+      for (int32_t e = 0; e < E; ++e) all += exp((double)l[e] - l0);
+      for (int32_t j = 0; j < k; ++j) wt[j] = exp((double)l[ids[t * k + j]] - l0) / all;
+      continue;
+    }
+    for (int32_t j = 0; j < k; ++j) {
+      const double lj = (double)l[ids[t * k + j]];
+      wt[j] = kind == 0 ? exp(lj - l0) : 1.0 / (1.0 + exp(-lj));
+    }
+    const int no_mass = kind == 0 && l0 == -INFINITY;
+    for (int32_t j = 0; j < k; ++j) sum += wt[j];
+    for (int32_t j = 0; j < k; ++j) wt[j] = (no_mass || sum == 0.0) ? 0.0 : wt[j] / sum;
+  }
+  free(taken);
+  return 0;
 }

@@ -14,6 +14,11 @@ What pins what:
   quantiser  a torch re-derivation (amax, IEEE divide, torch float8 cast) and
              invariants (amax element -> +-448, error bounds).
   plan       numpy's stable argsort.
+  router     a sort by (logit descending, id ascending) in plain Python with
+             NaN last; scipy's full softmax renormalised over the chosen
+             experts and scipy's expit; the generator's own FP64 top-k on the
+             same draws; tie, -inf, NaN and k = E cases; shift invariance of
+             the softmax weights.
   layer      the FP64 dense brute force (different loop structure, FP64,
              exhaustive-search encoder); a dense gated FFN evaluated with torch
              float8 casts and float64 matmuls; an integer-exact case compared
@@ -237,6 +242,94 @@ def pin_plan_vs_numpy():
     ok = (np.array_equal(counts, c_ref) and np.array_equal(offsets, o_ref)
           and np.array_equal(perm, order) and np.array_equal(inv, inv_ref) and bad == 2)
     return _ok(ok, "plan differs from numpy stable argsort")
+
+
+# ---------------------------------------------------------------- router ---
+
+def router_logits(seed=9):
+    rng = np.random.default_rng(seed)
+    l = rng.standard_normal((64, 23)).astype(np.float32)
+    l[3, [2, 7, 11]] = 1.5                    # three-way tie
+    l[4, :] = 0.25                            # all equal
+    l[5, [0, 1]] = -np.inf                    # masked experts
+    l[6, 4] = np.nan                          # a NaN logit ranks last
+    l[7, :] = -np.inf                         # no mass at all
+    l[8, 5] = np.inf
+    return l
+
+
+def _sorted_topk(row, k):
+    key = [((1, 0.0) if np.isnan(v) else (0, -float(v)), e) for e, v in enumerate(row)]
+    return [e for _, e in sorted(key)[:k]]
+
+
+def pin_route_ids_vs_sort():
+    l = router_logits()
+    ok = True
+    for kind in (oracle.ROUTE_SOFTMAX, oracle.ROUTE_SIGMOID):
+        for k in (1, 4, 8, l.shape[1]):
+            ids, _ = oracle.route(l, k, kind)
+            ref = np.array([_sorted_topk(r, k) for r in l], np.int32)
+            ok &= np.array_equal(ids, ref)
+    return _ok(ok, "router ids differ from a (logit desc, id asc) sort")
+
+
+def pin_route_weights_vs_scipy():
+    from scipy.special import expit, softmax
+    l = router_logits()
+    good = np.isfinite(l).all(axis=1)
+    ok = True
+    for k in (2, 8):
+        ids, w = oracle.route(l, k, oracle.ROUTE_SOFTMAX)
+        full = softmax(l[good].astype(np.float64), axis=1)
+        ch = np.take_along_axis(full, ids[good].astype(np.int64), axis=1)
+        ok &= np.allclose(w[good], ch / ch.sum(axis=1, keepdims=True), rtol=1e-12, atol=1e-15)
+        ids, w = oracle.route(l, k, oracle.ROUTE_SIGMOID)
+        sg = expit(np.take_along_axis(l[good].astype(np.float64), ids[good].astype(np.int64), axis=1))
+        ok &= np.allclose(w[good], sg / sg.sum(axis=1, keepdims=True), rtol=1e-12, atol=1e-15)
+    return _ok(ok, "router weights differ from scipy softmax / expit")
+
+
+def pin_route_special_rows():
+    l = router_logits()
+    ok = True
+    for kind in (oracle.ROUTE_SOFTMAX, oracle.ROUTE_SIGMOID):
+        ids, w = oracle.route(l, 4, kind)
+        full, _ = oracle.route(l[3:4], l.shape[1], kind)           # three-way tie
+        pos = [list(full[0]).index(e) for e in (2, 7, 11)]
+        ok &= pos == sorted(pos) and pos[2] - pos[0] == 2
+        ok &= list(ids[4]) == [0, 1, 2, 3]                       # ties -> lower ids
+        ok &= 0 not in ids[5] and 1 not in ids[5]                # -inf never chosen first
+        ok &= 4 not in ids[6]                                    # NaN ranks last
+        ok &= np.all(w[7] == 0.0)                                # no mass
+        ok &= bool(np.all(np.abs(w[:7].sum(axis=1) - 1.0) < 1e-12))
+        ok &= ids[8, 0] == 5
+    ids4, w4 = oracle.route(l[4:5], 4, oracle.ROUTE_SOFTMAX)
+    ok &= np.allclose(w4, 0.25, rtol=0, atol=1e-15)
+    return _ok(ok, "router tie / -inf / NaN / no-mass rows")
+
+
+def pin_route_shift_invariance():
+    l = router_logits()[:3]
+    ids, w = oracle.route(l, 5, oracle.ROUTE_SOFTMAX)
+    ids2, w2 = oracle.route(l + np.float32(8.0), 5, oracle.ROUTE_SOFTMAX)
+    idsg, _ = oracle.route(l, 5, oracle.ROUTE_SIGMOID)
+    ok = np.array_equal(ids, ids2) and np.allclose(w, w2, rtol=1e-5) and np.array_equal(ids, idsg)
+    return _ok(ok, "softmax weights not shift invariant or kinds choose differently")
+
+
+def pin_route_vs_generator():
+    """The generator's routing (its own FP64 top-k over the same draws) must
+    agree with the oracle's router on the FP32-rounded logits."""
+    ok = True
+    for (T, E, k, kind, masked, okind) in ((64, 8, 2, gen.ROUTE_SOFTMAX, 0, oracle.ROUTE_SOFTMAX),
+                                          (256, 256, 8, gen.ROUTE_SIGMOID_NORMAL, 0, oracle.ROUTE_SIGMOID),
+                                          (512, 256, 8, gen.ROUTE_ZIPF, 8, oracle.ROUTE_SIGMOID)):
+        ids_g, w_g = gen.make_routing(T, E, k, kind, 0, masked)
+        ids_o, w_o = oracle.route(gen.make_logits(T, E, kind, 0, masked), k, okind)
+        ok &= np.array_equal(ids_g, ids_o)
+        ok &= np.allclose(w_g, w_o, rtol=1e-5, atol=1e-7)
+    return _ok(ok, "oracle router disagrees with the generator's routing")
 
 
 # ----------------------------------------------------------------- layer ---
@@ -475,6 +568,11 @@ ALL_PINS = {
     "quantize_vs_torch": pin_quantize_vs_torch,
     "quantize_invariants": pin_quantize_invariants,
     "plan_vs_numpy": pin_plan_vs_numpy,
+    "route_ids_vs_sort": pin_route_ids_vs_sort,
+    "route_weights_vs_scipy": pin_route_weights_vs_scipy,
+    "route_special_rows": pin_route_special_rows,
+    "route_shift_invariance": pin_route_shift_invariance,
+    "route_vs_generator": pin_route_vs_generator,
     "ffn_vs_bruteforce": pin_ffn_vs_bruteforce,
     "dense_textbook": pin_dense_textbook,
     "integer_exact_gate_up": pin_integer_exact_gate_up,

@@ -22,6 +22,8 @@ CAUGHT_BY = {
     "drop_rho": ["ffn_vs_bruteforce"],
     "silu_sign": ["ffn_vs_bruteforce", "activation_from_gu"],
     "gate_up_swap": ["ffn_vs_bruteforce", "activation_from_gu"],
+    "route_tie_high": ["route_ids_vs_sort", "route_special_rows"],
+    "route_all_experts": ["route_weights_vs_scipy", "route_special_rows"],
 }
 
 
