@@ -78,9 +78,15 @@ def algorithmic_work(wl, counts):
     n_small = int(counts[small].sum())
     gu_bytes = int(small.sum()) * (2 * Ip * H + 8 * nI * nH) + n_small * (H + 4 * nH + Ip + 4 * nI)
     gu_flops = 4 * n_small * Ip * H
+    big = counts > 16
+    n_big = int(counts[big].sum())
+    gu_big_bytes = int(big.sum()) * (2 * Ip * H + 8 * nI * nH) + n_big * (H + 4 * nH + Ip + 4 * nI)
+    gu_big_flops = 4 * n_big * Ip * H
     return dict(path_bytes=path_bytes, path_flops=path_flops, gu_small_bytes=gu_bytes,
-                gu_small_flops=gu_flops, experts_hit=int(hit.sum()), experts_small=int(small.sum()),
-                slots=P, per_expert_gate_up_bytes=2 * Ip * H + 8 * nI * nH)
+                gu_small_flops=gu_flops, gu_big_bytes=gu_big_bytes, gu_big_flops=gu_big_flops,
+                experts_hit=int(hit.sum()), experts_small=int(small.sum()),
+                experts_big=int(big.sum()), slots=P,
+                per_expert_gate_up_bytes=2 * Ip * H + 8 * nI * nH)
 
 
 def read_traffic():
@@ -202,6 +208,9 @@ def main() -> int:
     ap.add_argument("--no-timing-events", action="store_true",
                     help="skip the per-launch HIP events (roofline needs them)")
     ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--router", action="store_true",
+                    help="start each step from FP32 router logits (run_logits: on-device top-k "
+                         "router, then the path) instead of given ids and weights")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 CSV output under DIR")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -245,9 +254,16 @@ def main() -> int:
     wd = torch.from_numpy(w).cuda()
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
+    router = pkg.MOE_ROUTER_SOFTMAX if wl.route == gen.ROUTE_SOFTMAX else pkg.MOE_ROUTER_SIGMOID
+    if args.router:
+        logits = gen.make_logits(wl.T, wl.E, wl.route, wl.seed, wl.n_masked)
+        ld = torch.from_numpy(logits).cuda()
 
     def step():
-        rc = pkg.moe_fp8_prefill_run(moe.handle, xd, idd, wd, wl.T, out, stream)
+        if args.router:
+            rc = pkg.moe_fp8_prefill_run_logits(moe.handle, xd, ld, router, wl.T, out, stream)
+        else:
+            rc = pkg.moe_fp8_prefill_run(moe.handle, xd, idd, wd, wl.T, out, stream)
         if rc != pkg.MOE_OK:
             raise pkg.MoeError(rc, "run")
 
@@ -295,16 +311,55 @@ def main() -> int:
         mean = stages.mean(axis=0)
         res["stages_ms"] = {name: float(v) for name, v in zip(pkg.STAGES, mean)}
         gu_ms = float(mean[pkg.STAGES.index("gate_up_small")])
-        achieved = work["gu_small_bytes"] / (gu_ms * 1e-3) / 1e9
-        traffic = read_traffic()
-        res["roofline"] = {
-            "kernel": "gate_up_stream_kernel (experts with 1..16 rows)",
-            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-            "algorithmic_bytes_per_launch": work["gu_small_bytes"],
-            "experts_in_launch": work["experts_small"],
-            "avg_launch_ms": gu_ms,
-        }
+        big_ms = float(mean[pkg.STAGES.index("gate_up_big")])
+        if gu_ms >= big_ms:
+            achieved = work["gu_small_bytes"] / (gu_ms * 1e-3) / 1e9
+            res["roofline"] = {
+                "kernel": "gate_up_stream_kernel (experts with 1..16 rows)",
+                "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic(),
+                "algorithmic_bytes_per_launch": work["gu_small_bytes"],
+                "experts_in_launch": work["experts_small"],
+                "avg_launch_ms": gu_ms,
+            }
+        else:
+            # the 128-row tile launch dominates: bound by whichever roof its
+            # algorithmic work reaches first
+            t_hbm = work["gu_big_bytes"] / (PEAK_HBM_GBS * 1e9)
+            t_mfma = work["gu_big_flops"] / (PEAK_FP8_TFLOPS * 1e12)
+            if t_mfma >= t_hbm:
+                achieved = work["gu_big_flops"] / (big_ms * 1e-3) / 1e12
+                bound, peak, unit = "mfma", PEAK_FP8_TFLOPS, "TFLOP/s"
+            else:
+                achieved = work["gu_big_bytes"] / (big_ms * 1e-3) / 1e9
+                bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
+            res["roofline"] = {
+                "kernel": "gate_up_tile_kernel (experts with more than 16 rows)",
+                "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": None,
+                "algorithmic_bytes_per_launch": work["gu_big_bytes"],
+                "algorithmic_flops_per_launch": work["gu_big_flops"],
+                "experts_in_launch": work["experts_big"],
+                "avg_launch_ms": big_ms,
+            }
+    if args.router:
+        # the router alone, timed with HIP events on the run stream
+        ids_r = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+        w_r = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 50
+        e0.record(stream)
+        for _ in range(reps):
+            pkg.moe_fp8_prefill_route(moe.handle, ld, router, wl.T, ids_r, w_r, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        r_us = e0.elapsed_time(e1) * 1e3 / reps
+        r_bytes = wl.T * wl.E * 4 + wl.T * wl.k * 8
+        res["router"] = {"kernel": "route_kernel", "kind": "softmax" if router == 0 else "sigmoid",
+                         "avg_launch_us": r_us, "algorithmic_bytes": r_bytes,
+                         "GBs": r_bytes / (r_us * 1e-6) / 1e9,
+                         "ids_equal_given": bool(torch.equal(ids_r, idd))}
+        res["config"]["input"] = "router logits"
     if args.cpu_tokens > 0:
         log(f"[bench] CPU oracle on {args.cpu_tokens} rows")
         res["cpu_baseline"] = cpu_baseline(layer, wl, x, ids, w, min(args.cpu_tokens, wl.T),

@@ -29,6 +29,8 @@ MOE_ERR_BAD_EXPERT_ID = 7
 MOE_DTYPE_BF16 = 0
 MOE_DTYPE_F32 = 1
 MOE_ACT_SILU_UNCLAMPED = 0
+MOE_ROUTER_SOFTMAX = 0
+MOE_ROUTER_SIGMOID = 1
 MOE_NUM_STAGES = 7
 STAGES = ("plan", "quant", "gate_up_small", "gate_up_big", "down_small", "down_big", "combine")
 
@@ -40,6 +42,7 @@ EXPORTED = (
     "moe_fp8_prefill_debug_gate_up",
     "moe_fp8_prefill_debug_unpack", "moe_fp8_prefill_debug_mfma", "moe_fp8_prefill_set_timing",
     "moe_fp8_prefill_read_timing", "moe_fp8_prefill_debug_inject_failure",
+    "moe_fp8_prefill_route", "moe_fp8_prefill_run_logits",
 )
 
 
@@ -92,6 +95,8 @@ def load_library() -> ctypes.CDLL:
         "moe_fp8_prefill_set_timing": ([P, I32], ctypes.c_int),
         "moe_fp8_prefill_read_timing": ([P, P, I32, ctypes.POINTER(I32)], ctypes.c_int),
         "moe_fp8_prefill_debug_inject_failure": ([P], ctypes.c_int),
+        "moe_fp8_prefill_route": ([P, P, I32, I64, P, P, P], ctypes.c_int),
+        "moe_fp8_prefill_run_logits": ([P, P, P, I32, I64, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -179,6 +184,19 @@ def moe_fp8_prefill_run(handle: int, x, ids, w, T: int, out, stream=None) -> int
     """Returns the MOE_* code (does not raise) so callers can test error paths."""
     return int(load_library().moe_fp8_prefill_run(ctypes.c_void_p(handle), _dev_ptr(x), _dev_ptr(ids),
                                                   _dev_ptr(w), T, _dev_ptr(out), _stream_ptr(stream)))
+
+
+def moe_fp8_prefill_route(handle: int, logits, router: int, T: int, ids, w, stream=None) -> int:
+    """Returns the MOE_* code."""
+    return int(load_library().moe_fp8_prefill_route(ctypes.c_void_p(handle), _dev_ptr(logits), router, T,
+                                                    _dev_ptr(ids), _dev_ptr(w), _stream_ptr(stream)))
+
+
+def moe_fp8_prefill_run_logits(handle: int, x, logits, router: int, T: int, out, stream=None) -> int:
+    """Returns the MOE_* code."""
+    return int(load_library().moe_fp8_prefill_run_logits(ctypes.c_void_p(handle), _dev_ptr(x),
+                                                         _dev_ptr(logits), router, T, _dev_ptr(out),
+                                                         _stream_ptr(stream)))
 
 
 def moe_fp8_prefill_status(handle: int) -> int:
@@ -299,6 +317,26 @@ class MoeFp8Prefill:
             dt = torch.float32 if self.out_dtype == MOE_DTYPE_F32 else torch.bfloat16
             out = torch.empty((T, self.H), dtype=dt, device=x.device)
         _check(moe_fp8_prefill_run(self.handle, x, ids, w, T, out, stream), "moe_fp8_prefill_run")
+        return out
+
+    def route(self, logits, router: int, stream=None):
+        """logits: float32 [T][E] device tensor -> (ids int32 [T][k], w float32 [T][k])."""
+        import torch
+        T = logits.shape[0]
+        ids = torch.empty((T, self.k), dtype=torch.int32, device=logits.device)
+        w = torch.empty((T, self.k), dtype=torch.float32, device=logits.device)
+        _check(moe_fp8_prefill_route(self.handle, logits, router, T, ids, w, stream), "moe_fp8_prefill_route")
+        return ids, w
+
+    def run_logits(self, x, logits, router: int, out=None, stream=None):
+        """x: bf16 [T][H], logits: float32 [T][E] (torch device tensors)."""
+        import torch
+        T = x.shape[0]
+        if out is None:
+            dt = torch.float32 if self.out_dtype == MOE_DTYPE_F32 else torch.bfloat16
+            out = torch.empty((T, self.H), dtype=dt, device=x.device)
+        _check(moe_fp8_prefill_run_logits(self.handle, x, logits, router, T, out, stream),
+               "moe_fp8_prefill_run_logits")
         return out
 
     def status(self) -> int:

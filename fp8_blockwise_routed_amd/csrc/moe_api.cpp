@@ -41,11 +41,13 @@ int64_t align256(int64_t n) { return (n + 255) & ~int64_t(255); }
 
 // Workspace pieces, in allocation order.
 struct WsSizes {
-  int64_t xq, sx, hq, sh, y, counts, offsets, perm, inv, small_tiles, big_tiles, n_tiles, err;
+  int64_t xq, sx, hq, sh, y, counts, offsets, perm, inv, small_tiles, big_tiles, n_tiles, err,
+      rids, rw;
   int64_t total() const {
     return align256(xq) + align256(sx) + align256(hq) + align256(sh) + align256(y) +
            align256(counts) + align256(offsets) + align256(perm) + align256(inv) +
-           align256(small_tiles) + align256(big_tiles) + align256(n_tiles) + align256(err);
+           align256(small_tiles) + align256(big_tiles) + align256(n_tiles) + align256(err) +
+           align256(rids) + align256(rw);
   }
 };
 
@@ -64,6 +66,8 @@ WsSizes ws_sizes(const Dims& m) {
   w.big_tiles = (m.P / kSmallRows + m.E + 1) * (int64_t)sizeof(Tile);
   w.n_tiles = 2 * 4;
   w.err = 4;
+  w.rids = m.P * 4;  // one pass's routed ids and weights (run_logits)
+  w.rw = m.P * 4;
   return w;
 }
 
@@ -103,6 +107,8 @@ struct moe_fp8_prefill {
   Tile* big_tiles = nullptr;
   int32_t* n_tiles = nullptr;
   int32_t* err = nullptr;
+  int32_t* rids = nullptr;
+  float* rw = nullptr;
   std::vector<void*> allocations;
   // state
   std::atomic<int> busy{0};
@@ -249,6 +255,95 @@ int get_stage_events(moe_fp8_prefill* h, StageEvents* out) {
   return MOE_OK;
 }
 
+// Checks and per-call stream handling shared by run() and run_logits(),
+// then the passes.  Exactly one of (ids, w) and logits is given.
+int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const float* w,
+               const float* logits, int32_t router, int64_t T, void* out, void* stream_) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  if (h->failed) return MOE_ERR_FAILED_STATE;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !out || !aligned16(x) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  if (logits ? (router != MOE_ROUTER_SOFTMAX && router != MOE_ROUTER_SIGMOID) : (!ids || !w))
+    return MOE_ERR_INVALID_ARG;
+  if (logits && h->m.k > kRouteMaxK) return MOE_ERR_UNSUPPORTED;
+  int expected = 0;
+  if (!h->busy.compare_exchange_strong(expected, 1)) return MOE_ERR_BUSY;
+  struct Release {
+    std::atomic<int>& b;
+    ~Release() { b.store(0); }
+  } release{h->busy};
+
+  hipStream_t s = (hipStream_t)stream_;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return fail(h);
+  if (cap != hipStreamCaptureStatusNone) return MOE_ERR_UNSUPPORTED;
+  if (h->inject_failure) {
+    h->inject_failure = false;
+    return fail(h);
+  }
+  if (h->has_last && h->last_stream != s && hipStreamWaitEvent(s, h->done, 0) != hipSuccess)
+    return fail(h);
+
+  const Dims& m = h->m;
+  const int64_t out_elem = h->desc.out_dtype == MOE_DTYPE_F32 ? 4 : 2;
+  // Upper bounds of the tile lists; the kernels read the real counts.
+  const int nb_dn = (int)(m.H / kBlock);
+
+  for (int64_t r0 = 0; r0 < T; r0 += m.max_rows) {
+    const int64_t t = (T - r0) < m.max_rows ? (T - r0) : m.max_rows;
+    const int64_t P = t * m.k;
+    StageEvents ev{};
+    if (h->timing) {
+      if (get_stage_events(h, &ev) != MOE_OK) return fail(h);
+      if (hipEventRecord(ev.ev[0], s) != hipSuccess) return fail(h);
+    }
+    const int32_t* ids_p = ids ? ids + r0 * m.k : h->rids;
+    const float* w_p = w ? w + r0 * m.k : h->rw;
+    if (logits) {
+      RouteArgs ra{logits + r0 * m.E, t, (int32_t)m.E, (int32_t)m.k, router, h->rids, h->rw};
+      if (launch_route(ra, s) != hipSuccess) return fail(h);
+    }
+    PlanArgs pa{ids_p, (int32_t)t, (int32_t)m.k, (int32_t)m.E, h->counts, h->offsets,
+                h->perm, h->inv, h->small_tiles, h->big_tiles, h->n_tiles, h->err};
+    if (launch_plan(pa, s) != hipSuccess) return fail(h);
+    if (h->timing && hipEventRecord(ev.ev[1], s) != hipSuccess) return fail(h);
+
+    QuantArgs qa{(const uint16_t*)x + r0 * m.H, (int32_t)t, (int32_t)m.H, h->xq, h->sx};
+    if (launch_quant(qa, s) != hipSuccess) return fail(h);
+    if (h->timing && hipEventRecord(ev.ev[2], s) != hipSuccess) return fail(h);
+
+    int g_small, g_big;
+    if (launch_gate_up_pair(h, t, P, nullptr, s, h->timing ? ev.ev[3] : nullptr) != hipSuccess)
+      return fail(h);
+    if (h->timing && hipEventRecord(ev.ev[4], s) != hipSuccess) return fail(h);
+
+    g_small = gemm_grid(h, m.E * nb_dn, false, false);
+    g_big = gemm_grid(h, (P / kSmallRows + m.E) * ((nb_dn + 1) / 2), true, false);
+    DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2, h->small_tiles, h->n_tiles, h->y};
+    if (launch_down(da, false, g_small, s) != hipSuccess) return fail(h);
+    if (h->timing && hipEventRecord(ev.ev[5], s) != hipSuccess) return fail(h);
+    da.tiles = h->big_tiles;
+    da.n_tiles = h->n_tiles + 1;
+    if (launch_down(da, true, g_big, s) != hipSuccess) return fail(h);
+    if (h->timing && hipEventRecord(ev.ev[6], s) != hipSuccess) return fail(h);
+
+    CombineArgs ca{h->y, h->inv, w_p, (int32_t)t, (int32_t)m.k, (int32_t)m.H,
+                   h->desc.routed_scale, h->desc.out_dtype == MOE_DTYPE_F32 ? 1 : 0,
+                   (uint8_t*)out + r0 * m.H * out_elem};
+    if (launch_combine(ca, s) != hipSuccess) return fail(h);
+    if (h->timing) {
+      if (hipEventRecord(ev.ev[7], s) != hipSuccess) return fail(h);
+      h->pending.push_back(ev);
+    }
+    h->last_T = t;
+  }
+  if (hipEventRecord(h->done, s) != hipSuccess) return fail(h);
+  h->last_stream = s;
+  h->has_last = true;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -349,6 +444,8 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   h->big_tiles = (Tile*)get(w.big_tiles);
   h->n_tiles = (int32_t*)get(w.n_tiles);
   h->err = (int32_t*)get(w.err);
+  h->rids = (int32_t*)get(w.rids);
+  h->rw = (float*)get(w.rw);
   if (!ok) {
     free_all(h);
     delete h;
@@ -375,80 +472,26 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
 }
 
 int moe_fp8_prefill_run(moe_fp8_prefill* h, const void* x, const int32_t* ids, const float* w,
-                        int64_t T, void* out, void* stream_) {
+                        int64_t T, void* out, void* stream) {
+  return run_passes(h, x, ids, w, nullptr, 0, T, out, stream);
+}
+
+int moe_fp8_prefill_run_logits(moe_fp8_prefill* h, const void* x, const float* logits,
+                               int32_t router, int64_t T, void* out, void* stream) {
+  if (!logits) return MOE_ERR_INVALID_ARG;
+  return run_passes(h, x, nullptr, nullptr, logits, router, T, out, stream);
+}
+
+int moe_fp8_prefill_route(moe_fp8_prefill* h, const float* logits, int32_t router, int64_t T,
+                          int32_t* ids, float* w, void* stream) {
   if (!h) return MOE_ERR_INVALID_ARG;
   if (h->failed) return MOE_ERR_FAILED_STATE;
-  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || (T > 0 && (!logits || !ids || !w))) return MOE_ERR_INVALID_ARG;
+  if (router != MOE_ROUTER_SOFTMAX && router != MOE_ROUTER_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (h->m.k > kRouteMaxK) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!x || !ids || !w || !out || !aligned16(x) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
-  int expected = 0;
-  if (!h->busy.compare_exchange_strong(expected, 1)) return MOE_ERR_BUSY;
-  struct Release {
-    std::atomic<int>& b;
-    ~Release() { b.store(0); }
-  } release{h->busy};
-
-  hipStream_t s = (hipStream_t)stream_;
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return fail(h);
-  if (cap != hipStreamCaptureStatusNone) return MOE_ERR_UNSUPPORTED;
-  if (h->inject_failure) {
-    h->inject_failure = false;
-    return fail(h);
-  }
-  if (h->has_last && h->last_stream != s && hipStreamWaitEvent(s, h->done, 0) != hipSuccess)
-    return fail(h);
-
-  const Dims& m = h->m;
-  const int64_t out_elem = h->desc.out_dtype == MOE_DTYPE_F32 ? 4 : 2;
-  // Upper bounds of the tile lists; the kernels read the real counts.
-  const int nb_dn = (int)(m.H / kBlock);
-
-  for (int64_t r0 = 0; r0 < T; r0 += m.max_rows) {
-    const int64_t t = (T - r0) < m.max_rows ? (T - r0) : m.max_rows;
-    const int64_t P = t * m.k;
-    StageEvents ev{};
-    if (h->timing) {
-      if (get_stage_events(h, &ev) != MOE_OK) return fail(h);
-      if (hipEventRecord(ev.ev[0], s) != hipSuccess) return fail(h);
-    }
-    PlanArgs pa{ids + r0 * m.k, (int32_t)t, (int32_t)m.k, (int32_t)m.E, h->counts, h->offsets,
-                h->perm, h->inv, h->small_tiles, h->big_tiles, h->n_tiles, h->err};
-    if (launch_plan(pa, s) != hipSuccess) return fail(h);
-    if (h->timing && hipEventRecord(ev.ev[1], s) != hipSuccess) return fail(h);
-
-    QuantArgs qa{(const uint16_t*)x + r0 * m.H, (int32_t)t, (int32_t)m.H, h->xq, h->sx};
-    if (launch_quant(qa, s) != hipSuccess) return fail(h);
-    if (h->timing && hipEventRecord(ev.ev[2], s) != hipSuccess) return fail(h);
-
-    int g_small, g_big;
-    if (launch_gate_up_pair(h, t, P, nullptr, s, h->timing ? ev.ev[3] : nullptr) != hipSuccess)
-      return fail(h);
-    if (h->timing && hipEventRecord(ev.ev[4], s) != hipSuccess) return fail(h);
-
-    g_small = gemm_grid(h, m.E * nb_dn, false, false);
-    g_big = gemm_grid(h, (P / kSmallRows + m.E) * ((nb_dn + 1) / 2), true, false);
-    DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2, h->small_tiles, h->n_tiles, h->y};
-    if (launch_down(da, false, g_small, s) != hipSuccess) return fail(h);
-    if (h->timing && hipEventRecord(ev.ev[5], s) != hipSuccess) return fail(h);
-    da.tiles = h->big_tiles;
-    da.n_tiles = h->n_tiles + 1;
-    if (launch_down(da, true, g_big, s) != hipSuccess) return fail(h);
-    if (h->timing && hipEventRecord(ev.ev[6], s) != hipSuccess) return fail(h);
-
-    CombineArgs ca{h->y, h->inv, w + r0 * m.k, (int32_t)t, (int32_t)m.k, (int32_t)m.H,
-                   h->desc.routed_scale, h->desc.out_dtype == MOE_DTYPE_F32 ? 1 : 0,
-                   (uint8_t*)out + r0 * m.H * out_elem};
-    if (launch_combine(ca, s) != hipSuccess) return fail(h);
-    if (h->timing) {
-      if (hipEventRecord(ev.ev[7], s) != hipSuccess) return fail(h);
-      h->pending.push_back(ev);
-    }
-    h->last_T = t;
-  }
-  if (hipEventRecord(h->done, s) != hipSuccess) return fail(h);
-  h->last_stream = s;
-  h->has_last = true;
+  RouteArgs ra{logits, T, (int32_t)h->m.E, (int32_t)h->m.k, router, ids, w};
+  if (launch_route(ra, (hipStream_t)stream) != hipSuccess) return fail(h);
   return MOE_OK;
 }
 

@@ -58,6 +58,15 @@ struct PlanArgs {
   int32_t* err;        // sticky bad-id flag
 };
 
+struct RouteArgs {
+  const float* logits;  // [T][E]
+  int64_t T;
+  int32_t E, k, kind;   // kind: 0 softmax, 1 sigmoid
+  int32_t* ids;         // [T][k]
+  float* w;             // [T][k]
+};
+constexpr int kRouteMaxK = 64;           // one lane per chosen slot
+constexpr int kRoutePerLane = kMaxExperts / 64;
 struct QuantArgs {
   const uint16_t* x;   // bf16 [T][H]
   int32_t T, H;
@@ -119,6 +128,7 @@ struct LayoutArgs {
 
 // Launchers (return the launch status).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s);
 hipError_t launch_gate_up(const GateUpArgs& a, bool big, int grid, hipStream_t s);
 hipError_t launch_down(const DownArgs& a, bool big, int grid, hipStream_t s);

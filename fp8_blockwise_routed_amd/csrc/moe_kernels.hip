@@ -214,6 +214,81 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ router --
+// One wave per token.  Each lane holds up to kRoutePerLane logits (experts
+// lane, lane + 64, ...) as 64-bit keys that order the experts for top-k:
+// high word = the logit's bits mapped to an unsigned order (NaN -> 1 and an
+// absent expert -> 0, below every number; -0 is folded into +0), low word =
+// ~id, so the larger key is the larger logit and, among equal logits, the
+// lower id.  k rounds of a wave-wide max pick the slots in descending order;
+// lane j then keeps slot j and computes its score and weight.
+
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+  uint32_t ord;
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) ord = 1u;   // NaN
+  else ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o);
+    const uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;  // the whole wave leaves
+  const float* l = a.logits + t * a.E;
+  uint64_t key[kRoutePerLane];
+#pragma unroll
+  for (int i = 0; i < kRoutePerLane; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < a.E ? route_key(l[e], e) : 0ull;
+  }
+  int my_id = 0;
+  for (int j = 0; j < a.k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < kRoutePerLane; ++i) best = key[i] > best ? key[i] : best;
+    const uint64_t win = wave_max_u64(best);
+#pragma unroll
+    for (int i = 0; i < kRoutePerLane; ++i)
+      if (key[i] == win) key[i] = 0ull;  // keys are unique (they hold the id)
+    if (lane == j) my_id = (int)~(uint32_t)win;
+  }
+  const bool slot = lane < a.k;
+  const float lj = slot ? l[my_id] : 0.0f;
+  const float l0 = __shfl(lj, 0);
+  float sc = 0.0f;
+  if (slot) sc = a.kind == 0 ? expf(lj - l0) : 1.0f / (1.0f + expf(-lj));
+  const float sum = wave_sum_f32(sc);
+  const bool no_mass = (a.kind == 0 && l0 == -INFINITY) || sum == 0.0f;
+  if (slot) {
+    a.ids[t * a.k + lane] = my_id;
+    a.w[t * a.k + lane] = no_mass ? 0.0f : sc / sum;
+  }
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(route_kernel, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------- quant --
 // 16 lanes per 128-column group, 8 BF16 values (16 bytes) per lane.
 

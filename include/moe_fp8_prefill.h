@@ -57,6 +57,7 @@ enum {
 
 enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 };
 enum { MOE_ACT_SILU_UNCLAMPED = 0 };
+enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 };
 
 /*
  * Layer description for create().  Weight layout is the checkpoint's:
@@ -126,6 +127,33 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
 int moe_fp8_prefill_run(moe_fp8_prefill* h, const void* x, const int32_t* ids,
                         const float* w, int64_t T, void* out, void* stream);
 
+/*
+ * The top-k router, on the device ("hpc-ops #80", gap table: the router's
+ * top-k belongs to the fused MoE step; "TensorFold #2852": routed slots in
+ * descending score).  For each token: the k experts with the largest logits,
+ * in descending order, ties to the lower expert id, a NaN logit below every
+ * number (sigmoid and exp are increasing, so this is the order of the scores;
+ * +0 and -0 are equal).  Weights in FP32, normalised over the chosen experts:
+ *   MOE_ROUTER_SOFTMAX: s_j = exp(l_j - l_0), w_j = s_j / sum(s)
+ *   MOE_ROUTER_SIGMOID: s_j = 1 / (1 + exp(-l_j)), w_j = s_j / sum(s)
+ * A chosen set with no mass (sum 0, or softmax with l_0 = -inf) gets zero
+ * weights.  logits : f32 [T][E], ids : i32 [T][k], w : f32 [T][k], device
+ * memory owned by the caller, on `stream`.  Needs k <= 64 (else
+ * MOE_ERR_UNSUPPORTED).  Touches no handle state besides the failed flag.
+ */
+int moe_fp8_prefill_route(moe_fp8_prefill* h, const float* logits, int32_t router, int64_t T,
+                          int32_t* ids, float* w, void* stream);
+
+/*
+ * run() from router logits: each pass routes its rows with the router above
+ * into the handle's workspace, then runs plan .. combine on those ids and
+ * weights.  Same rules as run(); logits : f32 [T][E] device memory.  The
+ * output equals run() given the ids and weights moe_fp8_prefill_route()
+ * returns for the same logits, bit for bit.
+ */
+int moe_fp8_prefill_run_logits(moe_fp8_prefill* h, const void* x, const float* logits,
+                               int32_t router, int64_t T, void* out, void* stream);
+
 /* Synchronises the handle's last stream; returns and clears device-detected
  * errors (MOE_ERR_BAD_EXPERT_ID), or MOE_ERR_FAILED_STATE, else MOE_OK. */
 int moe_fp8_prefill_status(moe_fp8_prefill* h);
@@ -179,7 +207,8 @@ int moe_fp8_prefill_debug_mfma(const uint8_t* a, const uint8_t* b, float* d);
 /* Per-launch GPU timing with HIP events on the run stream.  When enabled,
  * every pass records events between its kernel launches; read_timing()
  * synchronises and returns up to max_records rows (one per pass) of
- * MOE_NUM_STAGES milliseconds: plan, quantise, gate_up (1-subtile tiles),
+ * MOE_NUM_STAGES milliseconds: plan (with the router in run_logits),
+ * quantise, gate_up (1-subtile tiles),
  * gate_up (multi-subtile tiles), down (1-subtile), down (multi-subtile),
  * combine; then clears the record. */
 #define MOE_NUM_STAGES 7

@@ -160,3 +160,23 @@ def test_slice_layer(wl):
         stagewise_on_sample(moe, layer, x, ids, w, wl.rho, got, S, wl.name)
     finally:
         moe.close()
+
+
+def test_glm_run_logits_t4096(glm):
+    """The GLM layer from router logits (uniform draws, sigmoid top-8): the
+    on-device router's ids equal the oracle's, and run_logits() equals run()
+    on the routed ids and weights, bit for bit."""
+    layer, moe = glm
+    wl = gen.GLM_T4096
+    x, _ = gen.make_tokens(wl.T, wl.H, wl.seed, wl.outlier_frac)
+    logits = gen.make_logits(wl.T, wl.E, wl.route, wl.seed)
+    note(f"{wl.name}: run_logits")
+    xd, ld = dev_bf16(x), dev(logits)
+    got = moe.run_logits(xd, ld, pkg.MOE_ROUTER_SIGMOID)
+    ids_d, w_d = moe.route(ld, pkg.MOE_ROUTER_SIGMOID)
+    ref = moe.run(xd, ids_d, w_d)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    ids_o, w_o = oracle.route(logits, wl.k, oracle.ROUTE_SIGMOID)
+    assert np.array_equal(ids_d.cpu().numpy(), ids_o)
+    assert np.allclose(w_d.cpu().numpy(), w_o, rtol=8e-6, atol=1e-12)
