@@ -34,6 +34,7 @@ FAULTS = {
     "gate_up_swap": 12,
     "route_tie_high": 13,
     "route_all_experts": 14,
+    "shared_inside_rho": 15,
 }
 
 ROUTE_SOFTMAX = 0
@@ -86,13 +87,16 @@ def _load():
         lib.orc_plan.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
         lib.orc_plan.restype = ctypes.c_int64
         lib.orc_forward.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int32, P, P, P, ctypes.c_int64,
-                                    ctypes.c_float, ctypes.c_int32, P, ctypes.POINTER(_Debug)]
+                                    ctypes.c_float, ctypes.c_int32, P, ctypes.POINTER(_Debug),
+                                    ctypes.c_int32]
         lib.orc_forward.restype = ctypes.c_int64
         lib.orc_down_combine.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int32, P, P, P, P,
-                                         ctypes.c_int64, ctypes.c_float, ctypes.c_int32, P, P]
+                                         ctypes.c_int64, ctypes.c_float, ctypes.c_int32, P, P,
+                                         ctypes.c_int32]
         lib.orc_down_combine.restype = ctypes.c_int64
         lib.orc_bruteforce_fp64.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int32, P, P, P,
-                                            ctypes.c_int64, ctypes.c_double, ctypes.c_int32, P]
+                                            ctypes.c_int64, ctypes.c_double, ctypes.c_int32, P,
+                                            ctypes.c_int32]
         lib.orc_bruteforce_fp64.restype = ctypes.c_int32
         lib.orc_set_fault.argtypes = [ctypes.c_int32]
         lib.orc_set_fault.restype = None
@@ -195,9 +199,11 @@ def _layer_struct(layer):
 
 
 def forward(layer, x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, rho: float,
-            out_dtype: int = OUT_BF16, debug: bool = False):
+            out_dtype: int = OUT_BF16, debug: bool = False, n_shared: int = 0):
     """The layer on T tokens.  Returns out (u16 bf16 bits or f32 [T][H]) and,
-    with debug=True, a dict of the intermediate arrays (sorted-order rows)."""
+    with debug=True, a dict of the intermediate arrays (sorted-order rows).
+    n_shared: the last n_shared columns of ids / w are shared-expert slots,
+    added outside rho."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     w = np.ascontiguousarray(w, dtype=np.float32)
@@ -218,7 +224,8 @@ def forward(layer, x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, rho: floa
         dbg = _Debug(*(d[n].ctypes.data for n in
                        ("xq", "sx", "gu", "hq", "sh", "y", "counts", "offsets", "perm", "inv")))
     bad = _load().orc_forward(ctypes.byref(st), k, _p(x_bits), _p(ids), _p(w), T, float(rho),
-                              out_dtype, _p(out), ctypes.byref(dbg) if dbg is not None else None)
+                              out_dtype, _p(out), ctypes.byref(dbg) if dbg is not None else None,
+                              n_shared)
     del keep
     if bad < 0:
         raise ValueError("bad arguments")
@@ -231,7 +238,7 @@ def forward(layer, x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, rho: floa
 
 
 def down_combine(layer, hq: np.ndarray, sh: np.ndarray, ids: np.ndarray, w: np.ndarray, rho: float,
-                 out_dtype: int = OUT_BF16):
+                 out_dtype: int = OUT_BF16, n_shared: int = 0):
     """Continue the layer from given h codes (sorted order of the plan of ids).
     Returns (out, y)."""
     ids = np.ascontiguousarray(ids, dtype=np.int32)
@@ -243,14 +250,14 @@ def down_combine(layer, hq: np.ndarray, sh: np.ndarray, ids: np.ndarray, w: np.n
     y = np.empty((max(hq.shape[0], 1), layer.H), np.float32)
     st, keep = _layer_struct(layer)
     P = _load().orc_down_combine(ctypes.byref(st), k, _p(hq), _p(sh), _p(ids), _p(w), T, float(rho),
-                                 out_dtype, _p(out), _p(y))
+                                 out_dtype, _p(out), _p(y), n_shared)
     del keep
     if P < 0 or P != hq.shape[0]:
         raise ValueError("bad arguments or h rows do not match the plan")
     return out, y[:P]
 
 
-def bruteforce_fp64(layer, x_bits, ids, w, rho, quantize_activations=True) -> np.ndarray:
+def bruteforce_fp64(layer, x_bits, ids, w, rho, quantize_activations=True, n_shared: int = 0) -> np.ndarray:
     """Dense FP64 evaluation (tiny inputs only).  out f64[T][H]."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
@@ -259,6 +266,6 @@ def bruteforce_fp64(layer, x_bits, ids, w, rho, quantize_activations=True) -> np
     out = np.empty((T, layer.H), np.float64)
     st, keep = _layer_struct(layer)
     _load().orc_bruteforce_fp64(ctypes.byref(st), k, _p(x_bits), _p(ids), _p(w), T, float(rho),
-                                1 if quantize_activations else 0, _p(out))
+                                1 if quantize_activations else 0, _p(out), n_shared)
     del keep
     return out

@@ -53,6 +53,7 @@ enum {
   FAULT_GATE_UP_SWAP = 12,      /* silu(u) * g                               */
   FAULT_ROUTE_TIE_HIGH = 13,    /* router ties go to the higher expert id    */
   FAULT_ROUTE_ALL_EXPERTS = 14, /* softmax weights normalised over all E     */
+  FAULT_SHARED_INSIDE_RHO = 15, /* shared slots scaled by rho too            */
 };
 static int g_fault = FAULT_NONE;
 void orc_set_fault(int32_t f) { g_fault = f; }
@@ -285,11 +286,15 @@ static float silu_mul(float g, float u) {
 
 /* Down projection of the decoded h rows (sorted order) and the weighted
  * combine: y[p] = D_e . h[p] blockwise as above; out[t] = cast(rho * sum_j
- * w[t,j] * y[inv[t*k+j]]), FP32, ascending j, one rounding at the end. */
+ * w[t,j] * y[inv[t*k+j]]), FP32, ascending j, one rounding at the end.
+ * The last n_shared slots of a token are always-on shared-expert slots
+ * ("TensorFold #2852": nine slots planned over E+1 expert ids): they are
+ * added after the routed sum is scaled, outside rho,
+ *   out[t] = cast(rho * sum_{j < k-n_shared} w y  +  sum_{j >= k-n_shared} w y). */
 static void down_and_combine(const orc_layer* L, int64_t k, const float* hd, const float* sh,
                              const int32_t* counts, const int32_t* offsets, const int32_t* inv,
                              const float* w, int64_t T, float rho, int32_t out_dtype, void* out,
-                             float* y) {
+                             float* y, int64_t n_shared) {
   const int64_t E = L->E, H = L->H, I = L->I;
   const int64_t Ip = 128 * ((I + 127) / 128), nH = H / 128, nI = Ip / 128;
 #pragma omp parallel
@@ -320,11 +325,15 @@ static void down_and_combine(const orc_layer* L, int64_t k, const float* hd, con
   for (int64_t t = 0; t < T; ++t) {
     for (int64_t n = 0; n < H; ++n) {
       float acc = 0.0f;
-      for (int64_t j = 0; j < k; ++j) {
+      for (int64_t j = 0; j < k - n_shared; ++j) {
         int32_t p = inv[t * k + j];
         if (p >= 0) acc = acc + w[t * k + j] * y[(int64_t)p * H + n];
       }
       float v = r * acc;
+      for (int64_t j = k - n_shared; j < k; ++j) {
+        int32_t p = inv[t * k + j];
+        if (p >= 0) v = v + (g_fault == FAULT_SHARED_INSIDE_RHO ? r : 1.0f) * w[t * k + j] * y[(int64_t)p * H + n];
+      }
       if (out_dtype == 0)
         ((uint16_t*)out)[t * H + n] = (uint16_t)orc_f32_to_bf16(v);
       else
@@ -337,14 +346,16 @@ static void down_and_combine(const orc_layer* L, int64_t k, const float* hd, con
  * The routed-expert layer on T tokens.
  * x: bf16 bits u16[T][H]; ids: i32[T][k]; w: f32[T][k].
  * out_dtype 0: out is bf16 bits u16[T][H]; 1: out is f32[T][H].
+ * n_shared: the last n_shared slots of each token are shared-expert slots
+ * (see down_and_combine); 0 for the routed layer alone.
  * Returns the number of bad expert ids (those slots are skipped), or -1 on a
  * bad argument.
  */
 int64_t orc_forward(const orc_layer* L, int32_t k, const uint16_t* x, const int32_t* ids,
                     const float* w, int64_t T, float rho, int32_t out_dtype, void* out,
-                    const orc_debug* dbg) {
+                    const orc_debug* dbg, int32_t n_shared) {
   const int64_t E = L->E, H = L->H, I = L->I;
-  if (E < 1 || k < 1 || H % 128 != 0 || I < 1 || T < 0) return -1;
+  if (E < 1 || k < 1 || H % 128 != 0 || I < 1 || T < 0 || n_shared < 0 || n_shared >= k) return -1;
   const int64_t Ip = 128 * ((I + 127) / 128), nH = H / 128, nI = Ip / 128;
   const int64_t S = T * k;
 
@@ -398,7 +409,7 @@ int64_t orc_forward(const orc_layer* L, int32_t k, const uint16_t* x, const int3
   for (int64_t i = 0; i < P * Ip; ++i) hd[i] = orc_e4m3_decode(hq[i]);
 
   float* y = (float*)malloc(sizeof(float) * (size_t)(P * H + 1));
-  down_and_combine(L, k, hd, sh, counts, offsets, inv, w, T, rho, out_dtype, out, y);
+  down_and_combine(L, k, hd, sh, counts, offsets, inv, w, T, rho, out_dtype, out, y, n_shared);
 
   if (dbg) {
     if (dbg->xq) memcpy(dbg->xq, xq, (size_t)(T * H));
@@ -481,7 +492,7 @@ static void qdq_fp64(const double* v, int64_t n, double* out, const double* mag)
  */
 int32_t orc_bruteforce_fp64(const orc_layer* L, int32_t k, const uint16_t* x,
                             const int32_t* ids, const float* w, int64_t T, double rho,
-                            int32_t quantize_activations, double* out) {
+                            int32_t quantize_activations, double* out, int32_t n_shared) {
   const int64_t E = L->E, H = L->H, I = L->I;
   const int64_t nI = (I + 127) / 128, nH = H / 128, Ip = 128 * nI;
   double mag[127];
@@ -490,6 +501,7 @@ int32_t orc_bruteforce_fp64(const orc_layer* L, int32_t k, const uint16_t* x,
   double* xa = (double*)malloc(sizeof(double) * (size_t)H);
   double* hv = (double*)malloc(sizeof(double) * (size_t)Ip);
   double* ha = (double*)malloc(sizeof(double) * (size_t)Ip);
+  double* os = (double*)malloc(sizeof(double) * (size_t)H);
   for (int64_t t = 0; t < T; ++t) {
     for (int64_t c = 0; c < H; ++c) xv[c] = (double)orc_bf16_to_f32(x[t * H + c]);
     if (quantize_activations)
@@ -497,13 +509,16 @@ int32_t orc_bruteforce_fp64(const orc_layer* L, int32_t k, const uint16_t* x,
     else
       memcpy(xa, xv, sizeof(double) * (size_t)H);
     double* o = out + t * H;
-    for (int64_t n = 0; n < H; ++n) o[n] = 0.0;
+    for (int64_t n = 0; n < H; ++n) o[n] = os[n] = 0.0;
     for (int64_t e = 0; e < E; ++e) {
-      double coef = 0.0;
+      double coef = 0.0, coef_s = 0.0;  /* routed slots; shared slots (outside rho) */
       int chosen = 0;
       for (int64_t j = 0; j < k; ++j)
         if (ids[t * k + j] == e) {
-          coef += (double)w[t * k + j];
+          if (j < k - n_shared)
+            coef += (double)w[t * k + j];
+          else
+            coef_s += (double)w[t * k + j];
           chosen = 1;
         }
       if (!chosen) continue;
@@ -530,10 +545,12 @@ int32_t orc_bruteforce_fp64(const orc_layer* L, int32_t k, const uint16_t* x,
           yv += ha[i] * (double)orc_e4m3_decode(L->down[(e * H + n) * I + i]) *
                 (double)L->down_scale[(e * nH + n / 128) * nI + i / 128];
         o[n] += coef * yv;
+        os[n] += coef_s * yv;
       }
     }
-    for (int64_t n = 0; n < H; ++n) o[n] *= rho;
+    for (int64_t n = 0; n < H; ++n) o[n] = o[n] * rho + os[n];
   }
+  free(os);
   free(xv);
   free(xa);
   free(hv);
@@ -550,9 +567,9 @@ int32_t orc_bruteforce_fp64(const orc_layer* L, int32_t k, const uint16_t* x,
  */
 int64_t orc_down_combine(const orc_layer* L, int32_t k, const uint8_t* hq, const float* sh,
                          const int32_t* ids, const float* w, int64_t T, float rho,
-                         int32_t out_dtype, void* out, float* y_out) {
+                         int32_t out_dtype, void* out, float* y_out, int32_t n_shared) {
   const int64_t E = L->E, H = L->H, I = L->I;
-  if (E < 1 || k < 1 || H % 128 != 0 || I < 1 || T < 0) return -1;
+  if (E < 1 || k < 1 || H % 128 != 0 || I < 1 || T < 0 || n_shared < 0 || n_shared >= k) return -1;
   const int64_t Ip = 128 * ((I + 127) / 128), S = T * k;
   int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
   int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
@@ -563,7 +580,7 @@ int64_t orc_down_combine(const orc_layer* L, int32_t k, const uint8_t* hq, const
   float* hd = (float*)malloc(sizeof(float) * (size_t)(P * Ip + 1));
   for (int64_t i = 0; i < P * Ip; ++i) hd[i] = orc_e4m3_decode(hq[i]);
   float* y = (float*)malloc(sizeof(float) * (size_t)(P * H + 1));
-  down_and_combine(L, k, hd, sh, counts, offsets, inv, w, T, rho, out_dtype, out, y);
+  down_and_combine(L, k, hd, sh, counts, offsets, inv, w, T, rho, out_dtype, out, y, n_shared);
   if (y_out) memcpy(y_out, y, sizeof(float) * (size_t)(P * H));
   free(counts);
   free(offsets);

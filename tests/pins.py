@@ -19,6 +19,8 @@ What pins what:
              experts and scipy's expit; the generator's own FP64 top-k on the
              same draws; tie, -inf, NaN and k = E cases; shift invariance of
              the softmax weights.
+  shared     the FP64 brute force with the shared slot outside rho; the
+             routed layer plus the shared expert evaluated on its own.
   layer      the FP64 dense brute force (different loop structure, FP64,
              exhaustive-search encoder); a dense gated FFN evaluated with torch
              float8 casts and float64 matmuls; an integer-exact case compared
@@ -555,6 +557,42 @@ def pin_nan_row_isolation():
     return _ok(ok, "NaN/Inf did not stay in its row")
 
 
+def shared_case(seed=12):
+    """E=4 routed experts + 1 shared (index 4), k=2 routed slots + the shared slot."""
+    E, k, H, I, T = 4, 2, 256, 192, 20
+    layer = gen.make_layer(E + 1, H, I, seed=seed)
+    x, _ = gen.make_tokens(T, H, seed=seed, outlier_frac=0.1)
+    ids, w = gen.make_routing(T, E, k, gen.ROUTE_SIGMOID_NORMAL, seed=seed)
+    ids[3, 1] = -1
+    ids_x = np.concatenate([ids, np.full((T, 1), E, np.int32)], axis=1)
+    w_x = np.concatenate([w, np.ones((T, 1), np.float32)], axis=1)
+    return layer, x, ids, w, ids_x, w_x, E
+
+
+def pin_shared_vs_bruteforce(tol=2e-3):
+    layer, x, ids, w, ids_x, w_x, E = shared_case()
+    got = oracle.forward(layer, x, ids_x, w_x, 2.5, oracle.OUT_F32, n_shared=1)
+    ref = oracle.bruteforce_fp64(layer, x, ids_x, w_x, 2.5, n_shared=1)
+    worst = float(rel_l2_rows(got.astype(np.float64), ref).max())
+    return _ok(worst <= tol, f"shared slot vs brute force: worst rel L2 {worst:.2e}")
+
+
+def pin_shared_composition():
+    """Routed output (FP32) plus the shared expert's own output, added once:
+    the same bits as the layer with the shared slot."""
+    layer, x, ids, w, ids_x, w_x, E = shared_case()
+    got = oracle.forward(layer, x, ids_x, w_x, 2.5, oracle.OUT_F32, n_shared=1)
+    routed = oracle.forward(layer, x, ids, w, 2.5, oracle.OUT_F32)
+    one = gen.Layer(1, layer.H, layer.I, *(a[E:E + 1] for a in (layer.gate, layer.up, layer.down,
+                                                            layer.gate_scale, layer.up_scale,
+                                                            layer.down_scale)))
+    T = x.shape[0]
+    ys = oracle.forward(one, x, np.zeros((T, 1), np.int32), np.ones((T, 1), np.float32), 1.0,
+                           oracle.OUT_F32)
+    return _ok(np.array_equal((routed + ys).view(np.uint32), got.view(np.uint32)),
+               "shared slot is not the routed layer plus the shared expert")
+
+
 ALL_PINS = {
     "decode_golden": pin_decode_golden,
     "decode_vs_torch": pin_decode_vs_torch,
@@ -583,4 +621,6 @@ ALL_PINS = {
     "rows_independent": pin_rows_independent,
     "skip_slot_equals_removed": pin_skip_slot_equals_removed,
     "nan_row_isolation": pin_nan_row_isolation,
+    "shared_vs_bruteforce": pin_shared_vs_bruteforce,
+    "shared_composition": pin_shared_composition,
 }

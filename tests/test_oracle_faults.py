@@ -24,6 +24,7 @@ CAUGHT_BY = {
     "gate_up_swap": ["ffn_vs_bruteforce", "activation_from_gu"],
     "route_tie_high": ["route_ids_vs_sort", "route_special_rows"],
     "route_all_experts": ["route_weights_vs_scipy", "route_special_rows"],
+    "shared_inside_rho": ["shared_vs_bruteforce", "shared_composition"],
 }
 
 
