@@ -186,10 +186,15 @@ def cpu_baseline(layer, wl, x, ids, w, n_tokens, repeats):
     """The oracle, as it stands, on the first n_tokens rows of the same batch:
     median wall clock of `repeats` runs."""
     import oracle
+    import numpy as np
+    ids, w = ids[:n_tokens], w[:n_tokens]
+    if wl.shared:  # the shared expert's slot, id E and weight 1, last
+        ids = np.concatenate([ids, np.full((n_tokens, 1), wl.E, np.int32)], axis=1)
+        w = np.concatenate([w, np.ones((n_tokens, 1), np.float32)], axis=1)
     times = []
     for _ in range(repeats):
         t0 = time.perf_counter()
-        oracle.forward(layer, x[:n_tokens], ids[:n_tokens], w[:n_tokens], wl.rho, oracle.OUT_BF16)
+        oracle.forward(layer, x[:n_tokens], ids, w, wl.rho, oracle.OUT_BF16, n_shared=wl.shared)
         times.append(time.perf_counter() - t0)
     dt = sorted(times)[len(times) // 2]
     return dict(value=n_tokens / dt, unit="tokens/s", cores=oracle.max_threads(), kind="oracle",
@@ -244,11 +249,11 @@ def main() -> int:
     torch.cuda.set_device(0)
     log(f"[bench] generating {wl.name}")
     t0 = time.perf_counter()
-    layer = gen.make_layer(wl.E, wl.H, wl.I, seed=wl.seed)
+    layer = gen.make_layer(wl.E + wl.shared, wl.H, wl.I, seed=wl.seed)
     x, ids, w, _ = gen.make_inputs(wl)
     log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; creating the handle")
     moe = pkg.MoeFp8Prefill(layer, wl.k, routed_scale=wl.rho, max_rows=8192,
-                            out_dtype=pkg.MOE_DTYPE_BF16)
+                            out_dtype=pkg.MOE_DTYPE_BF16, shared_experts=wl.shared)
     xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
     idd = torch.from_numpy(ids).cuda()
     wd = torch.from_numpy(w).cuda()
@@ -271,7 +276,8 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    counts, _, _, _ = pkg.moe_fp8_prefill_debug_plan(moe.handle, wl.E, wl.T * wl.k)
+    counts, _, _, _ = pkg.moe_fp8_prefill_debug_plan(moe.handle, wl.E + wl.shared,
+                                                     wl.T * (wl.k + wl.shared))
     work = algorithmic_work(wl, counts)
 
     timing = not args.no_timing_events
@@ -297,7 +303,8 @@ def main() -> int:
         "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
         "config": {"workload": wl.name, "experts": wl.E, "top_k": wl.k, "hidden": wl.H,
                    "intermediate": wl.I, "rows": wl.T, "routed_scale": wl.rho,
-                   "outlier_rows": wl.outlier_frac, "seed": wl.seed},
+                   "outlier_rows": wl.outlier_frac, "seed": wl.seed,
+                   "shared_experts": wl.shared},
     }
     res["path"] = {
         "algorithmic_bytes": work["path_bytes"], "algorithmic_flops": work["path_flops"],

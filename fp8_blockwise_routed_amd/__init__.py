@@ -60,7 +60,7 @@ class moe_fp8_prefill_desc(ctypes.Structure):
         ("routed_scale", ctypes.c_float), ("weights_on_device", ctypes.c_int32),
         ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
         ("gate_scale", ctypes.c_void_p), ("up_scale", ctypes.c_void_p), ("down_scale", ctypes.c_void_p),
-        ("stream", ctypes.c_void_p),
+        ("stream", ctypes.c_void_p), ("shared_experts", ctypes.c_int32),
     ]
 
 
@@ -143,20 +143,22 @@ def _check(rc: int, where: str) -> None:
 
 def make_desc(layer, top_k: int, max_rows: int = 8192, out_dtype: int = MOE_DTYPE_BF16,
               routed_scale: float = 1.0, activation: int = MOE_ACT_SILU_UNCLAMPED,
-              block: int = 128, stream=None, on_device: bool = False):
+              block: int = 128, stream=None, on_device: bool = False, shared_experts: int = 0):
     """Description for a layer held as numpy arrays (or, with on_device=True,
     torch device tensors) with fields gate, up, down, gate_scale, up_scale,
-    down_scale, E, H, I.  Keep the returned arrays alive until create()."""
+    down_scale, E, H, I.  With shared_experts=1 the arrays hold layer.E
+    experts, the last one shared (E - 1 routed).  Keep the returned arrays
+    alive until create()."""
     arrs = [layer.gate, layer.up, layer.down, layer.gate_scale, layer.up_scale, layer.down_scale]
     if on_device:
         ptrs = [a.data_ptr() for a in arrs]
     else:
         arrs = [np.ascontiguousarray(a) for a in arrs]
         ptrs = [a.ctypes.data for a in arrs]
-    d = moe_fp8_prefill_desc(ctypes.sizeof(moe_fp8_prefill_desc), layer.E, top_k, layer.H, layer.I,
-                             max_rows, out_dtype, activation, block, routed_scale,
+    d = moe_fp8_prefill_desc(ctypes.sizeof(moe_fp8_prefill_desc), layer.E - shared_experts, top_k,
+                             layer.H, layer.I, max_rows, out_dtype, activation, block, routed_scale,
                              1 if on_device else 0, *ptrs,
-                             None if stream is None else _stream_ptr(stream).value)
+                             None if stream is None else _stream_ptr(stream).value, shared_experts)
     return d, arrs
 
 
@@ -300,12 +302,15 @@ class MoeFp8Prefill:
     up_scale, down_scale and E, H, I (the canonical checkpoint layout)."""
 
     def __init__(self, layer, top_k: int, routed_scale: float = 1.0, max_rows: int = 8192,
-                 out_dtype: int = MOE_DTYPE_BF16, on_device: bool = False):
-        self.E, self.H, self.I, self.k = layer.E, layer.H, layer.I, top_k
+                 out_dtype: int = MOE_DTYPE_BF16, on_device: bool = False, shared_experts: int = 0):
+        # E, k: routed experts and slots; the shared expert is the arrays' last
+        self.E, self.H, self.I, self.k = layer.E - shared_experts, layer.H, layer.I, top_k
+        self.shared = shared_experts
         self.Ip = 128 * ((layer.I + 127) // 128)
         self.out_dtype = out_dtype
         self.max_rows = max_rows
-        desc, keep = make_desc(layer, top_k, max_rows, out_dtype, routed_scale, on_device=on_device)
+        desc, keep = make_desc(layer, top_k, max_rows, out_dtype, routed_scale, on_device=on_device,
+                               shared_experts=shared_experts)
         self.handle = moe_fp8_prefill_create(desc)
         del keep
 

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstddef>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -20,13 +21,24 @@ using namespace moe;
 namespace {
 
 struct Dims {
+  // E, k count the shared expert and its slot; Er, kr are the routed ones
   int64_t E, k, H, I, Ip, nH, nI, max_rows, P;  // P = max_rows * k
+  int64_t Er, kr, shared;
 };
+
+constexpr int32_t kDescSizeNoShared = (int32_t)offsetof(moe_fp8_prefill_desc, shared_experts);
+
+bool has_shared_field(const moe_fp8_prefill_desc* d) {
+  return d->struct_size == (int32_t)sizeof(moe_fp8_prefill_desc);
+}
 
 Dims dims_of(const moe_fp8_prefill_desc* d) {
   Dims m;
-  m.E = d->num_experts;
-  m.k = d->top_k;
+  m.shared = has_shared_field(d) ? d->shared_experts : 0;
+  m.Er = d->num_experts;
+  m.kr = d->top_k;
+  m.E = m.Er + m.shared;
+  m.k = m.kr + m.shared;
   m.H = d->hidden;
   m.I = d->inter;
   m.Ip = kBlock * ((m.I + kBlock - 1) / kBlock);
@@ -66,8 +78,8 @@ WsSizes ws_sizes(const Dims& m) {
   w.big_tiles = (m.P / kSmallRows + m.E + 1) * (int64_t)sizeof(Tile);
   w.n_tiles = 2 * 4;
   w.err = 4;
-  w.rids = m.P * 4;  // one pass's routed ids and weights (run_logits)
-  w.rw = m.P * 4;
+  w.rids = m.max_rows * m.kr * 4;  // one pass's routed ids and weights (run_logits)
+  w.rw = m.max_rows * m.kr * 4;
   return w;
 }
 
@@ -266,7 +278,7 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
   if (!x || !out || !aligned16(x) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
   if (logits ? (router != MOE_ROUTER_SOFTMAX && router != MOE_ROUTER_SIGMOID) : (!ids || !w))
     return MOE_ERR_INVALID_ARG;
-  if (logits && h->m.k > kRouteMaxK) return MOE_ERR_UNSUPPORTED;
+  if (logits && h->m.kr > kRouteMaxK) return MOE_ERR_UNSUPPORTED;
   int expected = 0;
   if (!h->busy.compare_exchange_strong(expected, 1)) return MOE_ERR_BUSY;
   struct Release {
@@ -298,14 +310,15 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
       if (get_stage_events(h, &ev) != MOE_OK) return fail(h);
       if (hipEventRecord(ev.ev[0], s) != hipSuccess) return fail(h);
     }
-    const int32_t* ids_p = ids ? ids + r0 * m.k : h->rids;
-    const float* w_p = w ? w + r0 * m.k : h->rw;
+    const int32_t* ids_p = ids ? ids + r0 * m.kr : h->rids;
+    const float* w_p = w ? w + r0 * m.kr : h->rw;
     if (logits) {
-      RouteArgs ra{logits + r0 * m.E, t, (int32_t)m.E, (int32_t)m.k, router, h->rids, h->rw};
+      RouteArgs ra{logits + r0 * m.Er, t, (int32_t)m.Er, (int32_t)m.kr, router, h->rids, h->rw};
       if (launch_route(ra, s) != hipSuccess) return fail(h);
     }
-    PlanArgs pa{ids_p, (int32_t)t, (int32_t)m.k, (int32_t)m.E, h->counts, h->offsets,
-                h->perm, h->inv, h->small_tiles, h->big_tiles, h->n_tiles, h->err};
+    PlanArgs pa{ids_p, (int32_t)t, (int32_t)m.k, (int32_t)m.E, (int32_t)m.kr, (int32_t)m.Er,
+                h->counts, h->offsets, h->perm, h->inv, h->small_tiles, h->big_tiles,
+                h->n_tiles, h->err};
     if (launch_plan(pa, s) != hipSuccess) return fail(h);
     if (h->timing && hipEventRecord(ev.ev[1], s) != hipSuccess) return fail(h);
 
@@ -328,7 +341,7 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
     if (launch_down(da, true, g_big, s) != hipSuccess) return fail(h);
     if (h->timing && hipEventRecord(ev.ev[6], s) != hipSuccess) return fail(h);
 
-    CombineArgs ca{h->y, h->inv, w_p, (int32_t)t, (int32_t)m.k, (int32_t)m.H,
+    CombineArgs ca{h->y, h->inv, w_p, (int32_t)t, (int32_t)m.k, (int32_t)m.H, (int32_t)m.kr,
                    h->desc.routed_scale, h->desc.out_dtype == MOE_DTYPE_F32 ? 1 : 0,
                    (uint8_t*)out + r0 * m.H * out_elem};
     if (launch_combine(ca, s) != hipSuccess) return fail(h);
@@ -364,7 +377,10 @@ const char* moe_fp8_prefill_strerror(int code) {
 
 int moe_fp8_prefill_validate(const moe_fp8_prefill_desc* d) {
   if (!d) return MOE_ERR_INVALID_ARG;
-  if (d->struct_size != (int32_t)sizeof(moe_fp8_prefill_desc)) return MOE_ERR_INVALID_ARG;
+  if (d->struct_size != (int32_t)sizeof(moe_fp8_prefill_desc) && d->struct_size != kDescSizeNoShared)
+    return MOE_ERR_INVALID_ARG;
+  const int32_t shared = has_shared_field(d) ? d->shared_experts : 0;
+  if (shared != 0 && shared != 1) return MOE_ERR_UNSUPPORTED;
   if (!d->gate || !d->up || !d->down || !d->gate_scale || !d->up_scale || !d->down_scale)
     return MOE_ERR_INVALID_ARG;
   if (d->num_experts < 1 || d->top_k < 1 || d->hidden < 1 || d->inter < 1 || d->max_rows < 1)
@@ -374,7 +390,7 @@ int moe_fp8_prefill_validate(const moe_fp8_prefill_desc* d) {
   if (d->out_dtype != MOE_DTYPE_BF16 && d->out_dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
   if (d->hidden % kBlock != 0) return MOE_ERR_UNSUPPORTED;
   if (d->hidden > kMaxKBlocks * kBlock || d->inter > kMaxKBlocks * kBlock) return MOE_ERR_UNSUPPORTED;
-  if (d->num_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (d->num_experts + shared > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (d->top_k > d->num_experts || d->top_k > 256) return MOE_ERR_UNSUPPORTED;
   if (!std::isfinite(d->routed_scale)) return MOE_ERR_INVALID_ARG;
   const Dims m = dims_of(d);
@@ -405,7 +421,10 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   if (rc != MOE_OK) return rc;
   moe_fp8_prefill* h = new (std::nothrow) moe_fp8_prefill();
   if (!h) return MOE_ERR_OUT_OF_MEMORY;
-  h->desc = *d;
+  // a caller's description may end before shared_experts: copy what it has
+  memcpy(&h->desc, d, (size_t)d->struct_size);
+  if (!has_shared_field(d)) h->desc.shared_experts = 0;
+  h->desc.struct_size = (int32_t)sizeof(moe_fp8_prefill_desc);
   h->m = dims_of(d);
   const Dims& m = h->m;
   if (hipGetDevice(&h->device) != hipSuccess) {
@@ -488,9 +507,9 @@ int moe_fp8_prefill_route(moe_fp8_prefill* h, const float* logits, int32_t route
   if (h->failed) return MOE_ERR_FAILED_STATE;
   if (T < 0 || (T > 0 && (!logits || !ids || !w))) return MOE_ERR_INVALID_ARG;
   if (router != MOE_ROUTER_SOFTMAX && router != MOE_ROUTER_SIGMOID) return MOE_ERR_INVALID_ARG;
-  if (h->m.k > kRouteMaxK) return MOE_ERR_UNSUPPORTED;
+  if (h->m.kr > kRouteMaxK) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  RouteArgs ra{logits, T, (int32_t)h->m.E, (int32_t)h->m.k, router, ids, w};
+  RouteArgs ra{logits, T, (int32_t)h->m.Er, (int32_t)h->m.kr, router, ids, w};
   if (launch_route(ra, (hipStream_t)stream) != hipSuccess) return fail(h);
   return MOE_OK;
 }

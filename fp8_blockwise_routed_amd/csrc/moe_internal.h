@@ -46,8 +46,9 @@ struct Tile {
 };
 
 struct PlanArgs {
-  const int32_t* ids;  // [T*k]
-  int32_t T, k, E;
+  const int32_t* ids;  // [T][k_routed]
+  int32_t T, k, E;     // slots per token and experts, a shared expert included
+  int32_t k_routed, E_routed;  // slots k_routed..k-1 of a token are the shared expert E-1
   int32_t* counts;     // [E]
   int32_t* offsets;    // [E+1]
   int32_t* perm;       // [T*k]
@@ -104,8 +105,9 @@ struct DownArgs {
 struct CombineArgs {
   const float* y;      // [P][H]
   const int32_t* inv;  // [T*k]
-  const float* w;      // [T][k]
-  int32_t T, k, H;
+  const float* w;      // [T][k_routed]
+  int32_t T, k, H;     // k: slots per token, the shared slot (weight 1) last
+  int32_t k_routed;
   float rho;
   int32_t out_f32;
   void* out;

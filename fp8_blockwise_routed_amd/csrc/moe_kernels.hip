@@ -123,6 +123,20 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   return base + x - v;
 }
 
+// Expert of slot f = t*k + j: the caller's id for a routed slot (ids >= the
+// routed expert count are flagged and skipped), the shared expert for the
+// trailing slot.
+__device__ __forceinline__ int slot_expert(const PlanArgs& a, int f, bool& bad) {
+  const int t = f / a.k, j = f - t * a.k;
+  if (j >= a.k_routed) return a.E - 1;
+  const int e = a.ids[t * a.k_routed + j];
+  if (e >= a.E_routed) {
+    bad = true;
+    return -1;
+  }
+  return e;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int cursor[kMaxExperts];
@@ -134,11 +148,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   for (int e = tid; e < kMaxExperts; e += kPlanThreads) cnt[e] = 0;
   for (int i = tid; i < kPlanWaves * kMaxExperts; i += kPlanThreads) (&wcnt[0][0])[i] = 0;
   __syncthreads();
-  int bad = 0;
+  bool bad = false;
   for (int f = tid; f < P; f += kPlanThreads) {
-    const int e = a.ids[f];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-    else if (e >= E) bad = 1;
+    const int e = slot_expert(a, f, bad);
+    if (e >= 0) atomicAdd(&cnt[e], 1);
   }
   if (bad) *a.err = 1;
   __syncthreads();
@@ -178,8 +191,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int c0 = 0; c0 < P; c0 += kPlanThreads) {
     const int f = c0 + tid;
-    const int e = f < P ? a.ids[f] : -1;
-    const bool valid = e >= 0 && e < E;
+    bool ignored = false;
+    const int e = f < P ? slot_expert(a, f, ignored) : -1;
+    const bool valid = e >= 0;
     uint64_t same = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 10; ++b) {
@@ -1128,14 +1142,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int k = a.k, H = a.H;
   __shared__ int pos[256];
   __shared__ float wt[256];
+  const int kr = a.k_routed;
   for (int j = threadIdx.x; j < k; j += 256) {
     pos[j] = a.inv[(size_t)t * k + j];
-    wt[j] = a.w[(size_t)t * k + j];
+    wt[j] = j < kr ? a.w[(size_t)t * kr + j] : 1.0f;
   }
   __syncthreads();
   for (int c = (blockIdx.y * 256 + threadIdx.x) * 4; c < H; c += gridDim.y * 256 * 4) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
+    for (int j = 0; j < kr; ++j) {
       const int p = pos[j];
       if (p >= 0) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(a.y + (size_t)p * H + c);
@@ -1146,7 +1161,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
         acc[3] = acc[3] + wj * v[3];
       }
     }
-    const f32x4 o = {a.rho * acc[0], a.rho * acc[1], a.rho * acc[2], a.rho * acc[3]};
+    f32x4 o = {a.rho * acc[0], a.rho * acc[1], a.rho * acc[2], a.rho * acc[3]};
+    // the shared-expert slot is added after the routed sum is scaled
+    for (int j = kr; j < k; ++j) {
+      const int p = pos[j];
+      if (p >= 0) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(a.y + (size_t)p * H + c);
+        const float wj = wt[j];
+        o[0] = o[0] + wj * v[0];
+        o[1] = o[1] + wj * v[1];
+        o[2] = o[2] + wj * v[2];
+        o[3] = o[3] + wj * v[3];
+      }
+    }
     if (a.out_f32) {
       *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + (size_t)t * H + c) = o;
     } else {

@@ -165,6 +165,7 @@ class Workload:
     outlier_frac: float
     n_masked: int = 0
     seed: int = 0
+    shared: int = 0      # 1: the layer holds E + 1 experts, the last always on
 
 
 # The five configurations: a tiny layer, the GLM-class layer at 256 / 4096 /
@@ -187,8 +188,12 @@ SLICE_T1024 = dataclasses.replace(SLICE_T16, name="slice_e160_k8_h5120_i192_t102
 PROBE_T4096 = Workload("probe_e8_k8_h6144_i2048_t4096", 8, 8, 6144, 2048, 4096,
                        ROUTE_SIGMOID_UNIFORM, 1.0, 0.0)
 
+# The GLM-class layer with one always-on shared expert in the same grouped
+# GEMMs (nine slots per token over E + 1 experts), at T=256.
+GLM_T256_SHARED = dataclasses.replace(GLM_T256, name="glm_e256s1_k8_h6144_i2048_t256", shared=1)
+
 WORKLOADS = {w.name: w for w in (TINY, GLM_T256, GLM_T4096, GLM_T8192_ZIPF,
-                                 SLICE_T16, SLICE_T64, SLICE_T1024, PROBE_T4096)}
+                                 SLICE_T16, SLICE_T64, SLICE_T1024, PROBE_T4096, GLM_T256_SHARED)}
 
 
 def make_inputs(wl: Workload):

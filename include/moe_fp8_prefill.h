@@ -72,7 +72,7 @@ enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 };
  * once create() returns.
  */
 typedef struct moe_fp8_prefill_desc {
-  int32_t struct_size;      /* sizeof(moe_fp8_prefill_desc) */
+  int32_t struct_size;      /* sizeof(moe_fp8_prefill_desc), or the size up to shared_experts */
   int32_t num_experts;      /* E, 1..1024 */
   int32_t top_k;            /* k, 1..min(E, 256) */
   int32_t hidden;           /* H, multiple of 128 */
@@ -90,6 +90,15 @@ typedef struct moe_fp8_prefill_desc {
   const float* up_scale;
   const float* down_scale;
   void* stream;             /* hipStream_t used for the upload; NULL = null stream */
+  /* Always-on shared expert, 0 or 1 ("TensorFold #2852": nine slots planned
+   * over E+1 expert ids).  With 1, every weight and scale array holds E+1
+   * experts and expert E is the shared one: each token gets a (k+1)-th slot
+   * on it with weight 1, computed in the same grouped GEMMs and added after
+   * the routed sum is scaled by routed_scale:
+   *   out[t] = cast( rho * sum_{j<k} w[t,j] * y[t,j]  +  y_shared[t] ).
+   * ids and w stay [T][k]; a routed id >= E (including E) is a bad id.  A
+   * caller built before this field (struct_size without it) gets 0. */
+  int32_t shared_experts;
 } moe_fp8_prefill_desc;
 
 typedef struct moe_fp8_prefill moe_fp8_prefill;
@@ -168,7 +177,9 @@ const char* moe_fp8_prefill_strerror(int code);
 
 /* The last pass's plan, copied to host buffers: counts i32[E], offsets
  * i32[E+1], perm i32[cap] (sorted position -> slot t*k+j), inv i32[cap]
- * (slot -> sorted position or -1).  cap must be >= that pass's T*k. */
+ * (slot -> sorted position or -1).  cap must be >= that pass's T*k.  With a
+ * shared expert, E and k here count it (E+1 experts, k+1 slots per token,
+ * the shared slot last). */
 int moe_fp8_prefill_debug_plan(moe_fp8_prefill* h, int32_t* counts, int32_t* offsets,
                                int32_t* perm, int32_t* inv, int64_t cap);
 

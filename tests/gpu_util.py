@@ -128,11 +128,19 @@ def check_h_codes(hq_k, sh_k, gu_k, Ip):
     return int(differ.sum())
 
 
-def compare_with_oracle(moe, layer, x, ids, w, rho, got, what=""):
-    """Staged comparison of a finished run whose last pass was the whole call."""
+def with_shared_slot(ids, w, E_routed):
+    """ids / w with the shared expert's slot (id E_routed, weight 1) appended."""
+    T = ids.shape[0]
+    return (np.concatenate([ids, np.full((T, 1), E_routed, np.int32)], axis=1),
+            np.concatenate([w, np.ones((T, 1), np.float32)], axis=1))
+
+
+def compare_with_oracle(moe, layer, x, ids, w, rho, got, what="", n_shared=0):
+    """Staged comparison of a finished run whose last pass was the whole call.
+    With n_shared, ids / w already carry the shared slot column."""
     import oracle
     od = oracle.OUT_F32 if got.dtype == np.float32 else oracle.OUT_BF16
-    ref, d = oracle.forward(layer, x, ids, w, rho, od, debug=True)
+    ref, d = oracle.forward(layer, x, ids, w, rho, od, debug=True, n_shared=n_shared)
     Ip = 128 * ((layer.I + 127) // 128)
     n = d["hq"].shape[0]
     gu = pkg.moe_fp8_prefill_debug_gate_up(moe.handle, n, Ip)
@@ -141,7 +149,7 @@ def compare_with_oracle(moe, layer, x, ids, w, rho, got, what=""):
     rel_gu = rel_l2_rows(gu[fin], d["gu"][fin])
     ties = check_h_codes(hq[fin], sh[fin], gu[fin], Ip)
     flips = int((hq[fin] != d["hq"][fin]).sum())
-    out2, y2 = oracle.down_combine(layer, hq, sh, ids, w, rho, od)
+    out2, y2 = oracle.down_combine(layer, hq, sh, ids, w, rho, od, n_shared=n_shared)
     rel_y = rel_l2_rows(y[fin], y2[fin])
     note(f"  {what}: gate/up rel L2 max {rel_gu.max() if rel_gu.size else 0:.2e}; h codes vs oracle's "
          f"{flips}/{hq[fin].size} differ ({ties} at SiLU ties); y rel max {rel_y.max() if rel_y.size else 0:.2e}")

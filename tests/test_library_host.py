@@ -96,3 +96,24 @@ def test_strerror_covers_all_codes():
     for c in range(8):
         assert pkg.moe_fp8_prefill_strerror(c) != "unknown error code"
     assert pkg.moe_fp8_prefill_strerror(99) == "unknown error code"
+
+
+def test_shared_expert_field():
+    d, keep = _desc()
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_OK
+    base = pkg.moe_fp8_prefill_workspace_bytes(d)
+    d.shared_experts = 1
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_OK
+    assert pkg.moe_fp8_prefill_workspace_bytes(d) > base      # k+1 slots per row
+    d.shared_experts = 2
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_ERR_UNSUPPORTED
+    d.shared_experts = 1
+    d.num_experts = 1024                                       # 1024 + 1 experts
+    d.top_k = 2
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_ERR_UNSUPPORTED
+    # a description built without the field (the size up to it) still validates
+    d2, keep2 = _desc()
+    d2.struct_size = pkg.moe_fp8_prefill_desc.shared_experts.offset
+    assert pkg.moe_fp8_prefill_validate(d2) == pkg.MOE_OK
+    d2.struct_size = 12
+    assert pkg.moe_fp8_prefill_validate(d2) == pkg.MOE_ERR_INVALID_ARG
