@@ -29,6 +29,7 @@ MOE_ERR_BAD_EXPERT_ID = 7
 MOE_DTYPE_BF16 = 0
 MOE_DTYPE_F32 = 1
 MOE_ACT_SILU_UNCLAMPED = 0
+MOE_ACT_SILU_CLAMPED = 1
 MOE_ROUTER_SOFTMAX = 0
 MOE_ROUTER_SIGMOID = 1
 MOE_NUM_STAGES = 7
@@ -61,6 +62,7 @@ class moe_fp8_prefill_desc(ctypes.Structure):
         ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
         ("gate_scale", ctypes.c_void_p), ("up_scale", ctypes.c_void_p), ("down_scale", ctypes.c_void_p),
         ("stream", ctypes.c_void_p), ("shared_experts", ctypes.c_int32),
+        ("activation_limit", ctypes.c_float),
     ]
 
 
@@ -143,7 +145,8 @@ def _check(rc: int, where: str) -> None:
 
 def make_desc(layer, top_k: int, max_rows: int = 8192, out_dtype: int = MOE_DTYPE_BF16,
               routed_scale: float = 1.0, activation: int = MOE_ACT_SILU_UNCLAMPED,
-              block: int = 128, stream=None, on_device: bool = False, shared_experts: int = 0):
+              block: int = 128, stream=None, on_device: bool = False, shared_experts: int = 0,
+              activation_limit: float = 0.0):
     """Description for a layer held as numpy arrays (or, with on_device=True,
     torch device tensors) with fields gate, up, down, gate_scale, up_scale,
     down_scale, E, H, I.  With shared_experts=1 the arrays hold layer.E
@@ -158,7 +161,8 @@ def make_desc(layer, top_k: int, max_rows: int = 8192, out_dtype: int = MOE_DTYP
     d = moe_fp8_prefill_desc(ctypes.sizeof(moe_fp8_prefill_desc), layer.E - shared_experts, top_k,
                              layer.H, layer.I, max_rows, out_dtype, activation, block, routed_scale,
                              1 if on_device else 0, *ptrs,
-                             None if stream is None else _stream_ptr(stream).value, shared_experts)
+                             None if stream is None else _stream_ptr(stream).value, shared_experts,
+                             activation_limit)
     return d, arrs
 
 
@@ -302,15 +306,19 @@ class MoeFp8Prefill:
     up_scale, down_scale and E, H, I (the canonical checkpoint layout)."""
 
     def __init__(self, layer, top_k: int, routed_scale: float = 1.0, max_rows: int = 8192,
-                 out_dtype: int = MOE_DTYPE_BF16, on_device: bool = False, shared_experts: int = 0):
+                 out_dtype: int = MOE_DTYPE_BF16, on_device: bool = False, shared_experts: int = 0,
+                 activation_limit: float = 0.0):
+        """activation_limit > 0 selects the clamped SiLU with that limit."""
         # E, k: routed experts and slots; the shared expert is the arrays' last
         self.E, self.H, self.I, self.k = layer.E - shared_experts, layer.H, layer.I, top_k
         self.shared = shared_experts
         self.Ip = 128 * ((layer.I + 127) // 128)
         self.out_dtype = out_dtype
         self.max_rows = max_rows
-        desc, keep = make_desc(layer, top_k, max_rows, out_dtype, routed_scale, on_device=on_device,
-                               shared_experts=shared_experts)
+        act = MOE_ACT_SILU_CLAMPED if activation_limit > 0 else MOE_ACT_SILU_UNCLAMPED
+        desc, keep = make_desc(layer, top_k, max_rows, out_dtype, routed_scale, activation=act,
+                               on_device=on_device, shared_experts=shared_experts,
+                               activation_limit=activation_limit)
         self.handle = moe_fp8_prefill_create(desc)
         del keep
 

@@ -26,15 +26,25 @@ struct Dims {
   int64_t Er, kr, shared;
 };
 
-constexpr int32_t kDescSizeNoShared = (int32_t)offsetof(moe_fp8_prefill_desc, shared_experts);
+// Description sizes of older callers: without shared_experts, and without
+// activation_limit.  Fields past a caller's struct_size read as 0.
+constexpr int32_t kDescNoShared = (int32_t)offsetof(moe_fp8_prefill_desc, shared_experts);
+constexpr int32_t kDescNoLimit = (int32_t)offsetof(moe_fp8_prefill_desc, activation_limit);
 
-bool has_shared_field(const moe_fp8_prefill_desc* d) {
-  return d->struct_size == (int32_t)sizeof(moe_fp8_prefill_desc);
+bool desc_size_ok(const moe_fp8_prefill_desc* d) {
+  return d->struct_size == (int32_t)sizeof(moe_fp8_prefill_desc) || d->struct_size == kDescNoLimit ||
+         d->struct_size == kDescNoShared;
+}
+int32_t desc_shared(const moe_fp8_prefill_desc* d) {
+  return d->struct_size > kDescNoShared ? d->shared_experts : 0;
+}
+float desc_limit(const moe_fp8_prefill_desc* d) {
+  return d->struct_size > kDescNoLimit ? d->activation_limit : 0.0f;
 }
 
 Dims dims_of(const moe_fp8_prefill_desc* d) {
   Dims m;
-  m.shared = has_shared_field(d) ? d->shared_experts : 0;
+  m.shared = desc_shared(d);
   m.Er = d->num_experts;
   m.kr = d->top_k;
   m.E = m.Er + m.shared;
@@ -247,7 +257,8 @@ hipError_t launch_gate_up_pair(moe_fp8_prefill* h, int64_t t, int64_t P, float* 
   const Dims& m = h->m;
   const int64_t nb = m.Ip / kBlock;
   GateUpArgs ga{h->xq, h->sx, t * m.H, t * m.nH * 4, h->perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip,
-                h->w13, h->s13, h->small_tiles, h->n_tiles, h->hq, h->sh, gu_dbg};
+                h->w13, h->s13, h->small_tiles, h->n_tiles, h->hq, h->sh, gu_dbg,
+                h->desc.activation == MOE_ACT_SILU_CLAMPED ? h->desc.activation_limit : 0.0f};
   hipError_t e = launch_gate_up(ga, false, gemm_grid(h, m.E * nb, false, true), s);
   if (e != hipSuccess) return e;
   if (between && (e = hipEventRecord(between, s)) != hipSuccess) return e;
@@ -377,16 +388,19 @@ const char* moe_fp8_prefill_strerror(int code) {
 
 int moe_fp8_prefill_validate(const moe_fp8_prefill_desc* d) {
   if (!d) return MOE_ERR_INVALID_ARG;
-  if (d->struct_size != (int32_t)sizeof(moe_fp8_prefill_desc) && d->struct_size != kDescSizeNoShared)
-    return MOE_ERR_INVALID_ARG;
-  const int32_t shared = has_shared_field(d) ? d->shared_experts : 0;
+  if (!desc_size_ok(d)) return MOE_ERR_INVALID_ARG;
+  const int32_t shared = desc_shared(d);
+  const float limit = desc_limit(d);
   if (shared != 0 && shared != 1) return MOE_ERR_UNSUPPORTED;
   if (!d->gate || !d->up || !d->down || !d->gate_scale || !d->up_scale || !d->down_scale)
     return MOE_ERR_INVALID_ARG;
   if (d->num_experts < 1 || d->top_k < 1 || d->hidden < 1 || d->inter < 1 || d->max_rows < 1)
     return MOE_ERR_INVALID_ARG;
   if (d->block != kBlock) return MOE_ERR_UNSUPPORTED;
-  if (d->activation != MOE_ACT_SILU_UNCLAMPED) return MOE_ERR_UNSUPPORTED;
+  if (d->activation != MOE_ACT_SILU_UNCLAMPED && d->activation != MOE_ACT_SILU_CLAMPED)
+    return MOE_ERR_UNSUPPORTED;
+  if (d->activation == MOE_ACT_SILU_CLAMPED ? !(std::isfinite(limit) && limit > 0.0f) : limit != 0.0f)
+    return MOE_ERR_INVALID_ARG;
   if (d->out_dtype != MOE_DTYPE_BF16 && d->out_dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
   if (d->hidden % kBlock != 0) return MOE_ERR_UNSUPPORTED;
   if (d->hidden > kMaxKBlocks * kBlock || d->inter > kMaxKBlocks * kBlock) return MOE_ERR_UNSUPPORTED;
@@ -423,7 +437,8 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   if (!h) return MOE_ERR_OUT_OF_MEMORY;
   // a caller's description may end before shared_experts: copy what it has
   memcpy(&h->desc, d, (size_t)d->struct_size);
-  if (!has_shared_field(d)) h->desc.shared_experts = 0;
+  h->desc.shared_experts = desc_shared(d);
+  h->desc.activation_limit = desc_limit(d);
   h->desc.struct_size = (int32_t)sizeof(moe_fp8_prefill_desc);
   h->m = dims_of(d);
   const Dims& m = h->m;

@@ -88,6 +88,7 @@ struct GateUpArgs {
   uint8_t* hq;         // [P][Ip]
   float* sh;           // [P][Ip/128]
   float* gu_dbg;       // optional [P][2*Ip] FP32 gate|up before the epilogue
+  float act_limit;     // > 0: clamped SiLU (gate <= L, |up| <= L); 0: unclamped
 };
 
 struct DownArgs {

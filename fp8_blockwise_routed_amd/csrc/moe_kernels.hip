@@ -92,6 +92,16 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return __fdiv_rn(g, 1.0f + expf(-g)) * u;
 }
 
+// The clamped variant for L > 0: gate capped at L, up clipped to [-L, L]
+// (comparisons, so NaN passes through); L = 0 is the plain silu_mul.
+__device__ __forceinline__ float silu_mul_act(float g, float u, float L) {
+  if (L > 0.0f) {
+    g = g > L ? L : g;
+    u = u > L ? L : (u < -L ? -L : u);
+  }
+  return silu_mul(g, u);
+}
+
 // -------------------------------------------------------------------- plan --
 // One workgroup of 1024 threads.  Counting sort that keeps slot order within
 // an expert: histogram with LDS atomics, exclusive scan, then chunks of 1024
@@ -689,8 +699,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
       if (m < mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[m][0][i] = silu_mul(acc[m][0][i], acc[m][2][i]);
-          acc[m][1][i] = silu_mul(acc[m][1][i], acc[m][3][i]);
+          acc[m][0][i] = silu_mul_act(acc[m][0][i], acc[m][2][i], a.act_limit);
+          acc[m][1][i] = silu_mul_act(acc[m][1][i], acc[m][3][i], a.act_limit);
           const uint32_t mb = max16(umax(abs_bits(acc[m][0][i]), abs_bits(acc[m][1][i])));
           if (col == 0) red_lds[wave][m * 16 + grp * 4 + i] = mb;
         }
@@ -827,8 +837,8 @@ __global__ __launch_bounds__(kThreads, D <= 2 ? 4 : 3) void gate_up_stream_kerne
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[0][i] = silu_mul(acc[0][i], acc[2][i]);
-      acc[1][i] = silu_mul(acc[1][i], acc[3][i]);
+      acc[0][i] = silu_mul_act(acc[0][i], acc[2][i], a.act_limit);
+      acc[1][i] = silu_mul_act(acc[1][i], acc[3][i], a.act_limit);
       const uint32_t mb = max16(umax(abs_bits(acc[0][i]), abs_bits(acc[1][i])));
       if (col == 0) red_lds[wave][grp * 4 + i] = mb;
     }

@@ -56,7 +56,11 @@ enum {
 };
 
 enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 };
-enum { MOE_ACT_SILU_UNCLAMPED = 0 };
+/* Activations: full GLM's unclamped SiLU ("ktransformers #2244", Design), or
+ * the clamped variant GLM-5.3-Flash uses, whose formula the pages leave
+ * open; here the limit L is a parameter: gate capped at L, up clipped to
+ * [-L, L], then silu(gate) * up (NaN passes through). */
+enum { MOE_ACT_SILU_UNCLAMPED = 0, MOE_ACT_SILU_CLAMPED = 1 };
 enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 };
 
 /*
@@ -72,14 +76,15 @@ enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 };
  * once create() returns.
  */
 typedef struct moe_fp8_prefill_desc {
-  int32_t struct_size;      /* sizeof(moe_fp8_prefill_desc), or the size up to shared_experts */
+  int32_t struct_size;      /* sizeof(moe_fp8_prefill_desc), or the size up to
+                               shared_experts or activation_limit (older callers) */
   int32_t num_experts;      /* E, 1..1024 */
   int32_t top_k;            /* k, 1..min(E, 256) */
   int32_t hidden;           /* H, multiple of 128 */
   int32_t inter;            /* I >= 1; padded to Ip = 128*ceil(I/128) with zero codes */
   int32_t max_rows;         /* rows per internal pass; run() chunks larger T */
   int32_t out_dtype;        /* MOE_DTYPE_BF16 or MOE_DTYPE_F32 */
-  int32_t activation;       /* MOE_ACT_SILU_UNCLAMPED */
+  int32_t activation;       /* MOE_ACT_SILU_UNCLAMPED or MOE_ACT_SILU_CLAMPED */
   int32_t block;            /* 128 */
   float routed_scale;       /* rho, finite */
   int32_t weights_on_device;
@@ -99,6 +104,9 @@ typedef struct moe_fp8_prefill_desc {
    * ids and w stay [T][k]; a routed id >= E (including E) is a bad id.  A
    * caller built before this field (struct_size without it) gets 0. */
   int32_t shared_experts;
+  /* L of MOE_ACT_SILU_CLAMPED: finite and > 0 (ten for GLM-5.3-Flash); must
+   * be 0 with MOE_ACT_SILU_UNCLAMPED.  Absent (older struct_size) = 0. */
+  float activation_limit;
 } moe_fp8_prefill_desc;
 
 typedef struct moe_fp8_prefill moe_fp8_prefill;

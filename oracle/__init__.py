@@ -102,6 +102,8 @@ def _load():
         lib.orc_set_fault.restype = None
         lib.orc_max_threads.argtypes = []
         lib.orc_max_threads.restype = ctypes.c_int32
+        lib.orc_set_activation_limit.argtypes = [ctypes.c_float]
+        lib.orc_set_activation_limit.restype = None
         lib.orc_route.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P]
         lib.orc_route.restype = ctypes.c_int32
         _lib = lib
@@ -113,6 +115,11 @@ def _p(a):
         return None
     assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "need a C-contiguous array"
     return ctypes.c_void_p(a.ctypes.data)
+
+
+def set_activation_limit(limit: float) -> None:
+    """Clamped SiLU limit L for forward / bruteforce_fp64 (0 = unclamped)."""
+    _load().orc_set_activation_limit(float(limit))
 
 
 def set_fault(name: str) -> None:

@@ -58,6 +58,15 @@ enum {
 static int g_fault = FAULT_NONE;
 void orc_set_fault(int32_t f) { g_fault = f; }
 
+/* Clamped SwiGLU variant ("ktransformers #2244", Design: GLM-5.3-Flash clamps
+ * at ten, full GLM does not; the formula is not given, so the limit is an
+ * explicit parameter).  L > 0: the gate is capped at L and the up value
+ * clipped to [-L, L] before h = silu(gate) * up; NaN passes through.  0: the
+ * unclamped SiLU.  Applies to orc_forward and orc_bruteforce_fp64 until
+ * changed. */
+static float g_act_limit = 0.0f;
+void orc_set_activation_limit(float limit) { g_act_limit = limit; }
+
 int32_t orc_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
@@ -281,6 +290,12 @@ static float silu_mul(float g, float u) {
   }
   if (g_fault == FAULT_SILU_CLAMP && g > 10.0f) g = 10.0f;
   if (g_fault == FAULT_SILU_SIGN) g = -g;
+  if (g_act_limit > 0.0f) {
+    const float L = g_act_limit;
+    if (g > L) g = L;
+    if (u > L) u = L;
+    if (u < -L) u = -L;
+  }
   return (g / (1.0f + expf(-g))) * u;
 }
 
@@ -532,6 +547,11 @@ int32_t orc_bruteforce_fp64(const orc_layer* L, int32_t k, const uint16_t* x,
                       (double)L->up_scale[(e * nI + i / 128) * nH + c / 128];
           g += xa[c] * wg;
           u += xa[c] * wu;
+        }
+        if (g_act_limit > 0.0f) {
+          const double L = (double)g_act_limit;
+          g = g > L ? L : g;
+          u = u > L ? L : (u < -L ? -L : u);
         }
         hv[i] = g / (1.0 + exp(-g)) * u;
       }

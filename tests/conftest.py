@@ -18,8 +18,11 @@ def pytest_configure(config):
 
 @pytest.fixture(autouse=True)
 def _reset_oracle_fault():
-    """Every test starts and ends with no planted fault in the oracle."""
+    """Every test starts and ends with no planted fault in the oracle and the
+    unclamped SiLU."""
     import oracle
     oracle.set_fault("none")
+    oracle.set_activation_limit(0.0)
     yield
     oracle.set_fault("none")
+    oracle.set_activation_limit(0.0)

@@ -103,13 +103,16 @@ def _dec_table():
     return _DEC
 
 
-def check_h_codes(hq_k, sh_k, gu_k, Ip):
+def check_h_codes(hq_k, sh_k, gu_k, Ip, act_limit=0.0):
     """The kernel's h codes / scales are the E4M3 quantisation (per row and
     128-group, s = amax/448, round to nearest even) of its own h."""
     import oracle
     dec = _dec_table()
     g = gu_k[:, :Ip].astype(np.float64)
     u = gu_k[:, Ip:].astype(np.float64)
+    if act_limit > 0:
+        g = np.minimum(g, act_limit)
+        u = np.clip(u, -act_limit, act_limit)
     h = g / (1.0 + np.exp(-g)) * u
     rows, groups = sh_k.shape
     amax = np.abs(h).reshape(rows, groups, 128).max(axis=2)
@@ -135,19 +138,23 @@ def with_shared_slot(ids, w, E_routed):
             np.concatenate([w, np.ones((T, 1), np.float32)], axis=1))
 
 
-def compare_with_oracle(moe, layer, x, ids, w, rho, got, what="", n_shared=0):
+def compare_with_oracle(moe, layer, x, ids, w, rho, got, what="", n_shared=0, act_limit=0.0):
     """Staged comparison of a finished run whose last pass was the whole call.
     With n_shared, ids / w already carry the shared slot column."""
     import oracle
     od = oracle.OUT_F32 if got.dtype == np.float32 else oracle.OUT_BF16
-    ref, d = oracle.forward(layer, x, ids, w, rho, od, debug=True, n_shared=n_shared)
+    oracle.set_activation_limit(act_limit)
+    try:
+        ref, d = oracle.forward(layer, x, ids, w, rho, od, debug=True, n_shared=n_shared)
+    finally:
+        oracle.set_activation_limit(0.0)
     Ip = 128 * ((layer.I + 127) // 128)
     n = d["hq"].shape[0]
     gu = pkg.moe_fp8_prefill_debug_gate_up(moe.handle, n, Ip)
     hq, sh, y = pkg.moe_fp8_prefill_debug_intermediates(moe.handle, n, layer.H, Ip)
     fin = np.isfinite(d["gu"]).all(axis=1)
     rel_gu = rel_l2_rows(gu[fin], d["gu"][fin])
-    ties = check_h_codes(hq[fin], sh[fin], gu[fin], Ip)
+    ties = check_h_codes(hq[fin], sh[fin], gu[fin], Ip, act_limit)
     flips = int((hq[fin] != d["hq"][fin]).sum())
     out2, y2 = oracle.down_combine(layer, hq, sh, ids, w, rho, od, n_shared=n_shared)
     rel_y = rel_l2_rows(y[fin], y2[fin])

@@ -21,6 +21,9 @@ What pins what:
              the softmax weights.
   shared     the FP64 brute force with the shared slot outside rho; the
              routed layer plus the shared expert evaluated on its own.
+  clamp      the FP64 brute force with the clamped SwiGLU; h from the
+             oracle's own gate/up through a numpy clamp; a limit above every
+             |gate|, |up| reproduces the unclamped bits.
   layer      the FP64 dense brute force (different loop structure, FP64,
              exhaustive-search encoder); a dense gated FFN evaluated with torch
              float8 casts and float64 matmuls; an integer-exact case compared
@@ -593,6 +596,54 @@ def pin_shared_composition():
                "shared slot is not the routed layer plus the shared expert")
 
 
+CLAMP = 0.5  # low enough that the test rows' gate / up values cross it
+
+
+def pin_clamp_vs_bruteforce(tol=2e-3):
+    layer, x, ids, w, rho = small_case(SMALL_CASES[1])
+    oracle.set_activation_limit(CLAMP)
+    try:
+        got = oracle.forward(layer, x, ids, w, rho, oracle.OUT_F32)
+        ref = oracle.bruteforce_fp64(layer, x, ids, w, rho)
+    finally:
+        oracle.set_activation_limit(0.0)
+    unclamped = oracle.forward(layer, x, ids, w, rho, oracle.OUT_F32)
+    worst = float(rel_l2_rows(got.astype(np.float64), ref).max())
+    active = float(rel_l2_rows(got.astype(np.float64), unclamped.astype(np.float64)).max())
+    return _ok(worst <= tol and active > 1e-2,
+               f"clamped vs brute force {worst:.2e}; clamp changes rows by {active:.2e}")
+
+
+def pin_clamp_activation_from_gu():
+    layer, x, ids, w, rho = small_case(SMALL_CASES[1])
+    oracle.set_activation_limit(CLAMP)
+    try:
+        _, d = oracle.forward(layer, x, ids, w, rho, oracle.OUT_F32, debug=True)
+    finally:
+        oracle.set_activation_limit(0.0)
+    Ip = d["gu"].shape[1] // 2
+    g = np.minimum(d["gu"][:, :Ip].astype(np.float64), CLAMP)
+    u = np.clip(d["gu"][:, Ip:].astype(np.float64), -CLAMP, CLAMP)
+    h = g / (1.0 + np.exp(-g)) * u
+    q, s = oracle.quantize_rows(h.astype(np.float32))
+    dec = oracle.e4m3_decode(np.arange(256, dtype=np.uint8)).astype(np.float64)
+    back = dec[d["hq"]] * np.repeat(d["sh"].astype(np.float64), 128, axis=1)
+    rel = np.abs(back - h).max() / np.abs(h).max()
+    same = (q != d["hq"]).mean()
+    return _ok(rel < 0.07 and same < 1e-3, f"clamped h: max rel {rel:.3f}, code mismatch {same:.2e}")
+
+
+def pin_clamp_large_limit_is_unclamped():
+    layer, x, ids, w, rho = small_case(SMALL_CASES[1])
+    base = oracle.forward(layer, x, ids, w, rho, oracle.OUT_F32)
+    oracle.set_activation_limit(1e30)
+    try:
+        big = oracle.forward(layer, x, ids, w, rho, oracle.OUT_F32)
+    finally:
+        oracle.set_activation_limit(0.0)
+    return _ok(np.array_equal(base.view(np.uint32), big.view(np.uint32)), "a huge limit changed bits")
+
+
 ALL_PINS = {
     "decode_golden": pin_decode_golden,
     "decode_vs_torch": pin_decode_vs_torch,
@@ -623,4 +674,7 @@ ALL_PINS = {
     "nan_row_isolation": pin_nan_row_isolation,
     "shared_vs_bruteforce": pin_shared_vs_bruteforce,
     "shared_composition": pin_shared_composition,
+    "clamp_vs_bruteforce": pin_clamp_vs_bruteforce,
+    "clamp_activation_from_gu": pin_clamp_activation_from_gu,
+    "clamp_large_limit_is_unclamped": pin_clamp_large_limit_is_unclamped,
 }

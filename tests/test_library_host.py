@@ -59,7 +59,7 @@ def test_validate_accepts_the_configurations():
     ("inter", 0, pkg.MOE_ERR_INVALID_ARG),
     ("max_rows", 0, pkg.MOE_ERR_INVALID_ARG),
     ("block", 64, pkg.MOE_ERR_UNSUPPORTED),
-    ("activation", 1, pkg.MOE_ERR_UNSUPPORTED),
+    ("activation", 2, pkg.MOE_ERR_UNSUPPORTED),
     ("out_dtype", 5, pkg.MOE_ERR_UNSUPPORTED),
     ("routed_scale", float("nan"), pkg.MOE_ERR_INVALID_ARG),
     ("struct_size", 8, pkg.MOE_ERR_INVALID_ARG),
@@ -115,5 +115,25 @@ def test_shared_expert_field():
     d2, keep2 = _desc()
     d2.struct_size = pkg.moe_fp8_prefill_desc.shared_experts.offset
     assert pkg.moe_fp8_prefill_validate(d2) == pkg.MOE_OK
+    d2.struct_size = pkg.moe_fp8_prefill_desc.activation_limit.offset
+    assert pkg.moe_fp8_prefill_validate(d2) == pkg.MOE_OK
     d2.struct_size = 12
     assert pkg.moe_fp8_prefill_validate(d2) == pkg.MOE_ERR_INVALID_ARG
+
+
+def test_clamped_activation_field():
+    d, keep = _desc()
+    d.activation = pkg.MOE_ACT_SILU_CLAMPED
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_ERR_INVALID_ARG   # limit 0
+    d.activation_limit = 10.0
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_OK
+    d.activation_limit = float("inf")
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_ERR_INVALID_ARG
+    d.activation_limit = -1.0
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_ERR_INVALID_ARG
+    d.activation = pkg.MOE_ACT_SILU_UNCLAMPED
+    d.activation_limit = 10.0                                          # limit without the clamp
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_ERR_INVALID_ARG
+    d.activation = 7
+    d.activation_limit = 0.0
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_ERR_UNSUPPORTED
