@@ -43,7 +43,26 @@ PROFILE_COMMANDS = {
                   "python3 bench.py --copy-calibration",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_copy_write -o cw -- "
                   "python3 bench.py --copy-calibration",
+    "trace_zipf": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_kt_zipf -o kt -- "
+                  "python3 bench.py --workload glm_e256_k8_h6144_i2048_t8192_zipf --steps 5 "
+                  "--warmup 2 --cpu-tokens 0",
+    "trace_probe": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_kt_probe -o kt -- "
+                   "python3 bench.py --workload probe_e8_k8_h6144_i2048_t4096 --steps 5 "
+                   "--warmup 2 --cpu-tokens 0",
+    "trace_router": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_kt_router -o kt -- "
+                    "python3 bench.py --workload glm_e256_k8_h6144_i2048_t4096_uniform --router "
+                    "--steps 5 --warmup 2 --cpu-tokens 0",
 }
+
+# Extra kernel-time summaries: (command key, output dir, summary file, title).
+EXTRA_TRACES = [
+    ("trace_zipf", "prof_kt_zipf", "kernel_stats_glm_e256_t8192_zipf.md",
+     "GLM-class layer E=256 top-8 H=6144 I=2048, T=8192 rows, Zipf(1.2) routing, one pass"),
+    ("trace_probe", "prof_kt_probe", "kernel_stats_probe_e8_t4096.md",
+     "compute-bound probe: E=8, every token to all 8 experts, H=6144 I=2048, T=4096"),
+    ("trace_router", "prof_kt_router", "kernel_stats_glm_e256_t4096_router.md",
+     "GLM-class layer E=256 top-8, T=4096 rows from router logits (route_kernel + path)"),
+]
 
 
 def log(msg: str) -> None:
@@ -146,6 +165,22 @@ def summarize_profiles(out_dir: str) -> int:
     os.makedirs(PROFILES, exist_ok=True)
     with open(STATS_MD, "w") as f:
         f.write("\n".join(lines) + "\n")
+    for key, sub, md, title in EXTRA_TRACES:
+        rows = _csv_rows(os.path.join(out_dir, sub, "**", "*kernel_stats.csv"))
+        if not rows:
+            continue
+        lines = [f"# Kernel time, {title}", "",
+                 "Command (repository root, one MI355X):", "", f"    {PROFILE_COMMANDS[key]}", "",
+                 f"- kernel_source_sha256_16: `{src}`", "",
+                 "| kernel | calls | average us | min us | max us | % of GPU time |",
+                 "|---|---|---|---|---|---|"]
+        for r in rows:
+            lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                         f"{float(r['Percentage']):.2f} |")
+        lines += ["", "The layout kernels run once, inside create(), outside the timed steps."]
+        with open(os.path.join(PROFILES, md), "w") as f:
+            f.write("\n".join(lines) + "\n")
 
     fetch = _csv_rows(os.path.join(out_dir, "prof_fetch", "**", "*counter_collection.csv"))
     write = _csv_rows(os.path.join(out_dir, "prof_write", "**", "*counter_collection.csv"))
