@@ -217,6 +217,68 @@ def summarize_profiles(out_dir: str) -> int:
     return 0
 
 
+def streamed_bench(args, wl, layer, xd, idd, wd, out) -> int:
+    """Whole-model prefill through `L` layers whose weights are copied from
+    page-locked host memory into two device slots ("ktransformers #2244",
+    Design: one reusable per-layer slot refilled from the host): the copy of
+    layer i+1 (copy stream) overlaps the pass of layer i (compute stream).
+    Every layer stages the same host arrays (a repeated slot), so each pass
+    transfers the full slot."""
+    import torch
+
+    import fp8_blockwise_routed_amd as pkg
+    import gen
+    L = args.streamed_layers
+    log("[bench] pinning the host copy of the layer")
+    host = {}
+    for name in ("gate", "up", "down", "gate_scale", "up_scale", "down_scale"):
+        a = getattr(layer, name)
+        t = torch.empty(a.shape, dtype=torch.uint8 if a.dtype.itemsize == 1 else torch.float32,
+                        pin_memory=True)
+        t.numpy()[...] = a
+        host[name] = t
+    hl = gen.Layer(layer.E, layer.H, layer.I, *(host[n] for n in ("gate", "up", "down", "gate_scale",
+                                                                 "up_scale", "down_scale")))
+    slot_bytes = sum(int(t.numel() * t.element_size()) for t in host.values())
+    sm = pkg.StreamedMoeFp8Prefill(layer, wl.k, n_slots=2, routed_scale=wl.rho, max_rows=8192,
+                                   out_dtype=pkg.MOE_DTYPE_BF16, shared_experts=wl.shared)
+    copy = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+
+    def model(n):
+        sm.stage(0, hl, stream=copy)
+        for i in range(n):
+            if i + 1 < n:
+                sm.stage((i + 1) % 2, hl, stream=copy)
+            sm.select(i % 2)
+            sm.run(xd, idd, wd, out=out, stream=comp)
+
+    log("[bench] warmup (2 layers)")
+    model(2)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {L} layers")
+    t0 = time.perf_counter()
+    model(L)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if sm.status() != pkg.MOE_OK:
+        raise RuntimeError("device reported an error")
+    sm.close()
+    res = {
+        "metric": "whole-model prefill input tokens/sec through streamed layer slots (1 MI355X, "
+                  "host-link bound)",
+        "value": wl.T / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": L, "warmup": 2,
+        "ms_per_step": elapsed * 1e3 / L, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "slots": 2, "slot_bytes": slot_bytes,
+                   "host_memory": "page-locked, one layer staged L times"},
+        "h2d_GBs": L * slot_bytes / elapsed / 1e9,
+        "per_layer_tokens_s": wl.T * L / elapsed,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def cpu_baseline(layer, wl, x, ids, w, n_tokens, repeats):
     """The oracle, as it stands, on the first n_tokens rows of the same batch:
     median wall clock of `repeats` runs."""
@@ -248,6 +310,10 @@ def main() -> int:
     ap.add_argument("--no-timing-events", action="store_true",
                     help="skip the per-launch HIP events (roofline needs them)")
     ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--streamed-layers", type=int, default=0, metavar="L",
+                    help="instead of the resident-layer bench: whole-model prefill through L layers "
+                         "whose weights are staged from pinned host memory into two device slots "
+                         "(double-buffered H2D overlapped with compute)")
     ap.add_argument("--router", action="store_true",
                     help="start each step from FP32 router logits (run_logits: on-device top-k "
                          "router, then the path) instead of given ids and weights")
@@ -294,6 +360,9 @@ def main() -> int:
     wd = torch.from_numpy(w).cuda()
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
+    if args.streamed_layers > 0:
+        moe.close()
+        return streamed_bench(args, wl, layer, xd, idd, wd, out)
     router = pkg.MOE_ROUTER_SOFTMAX if wl.route == gen.ROUTE_SOFTMAX else pkg.MOE_ROUTER_SIGMOID
     if args.router:
         logits = gen.make_logits(wl.T, wl.E, wl.route, wl.seed, wl.n_masked)

@@ -44,6 +44,7 @@ EXPORTED = (
     "moe_fp8_prefill_debug_unpack", "moe_fp8_prefill_debug_mfma", "moe_fp8_prefill_set_timing",
     "moe_fp8_prefill_read_timing", "moe_fp8_prefill_debug_inject_failure",
     "moe_fp8_prefill_route", "moe_fp8_prefill_run_logits",
+    "moe_fp8_prefill_create_streamed", "moe_fp8_prefill_stage", "moe_fp8_prefill_select_slot",
 )
 
 
@@ -99,6 +100,9 @@ def load_library() -> ctypes.CDLL:
         "moe_fp8_prefill_debug_inject_failure": ([P], ctypes.c_int),
         "moe_fp8_prefill_route": ([P, P, I32, I64, P, P, P], ctypes.c_int),
         "moe_fp8_prefill_run_logits": ([P, P, P, I32, I64, P, P], ctypes.c_int),
+        "moe_fp8_prefill_create_streamed": ([D, I32, ctypes.POINTER(P)], ctypes.c_int),
+        "moe_fp8_prefill_stage": ([P, I32, P, P, P, P, P, P, P], ctypes.c_int),
+        "moe_fp8_prefill_select_slot": ([P, I32], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -205,6 +209,37 @@ def moe_fp8_prefill_run_logits(handle: int, x, logits, router: int, T: int, out,
                                                          _stream_ptr(stream)))
 
 
+def _host_ptr(a):
+    """Host address of a C-contiguous numpy array or a contiguous CPU torch
+    tensor (pinned or not)."""
+    if isinstance(a, np.ndarray):
+        return _np_ptr(a)
+    if a.is_cuda or not a.is_contiguous():
+        raise ValueError("need a contiguous host tensor")
+    return ctypes.c_void_p(a.data_ptr())
+
+
+def moe_fp8_prefill_create_streamed(desc, n_slots: int) -> int:
+    """Returns the handle of a streamed-slot layer (no weights uploaded)."""
+    h = ctypes.c_void_p()
+    _check(load_library().moe_fp8_prefill_create_streamed(ctypes.byref(desc), n_slots, ctypes.byref(h)),
+           "moe_fp8_prefill_create_streamed")
+    return h.value
+
+
+def moe_fp8_prefill_stage(handle: int, slot: int, gate, up, down, gate_scale, up_scale, down_scale,
+                          stream=None) -> int:
+    """Returns the MOE_* code.  Arrays: numpy or (pinned) CPU torch tensors in
+    the canonical layout; they must stay alive until the stream passes."""
+    return int(load_library().moe_fp8_prefill_stage(
+        ctypes.c_void_p(handle), slot, _host_ptr(gate), _host_ptr(up), _host_ptr(down),
+        _host_ptr(gate_scale), _host_ptr(up_scale), _host_ptr(down_scale), _stream_ptr(stream)))
+
+
+def moe_fp8_prefill_select_slot(handle: int, slot: int) -> int:
+    return int(load_library().moe_fp8_prefill_select_slot(ctypes.c_void_p(handle), slot))
+
+
 def moe_fp8_prefill_status(handle: int) -> int:
     return int(load_library().moe_fp8_prefill_status(ctypes.c_void_p(handle)))
 
@@ -299,7 +334,7 @@ def moe_fp8_prefill_debug_inject_failure(handle: int) -> None:
            "moe_fp8_prefill_debug_inject_failure")
 
 
-# ---- convenience wrapper ---------------------------------------------------
+# ---- convenience wrappers --------------------------------------------------
 
 class MoeFp8Prefill:
     """Owns one handle.  ``layer`` has numpy fields gate, up, down, gate_scale,
@@ -365,3 +400,31 @@ class MoeFp8Prefill:
             self.close()
         except Exception:
             pass
+
+
+class StreamedMoeFp8Prefill(MoeFp8Prefill):
+    """A layer handle with n_slots device weight slots that the caller fills
+    layer by layer with stage() (host arrays in the canonical layout) and
+    picks with select().  ``shape`` has E, H, I (E counting a shared expert)."""
+
+    def __init__(self, shape, top_k: int, n_slots: int = 2, routed_scale: float = 1.0,
+                 max_rows: int = 8192, out_dtype: int = MOE_DTYPE_BF16, shared_experts: int = 0,
+                 activation_limit: float = 0.0):
+        self.E, self.H, self.I, self.k = shape.E - shared_experts, shape.H, shape.I, top_k
+        self.Ip = 128 * ((shape.I + 127) // 128)
+        self.out_dtype = out_dtype
+        self.max_rows = max_rows
+        self.shared = shared_experts
+        act = MOE_ACT_SILU_CLAMPED if activation_limit > 0 else MOE_ACT_SILU_UNCLAMPED
+        desc = moe_fp8_prefill_desc(ctypes.sizeof(moe_fp8_prefill_desc), shape.E - shared_experts, top_k,
+                                    shape.H, shape.I, max_rows, out_dtype, act, 128, routed_scale, 0,
+                                    None, None, None, None, None, None, None, shared_experts,
+                                    activation_limit)
+        self.handle = moe_fp8_prefill_create_streamed(desc, n_slots)
+
+    def stage(self, slot: int, layer, stream=None) -> None:
+        _check(moe_fp8_prefill_stage(self.handle, slot, layer.gate, layer.up, layer.down, layer.gate_scale,
+                                     layer.up_scale, layer.down_scale, stream), "moe_fp8_prefill_stage")
+
+    def select(self, slot: int) -> None:
+        _check(moe_fp8_prefill_select_slot(self.handle, slot), "moe_fp8_prefill_select_slot")

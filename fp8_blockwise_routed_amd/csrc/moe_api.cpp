@@ -137,6 +137,24 @@ struct moe_fp8_prefill {
   bool failed = false;
   bool inject_failure = false;
   hipEvent_t done = nullptr;
+  // streamed layer slots (create_streamed); n_slots == 0 for a resident handle
+  struct Slot {
+    uint8_t* w13 = nullptr;
+    float* s13 = nullptr;
+    uint8_t* w2 = nullptr;
+    float* s2 = nullptr;
+    hipEvent_t ready = nullptr;  // recorded when its staging has been enqueued
+    hipEvent_t free = nullptr;   // recorded after the last pass that read it
+    bool staged = false;
+    bool used = false;
+  };
+  int n_slots = 0;
+  int active = 0;
+  Slot slots[2];
+  uint8_t* stage_codes = nullptr;  // one group of experts in the canonical layout
+  float* stage_scales = nullptr;
+  hipEvent_t stage_done = nullptr;  // orders stage() calls made on different streams
+  bool staged_once = false;
   hipStream_t last_stream = nullptr;
   bool has_last = false;
   int64_t last_T = 0;  // rows of the last pass
@@ -164,6 +182,11 @@ void free_all(moe_fp8_prefill* h) {
   for (void* p : h->allocations) (void)hipFree(p);
   h->allocations.clear();
   if (h->done) (void)hipEventDestroy(h->done);
+  for (auto& sl : h->slots) {
+    if (sl.ready) (void)hipEventDestroy(sl.ready);
+    if (sl.free) (void)hipEventDestroy(sl.free);
+  }
+  if (h->stage_done) (void)hipEventDestroy(h->stage_done);
   for (auto& s : h->pending)
     for (auto ev : s.ev) (void)hipEventDestroy(ev);
   for (auto& s : h->free_events)
@@ -176,6 +199,44 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Upload experts [e0, e0+n) from canonical buffers (host or device) and
 // re-lay them out into the handle's weight arrays.
+// Copies experts [0, E) of a layer from host memory in the canonical layout
+// to the device, a group of `group` experts at a time through the staging
+// buffers, and re-lays each group out into (w13, s13, w2, s2).  Everything
+// is enqueued on s in order (the staging buffers are reused by the next
+// group only after the layout kernels of this one, by stream order); no host
+// synchronisation.
+int enqueue_host_upload(moe_fp8_prefill* h, const uint8_t* gate, const uint8_t* up,
+                        const uint8_t* down, const float* gate_scale, const float* up_scale,
+                        const float* down_scale, uint8_t* w13, float* s13, uint8_t* w2, float* s2,
+                        uint8_t* stage, float* sstage, int64_t group, hipStream_t s) {
+  const Dims& m = h->m;
+  const int64_t wcode = m.I * m.H;
+  const int64_t wscale = ((m.I + 127) / 128) * m.nH;
+  for (int64_t e0 = 0; e0 < m.E; e0 += group) {
+    const int64_t n = (m.E - e0) < group ? (m.E - e0) : group;
+    uint8_t* g = stage;
+    uint8_t* u = stage + wcode * n;
+    uint8_t* dn = stage + 2 * wcode * n;
+    float* gs = sstage;
+    float* us = sstage + wscale * n;
+    float* ds = sstage + 2 * wscale * n;
+    const bool ok =
+        hipMemcpyAsync(g, gate + e0 * wcode, (size_t)(wcode * n), hipMemcpyHostToDevice, s) == hipSuccess &&
+        hipMemcpyAsync(u, up + e0 * wcode, (size_t)(wcode * n), hipMemcpyHostToDevice, s) == hipSuccess &&
+        hipMemcpyAsync(dn, down + e0 * wcode, (size_t)(wcode * n), hipMemcpyHostToDevice, s) == hipSuccess &&
+        hipMemcpyAsync(gs, gate_scale + e0 * wscale, (size_t)(wscale * n * 4), hipMemcpyHostToDevice, s) == hipSuccess &&
+        hipMemcpyAsync(us, up_scale + e0 * wscale, (size_t)(wscale * n * 4), hipMemcpyHostToDevice, s) == hipSuccess &&
+        hipMemcpyAsync(ds, down_scale + e0 * wscale, (size_t)(wscale * n * 4), hipMemcpyHostToDevice, s) == hipSuccess;
+    if (!ok) return MOE_ERR_DEVICE;
+    LayoutArgs a{g, u, dn, gs, us, ds, (int32_t)e0, (int32_t)n, (int32_t)m.H, (int32_t)m.I, (int32_t)m.Ip,
+                 w13, s13, w2, s2};
+    if (launch_layout(a, s) != hipSuccess) return MOE_ERR_DEVICE;
+  }
+  return MOE_OK;
+}
+
+constexpr int64_t kStageGroup = 8;  // experts per staging copy
+
 int upload_weights(moe_fp8_prefill* h, hipStream_t s) {
   const moe_fp8_prefill_desc* d = &h->desc;
   const Dims& m = h->m;
@@ -201,43 +262,17 @@ int upload_weights(moe_fp8_prefill* h, hipStream_t s) {
     return hipStreamSynchronize(s) == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
   }
   // host source: stage a group of experts at a time through device memory
-  const int64_t group = 8;
-  const int64_t n_g = m.E < group ? m.E : group;
+  const int64_t n_g = m.E < kStageGroup ? m.E : kStageGroup;
   uint8_t* stage = nullptr;
   float* sstage = nullptr;
-  const int64_t code_bytes = 3 * wcode * n_g;
-  const int64_t scale_bytes = 3 * wscale * n_g * 4;
-  if (hipMalloc((void**)&stage, (size_t)code_bytes) != hipSuccess) return MOE_ERR_OUT_OF_MEMORY;
-  if (hipMalloc((void**)&sstage, (size_t)scale_bytes) != hipSuccess) {
+  if (hipMalloc((void**)&stage, (size_t)(3 * wcode * n_g)) != hipSuccess) return MOE_ERR_OUT_OF_MEMORY;
+  if (hipMalloc((void**)&sstage, (size_t)(3 * wscale * n_g * 4)) != hipSuccess) {
     (void)hipFree(stage);
     return MOE_ERR_OUT_OF_MEMORY;
   }
-  int rc = MOE_OK;
-  for (int64_t e0 = 0; e0 < m.E && rc == MOE_OK; e0 += group) {
-    const int64_t n = (m.E - e0) < group ? (m.E - e0) : group;
-    uint8_t* g = stage;
-    uint8_t* u = stage + wcode * n;
-    uint8_t* dn = stage + 2 * wcode * n;
-    float* gs = sstage;
-    float* us = sstage + wscale * n;
-    float* ds = sstage + 2 * wscale * n;
-    bool ok = hipMemcpyAsync(g, d->gate + e0 * wcode, (size_t)(wcode * n), hipMemcpyHostToDevice, s) == hipSuccess &&
-              hipMemcpyAsync(u, d->up + e0 * wcode, (size_t)(wcode * n), hipMemcpyHostToDevice, s) == hipSuccess &&
-              hipMemcpyAsync(dn, d->down + e0 * wcode, (size_t)(wcode * n), hipMemcpyHostToDevice, s) == hipSuccess &&
-              hipMemcpyAsync(gs, d->gate_scale + e0 * wscale, (size_t)(wscale * n * 4), hipMemcpyHostToDevice, s) == hipSuccess &&
-              hipMemcpyAsync(us, d->up_scale + e0 * wscale, (size_t)(wscale * n * 4), hipMemcpyHostToDevice, s) == hipSuccess &&
-              hipMemcpyAsync(ds, d->down_scale + e0 * wscale, (size_t)(wscale * n * 4), hipMemcpyHostToDevice, s) == hipSuccess;
-    if (!ok) {
-      rc = MOE_ERR_DEVICE;
-      break;
-    }
-    LayoutArgs a{g, u, dn, gs, us, ds, (int32_t)e0, (int32_t)n, (int32_t)m.H, (int32_t)m.I, (int32_t)m.Ip,
-                 h->w13, h->s13, h->w2, h->s2};
-    if (launch_layout(a, s) != hipSuccess) rc = MOE_ERR_DEVICE;
-    // the staging buffer is reused by the next group
-    if (rc == MOE_OK && hipStreamSynchronize(s) != hipSuccess) rc = MOE_ERR_DEVICE;
-  }
-  (void)hipStreamSynchronize(s);
+  int rc = enqueue_host_upload(h, d->gate, d->up, d->down, d->gate_scale, d->up_scale, d->down_scale,
+                               h->w13, h->s13, h->w2, h->s2, stage, sstage, kStageGroup, s);
+  if (hipStreamSynchronize(s) != hipSuccess && rc == MOE_OK) rc = MOE_ERR_DEVICE;
   (void)hipFree(stage);
   (void)hipFree(sstage);
   return rc;
@@ -307,6 +342,12 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
   }
   if (h->has_last && h->last_stream != s && hipStreamWaitEvent(s, h->done, 0) != hipSuccess)
     return fail(h);
+  moe_fp8_prefill::Slot* slot = nullptr;
+  if (h->n_slots) {
+    slot = &h->slots[h->active];
+    if (!slot->staged) return MOE_ERR_INVALID_ARG;
+    if (hipStreamWaitEvent(s, slot->ready, 0) != hipSuccess) return fail(h);
+  }
 
   const Dims& m = h->m;
   const int64_t out_elem = h->desc.out_dtype == MOE_DTYPE_F32 ? 4 : 2;
@@ -363,6 +404,10 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
     h->last_T = t;
   }
   if (hipEventRecord(h->done, s) != hipSuccess) return fail(h);
+  if (slot) {
+    if (hipEventRecord(slot->free, s) != hipSuccess) return fail(h);
+    slot->used = true;
+  }
   h->last_stream = s;
   h->has_last = true;
   return MOE_OK;
@@ -722,6 +767,151 @@ int moe_fp8_prefill_read_timing(moe_fp8_prefill* h, float* stage_ms, int32_t max
 int moe_fp8_prefill_debug_inject_failure(moe_fp8_prefill* h) {
   if (!h) return MOE_ERR_INVALID_ARG;
   h->inject_failure = true;
+  return MOE_OK;
+}
+
+int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slots,
+                                    moe_fp8_prefill** out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!d || (n_slots != 1 && n_slots != 2)) return MOE_ERR_INVALID_ARG;
+  // the description's weight pointers are not used: validate a copy with
+  // placeholders in them
+  moe_fp8_prefill_desc v;
+  memset(&v, 0, sizeof(v));
+  if (!desc_size_ok(d)) return MOE_ERR_INVALID_ARG;
+  memcpy(&v, d, (size_t)d->struct_size);
+  v.struct_size = (int32_t)sizeof(v);
+  v.shared_experts = desc_shared(d);
+  v.activation_limit = desc_limit(d);
+  static const uint8_t placeholder[16] = {0};
+  v.gate = v.up = v.down = placeholder;
+  v.gate_scale = v.up_scale = v.down_scale = (const float*)placeholder;
+  v.weights_on_device = 0;
+  const int rc = moe_fp8_prefill_validate(&v);
+  if (rc != MOE_OK) return rc;
+  moe_fp8_prefill* h = new (std::nothrow) moe_fp8_prefill();
+  if (!h) return MOE_ERR_OUT_OF_MEMORY;
+  h->desc = v;
+  h->desc.gate = h->desc.up = h->desc.down = nullptr;
+  h->desc.gate_scale = h->desc.up_scale = h->desc.down_scale = nullptr;
+  h->m = dims_of(&v);
+  const Dims& m = h->m;
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return MOE_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, h->device) == hipSuccess && prop.multiProcessorCount > 0)
+    h->num_cus = prop.multiProcessorCount;
+  const WsSizes w = ws_sizes(m);
+  void* p;
+  bool ok = true;
+  auto get = [&](int64_t bytes) -> void* {
+    if (!ok) return nullptr;
+    if (dalloc(h, &p, bytes) != hipSuccess) {
+      ok = false;
+      return nullptr;
+    }
+    return p;
+  };
+  h->n_slots = n_slots;
+  for (int i = 0; i < n_slots; ++i) {
+    h->slots[i].w13 = (uint8_t*)get(m.E * 2 * m.Ip * m.H);
+    h->slots[i].s13 = (float*)get(m.E * m.nI * m.nH * 2 * 4);
+    h->slots[i].w2 = (uint8_t*)get(m.E * m.H * m.Ip);
+    h->slots[i].s2 = (float*)get(m.E * m.nH * m.nI * 4);
+  }
+  const int64_t n_g = m.E < kStageGroup ? m.E : kStageGroup;
+  h->stage_codes = (uint8_t*)get(3 * m.I * m.H * n_g);
+  h->stage_scales = (float*)get(3 * ((m.I + 127) / 128) * m.nH * n_g * 4);
+  h->xq = (uint8_t*)get(w.xq);
+  h->sx = (float*)get(w.sx);
+  h->hq = (uint8_t*)get(w.hq);
+  h->sh = (float*)get(w.sh);
+  h->y = (float*)get(w.y);
+  h->counts = (int32_t*)get(w.counts);
+  h->offsets = (int32_t*)get(w.offsets);
+  h->perm = (int32_t*)get(w.perm);
+  h->inv = (int32_t*)get(w.inv);
+  h->small_tiles = (Tile*)get(w.small_tiles);
+  h->big_tiles = (Tile*)get(w.big_tiles);
+  h->n_tiles = (int32_t*)get(w.n_tiles);
+  h->err = (int32_t*)get(w.err);
+  h->rids = (int32_t*)get(w.rids);
+  h->rw = (float*)get(w.rw);
+  if (!ok) {
+    free_all(h);
+    delete h;
+    return MOE_ERR_OUT_OF_MEMORY;
+  }
+  bool ev_ok = hipEventCreateWithFlags(&h->done, hipEventDisableTiming) == hipSuccess &&
+               hipEventCreateWithFlags(&h->stage_done, hipEventDisableTiming) == hipSuccess;
+  for (int i = 0; i < n_slots && ev_ok; ++i)
+    ev_ok = hipEventCreateWithFlags(&h->slots[i].ready, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&h->slots[i].free, hipEventDisableTiming) == hipSuccess;
+  hipStream_t s = (hipStream_t)v.stream;
+  if (!ev_ok || hipMemsetAsync(h->err, 0, 4, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
+    free_all(h);
+    delete h;
+    return MOE_ERR_DEVICE;
+  }
+  h->w13 = h->slots[0].w13;
+  h->s13 = h->slots[0].s13;
+  h->w2 = h->slots[0].w2;
+  h->s2 = h->slots[0].s2;
+  *out = h;
+  return MOE_OK;
+}
+
+int moe_fp8_prefill_stage(moe_fp8_prefill* h, int32_t slot, const uint8_t* gate, const uint8_t* up,
+                          const uint8_t* down, const float* gate_scale, const float* up_scale,
+                          const float* down_scale, void* stream_) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  if (h->failed) return MOE_ERR_FAILED_STATE;
+  if (!h->n_slots || slot < 0 || slot >= h->n_slots) return MOE_ERR_INVALID_ARG;
+  if (!gate || !up || !down || !gate_scale || !up_scale || !down_scale) return MOE_ERR_INVALID_ARG;
+  int expected = 0;
+  if (!h->busy.compare_exchange_strong(expected, 1)) return MOE_ERR_BUSY;
+  struct Release {
+    std::atomic<int>& b;
+    ~Release() { b.store(0); }
+  } release{h->busy};
+  hipStream_t s = (hipStream_t)stream_;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return fail(h);
+  if (cap != hipStreamCaptureStatusNone) return MOE_ERR_UNSUPPORTED;
+  if (h->inject_failure) {
+    h->inject_failure = false;
+    return fail(h);
+  }
+  moe_fp8_prefill::Slot& sl = h->slots[slot];
+  // stream-ordered reuse: the passes that read this slot, and the previous
+  // staging (it owns the staging buffers), come first
+  if (sl.used && hipStreamWaitEvent(s, sl.free, 0) != hipSuccess) return fail(h);
+  if (h->staged_once && hipStreamWaitEvent(s, h->stage_done, 0) != hipSuccess) return fail(h);
+  const int rc = enqueue_host_upload(h, gate, up, down, gate_scale, up_scale, down_scale, sl.w13, sl.s13,
+                                     sl.w2, sl.s2, h->stage_codes, h->stage_scales, kStageGroup, s);
+  if (rc != MOE_OK) return fail(h, rc);
+  if (hipEventRecord(sl.ready, s) != hipSuccess || hipEventRecord(h->stage_done, s) != hipSuccess)
+    return fail(h);
+  sl.staged = true;
+  h->staged_once = true;
+  return MOE_OK;
+}
+
+int moe_fp8_prefill_select_slot(moe_fp8_prefill* h, int32_t slot) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  if (h->failed) return MOE_ERR_FAILED_STATE;
+  if (!h->n_slots || slot < 0 || slot >= h->n_slots || !h->slots[slot].staged) return MOE_ERR_INVALID_ARG;
+  int expected = 0;
+  if (!h->busy.compare_exchange_strong(expected, 1)) return MOE_ERR_BUSY;
+  h->active = slot;
+  h->w13 = h->slots[slot].w13;
+  h->s13 = h->slots[slot].s13;
+  h->w2 = h->slots[slot].w2;
+  h->s2 = h->slots[slot].s2;
+  h->busy.store(0);
   return MOE_OK;
 }
 

@@ -171,6 +171,34 @@ int moe_fp8_prefill_route(moe_fp8_prefill* h, const float* logits, int32_t route
 int moe_fp8_prefill_run_logits(moe_fp8_prefill* h, const void* x, const float* logits,
                                int32_t router, int64_t T, void* out, void* stream);
 
+/*
+ * Streamed layer slots ("ktransformers #2244", Design: one reusable per-layer
+ * slot that the host refills layer after layer; synchronise before reusing a
+ * slot; fail closed after a staging failure).  create_streamed() validates
+ * like create() but ignores the description's weight pointers, and
+ * allocates n_slots (1 or 2) device weight slots plus one staging buffer;
+ * nothing is uploaded.
+ *
+ * stage() copies one layer's weights (host memory in the canonical layout of
+ * the description; pinned memory lets the copy overlap other work) into
+ * slot `slot` and re-lays them out there, asynchronously on `stream`.  It
+ * first makes `stream` wait for the last run() that read that slot and for
+ * the previous stage() (they share the staging buffer), so a slot is never
+ * overwritten while a queued pass still reads it.  The host arrays must stay
+ * valid until the stream passes the call.  A HIP failure leaves the handle
+ * FAILED.
+ *
+ * select_slot() (host only) picks the slot that later run() / run_logits()
+ * calls compute with; they wait for that slot's staging.  A slot that was
+ * never staged is MOE_ERR_INVALID_ARG.  Slot 0 is selected at creation.
+ */
+int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slots,
+                                    moe_fp8_prefill** out);
+int moe_fp8_prefill_stage(moe_fp8_prefill* h, int32_t slot, const uint8_t* gate, const uint8_t* up,
+                          const uint8_t* down, const float* gate_scale, const float* up_scale,
+                          const float* down_scale, void* stream);
+int moe_fp8_prefill_select_slot(moe_fp8_prefill* h, int32_t slot);
+
 /* Synchronises the handle's last stream; returns and clears device-detected
  * errors (MOE_ERR_BAD_EXPERT_ID), or MOE_ERR_FAILED_STATE, else MOE_OK. */
 int moe_fp8_prefill_status(moe_fp8_prefill* h);

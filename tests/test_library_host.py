@@ -89,6 +89,11 @@ def test_null_handle_calls():
     assert lib.moe_fp8_prefill_status(None) == pkg.MOE_ERR_INVALID_ARG
     assert lib.moe_fp8_prefill_route(None, None, 0, 1, None, None, None) == pkg.MOE_ERR_INVALID_ARG
     assert lib.moe_fp8_prefill_run_logits(None, None, None, 0, 1, None, None) == pkg.MOE_ERR_INVALID_ARG
+    assert lib.moe_fp8_prefill_stage(None, 0, None, None, None, None, None, None, None) == pkg.MOE_ERR_INVALID_ARG
+    assert lib.moe_fp8_prefill_select_slot(None, 0) == pkg.MOE_ERR_INVALID_ARG
+    h = ctypes.c_void_p()
+    assert lib.moe_fp8_prefill_create_streamed(None, 2, ctypes.byref(h)) == pkg.MOE_ERR_INVALID_ARG
+    assert h.value is None
     lib.moe_fp8_prefill_destroy(None)  # NULL-safe
 
 
