@@ -35,6 +35,7 @@ FAULTS = {
     "route_tie_high": 13,
     "route_all_experts": 14,
     "shared_inside_rho": 15,
+    "slice_scale_block": 16,
 }
 
 ROUTE_SOFTMAX = 0
@@ -102,6 +103,9 @@ def _load():
         lib.orc_set_fault.restype = None
         lib.orc_max_threads.argtypes = []
         lib.orc_max_threads.restype = ctypes.c_int32
+        lib.orc_slice_matrix.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_int64, ctypes.c_int64, P, P]
+        lib.orc_slice_matrix.restype = ctypes.c_int32
         lib.orc_set_activation_limit.argtypes = [ctypes.c_float]
         lib.orc_set_activation_limit.restype = None
         lib.orc_route.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P]
@@ -194,6 +198,36 @@ def route(logits: np.ndarray, k: int, kind: int):
     if _load().orc_route(_p(logits), T, E, k, kind, _p(ids), _p(w)) != 0:
         raise ValueError("bad router arguments")
     return ids, w
+
+
+def slice_matrix(codes: np.ndarray, scales: np.ndarray, axis: int, off: int, length: int):
+    """Slice one [R][C] code matrix (block scales [ceil(R/128)][ceil(C/128)])
+    along rows (axis 0) or columns (axis 1) to [off, off+length), with the
+    load-time requant when off is not a multiple of 128."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    R, C = codes.shape
+    oR, oC = (length, C) if axis == 0 else (R, length)
+    oc = np.empty((oR, oC), np.uint8)
+    os_ = np.empty(((oR + 127) // 128, (oC + 127) // 128), np.float32)
+    if _load().orc_slice_matrix(_p(codes), _p(scales), R, C, axis, off, length, _p(oc), _p(os_)) != 0:
+        raise ValueError("bad slice arguments")
+    return oc, os_
+
+
+def slice_layer(layer, off: int, inter: int):
+    """The layer's experts restricted to intermediate features [off, off+inter)
+    (gate / up rows, down columns), requantised when off % 128 != 0."""
+    E = layer.gate.shape[0]
+    out = {k: [] for k in ("gate", "up", "down", "gate_scale", "up_scale", "down_scale")}
+    for e in range(E):
+        for name, axis in (("gate", 0), ("up", 0), ("down", 1)):
+            c, s = slice_matrix(getattr(layer, name)[e], getattr(layer, name + "_scale")[e], axis, off, inter)
+            out[name].append(c)
+            out[name + "_scale"].append(s)
+    arrs = {k: np.stack(v) for k, v in out.items()}
+    return type(layer)(layer.E, layer.H, inter, arrs["gate"], arrs["up"], arrs["down"],
+                       arrs["gate_scale"], arrs["up_scale"], arrs["down_scale"])
 
 
 def _layer_struct(layer):

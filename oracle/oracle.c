@@ -54,6 +54,7 @@ enum {
   FAULT_ROUTE_TIE_HIGH = 13,    /* router ties go to the higher expert id    */
   FAULT_ROUTE_ALL_EXPERTS = 14, /* softmax weights normalised over all E     */
   FAULT_SHARED_INSIDE_RHO = 15, /* shared slots scaled by rho too            */
+  FAULT_SLICE_SCALE_BLOCK = 16, /* requant reads the next checkpoint block's scale */
 };
 static int g_fault = FAULT_NONE;
 void orc_set_fault(int32_t f) { g_fault = f; }
@@ -668,5 +669,70 @@ int32_t orc_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t 
     for (int32_t j = 0; j < k; ++j) wt[j] = (no_mass || sum == 0.0) ? 0.0 : wt[j] / sum;
   }
   free(taken);
+  return 0;
+}
+
+/* ---- load-time slice of the intermediate dimension ---------------------- */
+
+/*
+ * One matrix M [R][C] (E4M3 codes) with FP32 block scales [ceil(R/128)]
+ * [ceil(C/128)], sliced along the intermediate dimension: rows (axis 0, the
+ * gate / up matrices) or columns (axis 1, the down matrix), keeping
+ * [off, off + len).  ("hpc-ops #80", gap table row 6: a tensor-parallel
+ * rank's non-128-multiple share gets zero padding and a load-time weight
+ * requant.)  If off is a multiple of 128 the slice's blocks are the
+ * checkpoint's: codes and the covering blocks' scales are copied.  Otherwise
+ * every block of the slice is requantised: v = dec(code) * S_ckpt in FP32
+ * (S of the checkpoint block that held the element), s = max|v| / 448 over
+ * the slice's 128x128 block (IEEE division; 0 if the block is all zero),
+ * code = enc(v / s) (IEEE division, RNE to E4M3).
+ * out_codes: [len][C] or [R][len]; out_scales: [ceil(len/128)][ceil(C/128)]
+ * or [ceil(R/128)][ceil(len/128)].  Returns 0, or -1 on bad arguments.
+ */
+int32_t orc_slice_matrix(const uint8_t* codes, const float* scales, int64_t R, int64_t C,
+                         int32_t axis, int64_t off, int64_t len, uint8_t* out_codes,
+                         float* out_scales) {
+  const int64_t full = axis == 0 ? R : C;
+  if (R < 1 || C < 1 || (axis != 0 && axis != 1) || off < 0 || len < 1 || off + len > full) return -1;
+  const int64_t rb = (R + 127) / 128, cb = (C + 127) / 128;
+  const int64_t oR = axis == 0 ? len : R, oC = axis == 0 ? C : len;
+  const int64_t orb = (oR + 127) / 128, ocb = (oC + 127) / 128;
+  for (int64_t bi = 0; bi < orb; ++bi) {
+    for (int64_t bj = 0; bj < ocb; ++bj) {
+      const int64_t r0 = bi * 128, r1 = r0 + 128 < oR ? r0 + 128 : oR;
+      const int64_t c0 = bj * 128, c1 = c0 + 128 < oC ? c0 + 128 : oC;
+      if (off % 128 == 0) {
+        /* the block coincides with a checkpoint block (or its start) */
+        const int64_t sr = axis == 0 ? (r0 + off) / 128 : bi, sc = axis == 0 ? bj : (c0 + off) / 128;
+        out_scales[bi * ocb + bj] = scales[sr * cb + sc];
+        for (int64_t r = r0; r < r1; ++r)
+          for (int64_t c = c0; c < c1; ++c) {
+            const int64_t gr = axis == 0 ? r + off : r, gc = axis == 0 ? c : c + off;
+            out_codes[r * oC + c] = codes[gr * C + gc];
+          }
+        continue;
+      }
+      float amax = 0.0f;
+      for (int64_t pass = 0; pass < 2; ++pass) {
+        const float s = amax / 448.0f;
+        for (int64_t r = r0; r < r1; ++r)
+          for (int64_t c = c0; c < c1; ++c) {
+            const int64_t gr = axis == 0 ? r + off : r, gc = axis == 0 ? c : c + off;
+            int64_t sbr = gr / 128, sbc = gc / 128;
+            if (g_fault == FAULT_SLICE_SCALE_BLOCK) {
+              if (axis == 0) sbr = (sbr + 1) % rb; else sbc = (sbc + 1) % cb;
+            }
+            const float v = orc_e4m3_decode(codes[gr * C + gc]) * scales[sbr * cb + sbc];
+            if (pass == 0) {
+              const float a = fabsf(v);
+              if (a > amax) amax = a;
+            } else {
+              out_codes[r * oC + c] = (uint8_t)(amax == 0.0f ? 0u : orc_e4m3_encode(v / s));
+            }
+          }
+        if (pass == 0) out_scales[bi * ocb + bj] = amax / 448.0f;
+      }
+    }
+  }
   return 0;
 }

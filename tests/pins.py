@@ -24,6 +24,11 @@ What pins what:
   clamp      the FP64 brute force with the clamped SwiGLU; h from the
              oracle's own gate/up through a numpy clamp; a limit above every
              |gate|, |up| reproduces the unclamped bits.
+  slice      an aligned slice = numpy slicing of codes and scales; the
+             requant of an unaligned slice = a torch re-derivation (FP32
+             dequantise, block amax / 448, float8 cast) bit for bit, within
+             the E4M3 rounding bound of the checkpoint values; two slices'
+             FP64 brute forces add up to the full layer's.
   layer      the FP64 dense brute force (different loop structure, FP64,
              exhaustive-search encoder); a dense gated FFN evaluated with torch
              float8 casts and float64 matmuls; an integer-exact case compared
@@ -644,6 +649,74 @@ def pin_clamp_large_limit_is_unclamped():
     return _ok(np.array_equal(base.view(np.uint32), big.view(np.uint32)), "a huge limit changed bits")
 
 
+def slice_case(seed=21):
+    return gen.make_layer(3, 256, 384, seed=seed)
+
+
+def pin_slice_aligned_is_plain():
+    l = slice_case()
+    ok = True
+    for off, n in ((0, 192), (128, 192), (256, 128), (128, 256)):
+        a = oracle.slice_layer(l, off, n)
+        nb = (n + 127) // 128
+        ok &= np.array_equal(a.gate, l.gate[:, off:off + n]) and np.array_equal(a.up, l.up[:, off:off + n])
+        ok &= np.array_equal(a.down, l.down[:, :, off:off + n])
+        ok &= np.array_equal(a.gate_scale, l.gate_scale[:, off // 128:off // 128 + nb])
+        ok &= np.array_equal(a.down_scale, l.down_scale[:, :, off // 128:off // 128 + nb])
+    return _ok(ok, "aligned slices differ from plain slicing")
+
+
+def _torch_requant(v):
+    """Block-requantise FP32 values [R][C] per 128x128 block with torch."""
+    R, C = v.shape
+    codes = np.zeros((R, C), np.uint8)
+    scales = np.zeros(((R + 127) // 128, (C + 127) // 128), np.float32)
+    for bi in range(scales.shape[0]):
+        for bj in range(scales.shape[1]):
+            blk = torch.from_numpy(np.ascontiguousarray(v[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]))
+            amax = blk.abs().max()
+            sc = amax / 448.0
+            scales[bi, bj] = sc.item()
+            if amax.item() != 0.0:
+                codes[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128] = \
+                    (blk / sc).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scales
+
+
+def pin_slice_requant_vs_torch():
+    l = slice_case()
+    dec = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    ok, worst = True, 0.0
+    for off, n in ((192, 192), (64, 256), (200, 100)):
+        a = oracle.slice_layer(l, off, n)
+        for e in range(l.gate.shape[0]):
+            for name, axis in (("gate", 0), ("up", 0), ("down", 1)):
+                full = getattr(l, name)[e]
+                sc = np.repeat(np.repeat(getattr(l, name + "_scale")[e], 128, 0), 128, 1)[:full.shape[0], :full.shape[1]]
+                v = (dec[full] * sc).astype(np.float32)     # FP32 products, as the oracle forms them
+                v = v[off:off + n] if axis == 0 else v[:, off:off + n]
+                c_ref, s_ref = _torch_requant(v)
+                got_c, got_s = getattr(a, name)[e], getattr(a, name + "_scale")[e]
+                ok &= np.array_equal(got_c, c_ref) and np.array_equal(got_s.view(np.uint32), s_ref.view(np.uint32))
+                back = dec[got_c].astype(np.float64) * np.repeat(np.repeat(got_s, 128, 0), 128, 1)[:v.shape[0], :v.shape[1]]
+                worst = max(worst, float((np.abs(back - v) / np.maximum(np.abs(v), 1e-30))[np.abs(v) > 1e-4].max()))
+    return _ok(ok and worst <= 1 / 16 + 1e-6, f"requant bits equal={ok}, worst rel error {worst:.4f}")
+
+
+def pin_slices_add_up():
+    """Two tensor-parallel shares (one aligned, one requantised) through the
+    FP64 brute force add up to the full layer's output."""
+    l = slice_case()
+    T = 12
+    x, _ = gen.make_tokens(T, l.H, seed=4)
+    ids, w = gen.make_routing(T, 3, 2, gen.ROUTE_SIGMOID_NORMAL, seed=4)
+    full = oracle.bruteforce_fp64(l, x, ids, w, 1.0, quantize_activations=False)
+    parts = sum(oracle.bruteforce_fp64(oracle.slice_layer(l, off, 192), x, ids, w, 1.0,
+                                       quantize_activations=False) for off in (0, 192))
+    worst = float(rel_l2_rows(parts, full).max())
+    return _ok(worst <= 3e-2, f"slices add up to the full layer within {worst:.3e}")
+
+
 ALL_PINS = {
     "decode_golden": pin_decode_golden,
     "decode_vs_torch": pin_decode_vs_torch,
@@ -677,4 +750,7 @@ ALL_PINS = {
     "clamp_vs_bruteforce": pin_clamp_vs_bruteforce,
     "clamp_activation_from_gu": pin_clamp_activation_from_gu,
     "clamp_large_limit_is_unclamped": pin_clamp_large_limit_is_unclamped,
+    "slice_aligned_is_plain": pin_slice_aligned_is_plain,
+    "slice_requant_vs_torch": pin_slice_requant_vs_torch,
+    "slices_add_up": pin_slices_add_up,
 }

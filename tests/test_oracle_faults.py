@@ -25,6 +25,7 @@ CAUGHT_BY = {
     "route_tie_high": ["route_ids_vs_sort", "route_special_rows"],
     "route_all_experts": ["route_weights_vs_scipy", "route_special_rows"],
     "shared_inside_rho": ["shared_vs_bruteforce", "shared_composition"],
+    "slice_scale_block": ["slice_requant_vs_torch", "slices_add_up"],
 }
 
 
