@@ -63,7 +63,8 @@ class moe_fp8_prefill_desc(ctypes.Structure):
         ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
         ("gate_scale", ctypes.c_void_p), ("up_scale", ctypes.c_void_p), ("down_scale", ctypes.c_void_p),
         ("stream", ctypes.c_void_p), ("shared_experts", ctypes.c_int32),
-        ("activation_limit", ctypes.c_float),
+        ("activation_limit", ctypes.c_float), ("inter_full", ctypes.c_int32),
+        ("inter_offset", ctypes.c_int32),
     ]
 
 
@@ -150,23 +151,28 @@ def _check(rc: int, where: str) -> None:
 def make_desc(layer, top_k: int, max_rows: int = 8192, out_dtype: int = MOE_DTYPE_BF16,
               routed_scale: float = 1.0, activation: int = MOE_ACT_SILU_UNCLAMPED,
               block: int = 128, stream=None, on_device: bool = False, shared_experts: int = 0,
-              activation_limit: float = 0.0):
+              activation_limit: float = 0.0, share=None):
     """Description for a layer held as numpy arrays (or, with on_device=True,
     torch device tensors) with fields gate, up, down, gate_scale, up_scale,
     down_scale, E, H, I.  With shared_experts=1 the arrays hold layer.E
     experts, the last one shared (E - 1 routed).  Keep the returned arrays
-    alive until create()."""
+    alive until create().  share=(offset, length): use intermediate features
+    [offset, offset + length) of the arrays' layer.I."""
     arrs = [layer.gate, layer.up, layer.down, layer.gate_scale, layer.up_scale, layer.down_scale]
     if on_device:
         ptrs = [a.data_ptr() for a in arrs]
     else:
         arrs = [np.ascontiguousarray(a) for a in arrs]
         ptrs = [a.ctypes.data for a in arrs]
+    inter, i_full, i_off = layer.I, 0, 0
+    if share is not None:
+        i_off, inter = share
+        i_full = layer.I
     d = moe_fp8_prefill_desc(ctypes.sizeof(moe_fp8_prefill_desc), layer.E - shared_experts, top_k,
-                             layer.H, layer.I, max_rows, out_dtype, activation, block, routed_scale,
+                             layer.H, inter, max_rows, out_dtype, activation, block, routed_scale,
                              1 if on_device else 0, *ptrs,
                              None if stream is None else _stream_ptr(stream).value, shared_experts,
-                             activation_limit)
+                             activation_limit, i_full, i_off)
     return d, arrs
 
 
@@ -342,18 +348,22 @@ class MoeFp8Prefill:
 
     def __init__(self, layer, top_k: int, routed_scale: float = 1.0, max_rows: int = 8192,
                  out_dtype: int = MOE_DTYPE_BF16, on_device: bool = False, shared_experts: int = 0,
-                 activation_limit: float = 0.0):
-        """activation_limit > 0 selects the clamped SiLU with that limit."""
+                 activation_limit: float = 0.0, share=None):
+        """activation_limit > 0 selects the clamped SiLU with that limit;
+        share=(offset, length) takes intermediate features [offset,
+        offset + length) of the layer (requantised at load if unaligned)."""
         # E, k: routed experts and slots; the shared expert is the arrays' last
         self.E, self.H, self.I, self.k = layer.E - shared_experts, layer.H, layer.I, top_k
+        if share is not None:
+            self.I = share[1]
         self.shared = shared_experts
-        self.Ip = 128 * ((layer.I + 127) // 128)
+        self.Ip = 128 * ((self.I + 127) // 128)
         self.out_dtype = out_dtype
         self.max_rows = max_rows
         act = MOE_ACT_SILU_CLAMPED if activation_limit > 0 else MOE_ACT_SILU_UNCLAMPED
         desc, keep = make_desc(layer, top_k, max_rows, out_dtype, routed_scale, activation=act,
                                on_device=on_device, shared_experts=shared_experts,
-                               activation_limit=activation_limit)
+                               activation_limit=activation_limit, share=share)
         self.handle = moe_fp8_prefill_create(desc)
         del keep
 
@@ -409,17 +419,22 @@ class StreamedMoeFp8Prefill(MoeFp8Prefill):
 
     def __init__(self, shape, top_k: int, n_slots: int = 2, routed_scale: float = 1.0,
                  max_rows: int = 8192, out_dtype: int = MOE_DTYPE_BF16, shared_experts: int = 0,
-                 activation_limit: float = 0.0):
+                 activation_limit: float = 0.0, share=None):
         self.E, self.H, self.I, self.k = shape.E - shared_experts, shape.H, shape.I, top_k
-        self.Ip = 128 * ((shape.I + 127) // 128)
+        inter, i_full, i_off = shape.I, 0, 0
+        if share is not None:
+            i_off, inter = share
+            i_full = shape.I
+            self.I = inter
+        self.Ip = 128 * ((self.I + 127) // 128)
         self.out_dtype = out_dtype
         self.max_rows = max_rows
         self.shared = shared_experts
         act = MOE_ACT_SILU_CLAMPED if activation_limit > 0 else MOE_ACT_SILU_UNCLAMPED
         desc = moe_fp8_prefill_desc(ctypes.sizeof(moe_fp8_prefill_desc), shape.E - shared_experts, top_k,
-                                    shape.H, shape.I, max_rows, out_dtype, act, 128, routed_scale, 0,
+                                    shape.H, inter, max_rows, out_dtype, act, 128, routed_scale, 0,
                                     None, None, None, None, None, None, None, shared_experts,
-                                    activation_limit)
+                                    activation_limit, i_full, i_off)
         self.handle = moe_fp8_prefill_create_streamed(desc, n_slots)
 
     def stage(self, slot: int, layer, stream=None) -> None:

@@ -24,16 +24,24 @@ struct Dims {
   // E, k count the shared expert and its slot; Er, kr are the routed ones
   int64_t E, k, H, I, Ip, nH, nI, max_rows, P;  // P = max_rows * k
   int64_t Er, kr, shared;
+  int64_t I_full, I_off;  // checkpoint width and the share's start (I_full == I: no share)
 };
 
 // Description sizes of older callers: without shared_experts, and without
 // activation_limit.  Fields past a caller's struct_size read as 0.
 constexpr int32_t kDescNoShared = (int32_t)offsetof(moe_fp8_prefill_desc, shared_experts);
 constexpr int32_t kDescNoLimit = (int32_t)offsetof(moe_fp8_prefill_desc, activation_limit);
+constexpr int32_t kDescNoShare = (int32_t)offsetof(moe_fp8_prefill_desc, inter_full);
 
 bool desc_size_ok(const moe_fp8_prefill_desc* d) {
-  return d->struct_size == (int32_t)sizeof(moe_fp8_prefill_desc) || d->struct_size == kDescNoLimit ||
-         d->struct_size == kDescNoShared;
+  return d->struct_size == (int32_t)sizeof(moe_fp8_prefill_desc) || d->struct_size == kDescNoShare ||
+         d->struct_size == kDescNoLimit || d->struct_size == kDescNoShared;
+}
+int32_t desc_inter_full(const moe_fp8_prefill_desc* d) {
+  return d->struct_size > kDescNoShare ? d->inter_full : 0;
+}
+int32_t desc_inter_offset(const moe_fp8_prefill_desc* d) {
+  return d->struct_size > kDescNoShare ? d->inter_offset : 0;
 }
 int32_t desc_shared(const moe_fp8_prefill_desc* d) {
   return d->struct_size > kDescNoShared ? d->shared_experts : 0;
@@ -45,6 +53,8 @@ float desc_limit(const moe_fp8_prefill_desc* d) {
 Dims dims_of(const moe_fp8_prefill_desc* d) {
   Dims m;
   m.shared = desc_shared(d);
+  m.I_full = desc_inter_full(d) > 0 ? desc_inter_full(d) : d->inter;
+  m.I_off = desc_inter_full(d) > 0 ? desc_inter_offset(d) : 0;
   m.Er = d->num_experts;
   m.kr = d->top_k;
   m.E = m.Er + m.shared;
@@ -153,6 +163,8 @@ struct moe_fp8_prefill {
   Slot slots[2];
   uint8_t* stage_codes = nullptr;  // one group of experts in the canonical layout
   float* stage_scales = nullptr;
+  uint8_t* stage_full_codes = nullptr;  // the same at full checkpoint width (shares)
+  float* stage_full_scales = nullptr;
   hipEvent_t stage_done = nullptr;  // orders stage() calls made on different streams
   bool staged_once = false;
   hipStream_t last_stream = nullptr;
@@ -199,82 +211,115 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Upload experts [e0, e0+n) from canonical buffers (host or device) and
 // re-lay them out into the handle's weight arrays.
-// Copies experts [0, E) of a layer from host memory in the canonical layout
-// to the device, a group of `group` experts at a time through the staging
-// buffers, and re-lays each group out into (w13, s13, w2, s2).  Everything
-// is enqueued on s in order (the staging buffers are reused by the next
-// group only after the layout kernels of this one, by stream order); no host
-// synchronisation.
-int enqueue_host_upload(moe_fp8_prefill* h, const uint8_t* gate, const uint8_t* up,
-                        const uint8_t* down, const float* gate_scale, const float* up_scale,
-                        const float* down_scale, uint8_t* w13, float* s13, uint8_t* w2, float* s2,
-                        uint8_t* stage, float* sstage, int64_t group, hipStream_t s) {
+constexpr int64_t kStageGroup = 8;  // experts per staging copy
+
+// Staging buffers for one group of experts: the canonical layout of the
+// handle's I (`codes`, `scales`), and, when the handle takes a share of a
+// wider checkpoint, of the full width (`full_codes`, `full_scales`).
+struct Staging {
+  uint8_t* codes = nullptr;
+  float* scales = nullptr;
+  uint8_t* full_codes = nullptr;
+  float* full_scales = nullptr;
+};
+
+bool slicing(const Dims& m) { return m.I_full != m.I; }
+
+// Device bytes of the staging buffers (codes, scales, full codes, full scales).
+void staging_bytes(const Dims& m, bool src_on_device, int64_t out[4]) {
+  const int64_t n = m.E < kStageGroup ? m.E : kStageGroup;
+  const int64_t sc = (m.I + 127) / 128 * m.nH, scf = (m.I_full + 127) / 128 * m.nH;
+  out[0] = 3 * m.I * m.H * n;
+  out[1] = 3 * sc * n * 4;
+  out[2] = slicing(m) && !src_on_device ? 3 * m.I_full * m.H * n : 0;
+  out[3] = slicing(m) && !src_on_device ? 3 * scf * n * 4 : 0;
+}
+
+// Experts [0, E) of a layer in the checkpoint layout (the full width I_full
+// when the handle takes a share) -> (w13, s13, w2, s2), a group of experts at
+// a time: copied to the device (host source), cut to the share and
+// requantised if it is unaligned, re-laid out.  Everything is enqueued on s
+// in order, so each staging buffer is reused only after the kernels that
+// read it; no host synchronisation.
+int enqueue_upload(moe_fp8_prefill* h, const uint8_t* gate, const uint8_t* up, const uint8_t* down,
+                   const float* gate_scale, const float* up_scale, const float* down_scale,
+                   bool src_on_device, uint8_t* w13, float* s13, uint8_t* w2, float* s2,
+                   const Staging& st, hipStream_t s) {
   const Dims& m = h->m;
-  const int64_t wcode = m.I * m.H;
-  const int64_t wscale = ((m.I + 127) / 128) * m.nH;
-  for (int64_t e0 = 0; e0 < m.E; e0 += group) {
-    const int64_t n = (m.E - e0) < group ? (m.E - e0) : group;
-    uint8_t* g = stage;
-    uint8_t* u = stage + wcode * n;
-    uint8_t* dn = stage + 2 * wcode * n;
-    float* gs = sstage;
-    float* us = sstage + wscale * n;
-    float* ds = sstage + 2 * wscale * n;
-    const bool ok =
-        hipMemcpyAsync(g, gate + e0 * wcode, (size_t)(wcode * n), hipMemcpyHostToDevice, s) == hipSuccess &&
-        hipMemcpyAsync(u, up + e0 * wcode, (size_t)(wcode * n), hipMemcpyHostToDevice, s) == hipSuccess &&
-        hipMemcpyAsync(dn, down + e0 * wcode, (size_t)(wcode * n), hipMemcpyHostToDevice, s) == hipSuccess &&
-        hipMemcpyAsync(gs, gate_scale + e0 * wscale, (size_t)(wscale * n * 4), hipMemcpyHostToDevice, s) == hipSuccess &&
-        hipMemcpyAsync(us, up_scale + e0 * wscale, (size_t)(wscale * n * 4), hipMemcpyHostToDevice, s) == hipSuccess &&
-        hipMemcpyAsync(ds, down_scale + e0 * wscale, (size_t)(wscale * n * 4), hipMemcpyHostToDevice, s) == hipSuccess;
-    if (!ok) return MOE_ERR_DEVICE;
-    LayoutArgs a{g, u, dn, gs, us, ds, (int32_t)e0, (int32_t)n, (int32_t)m.H, (int32_t)m.I, (int32_t)m.Ip,
-                 w13, s13, w2, s2};
+  const int64_t wfull = m.I_full * m.H, sfull = (m.I_full + 127) / 128 * m.nH;
+  const int64_t wcode = m.I * m.H, wscale = (m.I + 127) / 128 * m.nH;
+  const hipMemcpyKind kind = src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+  for (int64_t e0 = 0; e0 < m.E; e0 += kStageGroup) {
+    const int64_t n = (m.E - e0) < kStageGroup ? (m.E - e0) : kStageGroup;
+    // this group's source, in the checkpoint layout at full width
+    const uint8_t* src[3] = {gate + e0 * wfull, up + e0 * wfull, down + e0 * wfull};
+    const float* ssrc[3] = {gate_scale + e0 * sfull, up_scale + e0 * sfull, down_scale + e0 * sfull};
+    uint8_t* dst[3] = {st.codes, st.codes + wcode * n, st.codes + 2 * wcode * n};
+    float* sdst[3] = {st.scales, st.scales + wscale * n, st.scales + 2 * wscale * n};
+    if (!slicing(m) && src_on_device) {
+      for (int i = 0; i < 3; ++i) {
+        dst[i] = const_cast<uint8_t*>(src[i]);
+        sdst[i] = const_cast<float*>(ssrc[i]);
+      }
+    } else if (!slicing(m)) {
+      for (int i = 0; i < 3; ++i)
+        if (hipMemcpyAsync(dst[i], src[i], (size_t)(wcode * n), kind, s) != hipSuccess ||
+            hipMemcpyAsync(sdst[i], ssrc[i], (size_t)(wscale * n * 4), kind, s) != hipSuccess)
+          return MOE_ERR_DEVICE;
+    } else {
+      if (!src_on_device) {
+        for (int i = 0; i < 3; ++i) {
+          uint8_t* fc = st.full_codes + i * wfull * n;
+          float* fs = st.full_scales + i * sfull * n;
+          if (hipMemcpyAsync(fc, src[i], (size_t)(wfull * n), kind, s) != hipSuccess ||
+              hipMemcpyAsync(fs, ssrc[i], (size_t)(sfull * n * 4), kind, s) != hipSuccess)
+            return MOE_ERR_DEVICE;
+          src[i] = fc;
+          ssrc[i] = fs;
+        }
+      }
+      for (int i = 0; i < 3; ++i) {
+        // gate / up: [I][H], share of the rows; down: [H][I], share of the columns
+        SliceArgs sa{src[i], ssrc[i], (int32_t)n, (int32_t)(i < 2 ? m.I_full : m.H),
+                     (int32_t)(i < 2 ? m.H : m.I_full), i < 2 ? 0 : 1, (int32_t)m.I_off, (int32_t)m.I,
+                     dst[i], sdst[i]};
+        if (launch_slice(sa, s) != hipSuccess) return MOE_ERR_DEVICE;
+      }
+    }
+    LayoutArgs a{dst[0], dst[1], dst[2], sdst[0], sdst[1], sdst[2], (int32_t)e0, (int32_t)n, (int32_t)m.H,
+                 (int32_t)m.I, (int32_t)m.Ip, w13, s13, w2, s2};
     if (launch_layout(a, s) != hipSuccess) return MOE_ERR_DEVICE;
   }
   return MOE_OK;
 }
 
-constexpr int64_t kStageGroup = 8;  // experts per staging copy
+// Allocates `st` (recorded in the handle's allocation list if `keep`, else
+// in `temp` for the caller to free).
+int alloc_staging(moe_fp8_prefill* h, bool src_on_device, Staging* st, std::vector<void*>* temp) {
+  int64_t bytes[4];
+  staging_bytes(h->m, src_on_device, bytes);
+  void** slots[4] = {(void**)&st->codes, (void**)&st->scales, (void**)&st->full_codes,
+                     (void**)&st->full_scales};
+  for (int i = 0; i < 4; ++i) {
+    if (bytes[i] == 0) continue;
+    if (hipMalloc(slots[i], (size_t)bytes[i]) != hipSuccess) return MOE_ERR_OUT_OF_MEMORY;
+    (temp ? *temp : h->allocations).push_back(*slots[i]);
+  }
+  return MOE_OK;
+}
 
 int upload_weights(moe_fp8_prefill* h, hipStream_t s) {
   const moe_fp8_prefill_desc* d = &h->desc;
-  const Dims& m = h->m;
-  const int64_t wcode = m.I * m.H;              // one gate (or up, or down) matrix
-  const int64_t wscale = ((m.I + 127) / 128) * m.nH;  // scales per matrix
-  if (d->weights_on_device) {
-    LayoutArgs a{d->gate, d->up, d->down, d->gate_scale, d->up_scale, d->down_scale,
-                 0, (int32_t)m.E, (int32_t)m.H, (int32_t)m.I, (int32_t)m.Ip,
-                 h->w13, h->s13, h->w2, h->s2};
-    // process in groups of experts so the launch grids stay moderate
-    for (int64_t e0 = 0; e0 < m.E; e0 += 8) {
-      const int64_t n = (m.E - e0) < 8 ? (m.E - e0) : 8;
-      a.gate = d->gate + e0 * wcode;
-      a.up = d->up + e0 * wcode;
-      a.down = d->down + e0 * wcode;
-      a.gate_scale = d->gate_scale + e0 * wscale;
-      a.up_scale = d->up_scale + e0 * wscale;
-      a.down_scale = d->down_scale + e0 * wscale;
-      a.e0 = (int32_t)e0;
-      a.n = (int32_t)n;
-      if (launch_layout(a, s) != hipSuccess) return MOE_ERR_DEVICE;
-    }
-    return hipStreamSynchronize(s) == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
-  }
-  // host source: stage a group of experts at a time through device memory
-  const int64_t n_g = m.E < kStageGroup ? m.E : kStageGroup;
-  uint8_t* stage = nullptr;
-  float* sstage = nullptr;
-  if (hipMalloc((void**)&stage, (size_t)(3 * wcode * n_g)) != hipSuccess) return MOE_ERR_OUT_OF_MEMORY;
-  if (hipMalloc((void**)&sstage, (size_t)(3 * wscale * n_g * 4)) != hipSuccess) {
-    (void)hipFree(stage);
-    return MOE_ERR_OUT_OF_MEMORY;
-  }
-  int rc = enqueue_host_upload(h, d->gate, d->up, d->down, d->gate_scale, d->up_scale, d->down_scale,
-                               h->w13, h->s13, h->w2, h->s2, stage, sstage, kStageGroup, s);
+  const bool on_dev = d->weights_on_device != 0;
+  Staging st;
+  std::vector<void*> temp;
+  int rc = MOE_OK;
+  if (!(on_dev && !slicing(h->m))) rc = alloc_staging(h, on_dev, &st, &temp);
+  if (rc == MOE_OK)
+    rc = enqueue_upload(h, d->gate, d->up, d->down, d->gate_scale, d->up_scale, d->down_scale, on_dev,
+                        h->w13, h->s13, h->w2, h->s2, st, s);
   if (hipStreamSynchronize(s) != hipSuccess && rc == MOE_OK) rc = MOE_ERR_DEVICE;
-  (void)hipFree(stage);
-  (void)hipFree(sstage);
+  for (void* p : temp) (void)hipFree(p);
   return rc;
 }
 
@@ -436,6 +481,10 @@ int moe_fp8_prefill_validate(const moe_fp8_prefill_desc* d) {
   if (!desc_size_ok(d)) return MOE_ERR_INVALID_ARG;
   const int32_t shared = desc_shared(d);
   const float limit = desc_limit(d);
+  const int32_t i_full = desc_inter_full(d), i_off = desc_inter_offset(d);
+  if (i_full < 0 || (i_full == 0 && i_off != 0)) return MOE_ERR_INVALID_ARG;
+  if (i_full > 0 && (i_off < 0 || d->inter < 1 || (int64_t)i_off + d->inter > i_full)) return MOE_ERR_INVALID_ARG;
+  if (i_full > kMaxKBlocks * kBlock) return MOE_ERR_UNSUPPORTED;
   if (shared != 0 && shared != 1) return MOE_ERR_UNSUPPORTED;
   if (!d->gate || !d->up || !d->down || !d->gate_scale || !d->up_scale || !d->down_scale)
     return MOE_ERR_INVALID_ARG;
@@ -484,6 +533,8 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   memcpy(&h->desc, d, (size_t)d->struct_size);
   h->desc.shared_experts = desc_shared(d);
   h->desc.activation_limit = desc_limit(d);
+  h->desc.inter_full = desc_inter_full(d);
+  h->desc.inter_offset = desc_inter_offset(d);
   h->desc.struct_size = (int32_t)sizeof(moe_fp8_prefill_desc);
   h->m = dims_of(d);
   const Dims& m = h->m;
@@ -784,6 +835,8 @@ int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slo
   v.struct_size = (int32_t)sizeof(v);
   v.shared_experts = desc_shared(d);
   v.activation_limit = desc_limit(d);
+  v.inter_full = desc_inter_full(d);
+  v.inter_offset = desc_inter_offset(d);
   static const uint8_t placeholder[16] = {0};
   v.gate = v.up = v.down = placeholder;
   v.gate_scale = v.up_scale = v.down_scale = (const float*)placeholder;
@@ -822,9 +875,14 @@ int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slo
     h->slots[i].w2 = (uint8_t*)get(m.E * m.H * m.Ip);
     h->slots[i].s2 = (float*)get(m.E * m.nH * m.nI * 4);
   }
-  const int64_t n_g = m.E < kStageGroup ? m.E : kStageGroup;
-  h->stage_codes = (uint8_t*)get(3 * m.I * m.H * n_g);
-  h->stage_scales = (float*)get(3 * ((m.I + 127) / 128) * m.nH * n_g * 4);
+  if (ok) {
+    Staging st;
+    ok = alloc_staging(h, false, &st, nullptr) == MOE_OK;
+    h->stage_codes = st.codes;
+    h->stage_scales = st.scales;
+    h->stage_full_codes = st.full_codes;
+    h->stage_full_scales = st.full_scales;
+  }
   h->xq = (uint8_t*)get(w.xq);
   h->sx = (float*)get(w.sx);
   h->hq = (uint8_t*)get(w.hq);
@@ -890,8 +948,13 @@ int moe_fp8_prefill_stage(moe_fp8_prefill* h, int32_t slot, const uint8_t* gate,
   // staging (it owns the staging buffers), come first
   if (sl.used && hipStreamWaitEvent(s, sl.free, 0) != hipSuccess) return fail(h);
   if (h->staged_once && hipStreamWaitEvent(s, h->stage_done, 0) != hipSuccess) return fail(h);
-  const int rc = enqueue_host_upload(h, gate, up, down, gate_scale, up_scale, down_scale, sl.w13, sl.s13,
-                                     sl.w2, sl.s2, h->stage_codes, h->stage_scales, kStageGroup, s);
+  Staging st;
+  st.codes = h->stage_codes;
+  st.scales = h->stage_scales;
+  st.full_codes = h->stage_full_codes;
+  st.full_scales = h->stage_full_scales;
+  const int rc = enqueue_upload(h, gate, up, down, gate_scale, up_scale, down_scale, false, sl.w13, sl.s13,
+                                sl.w2, sl.s2, st, s);
   if (rc != MOE_OK) return fail(h, rc);
   if (hipEventRecord(sl.ready, s) != hipSuccess || hipEventRecord(h->stage_done, s) != hipSuccess)
     return fail(h);

@@ -129,6 +129,16 @@ struct LayoutArgs {
   float* s2;
 };
 
+struct SliceArgs {
+  // n experts' matrices [R][C] (codes) with block scales [ceil(R/128)][ceil(C/128)],
+  // sliced along rows (axis 0) or columns (axis 1) to [off, off + len)
+  const uint8_t* src;
+  const float* src_s;
+  int32_t n, R, C, axis, off, len;
+  uint8_t* dst;    // [n][oR][oC]
+  float* dst_s;    // [n][ceil(oR/128)][ceil(oC/128)]
+};
+
 // Launchers (return the launch status).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
@@ -137,6 +147,7 @@ hipError_t launch_gate_up(const GateUpArgs& a, bool big, int grid, hipStream_t s
 hipError_t launch_down(const DownArgs& a, bool big, int grid, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
+hipError_t launch_slice(const SliceArgs& a, hipStream_t s);
 hipError_t launch_mfma_probe(const uint8_t* a, const uint8_t* b, float* d, hipStream_t s);
 
 }  // namespace moe

@@ -1282,6 +1282,85 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------- slice --
+// Load-time share of the intermediate dimension: one workgroup per 128x128
+// block of the share.  A share that starts on a 128 boundary keeps the
+// checkpoint's codes and block scales; otherwise the block is requantised:
+// v = dec(code) * S (FP32), s = max|v| / 448, code = E4M3(v / s).
+
+__device__ __forceinline__ float e4m3_dec(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float v;
+  if (e == 15u && m == 7u)
+    v = 0.0f;  // NaN codes act as signed zeros
+  else if (e == 0u)
+    v = (float)m * 0x1p-9f;
+  else
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -v : v;
+}
+
+__global__ __launch_bounds__(256) void slice_kernel(SliceArgs a) {
+  __shared__ uint32_t red[4];
+  const int tid = threadIdx.x;
+  const int oR = a.axis == 0 ? a.len : a.R, oC = a.axis == 0 ? a.C : a.len;
+  const int orb = (oR + 127) / 128, ocb = (oC + 127) / 128, cb = (a.C + 127) / 128;
+  int b = blockIdx.x;
+  const int e = b / (orb * ocb);
+  b -= e * orb * ocb;
+  const int bi = b / ocb, bj = b - (b / ocb) * ocb;
+  const int r0 = bi * 128, c0 = bj * 128;
+  const int nr = min(128, oR - r0), nc = min(128, oC - c0);
+  const uint8_t* src = a.src + (size_t)e * a.R * a.C;
+  const float* src_s = a.src_s + (size_t)e * ((a.R + 127) / 128) * cb;
+  uint8_t* dst = a.dst + (size_t)e * oR * oC;
+  const bool requant = (a.off & 127) != 0;
+  auto at = [&](int i, int& gr, int& gc, int& r, int& c) {
+    r = r0 + i / nc;
+    c = c0 + i - (i / nc) * nc;
+    gr = a.axis == 0 ? r + a.off : r;
+    gc = a.axis == 0 ? c : c + a.off;
+  };
+  float s;
+  if (requant) {
+    uint32_t m = 0;
+    for (int i = tid; i < nr * nc; i += 256) {
+      int gr, gc, r, c;
+      at(i, gr, gc, r, c);
+      const float v = e4m3_dec(src[(size_t)gr * a.C + gc]) * src_s[(gr / 128) * cb + gc / 128];
+      m = umax(m, abs_bits(v));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, o));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    const float amax = __uint_as_float(umax(umax(red[0], red[1]), umax(red[2], red[3])));
+    s = __fdiv_rn(amax, 448.0f);
+    for (int i = tid; i < nr * nc; i += 256) {
+      int gr, gc, r, c;
+      at(i, gr, gc, r, c);
+      const float v = e4m3_dec(src[(size_t)gr * a.C + gc]) * src_s[(gr / 128) * cb + gc / 128];
+      dst[(size_t)r * oC + c] = (uint8_t)(amax != 0.0f ? to_e4m3(__fdiv_rn(v, s)) : 0u);
+    }
+  } else {
+    const int sr = a.axis == 0 ? (r0 + a.off) / 128 : bi, sc = a.axis == 0 ? bj : (c0 + a.off) / 128;
+    s = src_s[sr * cb + sc];
+    for (int i = tid; i < nr * nc; i += 256) {
+      int gr, gc, r, c;
+      at(i, gr, gc, r, c);
+      dst[(size_t)r * oC + c] = src[(size_t)gr * a.C + gc];
+    }
+  }
+  if (tid == 0) a.dst_s[(size_t)e * orb * ocb + bi * ocb + bj] = s;
+}
+
+hipError_t launch_slice(const SliceArgs& a, hipStream_t s) {
+  const int oR = a.axis == 0 ? a.len : a.R, oC = a.axis == 0 ? a.C : a.len;
+  const int64_t blocks = (int64_t)a.n * ((oR + 127) / 128) * ((oC + 127) / 128);
+  hipLaunchKernelGGL(slice_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------- probe --
 
 __global__ __launch_bounds__(64) void mfma_probe_kernel(const uint8_t* a, const uint8_t* b, float* d) {

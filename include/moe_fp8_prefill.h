@@ -77,7 +77,8 @@ enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 };
  */
 typedef struct moe_fp8_prefill_desc {
   int32_t struct_size;      /* sizeof(moe_fp8_prefill_desc), or the size up to
-                               shared_experts or activation_limit (older callers) */
+                               shared_experts, activation_limit or inter_full
+                               (older callers) */
   int32_t num_experts;      /* E, 1..1024 */
   int32_t top_k;            /* k, 1..min(E, 256) */
   int32_t hidden;           /* H, multiple of 128 */
@@ -107,6 +108,18 @@ typedef struct moe_fp8_prefill_desc {
   /* L of MOE_ACT_SILU_CLAMPED: finite and > 0 (ten for GLM-5.3-Flash); must
    * be 0 with MOE_ACT_SILU_UNCLAMPED.  Absent (older struct_size) = 0. */
   float activation_limit;
+  /* Load-time share of a wider checkpoint ("hpc-ops #80", gap table row 6: a
+   * tensor-parallel rank's 192 of the intermediate features, zero-padded to
+   * 256, with a load-time weight requant).  inter_full > 0: the weight arrays
+   * hold inter_full intermediate features (gate/up rows, down columns, scale
+   * grids ceil(inter_full/128) wide) and the layer uses features
+   * [inter_offset, inter_offset + inter).  A share starting on a multiple of
+   * 128 keeps the checkpoint's codes and block scales; otherwise each of its
+   * 128x128 blocks is requantised at load: v = dec(code) * S in FP32,
+   * s = max|v| / 448, code = E4M3(v / s) (round to nearest even).
+   * inter_full = 0 (and inter_offset = 0): the arrays hold exactly inter. */
+  int32_t inter_full;
+  int32_t inter_offset;
 } moe_fp8_prefill_desc;
 
 typedef struct moe_fp8_prefill moe_fp8_prefill;

@@ -142,3 +142,19 @@ def test_clamped_activation_field():
     d.activation = 7
     d.activation_limit = 0.0
     assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_ERR_UNSUPPORTED
+
+
+def test_share_fields():
+    layer = gen.make_layer(4, 256, 384)
+    d, keep = pkg.make_desc(layer, 2, share=(192, 192))
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_OK
+    d, keep = pkg.make_desc(layer, 2, share=(300, 100))
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_ERR_INVALID_ARG
+    d, keep = pkg.make_desc(layer, 2, share=(-1, 100))
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_ERR_INVALID_ARG
+    d, keep = pkg.make_desc(layer, 2)
+    d.inter_offset = 5
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_ERR_INVALID_ARG
+    d.inter_offset = 0
+    d.struct_size = pkg.moe_fp8_prefill_desc.inter_full.offset   # a caller without the fields
+    assert pkg.moe_fp8_prefill_validate(d) == pkg.MOE_OK
