@@ -73,12 +73,13 @@ int64_t align256(int64_t n) { return (n + 255) & ~int64_t(255); }
 
 // Workspace pieces, in allocation order.
 struct WsSizes {
-  int64_t xq, sx, hq, sh, y, counts, offsets, perm, inv, small_tiles, big_tiles, n_tiles, err,
-      rids, rw;
+  int64_t xq, sx, hq, sh, y, counts, offsets, perm, inv, small_tiles, big_tiles, wide_tiles, n_tiles,
+      err, rids, rw;
   int64_t total() const {
     return align256(xq) + align256(sx) + align256(hq) + align256(sh) + align256(y) +
            align256(counts) + align256(offsets) + align256(perm) + align256(inv) +
-           align256(small_tiles) + align256(big_tiles) + align256(n_tiles) + align256(err) +
+           align256(small_tiles) + align256(big_tiles) + align256(wide_tiles) + align256(n_tiles) +
+           align256(err) +
            align256(rids) + align256(rw);
   }
 };
@@ -95,8 +96,9 @@ WsSizes ws_sizes(const Dims& m) {
   w.perm = m.P * 4;
   w.inv = m.P * 4;
   w.small_tiles = m.E * (int64_t)sizeof(Tile);
-  w.big_tiles = (m.P / kSmallRows + m.E + 1) * (int64_t)sizeof(Tile);
-  w.n_tiles = 2 * 4;
+  w.big_tiles = m.E * (int64_t)sizeof(Tile);
+  w.wide_tiles = (m.P / kBigRows + m.E + 1) * (int64_t)sizeof(Tile);
+  w.n_tiles = 4 * 4;
   w.err = 4;
   w.rids = m.max_rows * m.kr * 4;  // one pass's routed ids and weights (run_logits)
   w.rw = m.max_rows * m.kr * 4;
@@ -137,6 +139,7 @@ struct moe_fp8_prefill {
   int32_t* inv = nullptr;
   Tile* small_tiles = nullptr;
   Tile* big_tiles = nullptr;
+  Tile* wide_tiles = nullptr;
   int32_t* n_tiles = nullptr;
   int32_t* err = nullptr;
   int32_t* rids = nullptr;
@@ -325,26 +328,64 @@ int upload_weights(moe_fp8_prefill* h, hipStream_t s) {
 
 // Grid of a persistent GEMM launch: enough resident workgroups to fill the
 // chip, never more than the largest possible number of work items.
-int gemm_grid(const moe_fp8_prefill* h, int64_t max_items, bool big, bool gate_up) {
-  const int64_t per_cu = big ? 1 : (gate_up ? kGateUpWgPerCu : kDownWgPerCu);
+int gemm_grid(const moe_fp8_prefill* h, int64_t max_items, int kind, bool gate_up) {
+  const int64_t per_cu = kind != kGemmStream ? 1 : (gate_up ? kGateUpWgPerCu : kDownWgPerCu);
   return (int)std::max<int64_t>(1, std::min<int64_t>(max_items, h->num_cus * per_cu));
 }
 
-// The two gate_up launches (1-subtile tiles, then multi-subtile tiles) of a
-// pass over t rows / P slots whose plan and activations are in the workspace.
-hipError_t launch_gate_up_pair(moe_fp8_prefill* h, int64_t t, int64_t P, float* gu_dbg, hipStream_t s,
-                               hipEvent_t between = nullptr) {
+// Most tiles of one pass in each list (the kernels read the real counts).
+int64_t max_tiles(const Dims& m, int64_t P, int kind) {
+  if (kind == kGemmStream) return std::min<int64_t>(m.E, P);
+  if (kind == kGemmTile) return std::min<int64_t>(m.E, P / (kSmallRows + 1));
+  return P / kWideRows + std::min<int64_t>(m.E, P / (kBigRows + 1));
+}
+
+// The gate_up launches of a pass over t rows / P slots whose plan and
+// activations are in the workspace: streaming tiles, then 128-row tiles, then
+// 256-row tiles.
+hipError_t launch_gate_up_all(moe_fp8_prefill* h, int64_t t, int64_t P, float* gu_dbg, hipStream_t s,
+                              hipEvent_t between = nullptr) {
   const Dims& m = h->m;
   const int64_t nb = m.Ip / kBlock;
   GateUpArgs ga{h->xq, h->sx, t * m.H, t * m.nH * 4, h->perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip,
                 h->w13, h->s13, h->small_tiles, h->n_tiles, h->hq, h->sh, gu_dbg,
                 h->desc.activation == MOE_ACT_SILU_CLAMPED ? h->desc.activation_limit : 0.0f};
-  hipError_t e = launch_gate_up(ga, false, gemm_grid(h, m.E * nb, false, true), s);
-  if (e != hipSuccess) return e;
-  if (between && (e = hipEventRecord(between, s)) != hipSuccess) return e;
-  ga.tiles = h->big_tiles;
-  ga.n_tiles = h->n_tiles + 1;
-  return launch_gate_up(ga, true, gemm_grid(h, (P / kSmallRows + m.E) * nb, true, true), s);
+  Tile* lists[3] = {h->small_tiles, h->big_tiles, h->wide_tiles};
+  for (int kind = kGemmStream; kind <= kGemmWide; ++kind) {
+    const int64_t items = max_tiles(m, P, kind) * nb;
+    if (kind == kGemmTile && between) {
+      hipError_t e = hipEventRecord(between, s);
+      if (e != hipSuccess) return e;
+    }
+    if (items == 0) continue;
+    ga.tiles = lists[kind];
+    ga.n_tiles = h->n_tiles + kind;
+    hipError_t e = launch_gate_up(ga, kind, gemm_grid(h, items, kind, true), s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// The down launches, in the same order.
+hipError_t launch_down_all(moe_fp8_prefill* h, int64_t P, hipStream_t s, hipEvent_t between = nullptr) {
+  const Dims& m = h->m;
+  const int64_t nb = m.H / kBlock, nb2 = (nb + 1) / 2;
+  DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2,
+              h->small_tiles, h->n_tiles, h->y};
+  Tile* lists[3] = {h->small_tiles, h->big_tiles, h->wide_tiles};
+  for (int kind = kGemmStream; kind <= kGemmWide; ++kind) {
+    const int64_t items = max_tiles(m, P, kind) * (kind == kGemmStream ? nb : nb2);
+    if (kind == kGemmTile && between) {
+      hipError_t e = hipEventRecord(between, s);
+      if (e != hipSuccess) return e;
+    }
+    if (items == 0) continue;
+    da.tiles = lists[kind];
+    da.n_tiles = h->n_tiles + kind;
+    hipError_t e = launch_down(da, kind, gemm_grid(h, items, kind, false), s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 int get_stage_events(moe_fp8_prefill* h, StageEvents* out) {
@@ -396,8 +437,6 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
 
   const Dims& m = h->m;
   const int64_t out_elem = h->desc.out_dtype == MOE_DTYPE_F32 ? 4 : 2;
-  // Upper bounds of the tile lists; the kernels read the real counts.
-  const int nb_dn = (int)(m.H / kBlock);
 
   for (int64_t r0 = 0; r0 < T; r0 += m.max_rows) {
     const int64_t t = (T - r0) < m.max_rows ? (T - r0) : m.max_rows;
@@ -415,7 +454,7 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
     }
     PlanArgs pa{ids_p, (int32_t)t, (int32_t)m.k, (int32_t)m.E, (int32_t)m.kr, (int32_t)m.Er,
                 h->counts, h->offsets, h->perm, h->inv, h->small_tiles, h->big_tiles,
-                h->n_tiles, h->err};
+                h->wide_tiles, h->n_tiles, h->err};
     if (launch_plan(pa, s) != hipSuccess) return fail(h);
     if (h->timing && hipEventRecord(ev.ev[1], s) != hipSuccess) return fail(h);
 
@@ -423,19 +462,10 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
     if (launch_quant(qa, s) != hipSuccess) return fail(h);
     if (h->timing && hipEventRecord(ev.ev[2], s) != hipSuccess) return fail(h);
 
-    int g_small, g_big;
-    if (launch_gate_up_pair(h, t, P, nullptr, s, h->timing ? ev.ev[3] : nullptr) != hipSuccess)
+    if (launch_gate_up_all(h, t, P, nullptr, s, h->timing ? ev.ev[3] : nullptr) != hipSuccess)
       return fail(h);
     if (h->timing && hipEventRecord(ev.ev[4], s) != hipSuccess) return fail(h);
-
-    g_small = gemm_grid(h, m.E * nb_dn, false, false);
-    g_big = gemm_grid(h, (P / kSmallRows + m.E) * ((nb_dn + 1) / 2), true, false);
-    DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2, h->small_tiles, h->n_tiles, h->y};
-    if (launch_down(da, false, g_small, s) != hipSuccess) return fail(h);
-    if (h->timing && hipEventRecord(ev.ev[5], s) != hipSuccess) return fail(h);
-    da.tiles = h->big_tiles;
-    da.n_tiles = h->n_tiles + 1;
-    if (launch_down(da, true, g_big, s) != hipSuccess) return fail(h);
+    if (launch_down_all(h, P, s, h->timing ? ev.ev[5] : nullptr) != hipSuccess) return fail(h);
     if (h->timing && hipEventRecord(ev.ev[6], s) != hipSuccess) return fail(h);
 
     CombineArgs ca{h->y, h->inv, w_p, (int32_t)t, (int32_t)m.k, (int32_t)m.H, (int32_t)m.kr,
@@ -572,6 +602,7 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   h->inv = (int32_t*)get(w.inv);
   h->small_tiles = (Tile*)get(w.small_tiles);
   h->big_tiles = (Tile*)get(w.big_tiles);
+  h->wide_tiles = (Tile*)get(w.wide_tiles);
   h->n_tiles = (int32_t*)get(w.n_tiles);
   h->err = (int32_t*)get(w.err);
   h->rids = (int32_t*)get(w.rids);
@@ -708,7 +739,7 @@ int moe_fp8_prefill_debug_gate_up(moe_fp8_prefill* h, float* gu, int64_t cap_row
   if (hipMalloc((void**)&dbg, (size_t)bytes) != hipSuccess) return MOE_ERR_OUT_OF_MEMORY;
   // re-run the last pass's gate_up (deterministic: rewrites identical h)
   int rc = MOE_OK;
-  if (launch_gate_up_pair(h, h->last_T, h->last_T * h->m.k, dbg, nullptr) != hipSuccess ||
+  if (launch_gate_up_all(h, h->last_T, h->last_T * h->m.k, dbg, nullptr) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess ||
       hipMemcpy(gu, dbg, (size_t)bytes, hipMemcpyDeviceToHost) != hipSuccess)
     rc = fail(h);
@@ -894,6 +925,7 @@ int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slo
   h->inv = (int32_t*)get(w.inv);
   h->small_tiles = (Tile*)get(w.small_tiles);
   h->big_tiles = (Tile*)get(w.big_tiles);
+  h->wide_tiles = (Tile*)get(w.wide_tiles);
   h->n_tiles = (int32_t*)get(w.n_tiles);
   h->err = (int32_t*)get(w.err);
   h->rids = (int32_t*)get(w.rids);

@@ -11,7 +11,8 @@ constexpr int kBlock = 128;          // weight block edge and activation group
 constexpr int kWaves = 4;            // waves per GEMM workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSmallRows = 16;       // experts with <= this many rows use the 1-subtile GEMM
-constexpr int kBigRows = 128;        // rows per tile of the large-expert GEMMs
+constexpr int kBigRows = 128;        // rows per tile of the 4-wave large-expert GEMMs
+constexpr int kWideRows = 256;       // rows per tile of the 8-wave GEMMs (experts with > kBigRows rows)
 #ifndef MOE_STREAM_DEPTH
 #define MOE_STREAM_DEPTH 3
 #endif
@@ -54,8 +55,9 @@ struct PlanArgs {
   int32_t* perm;       // [T*k]
   int32_t* inv;        // [T*k]
   Tile* small_tiles;   // [E]
-  Tile* big_tiles;     // [T*k/16 + E]
-  int32_t* n_tiles;    // [2]: small, big
+  Tile* big_tiles;     // [E]: experts with kSmallRows < rows <= kBigRows, one tile each
+  Tile* wide_tiles;    // [T*k/kBigRows + E]: experts with more rows, tiles of <= kWideRows
+  int32_t* n_tiles;    // [3]: small, big, wide
   int32_t* err;        // sticky bad-id flag
 };
 
@@ -139,12 +141,15 @@ struct SliceArgs {
   float* dst_s;    // [n][ceil(oR/128)][ceil(oC/128)]
 };
 
+// GEMM variants (launch_gate_up / launch_down kind)
+constexpr int kGemmStream = 0, kGemmTile = 1, kGemmWide = 2;
+
 // Launchers (return the launch status).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s);
-hipError_t launch_gate_up(const GateUpArgs& a, bool big, int grid, hipStream_t s);
-hipError_t launch_down(const DownArgs& a, bool big, int grid, hipStream_t s);
+hipError_t launch_gate_up(const GateUpArgs& a, int kind, int grid, hipStream_t s);
+hipError_t launch_down(const DownArgs& a, int kind, int grid, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
 hipError_t launch_slice(const SliceArgs& a, hipStream_t s);

@@ -55,12 +55,13 @@ __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
-// Max over the 16 lanes that share l/16.
+// Max over the 16 lanes that share l/16 (one DPP row): lane pairs, then
+// quads, then the mirrored halves of 8 and of 16 lanes.
 __device__ __forceinline__ uint32_t max16(uint32_t v) {
-  v = umax(v, (uint32_t)__shfl_xor((int)v, 1));
-  v = umax(v, (uint32_t)__shfl_xor((int)v, 2));
-  v = umax(v, (uint32_t)__shfl_xor((int)v, 4));
-  v = umax(v, (uint32_t)__shfl_xor((int)v, 8));
+  v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row_mirror
   return v;
 }
 
@@ -88,8 +89,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16) & 0xFFFFu;
 }
 
+// silu(g) * u = g / (1 + e^-g) * u with the hardware exp2 and reciprocal
+// (each within a few ulp).  g = -inf gives NaN and g = +inf gives inf, as the
+// quotient does.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return __fdiv_rn(g, 1.0f + expf(-g)) * u;
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 // The clamped variant for L > 0: gate capped at L, up clipped to [-L, L]
@@ -170,23 +175,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int n = tid < E ? cnt[tid] : 0;
   int total;
   const int off = block_exclusive_scan(n, scan_scratch, &total);
+  // each expert's rows go to one list: <= kSmallRows rows one streaming tile,
+  // <= kBigRows one 128-row tile, more rows near-equal 256-row tiles
   const int is_small = (n >= 1 && n <= kSmallRows) ? 1 : 0;
-  const int n_big = n > kSmallRows ? (n + kBigRows - 1) / kBigRows : 0;
-  int n_small_all, n_big_all;
+  const int is_big = (n > kSmallRows && n <= kBigRows) ? 1 : 0;
+  const int n_wide = n > kBigRows ? (n + kWideRows - 1) / kWideRows : 0;
+  int n_small_all, n_big_all, n_wide_all;
   const int small_at = block_exclusive_scan(is_small, scan_scratch, &n_small_all);
-  const int big_at = block_exclusive_scan(n_big, scan_scratch, &n_big_all);
+  const int big_at = block_exclusive_scan(is_big, scan_scratch, &n_big_all);
+  const int wide_at = block_exclusive_scan(n_wide, scan_scratch, &n_wide_all);
   if (tid < E) {
     a.counts[tid] = n;
     a.offsets[tid] = off;
     cursor[tid] = off;
     if (is_small) a.small_tiles[small_at] = Tile{tid, off, n, small_at, 1, 0, 0, 0};
-    if (n_big) {
-      // split n rows into n_big tiles of near-equal size, multiples of 16 rows
-      const int per = ((n + n_big - 1) / n_big + 15) & ~15;
-      for (int i = 0; i < n_big; ++i) {
+    if (is_big) a.big_tiles[big_at] = Tile{tid, off, n, big_at, 1, 0, 0, 0};
+    if (n_wide) {
+      // split n rows into n_wide tiles of near-equal size, multiples of 16 rows
+      const int per = ((n + n_wide - 1) / n_wide + 15) & ~15;
+      for (int i = 0; i < n_wide; ++i) {
         const int r0 = i * per;
         const int r = (n - r0) < per ? (n - r0) : per;
-        a.big_tiles[big_at + i] = Tile{tid, off + r0, r, big_at, n_big, 0, 0, 0};
+        a.wide_tiles[wide_at + i] = Tile{tid, off + r0, r, wide_at, n_wide, 0, 0, 0};
       }
     }
   }
@@ -194,6 +204,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.offsets[E] = total;
     a.n_tiles[0] = n_small_all;
     a.n_tiles[1] = n_big_all;
+    a.n_tiles[2] = n_wide_all;
   }
   __syncthreads();
 
@@ -378,16 +389,21 @@ __device__ __forceinline__ float bloadf(rsrc_t r, uint32_t voff, uint32_t soff) 
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
-// Activation tile in LDS: BM rows x 128 bytes per K block, 16-byte chunks
-// XOR-swizzled by row so the MFMA fragment reads (16 rows, same chunk) hit
-// distinct banks.
-__device__ __forceinline__ int a_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// Activation tile in LDS: BM rows x 128 bytes per K block; logical 16-byte
+// chunk c of row r sits in slot c ^ swz(r).  An MFMA fragment read takes one
+// chunk of 16 consecutive rows: gfx950's LDS serves 256 bytes (64 banks) per
+// pass, so those 16 reads must fill 16 distinct 16-byte bank groups.  Rows
+// 128 bytes apart alternate between the two bank halves, and swz gives the 8
+// rows of each half 8 distinct slots (bit 3 of the row flips bit 0 of the
+// slot), so every 8- or 16-row group is conflict-free.  Only bits 0-3 of the
+// row matter, so subtiles of 16 rows share the lane's slot.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-__device__ __forceinline__ i32x8 a_frag(const uint8_t* lds, int m, int lane) {
-  const int row = m * 16 + (lane & 15);
-  const int g = lane >> 4;
-  return cat(ld16(lds + a_off(row, 2 * g)), ld16(lds + a_off(row, 2 * g + 1)));
-}
+// h staging tile of the gate_up epilogues: 128 bytes per row, 16-byte chunk c
+// of row r in slot c ^ ((r / 4) & 7).  The byte writes of one instruction
+// cover rows 4 apart (one per 16-lane group), which the XOR spreads over
+// distinct banks; the copy-out reads whole aligned chunks.
+__device__ __forceinline__ int h_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 2) & 7)) << 4); }
 
 // ----------------------------------------------------------------- gate_up --
 // Large-expert gate_up: a 256-thread workgroup computes a tile of up to 128
@@ -441,6 +457,22 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   for (int i = 0; i < NM; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+  }
+}
+
+// As interleave_mfma_valu, with NL vector-memory loads after the first MFMA:
+// a load that waits for room in the address queue then stalls the wave while
+// its MFMAs execute.
+template <int NM, int NV, int NL>
+__device__ __forceinline__ void interleave_mfma_valu_vmem() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+  __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);  // VMEM reads
+  __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+#pragma unroll
+  for (int i = 1; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
   }
 }
 
@@ -539,7 +571,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
   // wave w reads n-tiles g0, g1, u0, u1 of 32-column group w of the chunk
   const uint32_t b_off = (uint32_t)(wave * 4 * 2 * 1024 + lane * 16);
   const int afr = (lane & 15) * 128;
-  const int afc0 = ((2 * grp) ^ (lane & 7)) << 4, afc1 = ((2 * grp + 1) ^ (lane & 7)) << 4;
+  const int afc0 = ((2 * grp) ^ swz(lane)) << 4, afc1 = ((2 * grp + 1) ^ swz(lane)) << 4;
 
   for (int r = 0;; ++r) {
     const int item = item_index(r);
@@ -563,7 +595,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = (q * 4 + wave) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ (row & 7);
+      const int c = (lane & 7) ^ swz(row);
       avo[q] = (uint32_t)(tok_lds[row] * H + c * 16) + ((q * 4 + wave) * 8 < mt * 16 ? 0u : 0x80000000u);
     }
     const uint32_t svo = wave < 2 ? (uint32_t)(tok_lds[wave * 64 + lane] * nH * 4) : 0x80000000u;
@@ -721,7 +753,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const uint32_t c = amax != 0.0f ? to_e4m3(__fdiv_rn(acc[m][t][i], sc)) : 0u;
-            h_lds[row * 128 + wave * 32 + t * 16 + col] = (uint8_t)c;
+            h_lds[h_off(row, wave * 2 + t) + col] = (uint8_t)c;
           }
           if (wave == 0 && col == 0) sh_lds[row] = sc;
         }
@@ -729,7 +761,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
     }
     __syncthreads();
     for (int row = tid >> 3; row < rows; row += kTileThreads / 8)
-      st16(a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + (tid & 7) * 16, ld16(&h_lds[row * 128 + (tid & 7) * 16]));
+      st16(a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + (tid & 7) * 16, ld16(&h_lds[h_off(row, tid & 7)]));
     if (tid < rows) a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
   }
 }
@@ -866,8 +898,270 @@ __global__ __launch_bounds__(kThreads, D <= 2 ? 4 : 3) void gate_up_stream_kerne
   }
 }
 
-hipError_t launch_gate_up(const GateUpArgs& a, bool big, int grid, hipStream_t s) {
-  if (big)
+// Wide gate_up for experts with more than kBigRows rows: a 512-thread
+// workgroup (two waves per SIMD) computes a tile of up to 256 rows x (128 gate
+// + 128 up) columns of one 128-row block nb.  Both operands arrive in LDS by
+// buffer-load-to-LDS, double-buffered by K block: the gathered activation
+// rows (32 KiB per K block) and the expert's 32 KiB weight chunk, read once
+// per workgroup instead of once per wave.  Wave w = 4 mh + wn owns rows
+// 128 mh .. +127 and 32-column group wn of gate and up (4 n-tiles), the same
+// 16x16 tiles, MFMAs and promotion order as the other gate_up kernels.
+//
+// Per K block the tile moves 64 KiB through the vector memory pipe for
+// 256 x 256 x 128 MACs, about two thirds of the MFMA time, where a 128-row
+// tile would move 48 KiB for half the MACs.  With two waves per SIMD one wave
+// multiplies while the other waits for its loads to issue.
+constexpr int kWideThreads = 512;
+static_assert(kWideRows == 2 * kBigRows, "a wide tile is two 128-row halves");
+
+// kDbg: also write gate/up before the epilogue to a.gu_dbg (inspection
+// launches only; the pass launches the variant without that code).
+template <bool kDbg>
+__global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArgs a) {
+  constexpr int BM = kWideRows;
+  constexpr int NS = 2;  // LDS stages (1 K block ahead)
+  // one LDS object per stage, indexed only by compile-time stage numbers
+  // (see gate_up_tile_kernel)
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t w_lds0[kGateUpChunk];
+  __shared__ __attribute__((aligned(1024))) uint8_t w_lds1[kGateUpChunk];
+  // row scales: rows in the first half, the other half takes waves 4-7's
+  // out-of-range loads
+  __shared__ __attribute__((aligned(256))) float sx_lds0[2 * BM];
+  __shared__ __attribute__((aligned(256))) float sx_lds1[2 * BM];
+  __shared__ float ws_lds[2 * kMaxKBlocks];
+  __shared__ int tok_lds[BM];
+  __shared__ uint32_t red_lds[4][BM];
+  __shared__ float sh_lds[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mh = wave >> 2, wn = wave & 3;
+  const int col = lane & 15, grp = lane >> 4;
+  const int H = a.H, Ip = a.Ip, nH = H / kBlock, NB = Ip / kBlock;
+  const int n_items = a.n_tiles[0] * NB;
+  const rsrc_t xr = make_rsrc(a.xq, (uint32_t)a.xq_bytes);
+  const rsrc_t sr = make_rsrc(a.sx, (uint32_t)a.sx_bytes);
+  // B fragments of the wave: n-tiles g0, g1, u0, u1 of 32-column group wn
+  const int w_rd = wn * 8192 + lane * 16;
+  // A fragments: rows 128 mh + 16 m + lane % 16 (swz(row) = swz(lane))
+  const int afr = (mh * 128 + (lane & 15)) * 128;
+  const int afc0 = ((2 * grp) ^ swz(lane)) << 4, afc1 = ((2 * grp + 1) ^ swz(lane)) << 4;
+
+  for (int r = 0;; ++r) {
+    const int item = item_index(r);
+    if (item >= n_items) break;
+    const Item it = item_of(item, NB, a.tiles);
+    const int e = it.e, p0 = it.p0, rows = it.rows, nb = it.nb;
+    // 16-row subtiles of this wave's half that hold rows (wave-uniform)
+    const int rows_h = rows - mh * 128 < 0 ? 0 : (rows - mh * 128 > 128 ? 128 : rows - mh * 128);
+    const int mtw = (rows_h + 15) >> 4;
+
+    __syncthreads();  // LDS of the previous item is no longer read
+    if (tid < BM) tok_lds[tid] = a.perm[p0 + (tid < rows ? tid : 0)] / a.k;
+    {
+      const float* ws = a.s13 + (size_t)(e * NB + nb) * nH * 2;
+      for (int i = tid; i < 2 * nH; i += kWideThreads) ws_lds[i] = ws[i];
+    }
+    __syncthreads();
+
+    const rsrc_t wr = make_rsrc(a.w13 + (size_t)(e * NB + nb) * nH * kGateUpChunk, (uint32_t)(nH * kGateUpChunk));
+    // DMA instruction q of wave w moves LDS block b = 8q + w (1 KiB): rows
+    // 8b .. 8b + 7 of the activation tile (lane: row 8b + l/8, swizzled slot
+    // l % 8) and bytes 1024 b .. of the weight chunk; rows past the tile read
+    // out of range (zeros)
+    uint32_t avo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = (q * 8 + wave) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(row);
+      avo[q] = (uint32_t)(tok_lds[row] * H + c * 16) | (row < rows ? 0u : 0x80000000u);
+    }
+    // row scales: waves 0-3 load rows 64w + lane, waves 4-7 out of range
+    const int srow = (wave & 3) * 64 + lane;
+    const uint32_t svo = (uint32_t)(tok_lds[srow] * nH * 4) | (srow < rows && wave < 4 ? 0u : 0x80000000u);
+
+    // K block kb's loads in two-instruction parts 0-3 (weights, activations)
+    // and part 4 (row scales); past the last block every load
+    // reads out of range (zeros into the unused stage)
+    auto issue_part = [&](auto ST, auto PT, int kb) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value, p = decltype(PT)::value;
+      const bool in = kb < nH;
+      const uint32_t oob = in ? 0u : 0x80000000u;
+      if constexpr (p < 2) {
+        uint8_t* wl = st == 0 ? w_lds0 : w_lds1;
+        const uint32_t sw = in ? (uint32_t)(kb * kGateUpChunk) : 0u;
+#pragma unroll
+        for (int q = 2 * p; q < 2 * p + 2; ++q)
+          dma16<0>(wr, wl + (q * 8 + wave) * 1024, (uint32_t)((q * 8 + wave) * 1024 + lane * 16) | oob, sw);
+      } else if constexpr (p < 4) {
+        uint8_t* al = st == 0 ? a_lds0 : a_lds1;
+        const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
+#pragma unroll
+        for (int q = 2 * (p - 2); q < 2 * (p - 2) + 2; ++q) dma16<0>(xr, al + (q * 8 + wave) * 1024, avo[q] | oob, sa);
+      } else {
+        float* sl = st == 0 ? sx_lds0 : sx_lds1;
+        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * 4) : 0u);
+      }
+    };
+    auto issue = [&](auto ST, int kb) __attribute__((always_inline)) {
+      static_for<5>([&](auto PT) __attribute__((always_inline)) { issue_part(ST, PT, kb); });
+    };
+
+    // acc[m][t]: rows 128 mh + 16 m + 4 grp + i, n-tile t (gate 0-1, up 2-3)
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // one K block over MT subtiles: issue block kb + 1 into the other stage
+    // (read last step), multiply block kb out of stage s, wait for kb + 1
+    auto step = [&](auto S, auto MTC, int kb0) __attribute__((always_inline)) {
+      constexpr int s = decltype(S)::value, MT = decltype(MTC)::value;
+      const int kb = kb0 + s;
+      constexpr auto NEXT = std::integral_constant<int, 1 - s>{};
+      // without subtiles to interleave with, block kb + 1's loads go first
+      if constexpr (MT == 0) issue(NEXT, kb + 1);
+      if (MT > 0 && kb < nH) {
+        const float wsg = ws_lds[2 * kb], wsu = ws_lds[2 * kb + 1];
+        const uint8_t* wbuf = (s == 0 ? w_lds0 : w_lds1) + w_rd;
+        const uint8_t* abuf = (s == 0 ? a_lds0 : a_lds1) + afr;
+        const float* srow = (s == 0 ? sx_lds0 : sx_lds1) + mh * 128 + grp * 4;
+        i32x8 B[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) B[t] = cat(ld16(wbuf + t * 2048), ld16(wbuf + t * 2048 + 1024));
+        // Subtile m: its four MFMAs, the next subtile's fragment reads and a
+        // part of block kb + 1's loads under them, then the promotion of its
+        // own products (the other wave of the SIMD multiplies meanwhile).
+        i32x8 A2[2];
+        f32x4 R2[2], P[4];
+        A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
+        R2[0] = ld16f(srow);
+        static_for<MT>([&](auto M) __attribute__((always_inline)) {
+          constexpr int m = decltype(M)::value;
+          constexpr int per = MT >= 4 ? 1 : 4 / (MT > 0 ? MT : 1);  // load parts per subtile
+#pragma unroll
+          for (int t = 0; t < 4; ++t) P[t] = mfma_e4m3(A2[m & 1], B[t]);
+          if constexpr (m + 1 < MT) {
+            A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
+            R2[(m + 1) & 1] = ld16f(srow + (m + 1) * 16);
+          }
+          static_for<per>([&](auto J) __attribute__((always_inline)) {
+            constexpr int q = m * per + decltype(J)::value;
+            if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kb + 1);
+          });
+          if constexpr (m == 0) issue_part(NEXT, std::integral_constant<int, 4>{}, kb + 1);
+          float cg[4], cu[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            cg[i] = R2[m & 1][i] * wsg;
+            cu[i] = R2[m & 1][i] * wsu;
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][t][i] = __builtin_fmaf(P[t][i], t < 2 ? cg[i] : cu[i], acc[m][t][i]);
+          pin_in_place(acc[m]);
+          constexpr int nl = (m * per < 4 ? 2 * per : 0) + (m == 0 ? 1 : 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);  // VMEM reads
+          __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);  // VALU
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else if constexpr (MT > 0) {
+        issue(NEXT, kb + 1);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block kb + 1 has landed
+      ring_barrier();
+    };
+    auto kloop = [&](auto MTC) __attribute__((always_inline)) {
+      static_assert(NS == 2, "the K loop is unrolled by the stage count");
+      for (int kb0 = 0; kb0 < nH; kb0 += NS) {
+        step(std::integral_constant<int, 0>{}, MTC, kb0);
+        step(std::integral_constant<int, 1>{}, MTC, kb0);
+      }
+    };
+
+    issue(std::integral_constant<int, 0>{}, 0);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block 0 has landed
+    ring_barrier();
+    // every wave runs the same K loop and barriers; a half with few rows
+    // multiplies fewer subtiles
+    // every wave runs the same K loop and barriers; a half with few rows
+    // multiplies fewer subtiles
+    if (mtw > 4)
+      kloop(std::integral_constant<int, 8>{});
+    else if (mtw > 0)
+      kloop(std::integral_constant<int, 4>{});
+    else
+      kloop(std::integral_constant<int, 0>{});
+
+    // epilogue (activation stage 0 is free now: it becomes the h staging tile)
+    uint8_t* h_lds = a_lds0;
+    if constexpr (kDbg) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = mh * 128 + m * 16 + grp * 4 + i;
+          if (m < mtw && row < rows) {
+            float* g = a.gu_dbg + (size_t)(p0 + row) * 2 * Ip + nb * kBlock + wn * 32 + col;
+            g[0] = acc[m][0][i];
+            g[16] = acc[m][1][i];
+            g[Ip] = acc[m][2][i];
+            g[Ip + 16] = acc[m][3][i];
+          }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (m < mtw) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[m][0][i] = silu_mul_act(acc[m][0][i], acc[m][2][i], a.act_limit);
+          acc[m][1][i] = silu_mul_act(acc[m][1][i], acc[m][3][i], a.act_limit);
+          const uint32_t mb = max16(umax(abs_bits(acc[m][0][i]), abs_bits(acc[m][1][i])));
+          if (col == 0) red_lds[wn][mh * 128 + m * 16 + grp * 4 + i] = mb;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (m < mtw) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = mh * 128 + m * 16 + grp * 4 + i;
+          uint32_t mb = 0;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) mb = umax(mb, red_lds[w][row]);
+          const float amax = __uint_as_float(mb);
+          const float sc = __fdiv_rn(amax, 448.0f);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const uint32_t c = amax != 0.0f ? to_e4m3(__fdiv_rn(acc[m][t][i], sc)) : 0u;
+            h_lds[h_off(row, wn * 2 + t) + col] = (uint8_t)c;
+          }
+          if (wn == 0 && col == 0) sh_lds[row] = sc;
+        }
+      }
+    }
+    __syncthreads();
+    for (int row = tid >> 3; row < rows; row += kWideThreads / 8)
+      st16(a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + (tid & 7) * 16, ld16(&h_lds[h_off(row, tid & 7)]));
+    if (tid < rows) a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
+  }
+}
+
+hipError_t launch_gate_up(const GateUpArgs& a, int kind, int grid, hipStream_t s) {
+  if (kind == kGemmWide && a.gu_dbg)
+    hipLaunchKernelGGL(gate_up_wide_kernel<true>, dim3(grid), dim3(kWideThreads), 0, s, a);
+  else if (kind == kGemmWide)
+    hipLaunchKernelGGL(gate_up_wide_kernel<false>, dim3(grid), dim3(kWideThreads), 0, s, a);
+  else if (kind == kGemmTile)
     hipLaunchKernelGGL(gate_up_tile_kernel, dim3(grid), dim3(kTileThreads), 0, s, a);
   else
     hipLaunchKernelGGL(gate_up_stream_kernel<kStreamDepth>, dim3(grid), dim3(kThreads), 0, s, a);
@@ -905,7 +1199,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void down_tile_kernel(DownArgs a) 
   // n-tiles 0-3 of the wave are 32-column groups 2(w%2), 2(w%2)+1 of its block
   const uint32_t b_off = (uint32_t)((wave & 1) * 4 * 2 * 1024 + lane * 16);
   const int afr = (lane & 15) * 128;
-  const int afc0 = ((2 * grp) ^ (lane & 7)) << 4, afc1 = ((2 * grp + 1) ^ (lane & 7)) << 4;
+  const int afc0 = ((2 * grp) ^ swz(lane)) << 4, afc1 = ((2 * grp + 1) ^ swz(lane)) << 4;
 
   for (int r = 0;; ++r) {
     const int item = item_index(r);
@@ -935,7 +1229,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void down_tile_kernel(DownArgs a) 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = (q * 4 + wave) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ (row & 7);
+      const int c = (lane & 7) ^ swz(row);
       avo[q] = (uint32_t)((p0 + (row < rows ? row : 0)) * Ip + c * 16) +
                ((q * 4 + wave) * 8 < mt_all * 16 ? 0u : 0x80000000u);
     }
@@ -1136,8 +1430,196 @@ __global__ __launch_bounds__(kThreads, 4) void down_stream_kernel(DownArgs a) {
   }
 }
 
-hipError_t launch_down(const DownArgs& a, bool big, int grid, hipStream_t s) {
-  if (big)
+// Wide down for experts with more than kBigRows rows: a 512-thread workgroup
+// computes up to 256 rows x 256 hidden columns (weight blocks nb2, nb2 + 1),
+// both operands double-buffered in LDS by buffer-load-to-LDS as in
+// gate_up_wide_kernel.  Wave w = 4 mh + wn owns rows 128 mh .. +127 and 64
+// columns: block nb2 + wn / 2, 32-column groups 2 (wn % 2) and 2 (wn % 2) + 1.
+__global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) {
+  constexpr int BM = kWideRows;
+  constexpr int NS = 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t w_lds0[2 * kDownChunk];
+  __shared__ __attribute__((aligned(1024))) uint8_t w_lds1[2 * kDownChunk];
+  __shared__ __attribute__((aligned(256))) float s_lds0[2 * BM];
+  __shared__ __attribute__((aligned(256))) float s_lds1[2 * BM];
+  __shared__ float ws_lds[2][kMaxKBlocks];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mh = wave >> 2, wn = wave & 3, half = wn >> 1;
+  const int col = lane & 15, grp = lane >> 4;
+  const int H = a.H, Ip = a.Ip, nI = Ip / kBlock, NB = H / kBlock;
+  const int NB2 = (NB + 1) >> 1;
+  const int n_items = a.n_tiles[0] * NB2;
+  const rsrc_t hr = make_rsrc(a.hq, (uint32_t)a.hq_bytes);
+  const rsrc_t sr = make_rsrc(a.sh, (uint32_t)a.sh_bytes);
+  // the wave's 8 KiB of the stage: block wn / 2, groups 2 (wn % 2), +1
+  const int w_rd = wn * 8192 + lane * 16;
+  const int afr = (mh * 128 + (lane & 15)) * 128;
+  const int afc0 = ((2 * grp) ^ swz(lane)) << 4, afc1 = ((2 * grp + 1) ^ swz(lane)) << 4;
+
+  for (int r = 0;; ++r) {
+    const int item = item_index(r);
+    if (item >= n_items) break;
+    const Item it = item_of(item, NB2, a.tiles);
+    const int nb2 = it.nb * 2;
+    const bool two = nb2 + 1 < NB;  // second weight block present
+    const int e = it.e, p0 = it.p0, rows = it.rows;
+    const int rows_h = rows - mh * 128 < 0 ? 0 : (rows - mh * 128 > 128 ? 128 : rows - mh * 128);
+    const int mtw = (half == 1 && !two) ? 0 : (rows_h + 15) >> 4;
+
+    __syncthreads();  // LDS of the previous item is no longer read
+    {
+      const float* ws = a.s2 + (size_t)(e * NB + nb2) * nI;
+      for (int i = tid; i < nI; i += kWideThreads) {
+        ws_lds[0][i] = ws[i];
+        ws_lds[1][i] = two ? ws[nI + i] : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // blocks nb2 and nb2 + 1 are nI * kDownChunk bytes apart; a missing
+    // second block reads out of range
+    const int wblk = __builtin_amdgcn_readfirstlane(e * NB + nb2);
+    const int wbytes = __builtin_amdgcn_readfirstlane((two ? 2 : 1) * nI * kDownChunk);
+    const rsrc_t wr = make_rsrc(a.w2 + (size_t)wblk * nI * kDownChunk, (uint32_t)wbytes);
+    uint32_t wvo[4], avo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = q * 8 + wave;  // LDS block of instruction q (1 KiB)
+      wvo[q] = (uint32_t)((b >> 4) * nI * kDownChunk + (b & 15) * 1024 + lane * 16);
+      const int row = b * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(row);
+      avo[q] = (uint32_t)((p0 + (row < rows ? row : 0)) * Ip + c * 16) | (row < rows ? 0u : 0x80000000u);
+    }
+    const int srow = (wave & 3) * 64 + lane;
+    const uint32_t svo =
+        (uint32_t)((p0 + (srow < rows ? srow : 0)) * nI * 4) | (srow < rows && wave < 4 ? 0u : 0x80000000u);
+
+    // loads of K block kb in parts, as in gate_up_wide_kernel
+    auto issue_part = [&](auto ST, auto PT, int kb) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value, p = decltype(PT)::value;
+      const bool in = kb < nI;
+      const uint32_t oob = in ? 0u : 0x80000000u;
+      if constexpr (p < 2) {
+        uint8_t* wl = st == 0 ? w_lds0 : w_lds1;
+        const uint32_t sw = in ? (uint32_t)(kb * kDownChunk) : 0u;
+#pragma unroll
+        for (int q = 2 * p; q < 2 * p + 2; ++q) dma16<0>(wr, wl + (q * 8 + wave) * 1024, wvo[q] | oob, sw);
+      } else if constexpr (p < 4) {
+        uint8_t* al = st == 0 ? a_lds0 : a_lds1;
+        const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
+#pragma unroll
+        for (int q = 2 * (p - 2); q < 2 * (p - 2) + 2; ++q) dma16<0>(hr, al + (q * 8 + wave) * 1024, avo[q] | oob, sa);
+      } else {
+        float* sl = st == 0 ? s_lds0 : s_lds1;
+        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * 4) : 0u);
+      }
+    };
+    auto issue = [&](auto ST, int kb) __attribute__((always_inline)) {
+      static_for<5>([&](auto PT) __attribute__((always_inline)) { issue_part(ST, PT, kb); });
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto step = [&](auto S, auto MTC, int kb0) __attribute__((always_inline)) {
+      constexpr int s = decltype(S)::value, MT = decltype(MTC)::value;
+      const int kb = kb0 + s;
+      constexpr auto NEXT = std::integral_constant<int, 1 - s>{};
+      if constexpr (MT == 0) issue(NEXT, kb + 1);
+      if (MT > 0 && kb < nI) {
+        const float wsc = ws_lds[half][kb];
+        const uint8_t* wbuf = (s == 0 ? w_lds0 : w_lds1) + w_rd;
+        const uint8_t* abuf = (s == 0 ? a_lds0 : a_lds1) + afr;
+        const float* srw = (s == 0 ? s_lds0 : s_lds1) + mh * 128 + grp * 4;
+        i32x8 B[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) B[t] = cat(ld16(wbuf + t * 2048), ld16(wbuf + t * 2048 + 1024));
+        // subtile by subtile as in gate_up_wide_kernel
+        i32x8 A2[2];
+        f32x4 R2[2], Q[4];
+        A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
+        R2[0] = ld16f(srw);
+        static_for<MT>([&](auto M) __attribute__((always_inline)) {
+          constexpr int m = decltype(M)::value;
+          constexpr int per = MT >= 4 ? 1 : 4 / (MT > 0 ? MT : 1);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) Q[t] = mfma_e4m3(A2[m & 1], B[t]);
+          if constexpr (m + 1 < MT) {
+            A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
+            R2[(m + 1) & 1] = ld16f(srw + (m + 1) * 16);
+          }
+          static_for<per>([&](auto J) __attribute__((always_inline)) {
+            constexpr int q = m * per + decltype(J)::value;
+            if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kb + 1);
+          });
+          if constexpr (m == 0) issue_part(NEXT, std::integral_constant<int, 4>{}, kb + 1);
+          float sc[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[i] = R2[m & 1][i] * wsc;
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][t][i] = __builtin_fmaf(Q[t][i], sc[i], acc[m][t][i]);
+          pin_in_place(acc[m]);
+          constexpr int nl = (m * per < 4 ? 2 * per : 0) + (m == 0 ? 1 : 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);  // VMEM reads
+          __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);  // VALU
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else if constexpr (MT > 0) {
+        issue(NEXT, kb + 1);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block kb + 1 has landed
+      ring_barrier();
+    };
+    auto kloop = [&](auto MTC) __attribute__((always_inline)) {
+      static_assert(NS == 2, "the K loop is unrolled by the stage count");
+      for (int kb0 = 0; kb0 < nI; kb0 += NS) {
+        step(std::integral_constant<int, 0>{}, MTC, kb0);
+        step(std::integral_constant<int, 1>{}, MTC, kb0);
+      }
+    };
+
+    issue(std::integral_constant<int, 0>{}, 0);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block 0 has landed
+    ring_barrier();
+    if (mtw > 4)
+      kloop(std::integral_constant<int, 8>{});
+    else if (mtw > 0)
+      kloop(std::integral_constant<int, 4>{});
+    else
+      kloop(std::integral_constant<int, 0>{});
+
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (m < mtw) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = mh * 128 + m * 16 + grp * 4 + i;
+          if (row < rows) {
+            float* dst = a.y + (size_t)(p0 + row) * H + (nb2 + half) * kBlock + (wn & 1) * 64 + col;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dst[t * 16] = acc[m][t][i];
+          }
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_down(const DownArgs& a, int kind, int grid, hipStream_t s) {
+  if (kind == kGemmWide)
+    hipLaunchKernelGGL(down_wide_kernel, dim3(grid), dim3(kWideThreads), 0, s, a);
+  else if (kind == kGemmTile)
     hipLaunchKernelGGL(down_tile_kernel, dim3(grid), dim3(kTileThreads), 0, s, a);
   else
     hipLaunchKernelGGL(down_stream_kernel<kStreamDepthDown>, dim3(grid), dim3(kThreads), 0, s, a);

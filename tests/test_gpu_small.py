@@ -17,14 +17,18 @@ from gpu_util import TOL, assert_rows_close, compare_with_oracle, dev, dev_bf16,
 pytestmark = pytest.mark.gpu
 
 # (E, k, H, I, T, route, rho, outlier_frac): small enough for the oracle in
-# seconds; experts get from 0 to a few hundred rows (both GEMM variants, ragged
-# last tiles); I=192 exercises the zero padding to 256.
+# seconds; experts get from 0 to a few hundred rows (every GEMM variant: 16-row
+# streaming, 128-row and 256-row tiles, ragged last tiles); I=192 exercises the
+# zero padding to 256.
 CASES = [
     ("tiny", (8, 2, 256, 128, 64, gen.ROUTE_SOFTMAX, 1.0, 0.0)),
     ("pad192", (6, 3, 512, 192, 50, gen.ROUTE_SIGMOID_NORMAL, 2.5, 0.05)),
     ("i64", (5, 2, 384, 64, 37, gen.ROUTE_SIGMOID_NORMAL, 1.0, 0.0)),
     ("many_rows", (4, 2, 256, 256, 600, gen.ROUTE_SIGMOID_UNIFORM, 2.5, 0.01)),
     ("slice_t64", (160, 8, 5120, 192, 64, gen.ROUTE_SIGMOID_NORMAL, 1.0, 0.01)),
+    # ~470 rows per expert: 256-row tiles with both halves full; odd K-block
+    # counts (H/128 = 3, Ip/128 = 3) and an odd count of down column blocks
+    ("wide_odd", (3, 2, 384, 320, 700, gen.ROUTE_SIGMOID_UNIFORM, 2.5, 0.01)),
 ]
 
 
