@@ -73,10 +73,11 @@ int64_t align256(int64_t n) { return (n + 255) & ~int64_t(255); }
 
 // Workspace pieces, in allocation order.
 struct WsSizes {
-  int64_t xq, sx, hq, sh, y, counts, offsets, perm, inv, small_tiles, big_tiles, wide_tiles, n_tiles,
+  int64_t xq, sx, sxT, hq, sh, shT, y, counts, offsets, perm, inv, small_tiles, big_tiles, wide_tiles, n_tiles,
       err, rids, rw;
   int64_t total() const {
-    return align256(xq) + align256(sx) + align256(hq) + align256(sh) + align256(y) +
+    return align256(xq) + align256(sx) + align256(sxT) + align256(hq) + align256(sh) + align256(shT) +
+           align256(y) +
            align256(counts) + align256(offsets) + align256(perm) + align256(inv) +
            align256(small_tiles) + align256(big_tiles) + align256(wide_tiles) + align256(n_tiles) +
            align256(err) +
@@ -88,8 +89,10 @@ WsSizes ws_sizes(const Dims& m) {
   WsSizes w;
   w.xq = m.max_rows * m.H;
   w.sx = m.max_rows * m.nH * 4;
+  w.sxT = w.sx;
   w.hq = m.P * m.Ip;
   w.sh = m.P * m.nI * 4;
+  w.shT = w.sh;
   w.y = m.P * m.H * 4;
   w.counts = m.E * 4;
   w.offsets = (m.E + 1) * 4;
@@ -130,8 +133,10 @@ struct moe_fp8_prefill {
   // workspace
   uint8_t* xq = nullptr;
   float* sx = nullptr;
+  float* sxT = nullptr;
   uint8_t* hq = nullptr;
   float* sh = nullptr;
+  float* shT = nullptr;
   float* y = nullptr;
   int32_t* counts = nullptr;
   int32_t* offsets = nullptr;
@@ -349,7 +354,8 @@ hipError_t launch_gate_up_all(moe_fp8_prefill* h, int64_t t, int64_t P, float* g
   const int64_t nb = m.Ip / kBlock;
   GateUpArgs ga{h->xq, h->sx, t * m.H, t * m.nH * 4, h->perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip,
                 h->w13, h->s13, h->small_tiles, h->n_tiles, h->hq, h->sh, gu_dbg,
-                h->desc.activation == MOE_ACT_SILU_CLAMPED ? h->desc.activation_limit : 0.0f};
+                h->desc.activation == MOE_ACT_SILU_CLAMPED ? h->desc.activation_limit : 0.0f,
+                h->sxT, t * m.nH * 4, (int32_t)t, (int32_t)P, h->shT};
   Tile* lists[3] = {h->small_tiles, h->big_tiles, h->wide_tiles};
   for (int kind = kGemmStream; kind <= kGemmWide; ++kind) {
     const int64_t items = max_tiles(m, P, kind) * nb;
@@ -371,7 +377,7 @@ hipError_t launch_down_all(moe_fp8_prefill* h, int64_t P, hipStream_t s, hipEven
   const Dims& m = h->m;
   const int64_t nb = m.H / kBlock, nb2 = (nb + 1) / 2;
   DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2,
-              h->small_tiles, h->n_tiles, h->y};
+              h->small_tiles, h->n_tiles, h->y, h->shT, P * m.nI * 4, (int32_t)P};
   Tile* lists[3] = {h->small_tiles, h->big_tiles, h->wide_tiles};
   for (int kind = kGemmStream; kind <= kGemmWide; ++kind) {
     const int64_t items = max_tiles(m, P, kind) * (kind == kGemmStream ? nb : nb2);
@@ -458,7 +464,7 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
     if (launch_plan(pa, s) != hipSuccess) return fail(h);
     if (h->timing && hipEventRecord(ev.ev[1], s) != hipSuccess) return fail(h);
 
-    QuantArgs qa{(const uint16_t*)x + r0 * m.H, (int32_t)t, (int32_t)m.H, h->xq, h->sx};
+    QuantArgs qa{(const uint16_t*)x + r0 * m.H, (int32_t)t, (int32_t)m.H, h->xq, h->sx, h->sxT};
     if (launch_quant(qa, s) != hipSuccess) return fail(h);
     if (h->timing && hipEventRecord(ev.ev[2], s) != hipSuccess) return fail(h);
 
@@ -593,8 +599,10 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   h->s2 = (float*)get(m.E * m.nH * m.nI * 4);
   h->xq = (uint8_t*)get(w.xq);
   h->sx = (float*)get(w.sx);
+  h->sxT = (float*)get(w.sxT);
   h->hq = (uint8_t*)get(w.hq);
   h->sh = (float*)get(w.sh);
+  h->shT = (float*)get(w.shT);
   h->y = (float*)get(w.y);
   h->counts = (int32_t*)get(w.counts);
   h->offsets = (int32_t*)get(w.offsets);
@@ -916,8 +924,10 @@ int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slo
   }
   h->xq = (uint8_t*)get(w.xq);
   h->sx = (float*)get(w.sx);
+  h->sxT = (float*)get(w.sxT);
   h->hq = (uint8_t*)get(w.hq);
   h->sh = (float*)get(w.sh);
+  h->shT = (float*)get(w.shT);
   h->y = (float*)get(w.y);
   h->counts = (int32_t*)get(w.counts);
   h->offsets = (int32_t*)get(w.offsets);

@@ -75,6 +75,7 @@ struct QuantArgs {
   int32_t T, H;
   uint8_t* xq;         // [T][H]
   float* sx;           // [T][H/128]
+  float* sxT;          // [H/128][T]: the same scales, K-block major
 };
 
 struct GateUpArgs {
@@ -91,6 +92,12 @@ struct GateUpArgs {
   float* sh;           // [P][Ip/128]
   float* gu_dbg;       // optional [P][2*Ip] FP32 gate|up before the epilogue
   float act_limit;     // > 0: clamped SiLU (gate <= L, |up| <= L); 0: unclamped
+  // K-block-major copies of the row scales: a tile's rows for one K block are
+  // then adjacent words rather than one cache line per row
+  const float* sxT;    // [H/128][T]
+  int64_t sxT_bytes;
+  int32_t T, P;        // rows and slots of the pass (pitches of sxT and shT)
+  float* shT;          // [Ip/128][P]
 };
 
 struct DownArgs {
@@ -103,6 +110,9 @@ struct DownArgs {
   const Tile* tiles;
   const int32_t* n_tiles;
   float* y;            // [P][H]
+  const float* shT;    // [Ip/128][P], K-block major
+  int64_t shT_bytes;
+  int32_t P;
 };
 
 struct CombineArgs {

@@ -359,7 +359,10 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
   uint32_t* dst = reinterpret_cast<uint32_t*>(a.xq + t * a.H + kg * kBlock + sub * 8);
   dst[0] = lo;
   dst[1] = hi;
-  if (sub == 0) a.sx[g] = s;
+  if (sub == 0) {
+    a.sx[g] = s;
+    a.sxT[(int64_t)kg * a.T + t] = s;
+  }
 }
 
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s) {
@@ -499,6 +502,11 @@ __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "m
 // Item i: the tile at position i / NB in tile-major order has the same
 // expert, whose items start at first * NB.
 constexpr int kItemTiles = 4, kItemBlocks = 8, kXcds = 8;
+#ifndef MOE_WIDE_ITEM_TILES
+#define MOE_WIDE_ITEM_TILES 4
+#endif
+// 256-row tiles: row tiles x weight blocks per 32-item run
+constexpr int kWideItemTiles = MOE_WIDE_ITEM_TILES, kWideItemBlocks = 32 / kWideItemTiles;
 
 struct Item {
   int e, p0, rows, nb;
@@ -506,31 +514,32 @@ struct Item {
 
 // All fields are workgroup-uniform; readfirstlane keeps them in SGPRs so the
 // buffer descriptors built from them stay scalar.
+template <int IT = kItemTiles, int IB = kItemBlocks>
 __device__ __forceinline__ Item item_of(int i, int NB, const Tile* tiles) {
   const int tg = i / NB;
   const int first = __builtin_amdgcn_readfirstlane(tiles[tg].first);
   const int me = __builtin_amdgcn_readfirstlane(tiles[tg].count);
   const int li = i - first * NB;
-  const int full = NB / kItemBlocks;
-  int nbb = li / (me * kItemBlocks), rem, nbs;
+  const int full = NB / IB;
+  int nbb = li / (me * IB), rem, nbs;
   if (nbb < full) {
-    rem = li - nbb * me * kItemBlocks;
-    nbs = kItemBlocks;
+    rem = li - nbb * me * IB;
+    nbs = IB;
   } else {
     nbb = full;
-    rem = li - full * me * kItemBlocks;
-    nbs = NB - full * kItemBlocks;
+    rem = li - full * me * IB;
+    nbs = NB - full * IB;
   }
-  const int per_mb = kItemTiles * nbs;
+  const int per_mb = IT * nbs;
   const int mb = rem / per_mb;
   const int r2 = rem - mb * per_mb;
   const int m_in = r2 / nbs;
-  const Tile* t = tiles + first + mb * kItemTiles + m_in;
+  const Tile* t = tiles + first + mb * IT + m_in;
   Item it;
   it.e = __builtin_amdgcn_readfirstlane(t->e);
   it.p0 = __builtin_amdgcn_readfirstlane(t->p0);
   it.rows = __builtin_amdgcn_readfirstlane(t->rows);
-  it.nb = __builtin_amdgcn_readfirstlane(nbb * kItemBlocks + (r2 - m_in * nbs));
+  it.nb = __builtin_amdgcn_readfirstlane(nbb * IB + (r2 - m_in * nbs));
   return it;
 }
 
@@ -567,7 +576,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
   const int H = a.H, Ip = a.Ip, nH = H / kBlock, NB = Ip / kBlock;
   const int n_items = a.n_tiles[0] * NB;
   const rsrc_t xr = make_rsrc(a.xq, (uint32_t)a.xq_bytes);
-  const rsrc_t sr = make_rsrc(a.sx, (uint32_t)a.sx_bytes);
+  const rsrc_t sr = make_rsrc(a.sxT, (uint32_t)a.sxT_bytes);
   // wave w reads n-tiles g0, g1, u0, u1 of 32-column group w of the chunk
   const uint32_t b_off = (uint32_t)(wave * 4 * 2 * 1024 + lane * 16);
   const int afr = (lane & 15) * 128;
@@ -598,7 +607,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
       const int c = (lane & 7) ^ swz(row);
       avo[q] = (uint32_t)(tok_lds[row] * H + c * 16) + ((q * 4 + wave) * 8 < mt * 16 ? 0u : 0x80000000u);
     }
-    const uint32_t svo = wave < 2 ? (uint32_t)(tok_lds[wave * 64 + lane] * nH * 4) : 0x80000000u;
+    const uint32_t svo = wave < 2 ? (uint32_t)(tok_lds[wave * 64 + lane] * 4) : 0x80000000u;
 
     // K block kb goes to stage kb % NS.  Its 13 loads come in 7 parts: the
     // weight n-tiles (parts 0-3, two loads each), the activation DMAs (parts
@@ -622,7 +631,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
           dma16<0>(xr, al + (q * 4 + wave) * 1024, avo[q] | oob, sa);
       } else {
         float* sl = st == 0 ? sx_lds0 : sx_lds1;
-        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * 4) : 0u);
+        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * a.T * 4) : 0u);
       }
     };
     auto issue = [&](auto ST, int kb, i32x8(&b)[4]) __attribute__((always_inline)) {
@@ -762,7 +771,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
     __syncthreads();
     for (int row = tid >> 3; row < rows; row += kTileThreads / 8)
       st16(a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + (tid & 7) * 16, ld16(&h_lds[h_off(row, tid & 7)]));
-    if (tid < rows) a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
+    if (tid < rows) {
+      a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
+      a.shT[(size_t)nb * a.P + p0 + tid] = sh_lds[tid];
+    }
   }
 }
 
@@ -894,7 +906,10 @@ __global__ __launch_bounds__(kThreads, D <= 2 ? 4 : 3) void gate_up_stream_kerne
     if ((tid >> 3) < rows)
       st16(a.hq + (size_t)(p0 + (tid >> 3)) * Ip + nb * kBlock + (tid & 7) * 16,
            ld16(&h_lds[(tid >> 3) * 128 + (tid & 7) * 16]));
-    if (tid < rows) a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
+    if (tid < rows) {
+      a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
+      a.shT[(size_t)nb * a.P + p0 + tid] = sh_lds[tid];
+    }
   }
 }
 
@@ -942,7 +957,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
   const int H = a.H, Ip = a.Ip, nH = H / kBlock, NB = Ip / kBlock;
   const int n_items = a.n_tiles[0] * NB;
   const rsrc_t xr = make_rsrc(a.xq, (uint32_t)a.xq_bytes);
-  const rsrc_t sr = make_rsrc(a.sx, (uint32_t)a.sx_bytes);
+  const rsrc_t sr = make_rsrc(a.sxT, (uint32_t)a.sxT_bytes);
   // B fragments of the wave: n-tiles g0, g1, u0, u1 of 32-column group wn
   const int w_rd = wn * 8192 + lane * 16;
   // A fragments: rows 128 mh + 16 m + lane % 16 (swz(row) = swz(lane))
@@ -952,7 +967,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
   for (int r = 0;; ++r) {
     const int item = item_index(r);
     if (item >= n_items) break;
-    const Item it = item_of(item, NB, a.tiles);
+    const Item it = item_of<kWideItemTiles, kWideItemBlocks>(item, NB, a.tiles);
     const int e = it.e, p0 = it.p0, rows = it.rows, nb = it.nb;
     // 16-row subtiles of this wave's half that hold rows (wave-uniform)
     const int rows_h = rows - mh * 128 < 0 ? 0 : (rows - mh * 128 > 128 ? 128 : rows - mh * 128);
@@ -980,7 +995,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
     }
     // row scales: waves 0-3 load rows 64w + lane, waves 4-7 out of range
     const int srow = (wave & 3) * 64 + lane;
-    const uint32_t svo = (uint32_t)(tok_lds[srow] * nH * 4) | (srow < rows && wave < 4 ? 0u : 0x80000000u);
+    const uint32_t svo = (uint32_t)(tok_lds[srow] * 4) | (srow < rows && wave < 4 ? 0u : 0x80000000u);
 
     // K block kb's loads in two-instruction parts 0-3 (weights, activations)
     // and part 4 (row scales); past the last block every load
@@ -1002,7 +1017,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
         for (int q = 2 * (p - 2); q < 2 * (p - 2) + 2; ++q) dma16<0>(xr, al + (q * 8 + wave) * 1024, avo[q] | oob, sa);
       } else {
         float* sl = st == 0 ? sx_lds0 : sx_lds1;
-        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * 4) : 0u);
+        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * a.T * 4) : 0u);
       }
     };
     auto issue = [&](auto ST, int kb) __attribute__((always_inline)) {
@@ -1032,9 +1047,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
         i32x8 B[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) B[t] = cat(ld16(wbuf + t * 2048), ld16(wbuf + t * 2048 + 1024));
-        // Subtile m: its four MFMAs, the next subtile's fragment reads and a
-        // part of block kb + 1's loads under them, then the promotion of its
-        // own products (the other wave of the SIMD multiplies meanwhile).
+        // Subtile m: the next subtile's fragment reads, its four MFMAs, a part
+        // of block kb + 1's loads under them, then the promotion of its own
+        // products (the other wave of the SIMD multiplies meanwhile).
         i32x8 A2[2];
         f32x4 R2[2], P[4];
         A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
@@ -1042,12 +1057,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
         static_for<MT>([&](auto M) __attribute__((always_inline)) {
           constexpr int m = decltype(M)::value;
           constexpr int per = MT >= 4 ? 1 : 4 / (MT > 0 ? MT : 1);  // load parts per subtile
-#pragma unroll
-          for (int t = 0; t < 4; ++t) P[t] = mfma_e4m3(A2[m & 1], B[t]);
           if constexpr (m + 1 < MT) {
             A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
             R2[(m + 1) & 1] = ld16f(srow + (m + 1) * 16);
           }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) P[t] = mfma_e4m3(A2[m & 1], B[t]);
           static_for<per>([&](auto J) __attribute__((always_inline)) {
             constexpr int q = m * per + decltype(J)::value;
             if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kb + 1);
@@ -1065,8 +1080,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
             for (int i = 0; i < 4; ++i) acc[m][t][i] = __builtin_fmaf(P[t][i], t < 2 ? cg[i] : cu[i], acc[m][t][i]);
           pin_in_place(acc[m]);
           constexpr int nl = (m * per < 4 ? 2 * per : 0) + (m == 0 ? 1 : 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS reads (next subtile)
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS reads
           __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);  // VMEM reads
           __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);  // VALU
           __builtin_amdgcn_sched_barrier(0);
@@ -1152,7 +1167,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
     __syncthreads();
     for (int row = tid >> 3; row < rows; row += kWideThreads / 8)
       st16(a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + (tid & 7) * 16, ld16(&h_lds[h_off(row, tid & 7)]));
-    if (tid < rows) a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
+    if (tid < rows) {
+      a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
+      a.shT[(size_t)nb * a.P + p0 + tid] = sh_lds[tid];
+    }
   }
 }
 
@@ -1194,7 +1212,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void down_tile_kernel(DownArgs a) 
   const int NB2 = (NB + 1) >> 1;
   const int n_items = a.n_tiles[0] * NB2;
   const rsrc_t hr = make_rsrc(a.hq, (uint32_t)a.hq_bytes);
-  const rsrc_t sr = make_rsrc(a.sh, (uint32_t)a.sh_bytes);
+  const rsrc_t sr = make_rsrc(a.shT, (uint32_t)a.shT_bytes);
   const int half = wave >> 1;  // which of the two weight blocks
   // n-tiles 0-3 of the wave are 32-column groups 2(w%2), 2(w%2)+1 of its block
   const uint32_t b_off = (uint32_t)((wave & 1) * 4 * 2 * 1024 + lane * 16);
@@ -1236,7 +1254,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void down_tile_kernel(DownArgs a) 
     // row scales: waves 0-1 load rows 64w + lane, waves 2-3 load out of
     // range into the unused half of the stage
     const int srow = wave * 64 + lane;
-    const uint32_t svo = wave < 2 ? (uint32_t)((p0 + (srow < rows ? srow : 0)) * nI * 4) : 0x80000000u;
+    const uint32_t svo = wave < 2 ? (uint32_t)((p0 + (srow < rows ? srow : 0)) * 4) : 0x80000000u;
 
     // block kb's 13 loads in 7 parts, as in gate_up_tile_kernel
     auto issue_part = [&](auto ST, auto PT, int kb, i32x8(&b)[4]) __attribute__((always_inline)) {
@@ -1255,7 +1273,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void down_tile_kernel(DownArgs a) 
           dma16<0>(hr, al + (q * 4 + wave) * 1024, avo[q] | oob, sa);
       } else {
         float* sl = st == 0 ? s_lds0 : s_lds1;
-        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * 4) : 0u);
+        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * a.P * 4) : 0u);
       }
     };
     auto issue = [&](auto ST, int kb, i32x8(&b)[4]) __attribute__((always_inline)) {
@@ -1454,7 +1472,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
   const int NB2 = (NB + 1) >> 1;
   const int n_items = a.n_tiles[0] * NB2;
   const rsrc_t hr = make_rsrc(a.hq, (uint32_t)a.hq_bytes);
-  const rsrc_t sr = make_rsrc(a.sh, (uint32_t)a.sh_bytes);
+  const rsrc_t sr = make_rsrc(a.shT, (uint32_t)a.shT_bytes);
   // the wave's 8 KiB of the stage: block wn / 2, groups 2 (wn % 2), +1
   const int w_rd = wn * 8192 + lane * 16;
   const int afr = (mh * 128 + (lane & 15)) * 128;
@@ -1463,7 +1481,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
   for (int r = 0;; ++r) {
     const int item = item_index(r);
     if (item >= n_items) break;
-    const Item it = item_of(item, NB2, a.tiles);
+    const Item it = item_of<kWideItemTiles, kWideItemBlocks>(item, NB2, a.tiles);
     const int nb2 = it.nb * 2;
     const bool two = nb2 + 1 < NB;  // second weight block present
     const int e = it.e, p0 = it.p0, rows = it.rows;
@@ -1496,7 +1514,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
     }
     const int srow = (wave & 3) * 64 + lane;
     const uint32_t svo =
-        (uint32_t)((p0 + (srow < rows ? srow : 0)) * nI * 4) | (srow < rows && wave < 4 ? 0u : 0x80000000u);
+        (uint32_t)((p0 + (srow < rows ? srow : 0)) * 4) | (srow < rows && wave < 4 ? 0u : 0x80000000u);
 
     // loads of K block kb in parts, as in gate_up_wide_kernel
     auto issue_part = [&](auto ST, auto PT, int kb) __attribute__((always_inline)) {
@@ -1515,7 +1533,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
         for (int q = 2 * (p - 2); q < 2 * (p - 2) + 2; ++q) dma16<0>(hr, al + (q * 8 + wave) * 1024, avo[q] | oob, sa);
       } else {
         float* sl = st == 0 ? s_lds0 : s_lds1;
-        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * 4) : 0u);
+        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * a.P * 4) : 0u);
       }
     };
     auto issue = [&](auto ST, int kb) __attribute__((always_inline)) {
@@ -1549,12 +1567,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
         static_for<MT>([&](auto M) __attribute__((always_inline)) {
           constexpr int m = decltype(M)::value;
           constexpr int per = MT >= 4 ? 1 : 4 / (MT > 0 ? MT : 1);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) Q[t] = mfma_e4m3(A2[m & 1], B[t]);
           if constexpr (m + 1 < MT) {
             A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
             R2[(m + 1) & 1] = ld16f(srw + (m + 1) * 16);
           }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) Q[t] = mfma_e4m3(A2[m & 1], B[t]);
           static_for<per>([&](auto J) __attribute__((always_inline)) {
             constexpr int q = m * per + decltype(J)::value;
             if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kb + 1);
@@ -1569,8 +1587,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
             for (int i = 0; i < 4; ++i) acc[m][t][i] = __builtin_fmaf(Q[t][i], sc[i], acc[m][t][i]);
           pin_in_place(acc[m]);
           constexpr int nl = (m * per < 4 ? 2 * per : 0) + (m == 0 ? 1 : 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS reads (next subtile)
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS reads
           __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);  // VMEM reads
           __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);  // VALU
           __builtin_amdgcn_sched_barrier(0);
