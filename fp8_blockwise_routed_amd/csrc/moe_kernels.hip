@@ -81,6 +81,14 @@ __device__ __forceinline__ uint32_t to_e4m3(float v) {
   return sign | ((r >> 20) - (120u << 3));
 }
 
+// E4M3 codes of v0 and v1 in bytes 0 and 1 by the packed hardware
+// conversion, which rounds exactly as to_e4m3 for every |v| < 464 (checked
+// over all such floats on gfx950).  Used for h / s, where the choice of s
+// keeps |h / s| <= 448 (1 + 2^-23); NaN gives a NaN code instead of 0.
+__device__ __forceinline__ uint32_t e4m3_pair(float v0, float v1) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false) & 0xFFFFu;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
@@ -759,11 +767,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArg
           for (int w = 0; w < kTileThreads / 64; ++w) mb = umax(mb, red_lds[w][row]);
           const float amax = __uint_as_float(mb);
           const float sc = __fdiv_rn(amax, 448.0f);
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const uint32_t c = amax != 0.0f ? to_e4m3(__fdiv_rn(acc[m][t][i], sc)) : 0u;
-            h_lds[h_off(row, wave * 2 + t) + col] = (uint8_t)c;
-          }
+          const uint32_t c =
+              amax != 0.0f ? e4m3_pair(__fdiv_rn(acc[m][0][i], sc), __fdiv_rn(acc[m][1][i], sc)) : 0u;
+          h_lds[h_off(row, wave * 2) + col] = (uint8_t)c;
+          h_lds[h_off(row, wave * 2 + 1) + col] = (uint8_t)(c >> 8);
           if (wave == 0 && col == 0) sh_lds[row] = sc;
         }
       }
@@ -893,13 +900,9 @@ __global__ __launch_bounds__(kThreads, D <= 2 ? 4 : 3) void gate_up_stream_kerne
       const uint32_t mb = umax(umax(red_lds[0][r], red_lds[1][r]), umax(red_lds[2][r], red_lds[3][r]));
       const float amax = __uint_as_float(mb);
       const float sc = __fdiv_rn(amax, 448.0f);
-      uint32_t c0 = 0, c1 = 0;
-      if (amax != 0.0f) {
-        c0 = to_e4m3(__fdiv_rn(acc[0][i], sc));
-        c1 = to_e4m3(__fdiv_rn(acc[1][i], sc));
-      }
-      h_lds[r * 128 + wave * 32 + col] = (uint8_t)c0;
-      h_lds[r * 128 + wave * 32 + 16 + col] = (uint8_t)c1;
+      const uint32_t c = amax != 0.0f ? e4m3_pair(__fdiv_rn(acc[0][i], sc), __fdiv_rn(acc[1][i], sc)) : 0u;
+      h_lds[r * 128 + wave * 32 + col] = (uint8_t)c;
+      h_lds[r * 128 + wave * 32 + 16 + col] = (uint8_t)(c >> 8);
       if (wave == 0 && col == 0) sh_lds[r] = sc;
     }
     __syncthreads();
@@ -947,8 +950,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
   __shared__ __attribute__((aligned(256))) float sx_lds1[2 * BM];
   __shared__ float ws_lds[2 * kMaxKBlocks];
   __shared__ int tok_lds[BM];
-  __shared__ uint32_t red_lds[4][BM];
-  __shared__ float sh_lds[BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1114,16 +1115,21 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
     else
       kloop(std::integral_constant<int, 0>{});
 
-    // epilogue (activation stage 0 is free now: it becomes the h staging tile)
-    uint8_t* h_lds = a_lds0;
+    // epilogue (activation stage 0 is free now: it becomes the h staging tile).
+    // Its lane indices are re-derived from an opaque copy of the thread id,
+    // so the compiler cannot compute epilogue addresses before the K loop
+    // and keep them live (spilled) across it.
+    int etid = (int)threadIdx.x;
+    asm volatile("" : "+v"(etid));
+    const int ecol = etid & 15, egrp = (etid >> 4) & 3;
     if constexpr (kDbg) {
 #pragma unroll
       for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = mh * 128 + m * 16 + grp * 4 + i;
+          const int row = mh * 128 + m * 16 + egrp * 4 + i;
           if (m < mtw && row < rows) {
-            float* g = a.gu_dbg + (size_t)(p0 + row) * 2 * Ip + nb * kBlock + wn * 32 + col;
+            float* g = a.gu_dbg + (size_t)(p0 + row) * 2 * Ip + nb * kBlock + wn * 32 + ecol;
             g[0] = acc[m][0][i];
             g[16] = acc[m][1][i];
             g[Ip] = acc[m][2][i];
@@ -1131,45 +1137,77 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
           }
         }
     }
+    // h = silu(g) * u in FP32, staged in LDS (the four stage buffers, 64 rows
+    // of 512 bytes each), then quantised row by row: thread t takes half t % 2
+    // (64 columns) of row t / 2.  16-byte chunk c of row r sits in slot
+    // c ^ (r % 32) ^ 8 (c / 16): the stores of one instruction (4 rows 4 apart,
+    // 16 columns) and the loads (8 rows x 2 halves) then fill distinct banks.
+    auto hrow = [&](int obj) __attribute__((always_inline)) {
+      return obj == 0 ? a_lds0 : (obj == 1 ? a_lds1 : (obj == 2 ? w_lds0 : w_lds1));
+    };
+    auto hslot = [](int rr, int c) __attribute__((always_inline)) { return c ^ (rr & 31) ^ ((c >> 4) << 3); };
+    auto act = [&](auto CL) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      if (m < mtw) {
+      for (int m = 0; m < 8; ++m) {
+        if (m < mtw) {
+          uint8_t* hb = hrow(mh * 2 + (m >> 2));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[m][0][i] = silu_mul_act(acc[m][0][i], acc[m][2][i], a.act_limit);
-          acc[m][1][i] = silu_mul_act(acc[m][1][i], acc[m][3][i], a.act_limit);
-          const uint32_t mb = max16(umax(abs_bits(acc[m][0][i]), abs_bits(acc[m][1][i])));
-          if (col == 0) red_lds[wn][mh * 128 + m * 16 + grp * 4 + i] = mb;
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      if (m < mtw) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = mh * 128 + m * 16 + grp * 4 + i;
-          uint32_t mb = 0;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) mb = umax(mb, red_lds[w][row]);
-          const float amax = __uint_as_float(mb);
-          const float sc = __fdiv_rn(amax, 448.0f);
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const uint32_t c = amax != 0.0f ? to_e4m3(__fdiv_rn(acc[m][t][i], sc)) : 0u;
-            h_lds[h_off(row, wn * 2 + t) + col] = (uint8_t)c;
+          for (int i = 0; i < 4; ++i) {
+            float h0, h1;
+            if constexpr (decltype(CL)::value) {
+              h0 = silu_mul_act(acc[m][0][i], acc[m][2][i], a.act_limit);
+              h1 = silu_mul_act(acc[m][1][i], acc[m][3][i], a.act_limit);
+            } else {
+              h0 = silu_mul(acc[m][0][i], acc[m][2][i]);
+              h1 = silu_mul(acc[m][1][i], acc[m][3][i]);
+            }
+            const int rr = (m & 3) * 16 + egrp * 4 + i;
+            const int c0 = wn * 8 + (ecol >> 2), c1 = c0 + 4;
+            *reinterpret_cast<float*>(hb + rr * 512 + (hslot(rr, c0) << 4) + (ecol & 3) * 4) = h0;
+            *reinterpret_cast<float*>(hb + rr * 512 + (hslot(rr, c1) << 4) + (ecol & 3) * 4) = h1;
           }
-          if (wn == 0 && col == 0) sh_lds[row] = sc;
         }
       }
-    }
+    };
+    if (a.act_limit > 0.0f)
+      act(std::true_type{});
+    else
+      act(std::false_type{});
     __syncthreads();
-    for (int row = tid >> 3; row < rows; row += kWideThreads / 8)
-      st16(a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + (tid & 7) * 16, ld16(&h_lds[h_off(row, tid & 7)]));
-    if (tid < rows) {
-      a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
-      a.shT[(size_t)nb * a.P + p0 + tid] = sh_lds[tid];
+    {
+      const int row = etid >> 1, half = etid & 1, rr = row & 63;
+      const uint8_t* hb = hrow(__builtin_amdgcn_readfirstlane(etid >> 7)) + rr * 512;
+      float v[64];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const f32x4 q = ld16f(reinterpret_cast<const float*>(hb + (hslot(rr, half * 16 + j) << 4)));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[4 * j + k] = q[k];
+      }
+      uint32_t mb = 0;
+#pragma unroll
+      for (int k = 0; k < 64; ++k) mb = umax(mb, abs_bits(v[k]));
+      mb = umax(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0xB1, 0xF, 0xF, false));  // the other half
+      const float amax = __uint_as_float(mb);
+      const float sc = __fdiv_rn(amax, 448.0f);
+      uint32_t w[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t lo = e4m3_pair(__fdiv_rn(v[4 * k], sc), __fdiv_rn(v[4 * k + 1], sc));
+        const uint32_t hi = e4m3_pair(__fdiv_rn(v[4 * k + 2], sc), __fdiv_rn(v[4 * k + 3], sc));
+        // branch-free: an all-zero row (sc = 0) takes code 0 by the select
+        w[k] = amax != 0.0f ? (lo | (hi << 16)) : 0u;
+      }
+      if (row < rows) {
+        uint8_t* dst = a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + half * 64;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          st16(dst + q * 16, i32x4{(int)w[4 * q], (int)w[4 * q + 1], (int)w[4 * q + 2], (int)w[4 * q + 3]});
+        if (half == 0) {
+          a.sh[(size_t)(p0 + row) * NB + nb] = sc;
+          a.shT[(size_t)nb * a.P + p0 + row] = sc;
+        }
+      }
     }
   }
 }
