@@ -27,6 +27,11 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 METRIC = "input tokens/sec per MoE layer (1 MI355X) + % FP8 MFMA peak / % HBM peak"
 PROFILES = os.path.join(ROOT, "profiles")
 COUNTERS_MD = os.path.join(PROFILES, "gate_up_stream_glm_e256_t256_counters.md")
+GATE_UP_KERNELS = {
+    "stream": "gate_up_stream_kernel (experts with 1..16 rows)",
+    "tile": "gate_up_tile_kernel (experts with 17..128 rows)",
+    "wide": "gate_up_wide_kernel (experts with more than 128 rows)",
+}
 STATS_MD = os.path.join(PROFILES, "kernel_stats_glm_e256_t256.md")
 KERNEL_SOURCE = os.path.join(ROOT, "fp8_blockwise_routed_amd", "csrc", "moe_kernels.hip")
 DOMINANT = "gate_up_stream_kernel"   # the 1-subtile gate_up launch (experts with 1..16 rows)
@@ -80,9 +85,10 @@ def algorithmic_work(wl, counts):
     Per expert with n_e > 0 rows: weights 3*Ip*H code bytes + FP32 block
     scales 4*(2*nI*nH + nH*nI); per routed slot: 6*Ip*H FLOPs.  Plus the
     input rows (T*H*2) and output rows (T*H*2 for BF16) and ids/weights (8*P).
-    Returns the whole path and the gate_up 1-subtile launch (experts with
-    1..16 rows): its weights 2*Ip*H + 8*nI*nH per expert, the activation row
-    (H + 4*nH) read and the h row (Ip + 4*nI) written per slot.
+    Returns the whole path and, for each gate_up launch (experts with 1..16
+    rows: streaming; 17..128: 128-row tiles; more: 256-row tiles), its
+    weights 2*Ip*H + 8*nI*nH per expert, the activation row (H + 4*nH) read
+    and the h row (Ip + 4*nI) written per slot, and 4*Ip*H FLOPs per slot.
     """
     import numpy as np
     E, H, I, T, k = wl.E, wl.H, wl.I, wl.T, wl.k
@@ -93,18 +99,16 @@ def algorithmic_work(wl, counts):
     w_bytes = int(hit.sum()) * (3 * Ip * H + 4 * (2 * nI * nH + nH * nI))
     path_bytes = w_bytes + T * H * 2 + T * H * 2 + 8 * T * k
     path_flops = 6 * P * Ip * H
-    small = (counts >= 1) & (counts <= 16)
-    n_small = int(counts[small].sum())
-    gu_bytes = int(small.sum()) * (2 * Ip * H + 8 * nI * nH) + n_small * (H + 4 * nH + Ip + 4 * nI)
-    gu_flops = 4 * n_small * Ip * H
-    big = counts > 16
-    n_big = int(counts[big].sum())
-    gu_big_bytes = int(big.sum()) * (2 * Ip * H + 8 * nI * nH) + n_big * (H + 4 * nH + Ip + 4 * nI)
-    gu_big_flops = 4 * n_big * Ip * H
-    return dict(path_bytes=path_bytes, path_flops=path_flops, gu_small_bytes=gu_bytes,
-                gu_small_flops=gu_flops, gu_big_bytes=gu_big_bytes, gu_big_flops=gu_big_flops,
-                experts_hit=int(hit.sum()), experts_small=int(small.sum()),
-                experts_big=int(big.sum()), slots=P,
+    groups = {}
+    for name, lo, hi in (("stream", 1, 16), ("tile", 17, 128), ("wide", 129, None)):
+        sel = (counts >= lo) & ((counts <= hi) if hi is not None else True)
+        rows = int(counts[sel].sum())
+        groups[name] = dict(
+            experts=int(sel.sum()), rows=rows,
+            bytes=int(sel.sum()) * (2 * Ip * H + 8 * nI * nH) + rows * (H + 4 * nH + Ip + 4 * nI),
+            flops=4 * rows * Ip * H)
+    return dict(path_bytes=path_bytes, path_flops=path_flops, gate_up=groups,
+                experts_hit=int(hit.sum()), slots=P,
                 per_expert_gate_up_bytes=2 * Ip * H + 8 * nI * nH)
 
 
@@ -421,38 +425,28 @@ def main() -> int:
     if stages is not None and len(stages):
         mean = stages.mean(axis=0)
         res["stages_ms"] = {name: float(v) for name, v in zip(pkg.STAGES, mean)}
-        gu_ms = float(mean[pkg.STAGES.index("gate_up_small")])
-        big_ms = float(mean[pkg.STAGES.index("gate_up_big")])
-        if gu_ms >= big_ms:
-            achieved = work["gu_small_bytes"] / (gu_ms * 1e-3) / 1e9
-            res["roofline"] = {
-                "kernel": "gate_up_stream_kernel (experts with 1..16 rows)",
-                "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic(),
-                "algorithmic_bytes_per_launch": work["gu_small_bytes"],
-                "experts_in_launch": work["experts_small"],
-                "avg_launch_ms": gu_ms,
-            }
+        # the dominant gate_up launch, against the roof its algorithmic work
+        # reaches first
+        kind = max(("stream", "tile", "wide"), key=lambda k: float(mean[pkg.STAGES.index("gate_up_" + k)]))
+        g = work["gate_up"][kind]
+        launch_ms = float(mean[pkg.STAGES.index("gate_up_" + kind)])
+        t_hbm = g["bytes"] / (PEAK_HBM_GBS * 1e9)
+        t_mfma = g["flops"] / (PEAK_FP8_TFLOPS * 1e12)
+        if t_mfma >= t_hbm:
+            achieved = g["flops"] / (launch_ms * 1e-3) / 1e12
+            bound, peak, unit = "mfma", PEAK_FP8_TFLOPS, "TFLOP/s"
         else:
-            # the 128-row tile launch dominates: bound by whichever roof its
-            # algorithmic work reaches first
-            t_hbm = work["gu_big_bytes"] / (PEAK_HBM_GBS * 1e9)
-            t_mfma = work["gu_big_flops"] / (PEAK_FP8_TFLOPS * 1e12)
-            if t_mfma >= t_hbm:
-                achieved = work["gu_big_flops"] / (big_ms * 1e-3) / 1e12
-                bound, peak, unit = "mfma", PEAK_FP8_TFLOPS, "TFLOP/s"
-            else:
-                achieved = work["gu_big_bytes"] / (big_ms * 1e-3) / 1e9
-                bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
-            res["roofline"] = {
-                "kernel": "gate_up_tile_kernel (experts with more than 16 rows)",
-                "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                "frac": achieved / peak, "traffic": None,
-                "algorithmic_bytes_per_launch": work["gu_big_bytes"],
-                "algorithmic_flops_per_launch": work["gu_big_flops"],
-                "experts_in_launch": work["experts_big"],
-                "avg_launch_ms": big_ms,
-            }
+            achieved = g["bytes"] / (launch_ms * 1e-3) / 1e9
+            bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
+        res["roofline"] = {
+            "kernel": GATE_UP_KERNELS[kind],
+            "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "traffic": read_traffic() if kind == "stream" else None,
+            "algorithmic_bytes_per_launch": g["bytes"],
+            "algorithmic_flops_per_launch": g["flops"],
+            "experts_in_launch": g["experts"], "rows_in_launch": g["rows"],
+            "avg_launch_ms": launch_ms,
+        }
     if args.router:
         # the router alone, timed with HIP events on the run stream
         ids_r = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")

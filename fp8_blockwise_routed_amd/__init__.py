@@ -32,8 +32,9 @@ MOE_ACT_SILU_UNCLAMPED = 0
 MOE_ACT_SILU_CLAMPED = 1
 MOE_ROUTER_SOFTMAX = 0
 MOE_ROUTER_SIGMOID = 1
-MOE_NUM_STAGES = 7
-STAGES = ("plan", "quant", "gate_up_small", "gate_up_big", "down_small", "down_big", "combine")
+MOE_NUM_STAGES = 9
+STAGES = ("plan", "quant", "gate_up_stream", "gate_up_tile", "gate_up_wide", "down_stream", "down_tile",
+          "down_wide", "combine")
 
 EXPORTED = (
     "moe_fp8_prefill_validate", "moe_fp8_prefill_workspace_bytes", "moe_fp8_prefill_weight_bytes",
@@ -326,7 +327,7 @@ def moe_fp8_prefill_set_timing(handle: int, enable: bool) -> None:
 
 
 def moe_fp8_prefill_read_timing(handle: int, max_records: int = 4096) -> np.ndarray:
-    """[records][7] milliseconds, one row per pass, in the order of STAGES."""
+    """[records][MOE_NUM_STAGES] milliseconds, one row per pass, in the order of STAGES."""
     buf = np.zeros((max_records, MOE_NUM_STAGES), np.float32)
     n = ctypes.c_int32()
     _check(load_library().moe_fp8_prefill_read_timing(ctypes.c_void_p(handle), _np_ptr(buf),

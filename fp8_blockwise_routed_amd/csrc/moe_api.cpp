@@ -347,9 +347,10 @@ int64_t max_tiles(const Dims& m, int64_t P, int kind) {
 
 // The gate_up launches of a pass over t rows / P slots whose plan and
 // activations are in the workspace: streaming tiles, then 128-row tiles, then
-// 256-row tiles.
+// 256-row tiles.  after[kind], if given, is recorded after each of the three
+// (also when a launch is skipped for lack of work).
 hipError_t launch_gate_up_all(moe_fp8_prefill* h, int64_t t, int64_t P, float* gu_dbg, hipStream_t s,
-                              hipEvent_t between = nullptr) {
+                              hipEvent_t* after = nullptr) {
   const Dims& m = h->m;
   const int64_t nb = m.Ip / kBlock;
   GateUpArgs ga{h->xq, h->sx, t * m.H, t * m.nH * 4, h->perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip,
@@ -359,21 +360,22 @@ hipError_t launch_gate_up_all(moe_fp8_prefill* h, int64_t t, int64_t P, float* g
   Tile* lists[3] = {h->small_tiles, h->big_tiles, h->wide_tiles};
   for (int kind = kGemmStream; kind <= kGemmWide; ++kind) {
     const int64_t items = max_tiles(m, P, kind) * nb;
-    if (kind == kGemmTile && between) {
-      hipError_t e = hipEventRecord(between, s);
+    if (items > 0) {
+      ga.tiles = lists[kind];
+      ga.n_tiles = h->n_tiles + kind;
+      hipError_t e = launch_gate_up(ga, kind, gemm_grid(h, items, kind, true), s);
       if (e != hipSuccess) return e;
     }
-    if (items == 0) continue;
-    ga.tiles = lists[kind];
-    ga.n_tiles = h->n_tiles + kind;
-    hipError_t e = launch_gate_up(ga, kind, gemm_grid(h, items, kind, true), s);
-    if (e != hipSuccess) return e;
+    if (after) {
+      hipError_t e = hipEventRecord(after[kind], s);
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
 
 // The down launches, in the same order.
-hipError_t launch_down_all(moe_fp8_prefill* h, int64_t P, hipStream_t s, hipEvent_t between = nullptr) {
+hipError_t launch_down_all(moe_fp8_prefill* h, int64_t P, hipStream_t s, hipEvent_t* after = nullptr) {
   const Dims& m = h->m;
   const int64_t nb = m.H / kBlock, nb2 = (nb + 1) / 2;
   DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2,
@@ -381,15 +383,16 @@ hipError_t launch_down_all(moe_fp8_prefill* h, int64_t P, hipStream_t s, hipEven
   Tile* lists[3] = {h->small_tiles, h->big_tiles, h->wide_tiles};
   for (int kind = kGemmStream; kind <= kGemmWide; ++kind) {
     const int64_t items = max_tiles(m, P, kind) * (kind == kGemmStream ? nb : nb2);
-    if (kind == kGemmTile && between) {
-      hipError_t e = hipEventRecord(between, s);
+    if (items > 0) {
+      da.tiles = lists[kind];
+      da.n_tiles = h->n_tiles + kind;
+      hipError_t e = launch_down(da, kind, gemm_grid(h, items, kind, false), s);
       if (e != hipSuccess) return e;
     }
-    if (items == 0) continue;
-    da.tiles = lists[kind];
-    da.n_tiles = h->n_tiles + kind;
-    hipError_t e = launch_down(da, kind, gemm_grid(h, items, kind, false), s);
-    if (e != hipSuccess) return e;
+    if (after) {
+      hipError_t e = hipEventRecord(after[kind], s);
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
@@ -468,18 +471,16 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
     if (launch_quant(qa, s) != hipSuccess) return fail(h);
     if (h->timing && hipEventRecord(ev.ev[2], s) != hipSuccess) return fail(h);
 
-    if (launch_gate_up_all(h, t, P, nullptr, s, h->timing ? ev.ev[3] : nullptr) != hipSuccess)
+    if (launch_gate_up_all(h, t, P, nullptr, s, h->timing ? &ev.ev[3] : nullptr) != hipSuccess)
       return fail(h);
-    if (h->timing && hipEventRecord(ev.ev[4], s) != hipSuccess) return fail(h);
-    if (launch_down_all(h, P, s, h->timing ? ev.ev[5] : nullptr) != hipSuccess) return fail(h);
-    if (h->timing && hipEventRecord(ev.ev[6], s) != hipSuccess) return fail(h);
+    if (launch_down_all(h, P, s, h->timing ? &ev.ev[6] : nullptr) != hipSuccess) return fail(h);
 
     CombineArgs ca{h->y, h->inv, w_p, (int32_t)t, (int32_t)m.k, (int32_t)m.H, (int32_t)m.kr,
                    h->desc.routed_scale, h->desc.out_dtype == MOE_DTYPE_F32 ? 1 : 0,
                    (uint8_t*)out + r0 * m.H * out_elem};
     if (launch_combine(ca, s) != hipSuccess) return fail(h);
     if (h->timing) {
-      if (hipEventRecord(ev.ev[7], s) != hipSuccess) return fail(h);
+      if (hipEventRecord(ev.ev[MOE_NUM_STAGES], s) != hipSuccess) return fail(h);
       h->pending.push_back(ev);
     }
     h->last_T = t;

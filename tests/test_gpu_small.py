@@ -229,3 +229,25 @@ def test_output_guard_words_untouched():
     finally:
         moe.close()
     assert np.all(host[:pad] == -12345) and np.all(host[-pad:] == -12345)
+
+
+def test_stage_timing_records():
+    """Per-launch timing: one row of MOE_NUM_STAGES non-negative intervals per
+    pass; the 256-row group carries time when experts have more than 128
+    rows (E=4, ~300 rows each) and the streaming group when none has 1-16."""
+    spec = CASES[3][1]
+    layer, x, ids, w, rho = make_case(spec)
+    note("stage timing")
+    moe = pkg.MoeFp8Prefill(layer, spec[1], routed_scale=rho, out_dtype=pkg.MOE_DTYPE_BF16)
+    try:
+        pkg.moe_fp8_prefill_set_timing(moe.handle, True)
+        for _ in range(3):
+            run(moe, x, ids, w)
+        st = pkg.moe_fp8_prefill_read_timing(moe.handle)
+        pkg.moe_fp8_prefill_set_timing(moe.handle, False)
+    finally:
+        moe.close()
+    assert st.shape == (3, pkg.MOE_NUM_STAGES)
+    assert np.all(st >= 0)
+    s = dict(zip(pkg.STAGES, st.mean(axis=0)))
+    assert s["gate_up_wide"] > s["gate_up_stream"] and s["down_wide"] > s["down_stream"]
