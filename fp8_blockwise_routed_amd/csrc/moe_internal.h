@@ -11,8 +11,7 @@ constexpr int kBlock = 128;          // weight block edge and activation group
 constexpr int kWaves = 4;            // waves per GEMM workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSmallRows = 16;       // experts with <= this many rows use the 1-subtile GEMM
-constexpr int kBigRows = 128;        // rows per tile of the 4-wave large-expert GEMMs
-constexpr int kWideRows = 256;       // rows per tile of the 8-wave GEMMs (experts with > kBigRows rows)
+constexpr int kWideRows = 256;       // rows per tile of the 8-wave GEMMs (experts with > kSmallRows rows)
 #ifndef MOE_STREAM_DEPTH
 #define MOE_STREAM_DEPTH 3
 #endif
@@ -55,9 +54,8 @@ struct PlanArgs {
   int32_t* perm;       // [T*k]
   int32_t* inv;        // [T*k]
   Tile* small_tiles;   // [E]
-  Tile* big_tiles;     // [E]: experts with kSmallRows < rows <= kBigRows, one tile each
-  Tile* wide_tiles;    // [T*k/kBigRows + E]: experts with more rows, tiles of <= kWideRows
-  int32_t* n_tiles;    // [3]: small, big, wide
+  Tile* wide_tiles;    // [T*k/kWideRows + E]: experts with more rows, tiles of <= kWideRows
+  int32_t* n_tiles;    // [2]: small, wide
   int32_t* err;        // sticky bad-id flag
 };
 
@@ -152,7 +150,7 @@ struct SliceArgs {
 };
 
 // GEMM variants (launch_gate_up / launch_down kind)
-constexpr int kGemmStream = 0, kGemmTile = 1, kGemmWide = 2;
+constexpr int kGemmStream = 0, kGemmWide = 1;
 
 // Launchers (return the launch status).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);

@@ -184,20 +184,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   int total;
   const int off = block_exclusive_scan(n, scan_scratch, &total);
   // each expert's rows go to one list: <= kSmallRows rows one streaming tile,
-  // <= kBigRows one 128-row tile, more rows near-equal 256-row tiles
+  // more rows near-equal tiles of at most kWideRows
   const int is_small = (n >= 1 && n <= kSmallRows) ? 1 : 0;
-  const int is_big = (n > kSmallRows && n <= kBigRows) ? 1 : 0;
-  const int n_wide = n > kBigRows ? (n + kWideRows - 1) / kWideRows : 0;
-  int n_small_all, n_big_all, n_wide_all;
+  const int n_wide = n > kSmallRows ? (n + kWideRows - 1) / kWideRows : 0;
+  int n_small_all, n_wide_all;
   const int small_at = block_exclusive_scan(is_small, scan_scratch, &n_small_all);
-  const int big_at = block_exclusive_scan(is_big, scan_scratch, &n_big_all);
   const int wide_at = block_exclusive_scan(n_wide, scan_scratch, &n_wide_all);
   if (tid < E) {
     a.counts[tid] = n;
     a.offsets[tid] = off;
     cursor[tid] = off;
     if (is_small) a.small_tiles[small_at] = Tile{tid, off, n, small_at, 1, 0, 0, 0};
-    if (is_big) a.big_tiles[big_at] = Tile{tid, off, n, big_at, 1, 0, 0, 0};
     if (n_wide) {
       // split n rows into n_wide tiles of near-equal size, multiples of 16 rows
       const int per = ((n + n_wide - 1) / n_wide + 15) & ~15;
@@ -211,8 +208,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   if (tid == 0) {
     a.offsets[E] = total;
     a.n_tiles[0] = n_small_all;
-    a.n_tiles[1] = n_big_all;
-    a.n_tiles[2] = n_wide_all;
+    a.n_tiles[1] = n_wide_all;
   }
   __syncthreads();
 
@@ -416,26 +412,7 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 // distinct banks; the copy-out reads whole aligned chunks.
 __device__ __forceinline__ int h_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 2) & 7)) << 4); }
 
-// ----------------------------------------------------------------- gate_up --
-// Large-expert gate_up: a 256-thread workgroup computes a tile of up to 128
-// rows of one expert x (128 gate + 128 up) columns of one 128-row block nb,
-// so the epilogue sees one whole 128-wide group of h.  Wave w owns gate and
-// up columns 32w..32w+31 (4 n-tiles) for all rows: each activation fragment
-// it reads from LDS feeds four MFMAs, and its weight fragments (8 KiB per K
-// block) stream into registers one K block ahead.  The activation rows,
-// gathered through the plan's permutation, arrive in a double-buffered LDS
-// tile by buffer-load-to-LDS (each lane fetches the 16-byte chunk that lands
-// in its XOR-swizzled slot).  One wave per SIMD, up to 512 registers each.
-//
-// Block kb + 1 is loaded while block kb is multiplied, and each K step ends
-// by waiting for every load of the wave (vmcnt 0) before the barrier: the
-// completion of buffer-load-to-LDS and of loads into registers is not
-// ordered between the two kinds, so a partial count could pass with some of
-// block kb + 1's DMA still in flight.
-
-constexpr int kTileThreads = 256;
-constexpr int kTileRows = kBigRows;  // 128
-static_assert(kTileRows == 128, "the big-tile kernels cover 128 rows");
+// ----------------------------------------------------------- tile helpers --
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -455,35 +432,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
     f(std::integral_constant<int, I>{});
     static_for<N, I + 1>(static_cast<F&&>(f));
-  }
-}
-
-// Scheduling hint for the current basic block: the LDS reads first, then
-// NM times (one MFMA, NV VALU instructions), so the promotion FMAs issue
-// while the MFMAs execute.
-template <int NM, int NV>
-__device__ __forceinline__ void interleave_mfma_valu() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
-  }
-}
-
-// As interleave_mfma_valu, with NL vector-memory loads after the first MFMA:
-// a load that waits for room in the address queue then stalls the wave while
-// its MFMAs execute.
-template <int NM, int NV, int NL>
-__device__ __forceinline__ void interleave_mfma_valu_vmem() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-  __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);  // VMEM reads
-  __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
-#pragma unroll
-  for (int i = 1; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
   }
 }
 
@@ -510,11 +458,6 @@ __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "m
 // Item i: the tile at position i / NB in tile-major order has the same
 // expert, whose items start at first * NB.
 constexpr int kItemTiles = 4, kItemBlocks = 8, kXcds = 8;
-#ifndef MOE_WIDE_ITEM_TILES
-#define MOE_WIDE_ITEM_TILES 4
-#endif
-// 256-row tiles: row tiles x weight blocks per 32-item run
-constexpr int kWideItemTiles = MOE_WIDE_ITEM_TILES, kWideItemBlocks = 32 / kWideItemTiles;
 
 struct Item {
   int e, p0, rows, nb;
@@ -522,8 +465,8 @@ struct Item {
 
 // All fields are workgroup-uniform; readfirstlane keeps them in SGPRs so the
 // buffer descriptors built from them stay scalar.
-template <int IT = kItemTiles, int IB = kItemBlocks>
 __device__ __forceinline__ Item item_of(int i, int NB, const Tile* tiles) {
+  constexpr int IT = kItemTiles, IB = kItemBlocks;
   const int tg = i / NB;
   const int first = __builtin_amdgcn_readfirstlane(tiles[tg].first);
   const int me = __builtin_amdgcn_readfirstlane(tiles[tg].count);
@@ -558,231 +501,6 @@ __device__ __forceinline__ int item_index(int r) {
   if (G % kXcds) return b + r * G;
   const int slots = G / kXcds;
   return (r * kXcds + b % kXcds) * slots + b / kXcds;
-}
-
-__global__ __launch_bounds__(kTileThreads, 1) void gate_up_tile_kernel(GateUpArgs a) {
-  constexpr int BM = kTileRows;
-  constexpr int NS = 2;  // activation stages in LDS (1 K block ahead)
-  constexpr int DB = 2;  // weight register stages (1 K block ahead)
-  constexpr int MT = BM / 16;
-  // one LDS object per stage, indexed only by compile-time stage numbers, so
-  // the compiler can tell a DMA into one stage from reads of another and does
-  // not make the MFMA reads wait for the DMAs just issued
-  __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t a_lds1[BM * 128];
-  __shared__ __attribute__((aligned(256))) float sx_lds0[2 * BM];
-  __shared__ __attribute__((aligned(256))) float sx_lds1[2 * BM];
-  __shared__ float ws_lds[2 * kMaxKBlocks];
-  __shared__ int tok_lds[BM];
-  __shared__ uint32_t red_lds[kTileThreads / 64][BM];
-  __shared__ float sh_lds[BM];
-
-  // the wave index is uniform: keep it (and all that derives from it) scalar
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, grp = lane >> 4;
-  const int H = a.H, Ip = a.Ip, nH = H / kBlock, NB = Ip / kBlock;
-  const int n_items = a.n_tiles[0] * NB;
-  const rsrc_t xr = make_rsrc(a.xq, (uint32_t)a.xq_bytes);
-  const rsrc_t sr = make_rsrc(a.sxT, (uint32_t)a.sxT_bytes);
-  // wave w reads n-tiles g0, g1, u0, u1 of 32-column group w of the chunk
-  const uint32_t b_off = (uint32_t)(wave * 4 * 2 * 1024 + lane * 16);
-  const int afr = (lane & 15) * 128;
-  const int afc0 = ((2 * grp) ^ swz(lane)) << 4, afc1 = ((2 * grp + 1) ^ swz(lane)) << 4;
-
-  for (int r = 0;; ++r) {
-    const int item = item_index(r);
-    if (item >= n_items) break;
-    const Item it = item_of(item, NB, a.tiles);
-    const int e = it.e, p0 = it.p0, rows = it.rows, nb = it.nb;
-    const int mt = (rows + 15) >> 4;  // 16-row subtiles holding rows (uniform)
-
-    __syncthreads();  // LDS of the previous item is no longer read
-    if (tid < BM) tok_lds[tid] = a.perm[p0 + (tid < rows ? tid : 0)] / a.k;
-    {
-      const float* ws = a.s13 + (size_t)(e * NB + nb) * nH * 2;
-      for (int i = tid; i < 2 * nH; i += kTileThreads) ws_lds[i] = ws[i];
-    }
-    __syncthreads();
-
-    const rsrc_t wr = make_rsrc(a.w13 + (size_t)(e * NB + nb) * nH * kGateUpChunk, (uint32_t)(nH * kGateUpChunk));
-    // activation DMA: instruction q of wave w fills LDS bytes [(4q + w) * 1024,
-    // +1024) = rows 8(4q + w) .. +8; rows past the last subtile read out of range
-    uint32_t avo[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = (q * 4 + wave) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(row);
-      avo[q] = (uint32_t)(tok_lds[row] * H + c * 16) + ((q * 4 + wave) * 8 < mt * 16 ? 0u : 0x80000000u);
-    }
-    const uint32_t svo = wave < 2 ? (uint32_t)(tok_lds[wave * 64 + lane] * 4) : 0x80000000u;
-
-    // K block kb goes to stage kb % NS.  Its 13 loads come in 7 parts: the
-    // weight n-tiles (parts 0-3, two loads each), the activation DMAs (parts
-    // 4-5, two each) and the row-scale DMA (part 6; waves 2-3 load out of
-    // range into the unused half of the stage).  Every stage issues all of
-    // them, out of range past the last block, so the wait count is exact.
-    auto issue_part = [&](auto ST, auto PT, int kb, i32x8(&b)[4]) __attribute__((always_inline)) {
-      constexpr int st = decltype(ST)::value, p = decltype(PT)::value;
-      const bool in = kb < nH;
-      const uint32_t oob = in ? 0u : 0x80000000u;
-      if constexpr (p < 4) {
-        // default cache policy: the other row tiles of this expert read the
-        // same weight chunk soon after, from L2
-        const uint32_t so = in ? (uint32_t)(kb * kGateUpChunk) : 0u;
-        b[p] = cat(bload16(wr, b_off | oob, so + p * 2048), bload16(wr, b_off | oob, so + p * 2048 + 1024));
-      } else if constexpr (p < 6) {
-        uint8_t* al = st == 0 ? a_lds0 : a_lds1;
-        const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
-#pragma unroll
-        for (int q = 2 * (p - 4); q < 2 * (p - 4) + 2; ++q)
-          dma16<0>(xr, al + (q * 4 + wave) * 1024, avo[q] | oob, sa);
-      } else {
-        float* sl = st == 0 ? sx_lds0 : sx_lds1;
-        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * a.T * 4) : 0u);
-      }
-    };
-    auto issue = [&](auto ST, int kb, i32x8(&b)[4]) __attribute__((always_inline)) {
-      static_for<7>([&](auto PT) __attribute__((always_inline)) { issue_part(ST, PT, kb, b); });
-    };
-
-    // acc[m][t]: rows 16m + 4grp + i, n-tile t (gate 0-1, up 2-3)
-    f32x4 acc[MT][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    i32x8 B[DB][4];
-
-    // one K block: issue block kb + 1 into the other stage (read last step),
-    // multiply block kb out of stage s, then wait for block kb + 1
-    auto step = [&](auto S, int kb0) __attribute__((always_inline)) {
-      constexpr int s = decltype(S)::value;
-      const int kb = kb0 + s;
-      issue(std::integral_constant<int, 1 - s>{}, kb + 1, B[1 - s]);
-      if (kb < nH) {
-        const float wsg = ws_lds[2 * kb], wsu = ws_lds[2 * kb + 1];
-        const uint8_t* abuf = (s == 0 ? a_lds0 : a_lds1) + afr;
-        const float* srow = (s == 0 ? sx_lds0 : sx_lds1) + grp * 4;
-        // Software pipeline over the 16-row subtiles: while the four MFMAs
-        // of subtile m run, the VALU promotes subtile m - 1's products into
-        // the FP32 accumulators (one wave per SIMD: nothing else would fill
-        // the MFMA pipe during the promotion).  A fragments are read one
-        // subtile ahead, row scales kept for three subtiles, in rotating
-        // register sets.
-        i32x8 A2[2];
-        f32x4 R3[3], P[2][4];
-        A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
-        R3[0] = ld16f(srow);
-        auto promote = [&](auto J) __attribute__((always_inline)) {
-          constexpr int j = decltype(J)::value;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float rs = R3[j % 3][i];
-            const float cg = rs * wsg, cu = rs * wsu;
-            acc[j][0][i] = __builtin_fmaf(P[j & 1][0][i], cg, acc[j][0][i]);
-            acc[j][1][i] = __builtin_fmaf(P[j & 1][1][i], cg, acc[j][1][i]);
-            acc[j][2][i] = __builtin_fmaf(P[j & 1][2][i], cu, acc[j][2][i]);
-            acc[j][3][i] = __builtin_fmaf(P[j & 1][3][i], cu, acc[j][3][i]);
-          }
-          pin_in_place(acc[j]);
-        };
-        auto next = [&](auto M) __attribute__((always_inline)) {
-          constexpr int m = decltype(M)::value;
-          if constexpr (m + 1 < MT) {
-            A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
-            R3[(m + 1) % 3] = ld16f(srow + (m + 1) * 16);
-          }
-        };
-        // All MT subtiles are multiplied even when the tile holds fewer rows
-        // (the last tile of an expert): the rows past the end are zeros, the
-        // surplus MFMAs hide under the weight stream such tiles wait for, and
-        // a branch-free body lets subtile m's MFMAs run while the VALU
-        // promotes subtile m - 1 (one basic block per subtile).
-        static_for<MT>([&](auto M) __attribute__((always_inline)) {
-          constexpr int m = decltype(M)::value;
-          next(M);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) P[m & 1][t] = mfma_e4m3(A2[m & 1], B[s][t]);
-          if constexpr (m > 0) promote(std::integral_constant<int, m - 1>{});
-          interleave_mfma_valu<4, 6>();
-          __builtin_amdgcn_sched_barrier(0);
-        });
-        promote(std::integral_constant<int, MT - 1>{});
-      }
-      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block kb + 1 has landed
-      ring_barrier();
-    };
-
-    issue(std::integral_constant<int, 0>{}, 0, B[0]);
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block 0 has landed
-    ring_barrier();
-    static_assert(NS == 2 && DB == 2, "the K loop is unrolled by the stage count");
-    for (int kb0 = 0; kb0 < nH; kb0 += NS) {
-      step(std::integral_constant<int, 0>{}, kb0);
-      step(std::integral_constant<int, 1>{}, kb0);
-    }
-    // the out-of-range loads issued past the last block still write zeros
-    // to their stages: let them land before the LDS is reused
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-
-    // epilogue (activation stage 0 is free now: it becomes the h staging tile)
-    uint8_t* h_lds = a_lds0;
-    if (a.gu_dbg) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m * 16 + grp * 4 + i;
-          if (m < mt && row < rows) {
-            float* g = a.gu_dbg + (size_t)(p0 + row) * 2 * Ip + nb * kBlock + wave * 32 + col;
-            g[0] = acc[m][0][i];
-            g[16] = acc[m][1][i];
-            g[Ip] = acc[m][2][i];
-            g[Ip + 16] = acc[m][3][i];
-          }
-        }
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[m][0][i] = silu_mul_act(acc[m][0][i], acc[m][2][i], a.act_limit);
-          acc[m][1][i] = silu_mul_act(acc[m][1][i], acc[m][3][i], a.act_limit);
-          const uint32_t mb = max16(umax(abs_bits(acc[m][0][i]), abs_bits(acc[m][1][i])));
-          if (col == 0) red_lds[wave][m * 16 + grp * 4 + i] = mb;
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m * 16 + grp * 4 + i;
-          uint32_t mb = 0;
-#pragma unroll
-          for (int w = 0; w < kTileThreads / 64; ++w) mb = umax(mb, red_lds[w][row]);
-          const float amax = __uint_as_float(mb);
-          const float sc = __fdiv_rn(amax, 448.0f);
-          const uint32_t c =
-              amax != 0.0f ? e4m3_pair(__fdiv_rn(acc[m][0][i], sc), __fdiv_rn(acc[m][1][i], sc)) : 0u;
-          h_lds[h_off(row, wave * 2) + col] = (uint8_t)c;
-          h_lds[h_off(row, wave * 2 + 1) + col] = (uint8_t)(c >> 8);
-          if (wave == 0 && col == 0) sh_lds[row] = sc;
-        }
-      }
-    }
-    __syncthreads();
-    for (int row = tid >> 3; row < rows; row += kTileThreads / 8)
-      st16(a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + (tid & 7) * 16, ld16(&h_lds[h_off(row, tid & 7)]));
-    if (tid < rows) {
-      a.sh[(size_t)(p0 + tid) * NB + nb] = sh_lds[tid];
-      a.shT[(size_t)nb * a.P + p0 + tid] = sh_lds[tid];
-    }
-  }
 }
 
 // Streaming gate_up for experts with at most 16 rows (the HBM-bound regime):
@@ -916,21 +634,26 @@ __global__ __launch_bounds__(kThreads, D <= 2 ? 4 : 3) void gate_up_stream_kerne
   }
 }
 
-// Wide gate_up for experts with more than kBigRows rows: a 512-thread
-// workgroup (two waves per SIMD) computes a tile of up to 256 rows x (128 gate
-// + 128 up) columns of one 128-row block nb.  Both operands arrive in LDS by
-// buffer-load-to-LDS, double-buffered by K block: the gathered activation
-// rows (32 KiB per K block) and the expert's 32 KiB weight chunk, read once
-// per workgroup instead of once per wave.  Wave w = 4 mh + wn owns rows
-// 128 mh .. +127 and 32-column group wn of gate and up (4 n-tiles), the same
-// 16x16 tiles, MFMAs and promotion order as the other gate_up kernels.
+// gate_up for experts with more than kSmallRows rows: a 512-thread workgroup
+// (two waves per SIMD, up to 256 registers each) computes a tile of up to 256
+// rows x (128 gate + 128 up) columns of one 128-row block nb, so the epilogue
+// sees whole 128-wide groups of h.  Both operands arrive in LDS by
+// buffer-load-to-LDS, double-buffered by K block: the activation rows,
+// gathered through the plan's permutation (32 KiB per K block; each lane
+// fetches the 16-byte chunk that lands in its swizzled slot), and the
+// expert's 32 KiB weight chunk, read once per workgroup.  Wave w = 4 mh + wn
+// owns rows 128 mh .. +127 and 32-column group wn of gate and up (4 n-tiles):
+// each activation fragment it reads feeds four MFMAs.  Same 16x16 tiles,
+// MFMAs and promotion order as the streaming kernel.
 //
 // Per K block the tile moves 64 KiB through the vector memory pipe for
-// 256 x 256 x 128 MACs, about two thirds of the MFMA time, where a 128-row
-// tile would move 48 KiB for half the MACs.  With two waves per SIMD one wave
-// multiplies while the other waits for its loads to issue.
+// 256 x 256 x 128 MACs, about two thirds of the MFMA time at peak; a 128-row
+// tile would move 48 KiB for half the MACs.  Block kb + 1 is loaded while
+// block kb is multiplied, and each K step ends with vmcnt(0) and a barrier.
+// A half with few rows multiplies fewer 16-row subtiles (8, 4 or none) but
+// runs the same loads and barriers.
 constexpr int kWideThreads = 512;
-static_assert(kWideRows == 2 * kBigRows, "a wide tile is two 128-row halves");
+static_assert(kWideRows == 256, "a tile is two 128-row halves");
 
 // kDbg: also write gate/up before the epilogue to a.gu_dbg (inspection
 // launches only; the pass launches the variant without that code).
@@ -938,8 +661,9 @@ template <bool kDbg>
 __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArgs a) {
   constexpr int BM = kWideRows;
   constexpr int NS = 2;  // LDS stages (1 K block ahead)
-  // one LDS object per stage, indexed only by compile-time stage numbers
-  // (see gate_up_tile_kernel)
+  // one LDS object per stage, indexed only by compile-time stage numbers, so
+  // the compiler can tell a DMA into one stage from reads of another and does
+  // not make the MFMA reads wait for the DMAs just issued
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[BM * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds1[BM * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t w_lds0[kGateUpChunk];
@@ -968,7 +692,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
   for (int r = 0;; ++r) {
     const int item = item_index(r);
     if (item >= n_items) break;
-    const Item it = item_of<kWideItemTiles, kWideItemBlocks>(item, NB, a.tiles);
+    const Item it = item_of(item, NB, a.tiles);
     const int e = it.e, p0 = it.p0, rows = it.rows, nb = it.nb;
     // 16-row subtiles of this wave's half that hold rows (wave-uniform)
     const int rows_h = rows - mh * 128 < 0 ? 0 : (rows - mh * 128 > 128 ? 128 : rows - mh * 128);
@@ -1217,193 +941,12 @@ hipError_t launch_gate_up(const GateUpArgs& a, int kind, int grid, hipStream_t s
     hipLaunchKernelGGL(gate_up_wide_kernel<true>, dim3(grid), dim3(kWideThreads), 0, s, a);
   else if (kind == kGemmWide)
     hipLaunchKernelGGL(gate_up_wide_kernel<false>, dim3(grid), dim3(kWideThreads), 0, s, a);
-  else if (kind == kGemmTile)
-    hipLaunchKernelGGL(gate_up_tile_kernel, dim3(grid), dim3(kTileThreads), 0, s, a);
   else
     hipLaunchKernelGGL(gate_up_stream_kernel<kStreamDepth>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 // -------------------------------------------------------------------- down --
-// Large-expert down: a 256-thread workgroup computes up to 128 rows x 256
-// hidden columns (weight blocks nb2, nb2+1).  As in gate_up_tile_kernel, wave
-// w owns 64 columns for all rows (block nb2 + w/2, columns 64(w%2)..+63, 4
-// n-tiles): its weight fragments stream into registers one K block ahead and
-// the shared h rows arrive in a double-buffered LDS tile by
-// buffer-load-to-LDS, with the same exact waits.
-
-__global__ __launch_bounds__(kTileThreads, 1) void down_tile_kernel(DownArgs a) {
-  constexpr int BM = kTileRows;
-  constexpr int NS = 2, DB = 2;
-  constexpr int MT = BM / 16;
-  // one LDS object per stage (see gate_up_tile_kernel)
-  __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t a_lds1[BM * 128];
-  __shared__ __attribute__((aligned(256))) float s_lds0[2 * BM];
-  __shared__ __attribute__((aligned(256))) float s_lds1[2 * BM];
-  __shared__ float ws_lds[2][kMaxKBlocks];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, grp = lane >> 4;
-  const int H = a.H, Ip = a.Ip, nI = Ip / kBlock, NB = H / kBlock;
-  const int NB2 = (NB + 1) >> 1;
-  const int n_items = a.n_tiles[0] * NB2;
-  const rsrc_t hr = make_rsrc(a.hq, (uint32_t)a.hq_bytes);
-  const rsrc_t sr = make_rsrc(a.shT, (uint32_t)a.shT_bytes);
-  const int half = wave >> 1;  // which of the two weight blocks
-  // n-tiles 0-3 of the wave are 32-column groups 2(w%2), 2(w%2)+1 of its block
-  const uint32_t b_off = (uint32_t)((wave & 1) * 4 * 2 * 1024 + lane * 16);
-  const int afr = (lane & 15) * 128;
-  const int afc0 = ((2 * grp) ^ swz(lane)) << 4, afc1 = ((2 * grp + 1) ^ swz(lane)) << 4;
-
-  for (int r = 0;; ++r) {
-    const int item = item_index(r);
-    if (item >= n_items) break;
-    const Item it = item_of(item, NB2, a.tiles);
-    const int nb2 = it.nb * 2;
-    const bool two = nb2 + 1 < NB;  // second weight block present
-    const int e = it.e, p0 = it.p0, rows = it.rows;
-    const int mt_all = (rows + 15) >> 4;
-    const int mt = (half == 1 && !two) ? 0 : mt_all;
-
-    __syncthreads();  // LDS of the previous item is no longer read
-    {
-      const float* ws = a.s2 + (size_t)(e * NB + nb2) * nI;
-      for (int i = tid; i < nI; i += kTileThreads) {
-        ws_lds[0][i] = ws[i];
-        ws_lds[1][i] = two ? ws[nI + i] : 0.f;
-      }
-    }
-    __syncthreads();
-
-    // this wave's weight block: nb2 + half (absent -> out of range)
-    const rsrc_t wr = make_rsrc(a.w2 + (size_t)(e * NB + nb2 + (two ? half : 0)) * nI * kDownChunk,
-                                (uint32_t)(nI * kDownChunk));
-    const uint32_t wmask = (half == 1 && !two) ? 0x80000000u : 0u;
-    uint32_t avo[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = (q * 4 + wave) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(row);
-      avo[q] = (uint32_t)((p0 + (row < rows ? row : 0)) * Ip + c * 16) +
-               ((q * 4 + wave) * 8 < mt_all * 16 ? 0u : 0x80000000u);
-    }
-    // row scales: waves 0-1 load rows 64w + lane, waves 2-3 load out of
-    // range into the unused half of the stage
-    const int srow = wave * 64 + lane;
-    const uint32_t svo = wave < 2 ? (uint32_t)((p0 + (srow < rows ? srow : 0)) * 4) : 0x80000000u;
-
-    // block kb's 13 loads in 7 parts, as in gate_up_tile_kernel
-    auto issue_part = [&](auto ST, auto PT, int kb, i32x8(&b)[4]) __attribute__((always_inline)) {
-      constexpr int st = decltype(ST)::value, p = decltype(PT)::value;
-      const bool in = kb < nI;
-      const uint32_t oob = in ? 0u : 0x80000000u;
-      if constexpr (p < 4) {
-        const uint32_t so = in ? (uint32_t)(kb * kDownChunk) : 0u;
-        b[p] = cat(bload16(wr, b_off | oob | wmask, so + p * 2048),
-                   bload16(wr, b_off | oob | wmask, so + p * 2048 + 1024));
-      } else if constexpr (p < 6) {
-        uint8_t* al = st == 0 ? a_lds0 : a_lds1;
-        const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
-#pragma unroll
-        for (int q = 2 * (p - 4); q < 2 * (p - 4) + 2; ++q)
-          dma16<0>(hr, al + (q * 4 + wave) * 1024, avo[q] | oob, sa);
-      } else {
-        float* sl = st == 0 ? s_lds0 : s_lds1;
-        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * a.P * 4) : 0u);
-      }
-    };
-    auto issue = [&](auto ST, int kb, i32x8(&b)[4]) __attribute__((always_inline)) {
-      static_for<7>([&](auto PT) __attribute__((always_inline)) { issue_part(ST, PT, kb, b); });
-    };
-
-    f32x4 acc[MT][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    i32x8 B[DB][4];
-
-    auto step = [&](auto S, int kb0) __attribute__((always_inline)) {
-      constexpr int s = decltype(S)::value;
-      const int kb = kb0 + s;
-      issue(std::integral_constant<int, 1 - s>{}, kb + 1, B[1 - s]);
-      if (kb < nI) {
-        const float wsc = ws_lds[half][kb];
-        const uint8_t* abuf = (s == 0 ? a_lds0 : a_lds1) + afr;
-        const float* srw = (s == 0 ? s_lds0 : s_lds1) + grp * 4;
-        // software pipeline as in gate_up_tile_kernel
-        i32x8 A2[2];
-        f32x4 R3[3], Q[2][4];
-        A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
-        R3[0] = ld16f(srw);
-        auto promote = [&](auto J) __attribute__((always_inline)) {
-          constexpr int j = decltype(J)::value;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float sc = R3[j % 3][i] * wsc;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc[j][t][i] = __builtin_fmaf(Q[j & 1][t][i], sc, acc[j][t][i]);
-          }
-          pin_in_place(acc[j]);
-        };
-        auto next = [&](auto M) __attribute__((always_inline)) {
-          constexpr int m = decltype(M)::value;
-          if constexpr (m + 1 < MT) {
-            A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
-            R3[(m + 1) % 3] = ld16f(srw + (m + 1) * 16);
-          }
-        };
-        // All MT subtiles are multiplied even when the tile holds fewer rows
-        // (the last tile of an expert): the rows past the end are zeros, the
-        // surplus MFMAs hide under the weight stream such tiles wait for, and
-        // a branch-free body lets subtile m's MFMAs run while the VALU
-        // promotes subtile m - 1 (one basic block per subtile).
-        static_for<MT>([&](auto M) __attribute__((always_inline)) {
-          constexpr int m = decltype(M)::value;
-          next(M);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) Q[m & 1][t] = mfma_e4m3(A2[m & 1], B[s][t]);
-          if constexpr (m > 0) promote(std::integral_constant<int, m - 1>{});
-          interleave_mfma_valu<4, 5>();
-          __builtin_amdgcn_sched_barrier(0);
-        });
-        promote(std::integral_constant<int, MT - 1>{});
-      }
-      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block kb + 1 has landed
-      ring_barrier();
-    };
-
-    issue(std::integral_constant<int, 0>{}, 0, B[0]);
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block 0 has landed
-    ring_barrier();
-    static_assert(NS == 2 && DB == 2, "the K loop is unrolled by the stage count");
-    for (int kb0 = 0; kb0 < nI; kb0 += NS) {
-      step(std::integral_constant<int, 0>{}, kb0);
-      step(std::integral_constant<int, 1>{}, kb0);
-    }
-    // the out-of-range loads issued past the last block still write zeros
-    // to their stages: let them land before the next item's loads
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m * 16 + grp * 4 + i;
-          if (row < rows) {
-            float* dst = a.y + (size_t)(p0 + row) * H + (nb2 + half) * kBlock + (wave & 1) * 64 + col;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) dst[t * 16] = acc[m][t][i];
-          }
-        }
-      }
-    }
-  }
-}
-
 // Streaming down for experts with at most 16 rows; structure as
 // gate_up_stream_kernel (no LDS tile, no barrier in the K loop, D blocks of
 // prefetch), arithmetic as down_kernel.
@@ -1486,7 +1029,7 @@ __global__ __launch_bounds__(kThreads, 4) void down_stream_kernel(DownArgs a) {
   }
 }
 
-// Wide down for experts with more than kBigRows rows: a 512-thread workgroup
+// down for experts with more than kSmallRows rows: a 512-thread workgroup
 // computes up to 256 rows x 256 hidden columns (weight blocks nb2, nb2 + 1),
 // both operands double-buffered in LDS by buffer-load-to-LDS as in
 // gate_up_wide_kernel.  Wave w = 4 mh + wn owns rows 128 mh .. +127 and 64
@@ -1519,7 +1062,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
   for (int r = 0;; ++r) {
     const int item = item_index(r);
     if (item >= n_items) break;
-    const Item it = item_of<kWideItemTiles, kWideItemBlocks>(item, NB2, a.tiles);
+    const Item it = item_of(item, NB2, a.tiles);
     const int nb2 = it.nb * 2;
     const bool two = nb2 + 1 < NB;  // second weight block present
     const int e = it.e, p0 = it.p0, rows = it.rows;
@@ -1675,8 +1218,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
 hipError_t launch_down(const DownArgs& a, int kind, int grid, hipStream_t s) {
   if (kind == kGemmWide)
     hipLaunchKernelGGL(down_wide_kernel, dim3(grid), dim3(kWideThreads), 0, s, a);
-  else if (kind == kGemmTile)
-    hipLaunchKernelGGL(down_tile_kernel, dim3(grid), dim3(kTileThreads), 0, s, a);
   else
     hipLaunchKernelGGL(down_stream_kernel<kStreamDepthDown>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();

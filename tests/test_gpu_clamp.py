@@ -2,7 +2,7 @@
 
 MOE_ACT_SILU_CLAMPED with limit L caps the gate at L and clips up to [-L, L]
 before silu(gate) * up.  Compared stage by stage with the oracle set to the
-same limit, on the 1-subtile and the 128-row tile GEMMs; a limit chosen
+same limit, on the 1-subtile and the 256-row tile GEMMs; a limit chosen
 below the layers' typical |gate| so the clamp is active; a huge limit gives
 the unclamped bits.
 """

@@ -17,8 +17,9 @@ from gpu_util import TOL, assert_rows_close, compare_with_oracle, dev, dev_bf16,
 pytestmark = pytest.mark.gpu
 
 # (E, k, H, I, T, route, rho, outlier_frac): small enough for the oracle in
-# seconds; experts get from 0 to a few hundred rows (every GEMM variant: 16-row
-# streaming, 128-row and 256-row tiles, ragged last tiles); I=192 exercises the
+# seconds; experts get from 0 to a few hundred rows (both GEMM variants:
+# 16-row streaming and 256-row tiles, one or both halves used, ragged last
+# tiles); I=192 exercises the
 # zero padding to 256.
 CASES = [
     ("tiny", (8, 2, 256, 128, 64, gen.ROUTE_SOFTMAX, 1.0, 0.0)),
