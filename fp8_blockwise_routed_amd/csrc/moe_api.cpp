@@ -73,13 +73,13 @@ int64_t align256(int64_t n) { return (n + 255) & ~int64_t(255); }
 
 // Workspace pieces, in allocation order.
 struct WsSizes {
-  int64_t xq, sx, sxT, hq, sh, shT, y, counts, offsets, perm, inv, small_tiles, wide_tiles, n_tiles,
+  int64_t xq, sx, sxT, hq, sh, shT, y, counts, offsets, perm, inv, small_tiles, wide_tiles, n_tiles, chunk,
       err, rids, rw;
   int64_t total() const {
     return align256(xq) + align256(sx) + align256(sxT) + align256(hq) + align256(sh) + align256(shT) +
            align256(y) +
            align256(counts) + align256(offsets) + align256(perm) + align256(inv) +
-           align256(small_tiles) + align256(wide_tiles) + align256(n_tiles) +
+           align256(small_tiles) + align256(wide_tiles) + align256(n_tiles) + align256(chunk) +
            align256(err) +
            align256(rids) + align256(rw);
   }
@@ -101,6 +101,7 @@ WsSizes ws_sizes(const Dims& m) {
   w.small_tiles = m.E * (int64_t)sizeof(Tile);
   w.wide_tiles = (m.P / kWideRows + m.E + 1) * (int64_t)sizeof(Tile);
   w.n_tiles = 4 * 4;
+  w.chunk = (m.P + 1023) / 1024 * m.E * 4;  // the plan's per-chunk counts
   w.err = 4;
   w.rids = m.max_rows * m.kr * 4;  // one pass's routed ids and weights (run_logits)
   w.rw = m.max_rows * m.kr * 4;
@@ -144,6 +145,7 @@ struct moe_fp8_prefill {
   Tile* small_tiles = nullptr;
   Tile* wide_tiles = nullptr;
   int32_t* n_tiles = nullptr;
+  int32_t* chunk = nullptr;
   int32_t* err = nullptr;
   int32_t* rids = nullptr;
   float* rw = nullptr;
@@ -460,7 +462,7 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
     }
     PlanArgs pa{ids_p, (int32_t)t, (int32_t)m.k, (int32_t)m.E, (int32_t)m.kr, (int32_t)m.Er,
                 h->counts, h->offsets, h->perm, h->inv, h->small_tiles,
-                h->wide_tiles, h->n_tiles, h->err};
+                h->wide_tiles, h->n_tiles, h->err, h->chunk};
     if (launch_plan(pa, s) != hipSuccess) return fail(h);
     if (h->timing && hipEventRecord(ev.ev[1], s) != hipSuccess) return fail(h);
 
@@ -609,6 +611,7 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   h->small_tiles = (Tile*)get(w.small_tiles);
   h->wide_tiles = (Tile*)get(w.wide_tiles);
   h->n_tiles = (int32_t*)get(w.n_tiles);
+  h->chunk = (int32_t*)get(w.chunk);
   h->err = (int32_t*)get(w.err);
   h->rids = (int32_t*)get(w.rids);
   h->rw = (float*)get(w.rw);
@@ -933,6 +936,7 @@ int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slo
   h->small_tiles = (Tile*)get(w.small_tiles);
   h->wide_tiles = (Tile*)get(w.wide_tiles);
   h->n_tiles = (int32_t*)get(w.n_tiles);
+  h->chunk = (int32_t*)get(w.chunk);
   h->err = (int32_t*)get(w.err);
   h->rids = (int32_t*)get(w.rids);
   h->rw = (float*)get(w.rw);

@@ -57,6 +57,7 @@ struct PlanArgs {
   Tile* wide_tiles;    // [T*k/kWideRows + E]: experts with more rows, tiles of <= kWideRows
   int32_t* n_tiles;    // [2]: small, wide
   int32_t* err;        // sticky bad-id flag
+  int32_t* chunk;      // [ceil(T*k/1024)][E] scratch: per-chunk counts, then first positions
 };
 
 struct RouteArgs {

@@ -116,10 +116,10 @@ __device__ __forceinline__ float silu_mul_act(float g, float u, float L) {
 }
 
 // -------------------------------------------------------------------- plan --
-// One workgroup of 1024 threads.  Counting sort that keeps slot order within
-// an expert: histogram with LDS atomics, exclusive scan, then chunks of 1024
-// slots ranked inside each wave by a ballot match on the expert id and across
-// waves by per-wave counts.
+// Counting sort of the (token, slot) pairs by expert that keeps slot order
+// within an expert, in three passes over chunks of 1024 slots: per-chunk
+// histograms, one workgroup for the offsets and tile lists, per-chunk stable
+// scatter.
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
@@ -160,27 +160,33 @@ __device__ __forceinline__ int slot_expert(const PlanArgs& a, int f, bool& bad) 
   return e;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+// Pass 1, one workgroup per chunk of kPlanThreads slots: the chunk's count
+// per expert, chunk[c][e].
+__global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(PlanArgs a) {
   __shared__ int cnt[kMaxExperts];
-  __shared__ int cursor[kMaxExperts];
-  __shared__ int wcnt[kPlanWaves][kMaxExperts];
-  __shared__ int scan_scratch[kPlanWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = a.E, P = a.T * a.k;
-
+  const int tid = threadIdx.x, E = a.E, P = a.T * a.k;
   for (int e = tid; e < kMaxExperts; e += kPlanThreads) cnt[e] = 0;
-  for (int i = tid; i < kPlanWaves * kMaxExperts; i += kPlanThreads) (&wcnt[0][0])[i] = 0;
   __syncthreads();
+  const int f = blockIdx.x * kPlanThreads + tid;
   bool bad = false;
-  for (int f = tid; f < P; f += kPlanThreads) {
+  if (f < P) {
     const int e = slot_expert(a, f, bad);
     if (e >= 0) atomicAdd(&cnt[e], 1);
   }
   if (bad) *a.err = 1;
   __syncthreads();
+  for (int e = tid; e < E; e += kPlanThreads) a.chunk[(size_t)blockIdx.x * E + e] = cnt[e];
+}
 
-  // offsets and tile lists; thread e owns expert e (E <= 1024)
-  const int n = tid < E ? cnt[tid] : 0;
+// Pass 2, one workgroup: per-expert totals, offsets and tile lists, and
+// chunk[c][e] turned into the position of chunk c's first row of expert e.
+__global__ __launch_bounds__(kPlanThreads) void plan_offsets_kernel(PlanArgs a) {
+  __shared__ int scan_scratch[kPlanWaves];
+  const int tid = threadIdx.x, E = a.E, P = a.T * a.k;
+  const int n_chunks = (P + kPlanThreads - 1) / kPlanThreads;
+  int n = 0;
+  if (tid < E)
+    for (int c = 0; c < n_chunks; ++c) n += a.chunk[(size_t)c * E + tid];
   int total;
   const int off = block_exclusive_scan(n, scan_scratch, &total);
   // each expert's rows go to one list: <= kSmallRows rows one streaming tile,
@@ -193,7 +199,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   if (tid < E) {
     a.counts[tid] = n;
     a.offsets[tid] = off;
-    cursor[tid] = off;
+    int run = off;
+    for (int c = 0; c < n_chunks; ++c) {
+      const int m = a.chunk[(size_t)c * E + tid];
+      a.chunk[(size_t)c * E + tid] = run;
+      run += m;
+    }
     if (is_small) a.small_tiles[small_at] = Tile{tid, off, n, small_at, 1, 0, 0, 0};
     if (n_wide) {
       // split n rows into n_wide tiles of near-equal size, multiples of 16 rows
@@ -210,46 +221,56 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.n_tiles[0] = n_small_all;
     a.n_tiles[1] = n_wide_all;
   }
-  __syncthreads();
+}
 
-  // stable scatter
+// Pass 3, one workgroup per chunk: stable scatter.  A slot's position is its
+// chunk's first position for its expert, plus the slots of that expert in
+// earlier waves of the chunk (per-wave counts), plus its rank among the
+// wave's lanes with the same expert (a ballot match on the id bits).
+__global__ __launch_bounds__(kPlanThreads) void plan_scatter_kernel(PlanArgs a) {
+  __shared__ int cursor[kMaxExperts];
+  __shared__ int wcnt[kPlanWaves][kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, P = a.T * a.k;
+  const int f = blockIdx.x * kPlanThreads + tid;
+  bool ignored = false;
+  const int e = f < P ? slot_expert(a, f, ignored) : -1;
+  const bool valid = e >= 0;
+  for (int x = tid; x < E; x += kPlanThreads) cursor[x] = a.chunk[(size_t)blockIdx.x * E + x];
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < P; c0 += kPlanThreads) {
-    const int f = c0 + tid;
-    bool ignored = false;
-    const int e = f < P ? slot_expert(a, f, ignored) : -1;
-    const bool valid = e >= 0;
-    uint64_t same = __ballot(valid);
+  uint64_t same = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < 10; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t bm = __ballot(bit);
-      same &= bit ? bm : ~bm;
-    }
-    const int rank = __popcll(same & lt_mask);
-    const int group = __popcll(same);
-    if (valid && rank == 0) wcnt[wave][e] = group;
-    __syncthreads();
-    if (valid) {
-      int before = 0;
-      for (int w = 0; w < wave; ++w) before += wcnt[w][e];
-      const int pos = cursor[e] + before + rank;
-      a.perm[pos] = f;
-      a.inv[f] = pos;
-    } else if (f < P) {
-      a.inv[f] = -1;
-    }
-    __syncthreads();
-    if (valid && rank == 0) {
-      atomicAdd(&cursor[e], group);
-      wcnt[wave][e] = 0;
-    }
-    __syncthreads();
+  for (int b = 0; b < 10; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t bm = __ballot(bit);
+    same &= bit ? bm : ~bm;
+  }
+  const int rank = __popcll(same & lt_mask);
+  const int group = __popcll(same);
+  // every wave's count for every expert present in the chunk (0 elsewhere)
+  for (int w = 0; w < kPlanWaves; ++w)
+    if (valid) wcnt[w][e] = 0;
+  __syncthreads();
+  if (valid && rank == 0) wcnt[wave][e] = group;
+  __syncthreads();
+  if (valid) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wcnt[w][e];
+    const int pos = cursor[e] + before + rank;
+    a.perm[pos] = f;
+    a.inv[f] = pos;
+  } else if (f < P) {
+    a.inv[f] = -1;
   }
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  const int P = a.T * a.k;
+  const int n_chunks = (P + kPlanThreads - 1) / kPlanThreads;
+  if (n_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(plan_count_kernel, dim3(n_chunks), dim3(kPlanThreads), 0, s, a);
+  hipLaunchKernelGGL(plan_offsets_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  hipLaunchKernelGGL(plan_scatter_kernel, dim3(n_chunks), dim3(kPlanThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1224,7 +1245,22 @@ hipError_t launch_down(const DownArgs& a, int kind, int grid, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------- combine --
-// One workgroup per token; 4 consecutive columns per thread.
+// A workgroup per token and 2048 columns; 8 consecutive columns per thread.
+// All of a token's y loads are issued before the sums (a skipped slot reads
+// row 0 and contributes through a select, never through arithmetic), so each
+// thread has its k rows in flight at once; the sums keep the slot order.
+
+constexpr int kCombineSlots = 8;  // routed slots loaded together (more: in groups of 8)
+
+__device__ __forceinline__ void acc_slot(f32x4 (&acc)[2], const f32x4 (&v)[2], float wj, bool on) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float term = wj * v[h][q];
+      acc[h][q] = on ? acc[h][q] + term : acc[h][q];
+    }
+}
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x;
@@ -1237,46 +1273,51 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     wt[j] = j < kr ? a.w[(size_t)t * kr + j] : 1.0f;
   }
   __syncthreads();
-  for (int c = (blockIdx.y * 256 + threadIdx.x) * 4; c < H; c += gridDim.y * 256 * 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < kr; ++j) {
-      const int p = pos[j];
-      if (p >= 0) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(a.y + (size_t)p * H + c);
-        const float wj = wt[j];
-        acc[0] = acc[0] + wj * v[0];
-        acc[1] = acc[1] + wj * v[1];
-        acc[2] = acc[2] + wj * v[2];
-        acc[3] = acc[3] + wj * v[3];
-      }
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c >= H) return;
+  auto load = [&](int j, f32x4 (&v)[2]) __attribute__((always_inline)) {
+    const int p = pos[j];
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.y + (size_t)(p >= 0 ? p : 0) * H + c);
+    v[0] = __builtin_nontemporal_load(src);
+    v[1] = __builtin_nontemporal_load(src + 1);
+  };
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // routed slots, in order
+  for (int j0 = 0; j0 < kr; j0 += kCombineSlots) {
+    f32x4 v[kCombineSlots][2];
+#pragma unroll
+    for (int j = 0; j < kCombineSlots; ++j)
+      if (j0 + j < kr) load(j0 + j, v[j]);
+#pragma unroll
+    for (int j = 0; j < kCombineSlots; ++j)
+      if (j0 + j < kr) acc_slot(acc, v[j], wt[j0 + j], pos[j0 + j] >= 0);
+  }
+  f32x4 o[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) o[h] = f32x4{a.rho * acc[h][0], a.rho * acc[h][1], a.rho * acc[h][2], a.rho * acc[h][3]};
+  // the shared-expert slot is added after the routed sum is scaled
+  for (int j = kr; j < k; ++j) {
+    f32x4 v[2];
+    load(j, v);
+    acc_slot(o, v, wt[j], pos[j] >= 0);
+  }
+  if (a.out_f32) {
+    f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + (size_t)t * H + c);
+    dst[0] = o[0];
+    dst[1] = o[1];
+  } else {
+    i32x4 b;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      b[2 * h] = (int)(f32_to_bf16(o[h][0]) | (f32_to_bf16(o[h][1]) << 16));
+      b[2 * h + 1] = (int)(f32_to_bf16(o[h][2]) | (f32_to_bf16(o[h][3]) << 16));
     }
-    f32x4 o = {a.rho * acc[0], a.rho * acc[1], a.rho * acc[2], a.rho * acc[3]};
-    // the shared-expert slot is added after the routed sum is scaled
-    for (int j = kr; j < k; ++j) {
-      const int p = pos[j];
-      if (p >= 0) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(a.y + (size_t)p * H + c);
-        const float wj = wt[j];
-        o[0] = o[0] + wj * v[0];
-        o[1] = o[1] + wj * v[1];
-        o[2] = o[2] + wj * v[2];
-        o[3] = o[3] + wj * v[3];
-      }
-    }
-    if (a.out_f32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + (size_t)t * H + c) = o;
-    } else {
-      const uint32_t lo = f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16);
-      const uint32_t hi = f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + (size_t)t * H + c);
-      dst[0] = lo;
-      dst[1] = hi;
-    }
+    st16(reinterpret_cast<uint16_t*>(a.out) + (size_t)t * H + c, b);
   }
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.T, (a.H + 1023) / 1024), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(a.T, (a.H + 2047) / 2048), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
