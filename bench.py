@@ -29,7 +29,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 COUNTERS_MD = os.path.join(PROFILES, "gate_up_stream_glm_e256_t256_counters.md")
 GATE_UP_KERNELS = {
     "stream": "gate_up_stream_kernel (experts with 1..16 rows)",
-    "wide": "gate_up_wide_kernel (experts with more than 16 rows)",
+    "narrow": "gate_up_narrow_kernel (experts with 17..128 rows)",
+    "wide": "gate_up_wide_kernel (experts with more than 128 rows)",
 }
 STATS_MD = os.path.join(PROFILES, "kernel_stats_glm_e256_t256.md")
 KERNEL_SOURCE = os.path.join(ROOT, "fp8_blockwise_routed_amd", "csrc", "moe_kernels.hip")
@@ -85,7 +86,7 @@ def algorithmic_work(wl, counts):
     scales 4*(2*nI*nH + nH*nI); per routed slot: 6*Ip*H FLOPs.  Plus the
     input rows (T*H*2) and output rows (T*H*2 for BF16) and ids/weights (8*P).
     Returns the whole path and, for each gate_up launch (experts with 1..16
-    rows: streaming; more: tiles of up to 256 rows), its
+    rows: streaming; 17..128: 128-row tiles; more: 256-row tiles), its
     weights 2*Ip*H + 8*nI*nH per expert, the activation row (H + 4*nH) read
     and the h row (Ip + 4*nI) written per slot, and 4*Ip*H FLOPs per slot.
     """
@@ -99,7 +100,7 @@ def algorithmic_work(wl, counts):
     path_bytes = w_bytes + T * H * 2 + T * H * 2 + 8 * T * k
     path_flops = 6 * P * Ip * H
     groups = {}
-    for name, lo, hi in (("stream", 1, 16), ("wide", 17, None)):
+    for name, lo, hi in (("stream", 1, 16), ("narrow", 17, 128), ("wide", 129, None)):
         sel = (counts >= lo) & ((counts <= hi) if hi is not None else True)
         rows = int(counts[sel].sum())
         groups[name] = dict(
@@ -426,7 +427,7 @@ def main() -> int:
         res["stages_ms"] = {name: float(v) for name, v in zip(pkg.STAGES, mean)}
         # the dominant gate_up launch, against the roof its algorithmic work
         # reaches first
-        kind = max(("stream", "wide"), key=lambda k: float(mean[pkg.STAGES.index("gate_up_" + k)]))
+        kind = max(("stream", "narrow", "wide"), key=lambda k: float(mean[pkg.STAGES.index("gate_up_" + k)]))
         g = work["gate_up"][kind]
         launch_ms = float(mean[pkg.STAGES.index("gate_up_" + kind)])
         t_hbm = g["bytes"] / (PEAK_HBM_GBS * 1e9)

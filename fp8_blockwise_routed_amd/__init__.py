@@ -32,8 +32,9 @@ MOE_ACT_SILU_UNCLAMPED = 0
 MOE_ACT_SILU_CLAMPED = 1
 MOE_ROUTER_SOFTMAX = 0
 MOE_ROUTER_SIGMOID = 1
-MOE_NUM_STAGES = 7
-STAGES = ("plan", "quant", "gate_up_stream", "gate_up_wide", "down_stream", "down_wide", "combine")
+MOE_NUM_STAGES = 9
+STAGES = ("plan", "quant", "gate_up_stream", "gate_up_narrow", "gate_up_wide", "down_stream", "down_narrow",
+          "down_wide", "combine")
 
 EXPORTED = (
     "moe_fp8_prefill_validate", "moe_fp8_prefill_workspace_bytes", "moe_fp8_prefill_weight_bytes",

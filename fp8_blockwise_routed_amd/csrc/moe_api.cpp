@@ -73,13 +73,13 @@ int64_t align256(int64_t n) { return (n + 255) & ~int64_t(255); }
 
 // Workspace pieces, in allocation order.
 struct WsSizes {
-  int64_t xq, sx, sxT, hq, sh, shT, y, counts, offsets, perm, inv, small_tiles, wide_tiles, n_tiles, chunk,
+  int64_t xq, sx, sxT, hq, sh, shT, y, counts, offsets, perm, inv, small_tiles, narrow_tiles, wide_tiles, n_tiles, chunk,
       err, rids, rw;
   int64_t total() const {
     return align256(xq) + align256(sx) + align256(sxT) + align256(hq) + align256(sh) + align256(shT) +
            align256(y) +
            align256(counts) + align256(offsets) + align256(perm) + align256(inv) +
-           align256(small_tiles) + align256(wide_tiles) + align256(n_tiles) + align256(chunk) +
+           align256(small_tiles) + align256(narrow_tiles) + align256(wide_tiles) + align256(n_tiles) + align256(chunk) +
            align256(err) +
            align256(rids) + align256(rw);
   }
@@ -99,6 +99,7 @@ WsSizes ws_sizes(const Dims& m) {
   w.perm = m.P * 4;
   w.inv = m.P * 4;
   w.small_tiles = m.E * (int64_t)sizeof(Tile);
+  w.narrow_tiles = m.E * (int64_t)sizeof(Tile);
   w.wide_tiles = (m.P / kWideRows + m.E + 1) * (int64_t)sizeof(Tile);
   w.n_tiles = 4 * 4;
   w.chunk = (m.P + 1023) / 1024 * m.E * 4;  // the plan's per-chunk counts
@@ -143,6 +144,7 @@ struct moe_fp8_prefill {
   int32_t* perm = nullptr;
   int32_t* inv = nullptr;
   Tile* small_tiles = nullptr;
+  Tile* narrow_tiles = nullptr;
   Tile* wide_tiles = nullptr;
   int32_t* n_tiles = nullptr;
   int32_t* chunk = nullptr;
@@ -341,13 +343,15 @@ int gemm_grid(const moe_fp8_prefill* h, int64_t max_items, int kind, bool gate_u
 // Most tiles of one pass in each list (the kernels read the real counts).
 int64_t max_tiles(const Dims& m, int64_t P, int kind) {
   if (kind == kGemmStream) return std::min<int64_t>(m.E, P);
-  return P / kWideRows + std::min<int64_t>(m.E, P / (kSmallRows + 1));
+  if (kind == kGemmNarrow) return std::min<int64_t>(m.E, P / (kSmallRows + 1));
+  return P / kWideRows + std::min<int64_t>(m.E, P / (kNarrowRows + 1));
 }
 
 // The gate_up launches of a pass over t rows / P slots whose plan and
 // activations are in the workspace: streaming tiles (experts with 1..16
-// rows), then tiles of up to 256 rows.  after[kind], if given, is recorded
-// after each of the two (also when a launch is skipped for lack of work).
+// rows), 128-row tiles (17..128 rows), then tiles of up to 256 rows.
+// after[kind], if given, is recorded after each of the three (also when a
+// launch is skipped for lack of work).
 hipError_t launch_gate_up_all(moe_fp8_prefill* h, int64_t t, int64_t P, float* gu_dbg, hipStream_t s,
                               hipEvent_t* after = nullptr) {
   const Dims& m = h->m;
@@ -356,7 +360,7 @@ hipError_t launch_gate_up_all(moe_fp8_prefill* h, int64_t t, int64_t P, float* g
                 h->w13, h->s13, h->small_tiles, h->n_tiles, h->hq, h->sh, gu_dbg,
                 h->desc.activation == MOE_ACT_SILU_CLAMPED ? h->desc.activation_limit : 0.0f,
                 h->sxT, t * m.nH * 4, (int32_t)t, (int32_t)P, h->shT};
-  Tile* lists[2] = {h->small_tiles, h->wide_tiles};
+  Tile* lists[3] = {h->small_tiles, h->narrow_tiles, h->wide_tiles};
   for (int kind = kGemmStream; kind <= kGemmWide; ++kind) {
     const int64_t items = max_tiles(m, P, kind) * nb;
     if (items > 0) {
@@ -379,7 +383,7 @@ hipError_t launch_down_all(moe_fp8_prefill* h, int64_t P, hipStream_t s, hipEven
   const int64_t nb = m.H / kBlock, nb2 = (nb + 1) / 2;
   DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2,
               h->small_tiles, h->n_tiles, h->y, h->shT, P * m.nI * 4, (int32_t)P};
-  Tile* lists[2] = {h->small_tiles, h->wide_tiles};
+  Tile* lists[3] = {h->small_tiles, h->narrow_tiles, h->wide_tiles};
   for (int kind = kGemmStream; kind <= kGemmWide; ++kind) {
     const int64_t items = max_tiles(m, P, kind) * (kind == kGemmStream ? nb : nb2);
     if (items > 0) {
@@ -462,7 +466,7 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
     }
     PlanArgs pa{ids_p, (int32_t)t, (int32_t)m.k, (int32_t)m.E, (int32_t)m.kr, (int32_t)m.Er,
                 h->counts, h->offsets, h->perm, h->inv, h->small_tiles,
-                h->wide_tiles, h->n_tiles, h->err, h->chunk};
+                h->narrow_tiles, h->wide_tiles, h->n_tiles, h->err, h->chunk};
     if (launch_plan(pa, s) != hipSuccess) return fail(h);
     if (h->timing && hipEventRecord(ev.ev[1], s) != hipSuccess) return fail(h);
 
@@ -472,7 +476,7 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
 
     if (launch_gate_up_all(h, t, P, nullptr, s, h->timing ? &ev.ev[3] : nullptr) != hipSuccess)
       return fail(h);
-    if (launch_down_all(h, P, s, h->timing ? &ev.ev[5] : nullptr) != hipSuccess) return fail(h);
+    if (launch_down_all(h, P, s, h->timing ? &ev.ev[6] : nullptr) != hipSuccess) return fail(h);
 
     CombineArgs ca{h->y, h->inv, w_p, (int32_t)t, (int32_t)m.k, (int32_t)m.H, (int32_t)m.kr,
                    h->desc.routed_scale, h->desc.out_dtype == MOE_DTYPE_F32 ? 1 : 0,
@@ -609,6 +613,7 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   h->perm = (int32_t*)get(w.perm);
   h->inv = (int32_t*)get(w.inv);
   h->small_tiles = (Tile*)get(w.small_tiles);
+  h->narrow_tiles = (Tile*)get(w.narrow_tiles);
   h->wide_tiles = (Tile*)get(w.wide_tiles);
   h->n_tiles = (int32_t*)get(w.n_tiles);
   h->chunk = (int32_t*)get(w.chunk);
@@ -934,6 +939,7 @@ int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slo
   h->perm = (int32_t*)get(w.perm);
   h->inv = (int32_t*)get(w.inv);
   h->small_tiles = (Tile*)get(w.small_tiles);
+  h->narrow_tiles = (Tile*)get(w.narrow_tiles);
   h->wide_tiles = (Tile*)get(w.wide_tiles);
   h->n_tiles = (int32_t*)get(w.n_tiles);
   h->chunk = (int32_t*)get(w.chunk);

@@ -11,7 +11,8 @@ constexpr int kBlock = 128;          // weight block edge and activation group
 constexpr int kWaves = 4;            // waves per GEMM workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSmallRows = 16;       // experts with <= this many rows use the 1-subtile GEMM
-constexpr int kWideRows = 256;       // rows per tile of the 8-wave GEMMs (experts with > kSmallRows rows)
+constexpr int kNarrowRows = 128;     // experts with kSmallRows < rows <= kNarrowRows: one tile, 3-stage GEMMs
+constexpr int kWideRows = 256;       // rows per tile of the 8-wave GEMMs for experts with more rows
 #ifndef MOE_STREAM_DEPTH
 #define MOE_STREAM_DEPTH 3
 #endif
@@ -54,8 +55,9 @@ struct PlanArgs {
   int32_t* perm;       // [T*k]
   int32_t* inv;        // [T*k]
   Tile* small_tiles;   // [E]
+  Tile* narrow_tiles;  // [E]: experts with kSmallRows < rows <= kNarrowRows, one tile each
   Tile* wide_tiles;    // [T*k/kWideRows + E]: experts with more rows, tiles of <= kWideRows
-  int32_t* n_tiles;    // [2]: small, wide
+  int32_t* n_tiles;    // [3]: small, narrow, wide
   int32_t* err;        // sticky bad-id flag
   int32_t* chunk;      // [ceil(T*k/1024)][E] scratch: per-chunk counts, then first positions
 };
@@ -151,7 +153,7 @@ struct SliceArgs {
 };
 
 // GEMM variants (launch_gate_up / launch_down kind)
-constexpr int kGemmStream = 0, kGemmWide = 1;
+constexpr int kGemmStream = 0, kGemmNarrow = 1, kGemmWide = 2;
 
 // Launchers (return the launch status).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);

@@ -190,11 +190,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_offsets_kernel(PlanArgs a) 
   int total;
   const int off = block_exclusive_scan(n, scan_scratch, &total);
   // each expert's rows go to one list: <= kSmallRows rows one streaming tile,
-  // more rows near-equal tiles of at most kWideRows
+  // <= kNarrowRows one 128-row tile, more rows near-equal tiles of at most
+  // kWideRows
   const int is_small = (n >= 1 && n <= kSmallRows) ? 1 : 0;
-  const int n_wide = n > kSmallRows ? (n + kWideRows - 1) / kWideRows : 0;
-  int n_small_all, n_wide_all;
+  const int is_narrow = (n > kSmallRows && n <= kNarrowRows) ? 1 : 0;
+  const int n_wide = n > kNarrowRows ? (n + kWideRows - 1) / kWideRows : 0;
+  int n_small_all, n_narrow_all, n_wide_all;
   const int small_at = block_exclusive_scan(is_small, scan_scratch, &n_small_all);
+  const int narrow_at = block_exclusive_scan(is_narrow, scan_scratch, &n_narrow_all);
   const int wide_at = block_exclusive_scan(n_wide, scan_scratch, &n_wide_all);
   if (tid < E) {
     a.counts[tid] = n;
@@ -206,6 +209,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_offsets_kernel(PlanArgs a) 
       run += m;
     }
     if (is_small) a.small_tiles[small_at] = Tile{tid, off, n, small_at, 1, 0, 0, 0};
+    if (is_narrow) a.narrow_tiles[narrow_at] = Tile{tid, off, n, narrow_at, 1, 0, 0, 0};
     if (n_wide) {
       // split n rows into n_wide tiles of near-equal size, multiples of 16 rows
       const int per = ((n + n_wide - 1) / n_wide + 15) & ~15;
@@ -219,7 +223,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_offsets_kernel(PlanArgs a) 
   if (tid == 0) {
     a.offsets[E] = total;
     a.n_tiles[0] = n_small_all;
-    a.n_tiles[1] = n_wide_all;
+    a.n_tiles[1] = n_narrow_all;
+    a.n_tiles[2] = n_wide_all;
   }
 }
 
@@ -957,11 +962,314 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
   }
 }
 
+// gate_up for experts with 17..128 rows (one tile each; these stream their
+// weights once and are bound by HBM).  Waves 0-3 compute the same 128-row
+// half as in gate_up_wide_kernel; waves 4-7 only move data, through three
+// LDS stages: block kb + 2 is loaded while block kb is multiplied.  The two
+// producer pairs take turns (pair kb % 2 loads the blocks of its parity and
+// waits for them at the end of the next step), so every wait is a plain
+// vmcnt(0) on the waiting wave's own loads, and the matrix waves never wait
+// on memory.  While the matrix waves quantise one item's h, the producers
+// already fetch the next item's row list, weight scales and first K block,
+// so the weight stream does not stop between items.
+template <bool kDbg>
+__global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpArgs a) {
+  constexpr int BM = kNarrowRows;
+  // one LDS object per stage, indexed only by compile-time stage numbers
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds2[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t w_lds0[kGateUpChunk];
+  __shared__ __attribute__((aligned(1024))) uint8_t w_lds1[kGateUpChunk];
+  __shared__ __attribute__((aligned(1024))) uint8_t w_lds2[kGateUpChunk];
+  __shared__ __attribute__((aligned(256))) float sx_lds0[BM];
+  __shared__ __attribute__((aligned(256))) float sx_lds1[BM];
+  __shared__ __attribute__((aligned(256))) float sx_lds2[BM];
+  __shared__ float ws_lds[2 * kMaxKBlocks];
+  __shared__ int tok_lds[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool mma = wave < 4;  // matrix waves (32-column group wn = wave)
+  const int wn = wave & 3, pair = (wave >> 1) & 1, pw = wave & 1;
+  const int ptid = tid - 256;  // producer thread index
+  const int H = a.H, Ip = a.Ip, nH = H / kBlock, NB = Ip / kBlock;
+  const int n_items = a.n_tiles[0] * NB;
+  const rsrc_t xr = make_rsrc(a.xq, (uint32_t)a.xq_bytes);
+  const rsrc_t sr = make_rsrc(a.sxT, (uint32_t)a.sxT_bytes);
+  auto hslot = [](int rr, int c) __attribute__((always_inline)) { return c ^ (rr & 31) ^ ((c >> 4) << 3); };
+
+  // an item's row list and weight scales into LDS (producer threads)
+  auto load_meta = [&](const Item& it) __attribute__((always_inline)) {
+    if (ptid < BM) tok_lds[ptid] = a.perm[it.p0 + (ptid < it.rows ? ptid : 0)] / a.k;
+    const float* ws = a.s13 + (size_t)(it.e * NB + it.nb) * nH * 2;
+    for (int i = ptid; i < 2 * nH; i += 256) ws_lds[i] = ws[i];
+  };
+  auto wrsrc = [&](const Item& it) __attribute__((always_inline)) {
+    return make_rsrc(a.w13 + (size_t)(it.e * NB + it.nb) * nH * kGateUpChunk, (uint32_t)(nH * kGateUpChunk));
+  };
+  // producer pw of a pair moves the 1 KiB LDS blocks b = 2q + pw: weights
+  // q = 0..15, activation rows 8b .. 8b + 7 for q = 0..7 (lane: row 8b + l/8,
+  // swizzled slot l % 8), row scales 64 pw .. +63; past the last K block the
+  // loads read out of range (zeros)
+  auto issue = [&](auto ST, int kb, rsrc_t wr, int rows) __attribute__((always_inline)) {
+    constexpr int st = decltype(ST)::value;
+    uint8_t* wl = st == 0 ? w_lds0 : (st == 1 ? w_lds1 : w_lds2);
+    uint8_t* al = st == 0 ? a_lds0 : (st == 1 ? a_lds1 : a_lds2);
+    float* sl = st == 0 ? sx_lds0 : (st == 1 ? sx_lds1 : sx_lds2);
+    const bool in = kb < nH;
+    const uint32_t oob = in ? 0u : 0x80000000u;
+    const uint32_t sw = in ? (uint32_t)(kb * kGateUpChunk) : 0u, sa = in ? (uint32_t)(kb * kBlock) : 0u;
+    // lane offsets derived here from an opaque thread id, so that they are
+    // not kept live (and spilled) across the whole item loop
+    int ltid = (int)threadIdx.x;
+    asm volatile("" : "+v"(ltid));
+    const int lane = ltid & 63;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      dma16<0>(wr, wl + (2 * q + pw) * 1024, (uint32_t)((2 * q + pw) * 1024 + lane * 16) | oob, sw);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = (2 * q + pw) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(row);
+      const uint32_t avo = (uint32_t)(tok_lds[row] * H + c * 16) | (row < rows ? 0u : 0x80000000u);
+      dma16<0>(xr, al + (2 * q + pw) * 1024, avo | oob, sa);
+    }
+    const int srow = pw * 64 + lane;
+    const uint32_t svo = (uint32_t)(tok_lds[srow] * 4) | (srow < rows ? 0u : 0x80000000u);
+    dma4(sr, sl + pw * 64, svo | oob, in ? (uint32_t)(kb * a.T * 4) : 0u);
+  };
+
+  int item = item_index(0);
+  if (item >= n_items) return;
+  Item it = item_of(item, NB, a.tiles);
+  if (!mma) load_meta(it);
+  __syncthreads();
+  if (!mma && pair == 0) issue(std::integral_constant<int, 0>{}, 0, wrsrc(it), it.rows);
+
+  for (int r = 0;; ++r) {
+    const int e = it.e, p0 = it.p0, rows = it.rows, nb = it.nb;
+    const int mt = (rows + 15) >> 4;
+    const int next = item_index(r + 1);
+    int etid = (int)threadIdx.x;
+
+    // The two roles run separate loops with the same barriers: the matrix
+    // waves' accumulators are not live in the producers' code, which keeps
+    // both within 256 registers.
+    if (mma) {
+      f32x4 acc[8][4];
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // block kb out of stage s, then the step barrier
+      auto step = [&](auto S, auto MTC, int kb) __attribute__((always_inline)) {
+        constexpr int s = decltype(S)::value, MT = decltype(MTC)::value;
+        if (kb < nH) {
+          // lane offsets re-derived each step from an opaque thread id:
+          // cheaper than keeping them in registers across the K loop
+          int ltid = (int)threadIdx.x;
+          asm volatile("" : "+v"(ltid));
+          const int ll = ltid & 63, lg = (ll >> 4) & 3;
+          const int afc0 = ((2 * lg) ^ swz(ll)) << 4, afc1 = ((2 * lg + 1) ^ swz(ll)) << 4;
+          const float wsg = ws_lds[2 * kb], wsu = ws_lds[2 * kb + 1];
+          const uint8_t* wbuf = (s == 0 ? w_lds0 : (s == 1 ? w_lds1 : w_lds2)) + wn * 8192 + ll * 16;
+          const uint8_t* abuf = (s == 0 ? a_lds0 : (s == 1 ? a_lds1 : a_lds2)) + (ll & 15) * 128;
+          const float* srow = (s == 0 ? sx_lds0 : (s == 1 ? sx_lds1 : sx_lds2)) + lg * 4;
+          i32x8 B[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) B[t] = cat(ld16(wbuf + t * 2048), ld16(wbuf + t * 2048 + 1024));
+          // software pipeline over the subtiles: subtile m's MFMAs run while
+          // the VALU promotes subtile m - 1 (the matrix wave is alone on its
+          // SIMD, so nothing else would fill the MFMA pipe meanwhile)
+          i32x8 A2[2];
+          f32x4 R3[3], P[2][4];
+          A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
+          R3[0] = ld16f(srow);
+          auto promote = [&](auto J) __attribute__((always_inline)) {
+            constexpr int j = decltype(J)::value;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float rs = R3[j % 3][i];
+              const float cg = rs * wsg, cu = rs * wsu;
+              acc[j][0][i] = __builtin_fmaf(P[j & 1][0][i], cg, acc[j][0][i]);
+              acc[j][1][i] = __builtin_fmaf(P[j & 1][1][i], cg, acc[j][1][i]);
+              acc[j][2][i] = __builtin_fmaf(P[j & 1][2][i], cu, acc[j][2][i]);
+              acc[j][3][i] = __builtin_fmaf(P[j & 1][3][i], cu, acc[j][3][i]);
+            }
+            pin_in_place(acc[j]);
+          };
+          static_for<MT>([&](auto M) __attribute__((always_inline)) {
+            constexpr int m = decltype(M)::value;
+            if constexpr (m + 1 < MT) {
+              A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
+              R3[(m + 1) % 3] = ld16f(srow + (m + 1) * 16);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) P[m & 1][t] = mfma_e4m3(A2[m & 1], B[t]);
+            if constexpr (m > 0) promote(std::integral_constant<int, m - 1>{});
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads (next subtile)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          });
+          promote(std::integral_constant<int, MT - 1>{});
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's LDS reads are done
+        ring_barrier();
+      };
+      auto kloop = [&](auto MTC) __attribute__((always_inline)) {
+        for (int kb0 = 0; kb0 < nH; kb0 += 3) {
+          step(std::integral_constant<int, 0>{}, MTC, kb0);
+          step(std::integral_constant<int, 1>{}, MTC, kb0 + 1);
+          step(std::integral_constant<int, 2>{}, MTC, kb0 + 2);
+        }
+      };
+      ring_barrier();  // block 0 has landed
+      if (mt > 4)
+        kloop(std::integral_constant<int, 8>{});
+      else
+        kloop(std::integral_constant<int, 4>{});
+      ring_barrier();  // the producers' last loads have landed
+
+      // epilogue: h in FP32 staged in w_lds1 (rows 0-63) and w_lds2 (rows
+      // 64-127; stage 0 takes the next item's first block meanwhile), then
+      // two matrix threads per row quantise it (16-byte chunk c of row r in
+      // slot c ^ (r % 32) ^ 8 (c / 16), as in gate_up_wide_kernel)
+      asm volatile("" : "+v"(etid));
+      const int ecol = etid & 15, egrp = (etid >> 4) & 3;
+      if constexpr (kDbg) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = m * 16 + egrp * 4 + i;
+            if (m < mt && row < rows) {
+              float* g = a.gu_dbg + (size_t)(p0 + row) * 2 * Ip + nb * kBlock + wn * 32 + ecol;
+              g[0] = acc[m][0][i];
+              g[16] = acc[m][1][i];
+              g[Ip] = acc[m][2][i];
+              g[Ip + 16] = acc[m][3][i];
+            }
+          }
+      }
+      auto act = [&](auto CL) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          if (m < mt) {
+            uint8_t* hb = m < 4 ? w_lds1 : w_lds2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float h0, h1;
+              if constexpr (decltype(CL)::value) {
+                h0 = silu_mul_act(acc[m][0][i], acc[m][2][i], a.act_limit);
+                h1 = silu_mul_act(acc[m][1][i], acc[m][3][i], a.act_limit);
+              } else {
+                h0 = silu_mul(acc[m][0][i], acc[m][2][i]);
+                h1 = silu_mul(acc[m][1][i], acc[m][3][i]);
+              }
+              const int rr = (m & 3) * 16 + egrp * 4 + i;
+              const int c0 = wn * 8 + (ecol >> 2), c1 = c0 + 4;
+              *reinterpret_cast<float*>(hb + rr * 512 + (hslot(rr, c0) << 4) + (ecol & 3) * 4) = h0;
+              *reinterpret_cast<float*>(hb + rr * 512 + (hslot(rr, c1) << 4) + (ecol & 3) * 4) = h1;
+            }
+          }
+        }
+      };
+      if (a.act_limit > 0.0f)
+        act(std::true_type{});
+      else
+        act(std::false_type{});
+      __syncthreads();  // h staged
+      {
+        const int row = etid >> 1, half = etid & 1, rr = row & 63;
+        const uint8_t* hb = (row < 64 ? w_lds1 : w_lds2) + rr * 512;
+        float v[64];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const f32x4 q = ld16f(reinterpret_cast<const float*>(hb + (hslot(rr, half * 16 + j) << 4)));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[4 * j + k] = q[k];
+        }
+        uint32_t mb = 0;
+#pragma unroll
+        for (int k = 0; k < 64; ++k) mb = umax(mb, abs_bits(v[k]));
+        mb = umax(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0xB1, 0xF, 0xF, false));  // the other half
+        const float amax = __uint_as_float(mb);
+        const float sc = __fdiv_rn(amax, 448.0f);
+        uint32_t w[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const uint32_t lo = e4m3_pair(__fdiv_rn(v[4 * k], sc), __fdiv_rn(v[4 * k + 1], sc));
+          const uint32_t hi = e4m3_pair(__fdiv_rn(v[4 * k + 2], sc), __fdiv_rn(v[4 * k + 3], sc));
+          // branch-free: an all-zero row (sc = 0) takes code 0 by the select
+          w[k] = amax != 0.0f ? (lo | (hi << 16)) : 0u;
+        }
+        if (row < rows) {
+          uint8_t* dst = a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + half * 64;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            st16(dst + q * 16, i32x4{(int)w[4 * q], (int)w[4 * q + 1], (int)w[4 * q + 2], (int)w[4 * q + 3]});
+          if (half == 0) {
+            a.sh[(size_t)(p0 + row) * NB + nb] = sc;
+            a.shT[(size_t)nb * a.P + p0 + row] = sc;
+          }
+        }
+      }
+      __syncthreads();  // h read: stages 1-2 are free for the next item
+    } else {
+      // producers: pair kb % 2 loads block kb + 2 into the stage read last
+      // step while the other pair waits for block kb + 1
+      const rsrc_t wr = wrsrc(it);
+      auto pstep = [&](auto S, int kb) __attribute__((always_inline)) {
+        constexpr int s = decltype(S)::value;
+        if (pair == (kb & 1))
+          issue(std::integral_constant<int, (s + 2) % 3>{}, kb + 2, wr, rows);
+        else
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): block kb + 1 has landed
+        ring_barrier();
+      };
+      if (pair == 1)
+        issue(std::integral_constant<int, 1>{}, 1, wr, rows);
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): block 0 has landed
+      ring_barrier();
+      for (int kb0 = 0; kb0 < nH; kb0 += 3) {
+        pstep(std::integral_constant<int, 0>{}, kb0);
+        pstep(std::integral_constant<int, 1>{}, kb0 + 1);
+        pstep(std::integral_constant<int, 2>{}, kb0 + 2);
+      }
+      // the out-of-range loads issued past the last block still write zeros
+      // to their stages: let them land before the stages are reused
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      ring_barrier();
+      // the next item's row list and scales (this item's are no longer read)
+      if (next < n_items) load_meta(item_of(next, NB, a.tiles));
+      __syncthreads();  // h staged; the next item's row list is in LDS
+      if (next < n_items && pair == 0) {
+        const Item nit = item_of(next, NB, a.tiles);
+        issue(std::integral_constant<int, 0>{}, 0, wrsrc(nit), nit.rows);
+      }
+      __syncthreads();
+    }
+    if (next >= n_items) break;
+    item = next;
+    it = item_of(item, NB, a.tiles);
+  }
+}
+
 hipError_t launch_gate_up(const GateUpArgs& a, int kind, int grid, hipStream_t s) {
   if (kind == kGemmWide && a.gu_dbg)
     hipLaunchKernelGGL(gate_up_wide_kernel<true>, dim3(grid), dim3(kWideThreads), 0, s, a);
   else if (kind == kGemmWide)
     hipLaunchKernelGGL(gate_up_wide_kernel<false>, dim3(grid), dim3(kWideThreads), 0, s, a);
+  else if (kind == kGemmNarrow && a.gu_dbg)
+    hipLaunchKernelGGL(gate_up_narrow_kernel<true>, dim3(grid), dim3(kWideThreads), 0, s, a);
+  else if (kind == kGemmNarrow)
+    hipLaunchKernelGGL(gate_up_narrow_kernel<false>, dim3(grid), dim3(kWideThreads), 0, s, a);
   else
     hipLaunchKernelGGL(gate_up_stream_kernel<kStreamDepth>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
@@ -1237,7 +1545,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
 }
 
 hipError_t launch_down(const DownArgs& a, int kind, int grid, hipStream_t s) {
-  if (kind == kGemmWide)
+  if (kind == kGemmWide || kind == kGemmNarrow)
     hipLaunchKernelGGL(down_wide_kernel, dim3(grid), dim3(kWideThreads), 0, s, a);
   else
     hipLaunchKernelGGL(down_stream_kernel<kStreamDepthDown>, dim3(grid), dim3(kThreads), 0, s, a);

@@ -268,11 +268,11 @@ int moe_fp8_prefill_debug_mfma(const uint8_t* a, const uint8_t* b, float* d);
  * every pass records events between its kernel launches; read_timing()
  * synchronises and returns up to max_records rows (one per pass) of
  * MOE_NUM_STAGES milliseconds: plan (with the router in run_logits),
- * quantise, gate_up of experts with 1-16 rows (streaming) and with more
- * rows (256-row tiles), down in the same two groups, combine; then clears
- * the record.  A group with no work in the pass takes the time of an empty
- * stream interval. */
-#define MOE_NUM_STAGES 7
+ * quantise, gate_up of experts with 1-16 rows (streaming), 17-128 rows
+ * (128-row tiles) and more rows (256-row tiles), down in the same three
+ * groups, combine; then clears the record.  A group with no work in the
+ * pass takes the time of an empty stream interval. */
+#define MOE_NUM_STAGES 9
 int moe_fp8_prefill_set_timing(moe_fp8_prefill* h, int32_t enable);
 int moe_fp8_prefill_read_timing(moe_fp8_prefill* h, float* stage_ms, int32_t max_records,
                                 int32_t* n_records);
