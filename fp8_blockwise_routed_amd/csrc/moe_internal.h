@@ -17,7 +17,7 @@ constexpr int kWideRows = 256;       // rows per tile of the 8-wave GEMMs for ex
 #define MOE_STREAM_DEPTH 3
 #endif
 #ifndef MOE_STREAM_DEPTH_DOWN
-#define MOE_STREAM_DEPTH_DOWN 4
+#define MOE_STREAM_DEPTH_DOWN 6
 #endif
 #ifndef MOE_WEIGHT_AUX
 #define MOE_WEIGHT_AUX 2
@@ -26,7 +26,7 @@ constexpr int kWideRows = 256;       // rows per tile of the 8-wave GEMMs for ex
 #define MOE_GU_WG_PER_CU 3
 #endif
 #ifndef MOE_DN_WG_PER_CU
-#define MOE_DN_WG_PER_CU 4
+#define MOE_DN_WG_PER_CU 2
 #endif
 constexpr int kWeightAux = MOE_WEIGHT_AUX;          // cache-policy bits of the weight loads
 constexpr int kGateUpWgPerCu = MOE_GU_WG_PER_CU;  // persistent grid of the streaming gate_up

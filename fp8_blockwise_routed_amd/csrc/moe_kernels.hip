@@ -89,6 +89,23 @@ __device__ __forceinline__ uint32_t e4m3_pair(float v0, float v1) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false) & 0xFFFFu;
 }
 
+// v / sc rounded as an IEEE division rounds it, from the correctly rounded
+// reciprocal y = 1 / sc shared by a whole row: q0 = v y, then one correction
+// with the remainder v - q0 sc, which an FMA gives exactly whenever it is a
+// normal float (Markstein, "Computation of elementary functions on the IBM
+// RISC System/6000 processor", 1990: a correctly rounded reciprocal and a
+// quotient within one ulp give the correctly rounded quotient after one such
+// step).  With sc = amax / 448, |v| <= amax and amax >= 2^-80, a remainder
+// can only be subnormal where |v / sc| is far below 2^-10, whose E4M3 code is
+// +-0 either way, so the codes equal those of the divisions (three operations
+// instead of a division's ten).  A zero remainder keeps q0, so -0 stays -0.
+constexpr float kRowDivMin = 0x1p-80f;  // smaller nonzero amax: divide
+__device__ __forceinline__ float row_div(float v, float sc, float y) {
+  const float q0 = v * y;
+  const float r = __builtin_fmaf(-q0, sc, v);
+  return r == 0.0f ? q0 : __builtin_fmaf(r, y, q0);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
@@ -856,8 +873,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
     ring_barrier();
     // every wave runs the same K loop and barriers; a half with few rows
     // multiplies fewer subtiles
-    // every wave runs the same K loop and barriers; a half with few rows
-    // multiplies fewer subtiles
     if (mtw > 4)
       kloop(std::integral_constant<int, 8>{});
     else if (mtw > 0)
@@ -939,14 +954,20 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
       for (int k = 0; k < 64; ++k) mb = umax(mb, abs_bits(v[k]));
       mb = umax(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0xB1, 0xF, 0xF, false));  // the other half
       const float amax = __uint_as_float(mb);
-      const float sc = __fdiv_rn(amax, 448.0f);
+      const float sc = __fdiv_rn(amax, 448.0f), y = __fdiv_rn(1.0f, sc);
       uint32_t w[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        const uint32_t lo = e4m3_pair(__fdiv_rn(v[4 * k], sc), __fdiv_rn(v[4 * k + 1], sc));
-        const uint32_t hi = e4m3_pair(__fdiv_rn(v[4 * k + 2], sc), __fdiv_rn(v[4 * k + 3], sc));
+        const uint32_t lo = e4m3_pair(row_div(v[4 * k], sc, y), row_div(v[4 * k + 1], sc, y));
+        const uint32_t hi = e4m3_pair(row_div(v[4 * k + 2], sc, y), row_div(v[4 * k + 3], sc, y));
         // branch-free: an all-zero row (sc = 0) takes code 0 by the select
         w[k] = amax != 0.0f ? (lo | (hi << 16)) : 0u;
+      }
+      if (amax != 0.0f && amax < kRowDivMin) {  // tiny rows (never seen in practice): divide
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          w[k] = e4m3_pair(__fdiv_rn(v[4 * k], sc), __fdiv_rn(v[4 * k + 1], sc)) |
+                 (e4m3_pair(__fdiv_rn(v[4 * k + 2], sc), __fdiv_rn(v[4 * k + 3], sc)) << 16);
       }
       if (row < rows) {
         uint8_t* dst = a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + half * 64;
@@ -1199,14 +1220,20 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
         for (int k = 0; k < 64; ++k) mb = umax(mb, abs_bits(v[k]));
         mb = umax(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0xB1, 0xF, 0xF, false));  // the other half
         const float amax = __uint_as_float(mb);
-        const float sc = __fdiv_rn(amax, 448.0f);
+        const float sc = __fdiv_rn(amax, 448.0f), y = __fdiv_rn(1.0f, sc);
         uint32_t w[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          const uint32_t lo = e4m3_pair(__fdiv_rn(v[4 * k], sc), __fdiv_rn(v[4 * k + 1], sc));
-          const uint32_t hi = e4m3_pair(__fdiv_rn(v[4 * k + 2], sc), __fdiv_rn(v[4 * k + 3], sc));
+          const uint32_t lo = e4m3_pair(row_div(v[4 * k], sc, y), row_div(v[4 * k + 1], sc, y));
+          const uint32_t hi = e4m3_pair(row_div(v[4 * k + 2], sc, y), row_div(v[4 * k + 3], sc, y));
           // branch-free: an all-zero row (sc = 0) takes code 0 by the select
           w[k] = amax != 0.0f ? (lo | (hi << 16)) : 0u;
+        }
+        if (amax != 0.0f && amax < kRowDivMin) {  // tiny rows (never seen in practice): divide
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            w[k] = e4m3_pair(__fdiv_rn(v[4 * k], sc), __fdiv_rn(v[4 * k + 1], sc)) |
+                   (e4m3_pair(__fdiv_rn(v[4 * k + 2], sc), __fdiv_rn(v[4 * k + 3], sc)) << 16);
         }
         if (row < rows) {
           uint8_t* dst = a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + half * 64;
@@ -1276,85 +1303,134 @@ hipError_t launch_gate_up(const GateUpArgs& a, int kind, int grid, hipStream_t s
 }
 
 // -------------------------------------------------------------------- down --
-// Streaming down for experts with at most 16 rows; structure as
-// gate_up_stream_kernel (no LDS tile, no barrier in the K loop, D blocks of
-// prefetch), arithmetic as down_kernel.
-template <int D>
-__global__ __launch_bounds__(kThreads, 4) void down_stream_kernel(DownArgs a) {
-  constexpr int BM = kSmallRows;
-  __shared__ float sht[BM][kMaxKBlocks];
-  __shared__ float ws_lds[kMaxKBlocks];
+__device__ __forceinline__ int pick3(int i, int v0, int v1, int v2) { return i == 0 ? v0 : (i == 1 ? v1 : v2); }
 
+// Descriptor of the j-th item (b + j * G) of a streaming workgroup, j clamped
+// to its last item: weight block index e * NB + nb, first row, rows (uniform).
+__device__ __forceinline__ void stream_item(const Tile* tiles, int b, int j, int my_items, int G, int NB, int& wblk,
+                                            int& p0, int& rows) {
+  const int i = b + (j < my_items ? j : my_items - 1) * G;
+  const int t = i / NB;
+  wblk = __builtin_amdgcn_readfirstlane(tiles[t].e * NB + (i - t * NB));
+  p0 = __builtin_amdgcn_readfirstlane(tiles[t].p0);
+  rows = __builtin_amdgcn_readfirstlane(tiles[t].rows);
+}
+
+// Streaming down for experts with at most 16 rows (the HBM-bound regime).
+// The items (tile, 128-column block) of a workgroup form one flat sequence
+// of K steps, and each wave's loads run D - 1 steps ahead of its MFMAs
+// across item boundaries, so a workgroup's weight stream does not drain
+// between items (an item is only Ip / 128 steps long).  No LDS and no
+// barrier: every wave loads its activation fragment, its two weight
+// fragments, the scales of its four rows (from the K-block-major copy) and
+// the step's weight scale straight into registers.  Same MFMA, promotion
+// order and arithmetic as down_wide_kernel.
+//
+// The MFMA side finishes an item at most two items behind the load side
+// when D <= 2 Ip / 128, so the load side keeps the last three items' row
+// ranges for the output stores.
+template <int D>
+__global__ __launch_bounds__(kThreads, kDownWgPerCu) void down_stream_kernel(DownArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int H = a.H, Ip = a.Ip, nI = Ip / kBlock, NB = H / kBlock;
   const int n_items = a.n_tiles[0] * NB;
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  if (b >= n_items) return;
+  const int my_items = (n_items - 1 - b) / G + 1;
+  const int S = my_items * nI;  // K steps of this workgroup
   const rsrc_t hr = make_rsrc(a.hq, (uint32_t)a.hq_bytes);
+  const rsrc_t shr = make_rsrc(a.shT, (uint32_t)a.shT_bytes);
   const uint32_t bvoff = (uint32_t)(wave * 4096 + lane * 16);
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int tile = item / NB, nb = item - tile * NB;
-    const Tile td = a.tiles[tile];
-    const int e = td.e, p0 = td.p0, rows = td.rows;
+  // load side: step gl = item jl, block kbl.  Item descriptors (weight block
+  // e * NB + nb, first row p0, rows): c = current, n = next (prefetched),
+  // 1 and 2 = the two before c (for the MFMA side's stores)
+  int gl = 0, jl = 0, kbl = 0;
+  int c_w, c_p0, c_rows, n_w, n_p0, n_rows, w1 = 0, p1 = 0, r1 = 0, w2 = 0, p2 = 0, r2 = 0;
+  stream_item(a.tiles, b, 0, my_items, G, NB, c_w, c_p0, c_rows);
+  stream_item(a.tiles, b, 1, my_items, G, NB, n_w, n_p0, n_rows);
+  uint32_t avo = (uint32_t)((c_p0 + (col < c_rows ? col : 0)) * Ip + grp * 32);
+  uint32_t sho = (uint32_t)((c_p0 + grp * 4) * 4);
 
-    __syncthreads();  // LDS of the previous item is no longer read
-    {
-      const float* ws = a.s2 + (size_t)(e * NB + nb) * nI;
-      for (int i = tid; i < nI; i += kThreads) ws_lds[i] = ws[i];
-      for (int i = tid; i < BM * nI; i += kThreads) {
-        const int r = i / nI, kb = i - r * nI;
-        sht[r][kb] = a.sh[(size_t)(p0 + (r < rows ? r : 0)) * nI + kb];
-      }
+  i32x8 A[D], B[D][2];
+  f32x4 R[D];
+  float W[D];
+  // the buffer resources are rebuilt per load from the uniform block index
+  // (a resource carried around the loop would be kept in VGPRs)
+  auto load = [&](auto SL) __attribute__((always_inline)) {
+    constexpr int s = decltype(SL)::value;
+    const bool in = gl < S;
+    const uint32_t oob = in ? 0u : 0x80000000u;
+    const uint32_t sa = in ? (uint32_t)(kbl * kBlock) : 0u, so = in ? (uint32_t)(kbl * kDownChunk) : 0u;
+    const rsrc_t wr = make_rsrc(a.w2 + (size_t)c_w * nI * kDownChunk, (uint32_t)(nI * kDownChunk));
+    const rsrc_t sr = make_rsrc(a.s2 + (size_t)c_w * nI, (uint32_t)(nI * 4));
+    A[s] = cat(bload16(hr, avo + oob, sa), bload16(hr, avo + oob, sa + 16));
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      B[s][t] = cat(wload16(wr, bvoff + oob, so + t * 2048), wload16(wr, bvoff + oob, so + t * 2048 + 1024));
+    const uint32_t ss = in ? (uint32_t)(kbl * a.P * 4) : 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) R[s][i] = bloadf(shr, (sho + 4 * i) + oob, ss);
+    W[s] = bloadf(sr, oob, in ? (uint32_t)(kbl * 4) : 0u);
+    // advance the load side
+    ++gl;
+    if (++kbl == nI && gl < S) {
+      kbl = 0;
+      ++jl;
+      w2 = w1, p2 = p1, r2 = r1;
+      w1 = c_w, p1 = c_p0, r1 = c_rows;
+      c_w = n_w, c_p0 = n_p0, c_rows = n_rows;
+      stream_item(a.tiles, b, jl + 1, my_items, G, NB, n_w, n_p0, n_rows);
+      avo = (uint32_t)((c_p0 + (col < c_rows ? col : 0)) * Ip + grp * 32);
+      sho = (uint32_t)((c_p0 + grp * 4) * 4);
     }
-    __syncthreads();
+  };
 
-    const rsrc_t wr = make_rsrc(a.w2 + (size_t)(e * NB + nb) * nI * kDownChunk, (uint32_t)(nI * kDownChunk));
-    const uint32_t avo = (uint32_t)((p0 + (col < rows ? col : 0)) * Ip + grp * 32);
-    i32x8 A[D], B[D][2];
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-
-    // block kb's operands; kb >= nI reads out of range (zeros, no memory access)
-    auto load = [&](int kb, i32x8& af, i32x8(&bf)[2]) {
-      const bool in = kb < nI;
-      const uint32_t oob = in ? 0u : 0x80000000u;
-      const uint32_t so = in ? (uint32_t)(kb * kDownChunk) : 0u;
-      const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
-      af = cat(bload16(hr, avo + oob, sa), bload16(hr, avo + oob, sa + 16));
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        bf[t] = cat(wload16(wr, bvoff + oob, so + t * 2048), wload16(wr, bvoff + oob, so + t * 2048 + 1024));
-    };
-    auto compute = [&](int kb, const i32x8& af, const i32x8(&bf)[2]) {
-      const f32x4 q0 = mfma_e4m3(af, bf[0]);
-      const f32x4 q1 = mfma_e4m3(af, bf[1]);
-      const float wsc = ws_lds[kb];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sc = sht[grp * 4 + i][kb] * wsc;
-        acc[0][i] = __builtin_fmaf(q0[i], sc, acc[0][i]);
-        acc[1][i] = __builtin_fmaf(q1[i], sc, acc[1][i]);
-      }
-    };
-
-#pragma unroll
-    for (int s = 0; s < D - 1; ++s) load(s, A[s], B[s]);
-    for (int kb0 = 0; kb0 < nI; kb0 += D) {
-#pragma unroll
-      for (int s = 0; s < D; ++s) {
-        load(kb0 + s + D - 1, A[(s + D - 1) % D], B[(s + D - 1) % D]);
-        if (kb0 + s < nI) compute(kb0 + s, A[s], B[s]);
-      }
-    }
-
+  // MFMA side: item jc, block kbc
+  int jc = 0, kbc = 0;
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  auto compute = [&](auto SL) __attribute__((always_inline)) {
+    constexpr int s = decltype(SL)::value;
+    const f32x4 q0 = mfma_e4m3(A[s], B[s][0]);
+    const f32x4 q1 = mfma_e4m3(A[s], B[s][1]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = grp * 4 + i;
-      if (r < rows) {
-        float* dst = a.y + (size_t)(p0 + r) * H + nb * kBlock + wave * 32 + col;
-        dst[0] = acc[0][i];
-        dst[16] = acc[1][i];
-      }
+      const float sc = R[s][i] * W[s];
+      acc[0][i] = __builtin_fmaf(q0[i], sc, acc[0][i]);
+      acc[1][i] = __builtin_fmaf(q1[i], sc, acc[1][i]);
     }
+    if (++kbc == nI) {
+      const int lag = jl - jc;  // 0, 1 or 2
+      // (selects of values: a select of the variables' addresses would keep
+      // them all in scratch memory)
+      const int wb = pick3(lag, c_w, w1, w2);
+      const int p0 = pick3(lag, c_p0, p1, p2);
+      const int rows = pick3(lag, c_rows, r1, r2);
+      const int nb = wb % NB;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = grp * 4 + i;
+        if (r < rows) {
+          float* dst = a.y + (size_t)(p0 + r) * H + nb * kBlock + wave * 32 + col;
+          dst[0] = acc[0][i];
+          dst[16] = acc[1][i];
+        }
+        acc[0][i] = 0.f;
+        acc[1][i] = 0.f;
+      }
+      kbc = 0;
+      ++jc;
+    }
+  };
+
+  static_for<D - 1>([&](auto SL) __attribute__((always_inline)) { load(SL); });
+  for (int g0 = 0; g0 < S; g0 += D) {
+    static_for<D>([&](auto SL) __attribute__((always_inline)) {
+      constexpr int s = decltype(SL)::value;
+      load(std::integral_constant<int, (s + D - 1) % D>{});
+      if (g0 + s < S) compute(SL);
+    });
   }
 }
 
@@ -1547,8 +1623,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
 hipError_t launch_down(const DownArgs& a, int kind, int grid, hipStream_t s) {
   if (kind == kGemmWide || kind == kGemmNarrow)
     hipLaunchKernelGGL(down_wide_kernel, dim3(grid), dim3(kWideThreads), 0, s, a);
-  else
+  // the loads may run at most 2 Ip / 128 - 1 steps ahead
+  else if (2 * (a.Ip / kBlock) >= kStreamDepthDown)
     hipLaunchKernelGGL(down_stream_kernel<kStreamDepthDown>, dim3(grid), dim3(kThreads), 0, s, a);
+  else if (a.Ip >= 2 * kBlock)
+    hipLaunchKernelGGL(down_stream_kernel<(kStreamDepthDown < 4 ? kStreamDepthDown : 4)>, dim3(grid), dim3(kThreads), 0, s,
+                       a);
+  else
+    hipLaunchKernelGGL(down_stream_kernel<2>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
