@@ -43,7 +43,7 @@ EXPORTED = (
     "moe_fp8_prefill_debug_activations", "moe_fp8_prefill_debug_intermediates",
     "moe_fp8_prefill_debug_gate_up",
     "moe_fp8_prefill_debug_unpack", "moe_fp8_prefill_debug_mfma", "moe_fp8_prefill_set_timing",
-    "moe_fp8_prefill_read_timing", "moe_fp8_prefill_debug_inject_failure",
+    "moe_fp8_prefill_set_timing_stages", "moe_fp8_prefill_read_timing", "moe_fp8_prefill_debug_inject_failure",
     "moe_fp8_prefill_route", "moe_fp8_prefill_run_logits",
     "moe_fp8_prefill_create_streamed", "moe_fp8_prefill_stage", "moe_fp8_prefill_select_slot",
 )
@@ -98,6 +98,7 @@ def load_library() -> ctypes.CDLL:
         "moe_fp8_prefill_debug_unpack": ([P, I32, P, P, P, P, P, P], ctypes.c_int),
         "moe_fp8_prefill_debug_mfma": ([P, P, P], ctypes.c_int),
         "moe_fp8_prefill_set_timing": ([P, I32], ctypes.c_int),
+        "moe_fp8_prefill_set_timing_stages": ([P, ctypes.c_uint32], ctypes.c_int),
         "moe_fp8_prefill_read_timing": ([P, P, I32, ctypes.POINTER(I32)], ctypes.c_int),
         "moe_fp8_prefill_debug_inject_failure": ([P], ctypes.c_int),
         "moe_fp8_prefill_route": ([P, P, I32, I64, P, P, P], ctypes.c_int),
@@ -326,8 +327,18 @@ def moe_fp8_prefill_set_timing(handle: int, enable: bool) -> None:
            "moe_fp8_prefill_set_timing")
 
 
+def moe_fp8_prefill_set_timing_stages(handle: int, stages) -> None:
+    """Time only the named stages (names from STAGES); an empty list turns timing off."""
+    mask = 0
+    for name in stages:
+        mask |= 1 << STAGES.index(name)
+    _check(load_library().moe_fp8_prefill_set_timing_stages(ctypes.c_void_p(handle), mask),
+           "moe_fp8_prefill_set_timing_stages")
+
+
 def moe_fp8_prefill_read_timing(handle: int, max_records: int = 4096) -> np.ndarray:
-    """[records][MOE_NUM_STAGES] milliseconds, one row per pass, in the order of STAGES."""
+    """[records][MOE_NUM_STAGES] milliseconds, one row per pass, in the order of STAGES
+    (-1 for a stage that was not timed)."""
     buf = np.zeros((max_records, MOE_NUM_STAGES), np.float32)
     n = ctypes.c_int32()
     _check(load_library().moe_fp8_prefill_read_timing(ctypes.c_void_p(handle), _np_ptr(buf),

@@ -117,7 +117,13 @@ int64_t weight_bytes_of(const Dims& m) {
 
 struct StageEvents {
   hipEvent_t ev[MOE_NUM_STAGES + 1];
+  uint32_t mask;  // stages timed in this pass
 };
+
+// Event b sits between stage b - 1 and stage b; it is needed when either is timed.
+bool boundary_needed(uint32_t mask, int b) {
+  return (b > 0 && ((mask >> (b - 1)) & 1u)) || (b < MOE_NUM_STAGES && ((mask >> b) & 1u));
+}
 
 }  // namespace
 
@@ -181,7 +187,7 @@ struct moe_fp8_prefill {
   bool has_last = false;
   int64_t last_T = 0;  // rows of the last pass
   // timing
-  bool timing = false;
+  uint32_t timing = 0;  // mask of timed stages
   std::vector<StageEvents> pending;
   std::vector<StageEvents> free_events;
 };
@@ -350,8 +356,8 @@ int64_t max_tiles(const Dims& m, int64_t P, int kind) {
 // The gate_up launches of a pass over t rows / P slots whose plan and
 // activations are in the workspace: streaming tiles (experts with 1..16
 // rows), 128-row tiles (17..128 rows), then tiles of up to 256 rows.
-// after[kind], if given, is recorded after each of the three (also when a
-// launch is skipped for lack of work).
+// after[kind], if given and not null, is recorded after each of the three
+// (also when a launch is skipped for lack of work).
 hipError_t launch_gate_up_all(moe_fp8_prefill* h, int64_t t, int64_t P, float* gu_dbg, hipStream_t s,
                               hipEvent_t* after = nullptr) {
   const Dims& m = h->m;
@@ -369,7 +375,7 @@ hipError_t launch_gate_up_all(moe_fp8_prefill* h, int64_t t, int64_t P, float* g
       hipError_t e = launch_gate_up(ga, kind, gemm_grid(h, items, kind, true), s);
       if (e != hipSuccess) return e;
     }
-    if (after) {
+    if (after && after[kind]) {
       hipError_t e = hipEventRecord(after[kind], s);
       if (e != hipSuccess) return e;
     }
@@ -392,7 +398,7 @@ hipError_t launch_down_all(moe_fp8_prefill* h, int64_t P, hipStream_t s, hipEven
       hipError_t e = launch_down(da, kind, gemm_grid(h, items, kind, false), s);
       if (e != hipSuccess) return e;
     }
-    if (after) {
+    if (after && after[kind]) {
       hipError_t e = hipEventRecord(after[kind], s);
       if (e != hipSuccess) return e;
     }
@@ -400,14 +406,21 @@ hipError_t launch_down_all(moe_fp8_prefill* h, int64_t P, hipStream_t s, hipEven
   return hipSuccess;
 }
 
+#ifndef MOE_STAGE_EVENT_FLAGS
+#define MOE_STAGE_EVENT_FLAGS hipEventDisableSystemFence
+#endif
+constexpr unsigned kStageEventFlags = MOE_STAGE_EVENT_FLAGS;
+
 int get_stage_events(moe_fp8_prefill* h, StageEvents* out) {
   if (!h->free_events.empty()) {
     *out = h->free_events.back();
     h->free_events.pop_back();
     return MOE_OK;
   }
+  // timing only, on this device: no system-scope release (which would write
+  // the L2 back at every stage boundary and slow the next launch)
   for (int i = 0; i <= MOE_NUM_STAGES; ++i)
-    if (hipEventCreate(&out->ev[i]) != hipSuccess) return MOE_ERR_DEVICE;
+    if (hipEventCreateWithFlags(&out->ev[i], kStageEventFlags) != hipSuccess) return MOE_ERR_DEVICE;
   return MOE_OK;
 }
 
@@ -454,9 +467,13 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
     const int64_t t = (T - r0) < m.max_rows ? (T - r0) : m.max_rows;
     const int64_t P = t * m.k;
     StageEvents ev{};
+    hipEvent_t at[MOE_NUM_STAGES + 1] = {};  // the boundaries this pass records
     if (h->timing) {
       if (get_stage_events(h, &ev) != MOE_OK) return fail(h);
-      if (hipEventRecord(ev.ev[0], s) != hipSuccess) return fail(h);
+      ev.mask = h->timing;
+      for (int b = 0; b <= MOE_NUM_STAGES; ++b)
+        if (boundary_needed(ev.mask, b)) at[b] = ev.ev[b];
+      if (at[0] && hipEventRecord(at[0], s) != hipSuccess) return fail(h);
     }
     const int32_t* ids_p = ids ? ids + r0 * m.kr : h->rids;
     const float* w_p = w ? w + r0 * m.kr : h->rw;
@@ -468,22 +485,21 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
                 h->counts, h->offsets, h->perm, h->inv, h->small_tiles,
                 h->narrow_tiles, h->wide_tiles, h->n_tiles, h->err, h->chunk};
     if (launch_plan(pa, s) != hipSuccess) return fail(h);
-    if (h->timing && hipEventRecord(ev.ev[1], s) != hipSuccess) return fail(h);
+    if (at[1] && hipEventRecord(at[1], s) != hipSuccess) return fail(h);
 
     QuantArgs qa{(const uint16_t*)x + r0 * m.H, (int32_t)t, (int32_t)m.H, h->xq, h->sx, h->sxT};
     if (launch_quant(qa, s) != hipSuccess) return fail(h);
-    if (h->timing && hipEventRecord(ev.ev[2], s) != hipSuccess) return fail(h);
+    if (at[2] && hipEventRecord(at[2], s) != hipSuccess) return fail(h);
 
-    if (launch_gate_up_all(h, t, P, nullptr, s, h->timing ? &ev.ev[3] : nullptr) != hipSuccess)
-      return fail(h);
-    if (launch_down_all(h, P, s, h->timing ? &ev.ev[6] : nullptr) != hipSuccess) return fail(h);
+    if (launch_gate_up_all(h, t, P, nullptr, s, &at[3]) != hipSuccess) return fail(h);
+    if (launch_down_all(h, P, s, &at[6]) != hipSuccess) return fail(h);
 
     CombineArgs ca{h->y, h->inv, w_p, (int32_t)t, (int32_t)m.k, (int32_t)m.H, (int32_t)m.kr,
                    h->desc.routed_scale, h->desc.out_dtype == MOE_DTYPE_F32 ? 1 : 0,
                    (uint8_t*)out + r0 * m.H * out_elem};
     if (launch_combine(ca, s) != hipSuccess) return fail(h);
     if (h->timing) {
-      if (hipEventRecord(ev.ev[MOE_NUM_STAGES], s) != hipSuccess) return fail(h);
+      if (at[MOE_NUM_STAGES] && hipEventRecord(at[MOE_NUM_STAGES], s) != hipSuccess) return fail(h);
       h->pending.push_back(ev);
     }
     h->last_T = t;
@@ -833,7 +849,13 @@ int moe_fp8_prefill_debug_mfma(const uint8_t* a, const uint8_t* b, float* d) {
 
 int moe_fp8_prefill_set_timing(moe_fp8_prefill* h, int32_t enable) {
   if (!h) return MOE_ERR_INVALID_ARG;
-  h->timing = enable != 0;
+  h->timing = enable != 0 ? (1u << MOE_NUM_STAGES) - 1u : 0u;
+  return MOE_OK;
+}
+
+int moe_fp8_prefill_set_timing_stages(moe_fp8_prefill* h, uint32_t stage_mask) {
+  if (!h || (stage_mask >> MOE_NUM_STAGES) != 0) return MOE_ERR_INVALID_ARG;
+  h->timing = stage_mask;
   return MOE_OK;
 }
 
@@ -843,11 +865,13 @@ int moe_fp8_prefill_read_timing(moe_fp8_prefill* h, float* stage_ms, int32_t max
   if (h->failed) return MOE_ERR_FAILED_STATE;
   int32_t n = 0;
   for (auto& s : h->pending) {
-    if (hipEventSynchronize(s.ev[MOE_NUM_STAGES]) != hipSuccess) return fail(h);
+    int last = MOE_NUM_STAGES;
+    while (!boundary_needed(s.mask, last)) --last;
+    if (hipEventSynchronize(s.ev[last]) != hipSuccess) return fail(h);
     if (n < max_records) {
       for (int i = 0; i < MOE_NUM_STAGES; ++i) {
-        float ms = 0.f;
-        if (hipEventElapsedTime(&ms, s.ev[i], s.ev[i + 1]) != hipSuccess) return fail(h);
+        float ms = -1.f;
+        if (((s.mask >> i) & 1u) && hipEventElapsedTime(&ms, s.ev[i], s.ev[i + 1]) != hipSuccess) return fail(h);
         stage_ms[n * MOE_NUM_STAGES + i] = ms;
       }
       ++n;

@@ -274,6 +274,14 @@ int moe_fp8_prefill_debug_mfma(const uint8_t* a, const uint8_t* b, float* d);
  * pass takes the time of an empty stream interval. */
 #define MOE_NUM_STAGES 9
 int moe_fp8_prefill_set_timing(moe_fp8_prefill* h, int32_t enable);
+/* Timing of some stages only: events are recorded just at the boundaries of
+ * the stages whose bit (1 << stage) is set in stage_mask, so a timed loop
+ * can measure one launch with two events per pass instead of ten (each event
+ * costs the stream ~2 us); read_timing() reports -1 for the other stages.
+ * stage_mask 0 turns timing off; set_timing(h, 1) is the mask of all
+ * stages.  Errors: MOE_ERR_INVALID_ARG for a NULL handle or bits at or past
+ * MOE_NUM_STAGES. */
+int moe_fp8_prefill_set_timing_stages(moe_fp8_prefill* h, uint32_t stage_mask);
 int moe_fp8_prefill_read_timing(moe_fp8_prefill* h, float* stage_ms, int32_t max_records,
                                 int32_t* n_records);
 

@@ -245,10 +245,23 @@ def test_stage_timing_records():
         for _ in range(3):
             run(moe, x, ids, w)
         st = pkg.moe_fp8_prefill_read_timing(moe.handle)
+        # only two stages: the others read -1, the two agree with the full record
+        pkg.moe_fp8_prefill_set_timing_stages(moe.handle, ["gate_up_wide", "combine"])
+        for _ in range(2):
+            run(moe, x, ids, w)
+        part = pkg.moe_fp8_prefill_read_timing(moe.handle)
         pkg.moe_fp8_prefill_set_timing(moe.handle, False)
+        run(moe, x, ids, w)
+        none = pkg.moe_fp8_prefill_read_timing(moe.handle)
     finally:
         moe.close()
     assert st.shape == (3, pkg.MOE_NUM_STAGES)
     assert np.all(st >= 0)
     s = dict(zip(pkg.STAGES, st.mean(axis=0)))
     assert s["gate_up_wide"] > s["gate_up_stream"] and s["down_wide"] > s["down_stream"]
+    assert part.shape == (2, pkg.MOE_NUM_STAGES) and none.shape[0] == 0
+    timed = [pkg.STAGES.index("gate_up_wide"), pkg.STAGES.index("combine")]
+    others = [i for i in range(pkg.MOE_NUM_STAGES) if i not in timed]
+    assert np.all(part[:, others] == -1) and np.all(part[:, timed] > 0)
+    gu = part[:, timed[0]].mean()
+    assert 0.5 * s["gate_up_wide"] < gu < 2.0 * s["gate_up_wide"]
