@@ -715,8 +715,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
   // out-of-range loads
   __shared__ __attribute__((aligned(256))) float sx_lds0[2 * BM];
   __shared__ __attribute__((aligned(256))) float sx_lds1[2 * BM];
-  __shared__ float ws_lds[2 * kMaxKBlocks];
-  __shared__ int tok_lds[BM];
+  // row list and weight scales of the current item and of the next one
+  __shared__ float ws_lds[2][2 * kMaxKBlocks];
+  __shared__ int tok_lds[2][BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -726,71 +727,109 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
   const int n_items = a.n_tiles[0] * NB;
   const rsrc_t xr = make_rsrc(a.xq, (uint32_t)a.xq_bytes);
   const rsrc_t sr = make_rsrc(a.sxT, (uint32_t)a.sxT_bytes);
+  const rsrc_t pr = make_rsrc(a.perm, (uint32_t)a.P * 4u);
   // B fragments of the wave: n-tiles g0, g1, u0, u1 of 32-column group wn
   const int w_rd = wn * 8192 + lane * 16;
   // A fragments: rows 128 mh + 16 m + lane % 16 (swz(row) = swz(lane))
   const int afr = (mh * 128 + (lane & 15)) * 128;
   const int afc0 = ((2 * grp) ^ swz(lane)) << 4, afc1 = ((2 * grp + 1) ^ swz(lane)) << 4;
 
+  // An item's slot list (tile rows; the token is slot / k) and weight scales,
+  // straight into LDS buffer buf: waves 0-3 the slots of rows 64w .. + 63,
+  // waves 4-7 weight scales 64 (w - 4) .. + 63 (out of range past 2 nH)
+  auto meta_dma = [&](int buf, const Item& it) __attribute__((always_inline)) {
+    if (wave < 4) {
+      dma4(pr, &tok_lds[buf][wave * 64], (uint32_t)((it.p0 + (tid < it.rows ? tid : 0)) * 4), 0u);
+    } else {
+      const int i = tid - BM;
+      const rsrc_t wsr = make_rsrc(a.s13 + (size_t)(it.e * NB + it.nb) * nH * 2, (uint32_t)(2 * nH * 4));
+      dma4(wsr, &ws_lds[buf][(wave - 4) * 64], (uint32_t)(i * 4) | (i < 2 * nH ? 0u : 0x80000000u), 0u);
+    }
+  };
+  auto wrsrc = [&](const Item& it) __attribute__((always_inline)) {
+    return make_rsrc(a.w13 + (size_t)(it.e * NB + it.nb) * nH * kGateUpChunk, (uint32_t)(nH * kGateUpChunk));
+  };
+  // DMA instruction q of wave w moves LDS block b = 8q + w (1 KiB): rows
+  // 8b .. 8b + 7 of the activation tile (lane: row 8b + l/8, swizzled slot
+  // l % 8) and bytes 1024 b .. of the weight chunk; rows past the tile read
+  // out of range (zeros).  Row scales: waves 0-3 load rows 64w + lane, waves
+  // 4-7 out of range.
+  struct Src {
+    rsrc_t wr;
+    uint32_t avo[4], svo, wlo;
+  };
+  auto src_of = [&](int buf, const Item& it) __attribute__((always_inline)) {
+    Src q;
+    q.wr = wrsrc(it);
+    // lane terms from an opaque thread id: not shared with (and kept live
+    // from) the other call
+    int ltid = (int)threadIdx.x;
+    asm volatile("" : "+v"(ltid));
+    const int lane = ltid & 63;
+    q.wlo = (uint32_t)(lane * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = (j * 8 + wave) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(row);
+      q.avo[j] = (uint32_t)(tok_lds[buf][row] / a.k * H + c * 16) | (row < it.rows ? 0u : 0x80000000u);
+    }
+    const int srow = (wave & 3) * 64 + lane;
+    q.svo = (uint32_t)(tok_lds[buf][srow] / a.k * 4) | (srow < it.rows && wave < 4 ? 0u : 0x80000000u);
+    return q;
+  };
+  // K block kb's loads in two-instruction parts 0-3 (weights, activations)
+  // and part 4 (row scales); past the last block every load
+  // reads out of range (zeros into the unused stage)
+  auto issue_part = [&](auto ST, auto PT, int kb, const Src& q) __attribute__((always_inline)) {
+    constexpr int st = decltype(ST)::value, p = decltype(PT)::value;
+    const bool in = kb < nH;
+    const uint32_t oob = in ? 0u : 0x80000000u;
+    if constexpr (p < 2) {
+      uint8_t* wl = st == 0 ? w_lds0 : w_lds1;
+      const uint32_t sw = in ? (uint32_t)(kb * kGateUpChunk) : 0u;
+#pragma unroll
+      for (int j = 2 * p; j < 2 * p + 2; ++j)
+        dma16<0>(q.wr, wl + (j * 8 + wave) * 1024, ((uint32_t)((j * 8 + wave) * 1024) + q.wlo) | oob, sw);
+    } else if constexpr (p < 4) {
+      uint8_t* al = st == 0 ? a_lds0 : a_lds1;
+      const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
+#pragma unroll
+      for (int j = 2 * (p - 2); j < 2 * (p - 2) + 2; ++j) dma16<0>(xr, al + (j * 8 + wave) * 1024, q.avo[j] | oob, sa);
+    } else {
+      float* sl = st == 0 ? sx_lds0 : sx_lds1;
+      dma4(sr, sl + wave * 64, q.svo | oob, in ? (uint32_t)(kb * a.T * 4) : 0u);
+    }
+  };
+  auto issue = [&](auto ST, int kb, const Src& q) __attribute__((always_inline)) {
+    static_for<5>([&](auto PT) __attribute__((always_inline)) { issue_part(ST, PT, kb, q); });
+  };
+
+  int item = item_index(0);
+  if (item >= n_items) return;
+  Item it = item_of(item, NB, a.tiles);
+  meta_dma(0, it);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  ring_barrier();
+  issue(std::integral_constant<int, 0>{}, 0, src_of(0, it));
+
   for (int r = 0;; ++r) {
-    const int item = item_index(r);
-    if (item >= n_items) break;
-    const Item it = item_of(item, NB, a.tiles);
     const int e = it.e, p0 = it.p0, rows = it.rows, nb = it.nb;
+    const int buf = r & 1;
+    const int next = item_index(r + 1);
+    const bool has_next = next < n_items;
+    const Item nit = item_of(has_next ? next : item, NB, a.tiles);
     // 16-row subtiles of this wave's half that hold rows (wave-uniform)
     const int rows_h = rows - mh * 128 < 0 ? 0 : (rows - mh * 128 > 128 ? 128 : rows - mh * 128);
     const int mtw = (rows_h + 15) >> 4;
 
-    __syncthreads();  // LDS of the previous item is no longer read
-    if (tid < BM) tok_lds[tid] = a.perm[p0 + (tid < rows ? tid : 0)] / a.k;
-    {
-      const float* ws = a.s13 + (size_t)(e * NB + nb) * nH * 2;
-      for (int i = tid; i < 2 * nH; i += kWideThreads) ws_lds[i] = ws[i];
-    }
-    __syncthreads();
-
-    const rsrc_t wr = make_rsrc(a.w13 + (size_t)(e * NB + nb) * nH * kGateUpChunk, (uint32_t)(nH * kGateUpChunk));
-    // DMA instruction q of wave w moves LDS block b = 8q + w (1 KiB): rows
-    // 8b .. 8b + 7 of the activation tile (lane: row 8b + l/8, swizzled slot
-    // l % 8) and bytes 1024 b .. of the weight chunk; rows past the tile read
-    // out of range (zeros)
-    uint32_t avo[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = (q * 8 + wave) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(row);
-      avo[q] = (uint32_t)(tok_lds[row] * H + c * 16) | (row < rows ? 0u : 0x80000000u);
-    }
-    // row scales: waves 0-3 load rows 64w + lane, waves 4-7 out of range
-    const int srow = (wave & 3) * 64 + lane;
-    const uint32_t svo = (uint32_t)(tok_lds[srow] * 4) | (srow < rows && wave < 4 ? 0u : 0x80000000u);
-
-    // K block kb's loads in two-instruction parts 0-3 (weights, activations)
-    // and part 4 (row scales); past the last block every load
-    // reads out of range (zeros into the unused stage)
-    auto issue_part = [&](auto ST, auto PT, int kb) __attribute__((always_inline)) {
-      constexpr int st = decltype(ST)::value, p = decltype(PT)::value;
-      const bool in = kb < nH;
-      const uint32_t oob = in ? 0u : 0x80000000u;
-      if constexpr (p < 2) {
-        uint8_t* wl = st == 0 ? w_lds0 : w_lds1;
-        const uint32_t sw = in ? (uint32_t)(kb * kGateUpChunk) : 0u;
-#pragma unroll
-        for (int q = 2 * p; q < 2 * p + 2; ++q)
-          dma16<0>(wr, wl + (q * 8 + wave) * 1024, (uint32_t)((q * 8 + wave) * 1024 + lane * 16) | oob, sw);
-      } else if constexpr (p < 4) {
-        uint8_t* al = st == 0 ? a_lds0 : a_lds1;
-        const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
-#pragma unroll
-        for (int q = 2 * (p - 2); q < 2 * (p - 2) + 2; ++q) dma16<0>(xr, al + (q * 8 + wave) * 1024, avo[q] | oob, sa);
-      } else {
-        float* sl = st == 0 ? sx_lds0 : sx_lds1;
-        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * a.T * 4) : 0u);
-      }
-    };
-    auto issue = [&](auto ST, int kb) __attribute__((always_inline)) {
-      static_for<5>([&](auto PT) __attribute__((always_inline)) { issue_part(ST, PT, kb); });
-    };
+    // block 0 (issued before the previous epilogue) has landed everywhere,
+    // and the previous item's LDS is no longer read
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    ring_barrier();
+    const Src cur = src_of(buf, it);
+    // the next item's slots and weight scales into the other buffer (they
+    // land with block 1)
+    if (has_next) meta_dma(buf ^ 1, nit);
 
     // acc[m][t]: rows 128 mh + 16 m + 4 grp + i, n-tile t (gate 0-1, up 2-3)
     f32x4 acc[8][4];
@@ -806,9 +845,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
       const int kb = kb0 + s;
       constexpr auto NEXT = std::integral_constant<int, 1 - s>{};
       // without subtiles to interleave with, block kb + 1's loads go first
-      if constexpr (MT == 0) issue(NEXT, kb + 1);
+      if constexpr (MT == 0) issue(NEXT, kb + 1, cur);
       if (MT > 0 && kb < nH) {
-        const float wsg = ws_lds[2 * kb], wsu = ws_lds[2 * kb + 1];
+        const float wsg = ws_lds[buf][2 * kb], wsu = ws_lds[buf][2 * kb + 1];
         const uint8_t* wbuf = (s == 0 ? w_lds0 : w_lds1) + w_rd;
         const uint8_t* abuf = (s == 0 ? a_lds0 : a_lds1) + afr;
         const float* srow = (s == 0 ? sx_lds0 : sx_lds1) + mh * 128 + grp * 4;
@@ -833,9 +872,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
           for (int t = 0; t < 4; ++t) P[t] = mfma_e4m3(A2[m & 1], B[t]);
           static_for<per>([&](auto J) __attribute__((always_inline)) {
             constexpr int q = m * per + decltype(J)::value;
-            if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kb + 1);
+            if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kb + 1, cur);
           });
-          if constexpr (m == 0) issue_part(NEXT, std::integral_constant<int, 4>{}, kb + 1);
+          if constexpr (m == 0) issue_part(NEXT, std::integral_constant<int, 4>{}, kb + 1, cur);
           float cg[4], cu[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -855,7 +894,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
           __builtin_amdgcn_sched_barrier(0);
         });
       } else if constexpr (MT > 0) {
-        issue(NEXT, kb + 1);
+        issue(NEXT, kb + 1, cur);
       }
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block kb + 1 has landed
       ring_barrier();
@@ -867,10 +906,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
         step(std::integral_constant<int, 1>{}, MTC, kb0);
       }
     };
-
-    issue(std::integral_constant<int, 0>{}, 0);
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block 0 has landed
-    ring_barrier();
     // every wave runs the same K loop and barriers; a half with few rows
     // multiplies fewer subtiles
     if (mtw > 4)
@@ -880,10 +915,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
     else
       kloop(std::integral_constant<int, 0>{});
 
-    // epilogue (activation stage 0 is free now: it becomes the h staging tile).
-    // Its lane indices are re-derived from an opaque copy of the thread id,
-    // so the compiler cannot compute epilogue addresses before the K loop
-    // and keep them live (spilled) across it.
+    // The epilogue's lane indices are re-derived from an opaque copy of the
+    // thread id, so the compiler cannot compute epilogue addresses before the
+    // K loop and keep them live (spilled) across it.
     int etid = (int)threadIdx.x;
     asm volatile("" : "+v"(etid));
     const int ecol = etid & 15, egrp = (etid >> 4) & 3;
@@ -902,92 +936,108 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
           }
         }
     }
-    // h = silu(g) * u in FP32, staged in LDS (the four stage buffers, 64 rows
-    // of 512 bytes each), then quantised row by row: thread t takes half t % 2
-    // (64 columns) of row t / 2.  16-byte chunk c of row r sits in slot
-    // c ^ (r % 32) ^ 8 (c / 16): the stores of one instruction (4 rows 4 apart,
-    // 16 columns) and the loads (8 rows x 2 halves) then fill distinct banks.
-    auto hrow = [&](int obj) __attribute__((always_inline)) {
-      return obj == 0 ? a_lds0 : (obj == 1 ? a_lds1 : (obj == 2 ? w_lds0 : w_lds1));
-    };
+    // h = silu(g) * u in FP32, one 128-row half at a time (the half's waves
+    // write it to stage 1: a_lds1 rows 0-63, w_lds1 rows 64-127, 512 bytes
+    // each), then four threads per row quantise it: thread t takes 16-byte
+    // chunks 8 (t % 4) .. + 7 (32 columns) of row t / 4.  Chunk c of row r sits
+    // in slot c ^ (r % 32) ^ 8 (c / 16), so the stores of one instruction (4
+    // rows 4 apart, 16 columns) fill distinct banks.
     auto hslot = [](int rr, int c) __attribute__((always_inline)) { return c ^ (rr & 31) ^ ((c >> 4) << 3); };
+    // h of this wave's rows in registers first (the accumulators die here)
+    float hv[8][4][2];
     auto act = [&](auto CL) __attribute__((always_inline)) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        if (m < mtw) {
-          uint8_t* hb = hrow(mh * 2 + (m >> 2));
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float h0, h1;
-            if constexpr (decltype(CL)::value) {
-              h0 = silu_mul_act(acc[m][0][i], acc[m][2][i], a.act_limit);
-              h1 = silu_mul_act(acc[m][1][i], acc[m][3][i], a.act_limit);
-            } else {
-              h0 = silu_mul(acc[m][0][i], acc[m][2][i]);
-              h1 = silu_mul(acc[m][1][i], acc[m][3][i]);
-            }
-            const int rr = (m & 3) * 16 + egrp * 4 + i;
-            const int c0 = wn * 8 + (ecol >> 2), c1 = c0 + 4;
-            *reinterpret_cast<float*>(hb + rr * 512 + (hslot(rr, c0) << 4) + (ecol & 3) * 4) = h0;
-            *reinterpret_cast<float*>(hb + rr * 512 + (hslot(rr, c1) << 4) + (ecol & 3) * 4) = h1;
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (decltype(CL)::value) {
+            hv[m][i][0] = silu_mul_act(acc[m][0][i], acc[m][2][i], a.act_limit);
+            hv[m][i][1] = silu_mul_act(acc[m][1][i], acc[m][3][i], a.act_limit);
+          } else {
+            hv[m][i][0] = silu_mul(acc[m][0][i], acc[m][2][i]);
+            hv[m][i][1] = silu_mul(acc[m][1][i], acc[m][3][i]);
           }
         }
-      }
     };
     if (a.act_limit > 0.0f)
       act(std::true_type{});
     else
       act(std::false_type{});
-    __syncthreads();
-    {
-      const int row = etid >> 1, half = etid & 1, rr = row & 63;
-      const uint8_t* hb = hrow(__builtin_amdgcn_readfirstlane(etid >> 7)) + rr * 512;
-      float v[64];
+    // Both stages are free (the last step waited for its out-of-range loads
+    // and every wave has passed its barrier): the next item's first K block
+    // goes to stage 0 now, under the rest of this epilogue, which stages h in
+    // stage 1.
+    if (has_next) issue(std::integral_constant<int, 0>{}, 0, src_of(buf ^ 1, nit));
+    for (int half = 0; half < 2 && half * 128 < rows; ++half) {
+      if (mh == half) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const f32x4 q = ld16f(reinterpret_cast<const float*>(hb + (hslot(rr, half * 16 + j) << 4)));
+        for (int m = 0; m < 8; ++m) {
+          if (m < mtw) {
+            uint8_t* hb = m < 4 ? a_lds1 : w_lds1;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[4 * j + k] = q[k];
-      }
-      uint32_t mb = 0;
-#pragma unroll
-      for (int k = 0; k < 64; ++k) mb = umax(mb, abs_bits(v[k]));
-      mb = umax(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0xB1, 0xF, 0xF, false));  // the other half
-      const float amax = __uint_as_float(mb);
-      const float sc = __fdiv_rn(amax, 448.0f), y = __fdiv_rn(1.0f, sc);
-      uint32_t w[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint32_t lo = e4m3_pair(row_div(v[4 * k], sc, y), row_div(v[4 * k + 1], sc, y));
-        const uint32_t hi = e4m3_pair(row_div(v[4 * k + 2], sc, y), row_div(v[4 * k + 3], sc, y));
-        // branch-free: an all-zero row (sc = 0) takes code 0 by the select
-        w[k] = amax != 0.0f ? (lo | (hi << 16)) : 0u;
-      }
-      if (amax != 0.0f && amax < kRowDivMin) {  // tiny rows (never seen in practice): divide
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-          w[k] = e4m3_pair(__fdiv_rn(v[4 * k], sc), __fdiv_rn(v[4 * k + 1], sc)) |
-                 (e4m3_pair(__fdiv_rn(v[4 * k + 2], sc), __fdiv_rn(v[4 * k + 3], sc)) << 16);
-      }
-      if (row < rows) {
-        uint8_t* dst = a.hq + (size_t)(p0 + row) * Ip + nb * kBlock + half * 64;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          st16(dst + q * 16, i32x4{(int)w[4 * q], (int)w[4 * q + 1], (int)w[4 * q + 2], (int)w[4 * q + 3]});
-        if (half == 0) {
-          a.sh[(size_t)(p0 + row) * NB + nb] = sc;
-          a.shT[(size_t)nb * a.P + p0 + row] = sc;
+            for (int i = 0; i < 4; ++i) {
+              const int rr = (m & 3) * 16 + egrp * 4 + i;
+              const int c0 = wn * 8 + (ecol >> 2), c1 = c0 + 4;
+              *reinterpret_cast<float*>(hb + rr * 512 + (hslot(rr, c0) << 4) + (ecol & 3) * 4) = hv[m][i][0];
+              *reinterpret_cast<float*>(hb + rr * 512 + (hslot(rr, c1) << 4) + (ecol & 3) * 4) = hv[m][i][1];
+            }
+          }
         }
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's h stores are done
+      ring_barrier();
+      {
+        const int row = etid >> 2, qt = etid & 3, rr = row & 63;
+        const uint8_t* hb = (__builtin_amdgcn_readfirstlane(etid >> 8) == 0 ? a_lds1 : w_lds1) + rr * 512;
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const f32x4 q = ld16f(reinterpret_cast<const float*>(hb + (hslot(rr, qt * 8 + j) << 4)));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[4 * j + k] = q[k];
+        }
+        uint32_t mb = 0;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) mb = umax(mb, abs_bits(v[k]));
+        // the row's other three quarters: lanes 4 (row % 16) .. + 3
+        mb = umax(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0xB1, 0xF, 0xF, false));
+        mb = umax(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0x4E, 0xF, 0xF, false));
+        const float amax = __uint_as_float(mb);
+        const float sc = __fdiv_rn(amax, 448.0f), y = __fdiv_rn(1.0f, sc);
+        uint32_t w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t lo = e4m3_pair(row_div(v[4 * k], sc, y), row_div(v[4 * k + 1], sc, y));
+          const uint32_t hi = e4m3_pair(row_div(v[4 * k + 2], sc, y), row_div(v[4 * k + 3], sc, y));
+          // branch-free: an all-zero row (sc = 0) takes code 0 by the select
+          w[k] = amax != 0.0f ? (lo | (hi << 16)) : 0u;
+        }
+        if (amax != 0.0f && amax < kRowDivMin) {  // tiny rows (never seen in practice): divide
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            w[k] = e4m3_pair(__fdiv_rn(v[4 * k], sc), __fdiv_rn(v[4 * k + 1], sc)) |
+                   (e4m3_pair(__fdiv_rn(v[4 * k + 2], sc), __fdiv_rn(v[4 * k + 3], sc)) << 16);
+        }
+        const int trow = half * 128 + row;
+        if (trow < rows) {
+          uint8_t* dst = a.hq + (size_t)(p0 + trow) * Ip + nb * kBlock + qt * 32;
+          st16(dst, i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]});
+          st16(dst + 16, i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]});
+          if (qt == 0) {
+            a.sh[(size_t)(p0 + trow) * NB + nb] = sc;
+            a.shT[(size_t)nb * a.P + p0 + trow] = sc;
+          }
+        }
+      }
+      // the staged half has been read before the next one overwrites it
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      ring_barrier();
     }
+    if (!has_next) break;
+    item = next;
+    it = nit;
   }
 }
-
-// gate_up for experts with 17..128 rows (one tile each; these stream their
-// weights once and are bound by HBM).  Waves 0-3 compute the same 128-row
-// half as in gate_up_wide_kernel; waves 4-7 only move data, through three
-// LDS stages: block kb + 2 is loaded while block kb is multiplied.  The two
-// producer pairs take turns (pair kb % 2 loads the blocks of its parity and
 // waits for them at the end of the next step), so every wait is a plain
 // vmcnt(0) on the waiting wave's own loads, and the matrix waves never wait
 // on memory.  While the matrix waves quantise one item's h, the producers
@@ -1448,7 +1498,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
   __shared__ __attribute__((aligned(1024))) uint8_t w_lds1[2 * kDownChunk];
   __shared__ __attribute__((aligned(256))) float s_lds0[2 * BM];
   __shared__ __attribute__((aligned(256))) float s_lds1[2 * BM];
-  __shared__ float ws_lds[2][kMaxKBlocks];
+  // weight scales of blocks nb2 and nb2 + 1, for the current item and the next
+  __shared__ __attribute__((aligned(256))) float ws_lds[2][2][kMaxKBlocks];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1464,67 +1515,96 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
   const int afr = (mh * 128 + (lane & 15)) * 128;
   const int afc0 = ((2 * grp) ^ swz(lane)) << 4, afc1 = ((2 * grp + 1) ^ swz(lane)) << 4;
 
+  // An item's weight scales straight into LDS buffer buf: waves 0-1 block
+  // nb2, waves 2-3 block nb2 + 1 (out of range when it is missing or past nI)
+  auto ws_dma = [&](int buf, const Item& it) __attribute__((always_inline)) {
+    if (wave < 4) {
+      const int nb2 = it.nb * 2, hb = wave >> 1, i = (wave & 1) * 64 + lane;
+      const bool ok = i < nI && nb2 + hb < NB;
+      const rsrc_t wsr = make_rsrc(a.s2 + (size_t)(it.e * NB + nb2) * nI, (uint32_t)(2 * nI * 4));
+      dma4(wsr, &ws_lds[buf][hb][(wave & 1) * 64], (uint32_t)((hb * nI + i) * 4) | (ok ? 0u : 0x80000000u), 0u);
+    }
+  };
+  // DMA sources of an item: LDS block b = 8q + w (1 KiB) of instruction q
+  // of wave w; blocks nb2 and nb2 + 1 are nI * kDownChunk bytes apart and a
+  // missing second block reads out of range
+  struct Src {
+    rsrc_t wr;
+    uint32_t wvo[4], avo[4], svo;
+  };
+  auto src_of = [&](const Item& it) __attribute__((always_inline)) {
+    Src q;
+    const int nb2 = it.nb * 2;
+    const bool two = nb2 + 1 < NB;
+    const int wblk = __builtin_amdgcn_readfirstlane(it.e * NB + nb2);
+    const int wbytes = __builtin_amdgcn_readfirstlane((two ? 2 : 1) * nI * kDownChunk);
+    q.wr = make_rsrc(a.w2 + (size_t)wblk * nI * kDownChunk, (uint32_t)wbytes);
+    // lane terms from an opaque thread id: not shared with (and kept live
+    // from) the other call
+    int ltid = (int)threadIdx.x;
+    asm volatile("" : "+v"(ltid));
+    const int ln = ltid & 63;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = j * 8 + wave;
+      q.wvo[j] = (uint32_t)((b >> 4) * nI * kDownChunk + (b & 15) * 1024 + ln * 16);
+      const int row = b * 8 + (ln >> 3);
+      const int c = (ln & 7) ^ swz(row);
+      q.avo[j] = (uint32_t)((it.p0 + (row < it.rows ? row : 0)) * Ip + c * 16) | (row < it.rows ? 0u : 0x80000000u);
+    }
+    const int srow = (wave & 3) * 64 + ln;
+    q.svo = (uint32_t)((it.p0 + (srow < it.rows ? srow : 0)) * 4) | (srow < it.rows && wave < 4 ? 0u : 0x80000000u);
+    return q;
+  };
+  // loads of K block kb in parts, as in gate_up_wide_kernel
+  auto issue_part = [&](auto ST, auto PT, int kb, const Src& q) __attribute__((always_inline)) {
+    constexpr int st = decltype(ST)::value, p = decltype(PT)::value;
+    const bool in = kb < nI;
+    const uint32_t oob = in ? 0u : 0x80000000u;
+    if constexpr (p < 2) {
+      uint8_t* wl = st == 0 ? w_lds0 : w_lds1;
+      const uint32_t sw = in ? (uint32_t)(kb * kDownChunk) : 0u;
+#pragma unroll
+      for (int j = 2 * p; j < 2 * p + 2; ++j) dma16<0>(q.wr, wl + (j * 8 + wave) * 1024, q.wvo[j] | oob, sw);
+    } else if constexpr (p < 4) {
+      uint8_t* al = st == 0 ? a_lds0 : a_lds1;
+      const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
+#pragma unroll
+      for (int j = 2 * (p - 2); j < 2 * (p - 2) + 2; ++j) dma16<0>(hr, al + (j * 8 + wave) * 1024, q.avo[j] | oob, sa);
+    } else {
+      float* sl = st == 0 ? s_lds0 : s_lds1;
+      dma4(sr, sl + wave * 64, q.svo | oob, in ? (uint32_t)(kb * a.P * 4) : 0u);
+    }
+  };
+  auto issue = [&](auto ST, int kb, const Src& q) __attribute__((always_inline)) {
+    static_for<5>([&](auto PT) __attribute__((always_inline)) { issue_part(ST, PT, kb, q); });
+  };
+
+  int item = item_index(0);
+  if (item >= n_items) return;
+  Item it = item_of(item, NB2, a.tiles);
+  ws_dma(0, it);
+  issue(std::integral_constant<int, 0>{}, 0, src_of(it));
+
   for (int r = 0;; ++r) {
-    const int item = item_index(r);
-    if (item >= n_items) break;
-    const Item it = item_of(item, NB2, a.tiles);
+    const int buf = r & 1;
+    const int next = item_index(r + 1);
+    const bool has_next = next < n_items;
+    const Item nit = item_of(has_next ? next : item, NB2, a.tiles);
     const int nb2 = it.nb * 2;
     const bool two = nb2 + 1 < NB;  // second weight block present
-    const int e = it.e, p0 = it.p0, rows = it.rows;
+    const int p0 = it.p0, rows = it.rows;
     const int rows_h = rows - mh * 128 < 0 ? 0 : (rows - mh * 128 > 128 ? 128 : rows - mh * 128);
     const int mtw = (half == 1 && !two) ? 0 : (rows_h + 15) >> 4;
 
-    __syncthreads();  // LDS of the previous item is no longer read
-    {
-      const float* ws = a.s2 + (size_t)(e * NB + nb2) * nI;
-      for (int i = tid; i < nI; i += kWideThreads) {
-        ws_lds[0][i] = ws[i];
-        ws_lds[1][i] = two ? ws[nI + i] : 0.f;
-      }
-    }
-    __syncthreads();
-
-    // blocks nb2 and nb2 + 1 are nI * kDownChunk bytes apart; a missing
-    // second block reads out of range
-    const int wblk = __builtin_amdgcn_readfirstlane(e * NB + nb2);
-    const int wbytes = __builtin_amdgcn_readfirstlane((two ? 2 : 1) * nI * kDownChunk);
-    const rsrc_t wr = make_rsrc(a.w2 + (size_t)wblk * nI * kDownChunk, (uint32_t)wbytes);
-    uint32_t wvo[4], avo[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int b = q * 8 + wave;  // LDS block of instruction q (1 KiB)
-      wvo[q] = (uint32_t)((b >> 4) * nI * kDownChunk + (b & 15) * 1024 + lane * 16);
-      const int row = b * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(row);
-      avo[q] = (uint32_t)((p0 + (row < rows ? row : 0)) * Ip + c * 16) | (row < rows ? 0u : 0x80000000u);
-    }
-    const int srow = (wave & 3) * 64 + lane;
-    const uint32_t svo =
-        (uint32_t)((p0 + (srow < rows ? srow : 0)) * 4) | (srow < rows && wave < 4 ? 0u : 0x80000000u);
-
-    // loads of K block kb in parts, as in gate_up_wide_kernel
-    auto issue_part = [&](auto ST, auto PT, int kb) __attribute__((always_inline)) {
-      constexpr int st = decltype(ST)::value, p = decltype(PT)::value;
-      const bool in = kb < nI;
-      const uint32_t oob = in ? 0u : 0x80000000u;
-      if constexpr (p < 2) {
-        uint8_t* wl = st == 0 ? w_lds0 : w_lds1;
-        const uint32_t sw = in ? (uint32_t)(kb * kDownChunk) : 0u;
-#pragma unroll
-        for (int q = 2 * p; q < 2 * p + 2; ++q) dma16<0>(wr, wl + (q * 8 + wave) * 1024, wvo[q] | oob, sw);
-      } else if constexpr (p < 4) {
-        uint8_t* al = st == 0 ? a_lds0 : a_lds1;
-        const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
-#pragma unroll
-        for (int q = 2 * (p - 2); q < 2 * (p - 2) + 2; ++q) dma16<0>(hr, al + (q * 8 + wave) * 1024, avo[q] | oob, sa);
-      } else {
-        float* sl = st == 0 ? s_lds0 : s_lds1;
-        dma4(sr, sl + wave * 64, svo | oob, in ? (uint32_t)(kb * a.P * 4) : 0u);
-      }
-    };
-    auto issue = [&](auto ST, int kb) __attribute__((always_inline)) {
-      static_for<5>([&](auto PT) __attribute__((always_inline)) { issue_part(ST, PT, kb); });
-    };
+    // block 0 and the weight scales (issued before the previous item's
+    // stores) have landed everywhere, and the previous item's LDS is no
+    // longer read
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    ring_barrier();
+    const Src cur = src_of(it);
+    // the next item's weight scales into the other buffer (they land with block 1)
+    if (has_next) ws_dma(buf ^ 1, nit);
 
     f32x4 acc[8][4];
 #pragma unroll
@@ -1536,9 +1616,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
       constexpr int s = decltype(S)::value, MT = decltype(MTC)::value;
       const int kb = kb0 + s;
       constexpr auto NEXT = std::integral_constant<int, 1 - s>{};
-      if constexpr (MT == 0) issue(NEXT, kb + 1);
+      if constexpr (MT == 0) issue(NEXT, kb + 1, cur);
       if (MT > 0 && kb < nI) {
-        const float wsc = ws_lds[half][kb];
+        const float wsc = ws_lds[buf][half][kb];
         const uint8_t* wbuf = (s == 0 ? w_lds0 : w_lds1) + w_rd;
         const uint8_t* abuf = (s == 0 ? a_lds0 : a_lds1) + afr;
         const float* srw = (s == 0 ? s_lds0 : s_lds1) + mh * 128 + grp * 4;
@@ -1561,9 +1641,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
           for (int t = 0; t < 4; ++t) Q[t] = mfma_e4m3(A2[m & 1], B[t]);
           static_for<per>([&](auto J) __attribute__((always_inline)) {
             constexpr int q = m * per + decltype(J)::value;
-            if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kb + 1);
+            if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kb + 1, cur);
           });
-          if constexpr (m == 0) issue_part(NEXT, std::integral_constant<int, 4>{}, kb + 1);
+          if constexpr (m == 0) issue_part(NEXT, std::integral_constant<int, 4>{}, kb + 1, cur);
           float sc[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) sc[i] = R2[m & 1][i] * wsc;
@@ -1580,7 +1660,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
           __builtin_amdgcn_sched_barrier(0);
         });
       } else if constexpr (MT > 0) {
-        issue(NEXT, kb + 1);
+        issue(NEXT, kb + 1, cur);
       }
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block kb + 1 has landed
       ring_barrier();
@@ -1592,10 +1672,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
         step(std::integral_constant<int, 1>{}, MTC, kb0);
       }
     };
-
-    issue(std::integral_constant<int, 0>{}, 0);
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block 0 has landed
-    ring_barrier();
     if (mtw > 4)
       kloop(std::integral_constant<int, 8>{});
     else if (mtw > 0)
@@ -1603,20 +1679,31 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
     else
       kloop(std::integral_constant<int, 0>{});
 
+    // Both stages are free (the last step waited for its out-of-range loads
+    // and every wave has passed its barrier): the next item's first K block
+    // goes to stage 0 before this item's y rows are stored from registers.
+    if (has_next) issue(std::integral_constant<int, 0>{}, 0, src_of(nit));
+
+    int etid = (int)threadIdx.x;
+    asm volatile("" : "+v"(etid));
+    const int ecol = etid & 15, egrp = (etid >> 4) & 3;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       if (m < mtw) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = mh * 128 + m * 16 + grp * 4 + i;
+          const int row = mh * 128 + m * 16 + egrp * 4 + i;
           if (row < rows) {
-            float* dst = a.y + (size_t)(p0 + row) * H + (nb2 + half) * kBlock + (wn & 1) * 64 + col;
+            float* dst = a.y + (size_t)(p0 + row) * H + (nb2 + half) * kBlock + (wn & 1) * 64 + ecol;
 #pragma unroll
             for (int t = 0; t < 4; ++t) dst[t * 16] = acc[m][t][i];
           }
         }
       }
     }
+    if (!has_next) break;
+    item = next;
+    it = nit;
   }
 }
 
