@@ -36,6 +36,7 @@ FAULTS = {
     "route_all_experts": 14,
     "shared_inside_rho": 15,
     "slice_scale_block": 16,
+    "a16_h_truncate": 17,
 }
 
 ROUTE_SOFTMAX = 0
@@ -65,7 +66,7 @@ class _Layer(ctypes.Structure):
 
 class _Debug(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("xq", "sx", "gu", "hq", "sh", "y", "counts", "offsets", "perm", "inv")]
+                ("xq", "sx", "gu", "hq", "sh", "y", "counts", "offsets", "perm", "inv", "hb")]
 
 
 def _load():
@@ -91,6 +92,8 @@ def _load():
                                     ctypes.c_float, ctypes.c_int32, P, ctypes.POINTER(_Debug),
                                     ctypes.c_int32]
         lib.orc_forward.restype = ctypes.c_int64
+        lib.orc_forward_a16.argtypes = lib.orc_forward.argtypes
+        lib.orc_forward_a16.restype = ctypes.c_int64
         lib.orc_down_combine.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int32, P, P, P, P,
                                          ctypes.c_int64, ctypes.c_float, ctypes.c_int32, P, P,
                                          ctypes.c_int32]
@@ -240,11 +243,12 @@ def _layer_struct(layer):
 
 
 def forward(layer, x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, rho: float,
-            out_dtype: int = OUT_BF16, debug: bool = False, n_shared: int = 0):
+            out_dtype: int = OUT_BF16, debug: bool = False, n_shared: int = 0, a16: bool = False):
     """The layer on T tokens.  Returns out (u16 bf16 bits or f32 [T][H]) and,
     with debug=True, a dict of the intermediate arrays (sorted-order rows).
     n_shared: the last n_shared columns of ids / w are shared-expert slots,
-    added outside rho."""
+    added outside rho.  a16: the W8A16 form (x and h stay 16-bit; debug then
+    has hb, h as BF16 bits, instead of xq / sx / hq / sh)."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     w = np.ascontiguousarray(w, dtype=np.float32)
@@ -262,11 +266,15 @@ def forward(layer, x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, rho: floa
                  sh=np.empty((routed, Ip // 128), np.float32), y=np.empty((routed, H), np.float32),
                  counts=np.empty(E, np.int32), offsets=np.empty(E + 1, np.int32),
                  perm=np.empty(max(routed, 1), np.int32), inv=np.empty(max(T * k, 1), np.int32))
-        dbg = _Debug(*(d[n].ctypes.data for n in
-                       ("xq", "sx", "gu", "hq", "sh", "y", "counts", "offsets", "perm", "inv")))
-    bad = _load().orc_forward(ctypes.byref(st), k, _p(x_bits), _p(ids), _p(w), T, float(rho),
-                              out_dtype, _p(out), ctypes.byref(dbg) if dbg is not None else None,
-                              n_shared)
+        if a16:
+            d["hb"] = np.empty((routed, Ip), np.uint16)
+            for n in ("xq", "sx", "hq", "sh"):
+                del d[n]
+        dbg = _Debug(*(d[n].ctypes.data if n in d else None for n in
+                       ("xq", "sx", "gu", "hq", "sh", "y", "counts", "offsets", "perm", "inv", "hb")))
+    fn = _load().orc_forward_a16 if a16 else _load().orc_forward
+    bad = fn(ctypes.byref(st), k, _p(x_bits), _p(ids), _p(w), T, float(rho),
+             out_dtype, _p(out), ctypes.byref(dbg) if dbg is not None else None, n_shared)
     del keep
     if bad < 0:
         raise ValueError("bad arguments")
@@ -276,6 +284,12 @@ def forward(layer, x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, rho: floa
         d["n_bad"] = int(bad)
         return out, d
     return out
+
+
+def forward_a16(layer, x_bits, ids, w, rho, out_dtype: int = OUT_BF16, debug: bool = False,
+                n_shared: int = 0):
+    """The W8A16 form of forward (see orc_forward_a16 in oracle.c)."""
+    return forward(layer, x_bits, ids, w, rho, out_dtype, debug, n_shared, a16=True)
 
 
 def down_combine(layer, hq: np.ndarray, sh: np.ndarray, ids: np.ndarray, w: np.ndarray, rho: float,

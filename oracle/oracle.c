@@ -24,6 +24,7 @@
  * where Q is dynamic E4M3 quantisation per row and per 128-column group and
  * every matrix product is a sum over 128-wide K blocks of an FP32 dot of
  * decoded codes times (activation scale * weight block scale).
+ * orc_forward_a16 is the W8A16 form of the same layer (see forward_impl).
  *
  * parity pins: see tests/test_oracle_*.py.  Every function below is pinned
  * there against something other than itself.
@@ -55,6 +56,7 @@ enum {
   FAULT_ROUTE_ALL_EXPERTS = 14, /* softmax weights normalised over all E     */
   FAULT_SHARED_INSIDE_RHO = 15, /* shared slots scaled by rho too            */
   FAULT_SLICE_SCALE_BLOCK = 16, /* requant reads the next checkpoint block's scale */
+  FAULT_A16_H_TRUNCATE = 17,    /* W8A16: h to BF16 by truncation, not RNE   */
 };
 static int g_fault = FAULT_NONE;
 void orc_set_fault(int32_t f) { g_fault = f; }
@@ -231,7 +233,9 @@ typedef struct {
  * per-slot arrays are in sorted (plan) order; P = number of routed slots.
  * xq u8[T][H], sx f32[T][H/128], gu f32[P][2*Ip] (gate then up),
  * hq u8[P][Ip], sh f32[P][Ip/128], y f32[P][H],
- * counts i32[E], offsets i32[E+1], perm i32[T*k], inv i32[T*k]. */
+ * counts i32[E], offsets i32[E+1], perm i32[T*k], inv i32[T*k],
+ * hb u16[P][Ip] (W8A16 only: h as BF16 bits; xq, sx, hq, sh are not
+ * written in that mode). */
 typedef struct {
   uint8_t* xq;
   float* sx;
@@ -243,6 +247,7 @@ typedef struct {
   int32_t* offsets;
   int32_t* perm;
   int32_t* inv;
+  uint16_t* hb;
 } orc_debug;
 
 /* Padded gate/up row n in [0, 2*Ip) of expert e as codes (gate rows first);
@@ -364,12 +369,20 @@ static void down_and_combine(const orc_layer* L, int64_t k, const float* hd, con
  * out_dtype 0: out is bf16 bits u16[T][H]; 1: out is f32[T][H].
  * n_shared: the last n_shared slots of each token are shared-expert slots
  * (see down_and_combine); 0 for the routed layer alone.
+ * a16 = 0: W8A8 as stated at the top of this file.  a16 = 1: W8A16, the
+ * pages' path for decode and short continuations ("ktransformers #2244",
+ * Design: prefill of at least 256 tokens uses W8A8 on the GPU, shorter
+ * continuations and decode use W8A16): the activations entering each GEMM
+ * stay 16-bit, i.e. x as given (BF16, exact in FP32) and h = silu(g) * u
+ * rounded to BF16 (round to nearest even); every block product is then the
+ * FP32 dot of the activations and the decoded weight codes times the weight
+ * block scale (the activation scale of the W8A8 form is 1).
  * Returns the number of bad expert ids (those slots are skipped), or -1 on a
  * bad argument.
  */
-int64_t orc_forward(const orc_layer* L, int32_t k, const uint16_t* x, const int32_t* ids,
-                    const float* w, int64_t T, float rho, int32_t out_dtype, void* out,
-                    const orc_debug* dbg, int32_t n_shared) {
+static int64_t forward_impl(const orc_layer* L, int32_t k, const uint16_t* x, const int32_t* ids,
+                            const float* w, int64_t T, float rho, int32_t out_dtype, void* out,
+                            const orc_debug* dbg, int32_t n_shared, int32_t a16) {
   const int64_t E = L->E, H = L->H, I = L->I;
   if (E < 1 || k < 1 || H % 128 != 0 || I < 1 || T < 0 || n_shared < 0 || n_shared >= k) return -1;
   const int64_t Ip = 128 * ((I + 127) / 128), nH = H / 128, nI = Ip / 128;
@@ -380,9 +393,13 @@ int64_t orc_forward(const orc_layer* L, int32_t k, const uint16_t* x, const int3
   uint8_t* xq = (uint8_t*)malloc((size_t)(T * H + 1));
   float* sx = (float*)malloc(sizeof(float) * (size_t)(T * nH + 1));
   for (int64_t i = 0; i < T * H; ++i) xf[i] = orc_bf16_to_f32(x[i]);
-  orc_quantize_rows(xf, T, H, xq, sx);
-  float* xd = xf; /* reuse: decoded codes of xq */
-  for (int64_t i = 0; i < T * H; ++i) xd[i] = orc_e4m3_decode(xq[i]);
+  float* xd = xf; /* the activations of the first GEMM */
+  if (a16) {
+    for (int64_t i = 0; i < T * nH; ++i) sx[i] = 1.0f;
+  } else {
+    orc_quantize_rows(xf, T, H, xq, sx);
+    for (int64_t i = 0; i < T * H; ++i) xd[i] = orc_e4m3_decode(xq[i]); /* decoded codes of xq */
+  }
 
   /* plan */
   int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
@@ -420,19 +437,38 @@ int64_t orc_forward(const orc_layer* L, int32_t k, const uint16_t* x, const int3
     for (int64_t i = 0; i < Ip; ++i) h[p * Ip + i] = silu_mul(gu[p * 2 * Ip + i], gu[p * 2 * Ip + Ip + i]);
   uint8_t* hq = (uint8_t*)malloc((size_t)(P * Ip + 1));
   float* sh = (float*)malloc(sizeof(float) * (size_t)(P * nI + 1));
-  orc_quantize_rows(h, P, Ip, hq, sh);
-  float* hd = h; /* reuse: decoded codes of hq */
-  for (int64_t i = 0; i < P * Ip; ++i) hd[i] = orc_e4m3_decode(hq[i]);
+  uint16_t* hb = NULL;
+  float* hd = h; /* the activations of the second GEMM */
+  if (a16) {
+    hb = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(P * Ip + 1));
+    for (int64_t i = 0; i < P * Ip; ++i) {
+      uint32_t b;
+      if (g_fault == FAULT_A16_H_TRUNCATE) {
+        uint32_t u;
+        memcpy(&u, &h[i], 4);
+        b = u >> 16;
+      } else {
+        b = orc_f32_to_bf16(h[i]);
+      }
+      hb[i] = (uint16_t)b;
+      hd[i] = orc_bf16_to_f32(b);
+    }
+    for (int64_t i = 0; i < P * nI; ++i) sh[i] = 1.0f;
+  } else {
+    orc_quantize_rows(h, P, Ip, hq, sh);
+    for (int64_t i = 0; i < P * Ip; ++i) hd[i] = orc_e4m3_decode(hq[i]); /* decoded codes of hq */
+  }
 
   float* y = (float*)malloc(sizeof(float) * (size_t)(P * H + 1));
   down_and_combine(L, k, hd, sh, counts, offsets, inv, w, T, rho, out_dtype, out, y, n_shared);
 
   if (dbg) {
-    if (dbg->xq) memcpy(dbg->xq, xq, (size_t)(T * H));
-    if (dbg->sx) memcpy(dbg->sx, sx, sizeof(float) * (size_t)(T * nH));
+    if (dbg->xq && !a16) memcpy(dbg->xq, xq, (size_t)(T * H));
+    if (dbg->sx && !a16) memcpy(dbg->sx, sx, sizeof(float) * (size_t)(T * nH));
     if (dbg->gu) memcpy(dbg->gu, gu, sizeof(float) * (size_t)(P * 2 * Ip));
-    if (dbg->hq) memcpy(dbg->hq, hq, (size_t)(P * Ip));
-    if (dbg->sh) memcpy(dbg->sh, sh, sizeof(float) * (size_t)(P * nI));
+    if (dbg->hq && !a16) memcpy(dbg->hq, hq, (size_t)(P * Ip));
+    if (dbg->sh && !a16) memcpy(dbg->sh, sh, sizeof(float) * (size_t)(P * nI));
+    if (dbg->hb && a16) memcpy(dbg->hb, hb, sizeof(uint16_t) * (size_t)(P * Ip));
     if (dbg->y) memcpy(dbg->y, y, sizeof(float) * (size_t)(P * H));
     if (dbg->counts) memcpy(dbg->counts, counts, sizeof(int32_t) * (size_t)E);
     if (dbg->offsets) memcpy(dbg->offsets, offsets, sizeof(int32_t) * (size_t)(E + 1));
@@ -449,9 +485,22 @@ int64_t orc_forward(const orc_layer* L, int32_t k, const uint16_t* x, const int3
   free(gu);
   free(h);
   free(hq);
+  free(hb);
   free(sh);
   free(y);
   return bad;
+}
+
+int64_t orc_forward(const orc_layer* L, int32_t k, const uint16_t* x, const int32_t* ids,
+                    const float* w, int64_t T, float rho, int32_t out_dtype, void* out,
+                    const orc_debug* dbg, int32_t n_shared) {
+  return forward_impl(L, k, x, ids, w, T, rho, out_dtype, out, dbg, n_shared, 0);
+}
+
+int64_t orc_forward_a16(const orc_layer* L, int32_t k, const uint16_t* x, const int32_t* ids,
+                        const float* w, int64_t T, float rho, int32_t out_dtype, void* out,
+                        const orc_debug* dbg, int32_t n_shared) {
+  return forward_impl(L, k, x, ids, w, T, rho, out_dtype, out, dbg, n_shared, 1);
 }
 
 /* ---- brute force B (FP64, dense over experts, tiny inputs only) --------- */

@@ -515,6 +515,61 @@ def pin_activation_from_gu():
     return _ok(err <= 1e-2, f"worst rel L2 {err:.3g}")
 
 
+def pin_a16_vs_bruteforce(tol=4e-3):
+    """The W8A16 form against the dense FP64 evaluation without activation
+    quantisation.  tol = 2 x 2^-9: the BF16 rounding of h (relative error at
+    most 2^-9 per element, which the FP64 evaluation does not apply), doubled
+    for the FP32 sums; W8A8 is ~5e-2 away on the same cases."""
+    worst = 0.0
+    for case in SMALL_CASES:
+        layer, x, ids, w, rho = small_case(case)
+        out = oracle.forward_a16(layer, x, ids, w, rho, oracle.OUT_F32)
+        ref = oracle.bruteforce_fp64(layer, x, ids, w, rho, False)
+        if not np.all(np.isfinite(out)):
+            return _ok(False, f"non-finite output in case {case}")
+        worst = max(worst, float(rel_l2_rows(out, ref).max()))
+    return _ok(worst <= tol, f"worst per-row rel L2 {worst:.3g}")
+
+
+def pin_a16_activation_from_gu():
+    """W8A16 h (BF16 bits) equals torch's BF16 rounding of silu(g)*u computed
+    in FP64 from the oracle's own gate/up, except where the FP32 h of the
+    oracle sits within an FP32 ulp of a BF16 tie (one BF16 step) and where
+    e^-g overflows FP32 (g < -88.7: the FP32 SiLU is 0, the FP64 one below
+    1e-36)."""
+    layer, x, ids, w, rho = small_case(SMALL_CASES[1])
+    _, d = oracle.forward_a16(layer, x, ids, w, rho, oracle.OUT_F32, debug=True)
+    Ip = d["hb"].shape[1]
+    g = torch.from_numpy(d["gu"][:, :Ip]).double()
+    u = torch.from_numpy(d["gu"][:, Ip:]).double()
+    ref_t = (torch.nn.functional.silu(g) * u).to(torch.bfloat16)
+    ref = ref_t.view(torch.int16).numpy().view(np.uint16)
+    got = d["hb"]
+    tiny = (np.abs(oracle.bf16_to_f32(got)) < 1e-30) & (np.abs(ref_t.float().numpy()) < 1e-30)
+    diff = (got != ref) & ~tiny
+    steps = np.abs(got.astype(np.int64) - ref.astype(np.int64))[diff]
+    frac = float(diff.mean())
+    return _ok(frac <= 1e-3 and (steps.size == 0 or steps.max() == 1),
+               f"{int(diff.sum())} of {diff.size} BF16 values differ")
+
+
+def pin_a16_exact_inputs_match_a8():
+    """When every 128-group of x is already E4M3 at scale 1 (values from the
+    decoded codes, one of +-448 in each group), the W8A8 quantisation of x is
+    lossless, so the W8A16 gate/up equal the W8A8 ones bit for bit."""
+    layer, _, ids, w, rho = small_case(SMALL_CASES[1])
+    T, H = ids.shape[0], layer.H
+    rng = np.random.default_rng(21)
+    codes = rng.integers(0, 0x7F, size=(T, H)).astype(np.uint8) | (rng.integers(0, 2, size=(T, H)).astype(np.uint8) << 7)
+    xv = oracle.e4m3_decode(codes).astype(np.float32)
+    xv[:, ::128] = np.where(rng.integers(0, 2, size=(T, H // 128)) == 1, 448.0, -448.0)
+    xb = oracle.f32_to_bf16(xv)
+    _, d8 = oracle.forward(layer, xb, ids, w, rho, oracle.OUT_F32, debug=True)
+    _, d16 = oracle.forward_a16(layer, xb, ids, w, rho, oracle.OUT_F32, debug=True)
+    ok = np.array_equal(d8["gu"], d16["gu"]) and np.all(d8["sx"] == 1.0)
+    return _ok(ok, "W8A16 gate/up differ from W8A8 on lossless inputs")
+
+
 def pin_linearity():
     layer, x, ids, w, _ = small_case(SMALL_CASES[1])
     o1 = oracle.forward(layer, x, ids, w, 1.0, oracle.OUT_F32)
@@ -753,4 +808,7 @@ ALL_PINS = {
     "slice_aligned_is_plain": pin_slice_aligned_is_plain,
     "slice_requant_vs_torch": pin_slice_requant_vs_torch,
     "slices_add_up": pin_slices_add_up,
+    "a16_vs_bruteforce": pin_a16_vs_bruteforce,
+    "a16_activation_from_gu": pin_a16_activation_from_gu,
+    "a16_exact_inputs_match_a8": pin_a16_exact_inputs_match_a8,
 }

@@ -26,6 +26,7 @@ CAUGHT_BY = {
     "route_all_experts": ["route_weights_vs_scipy", "route_special_rows"],
     "shared_inside_rho": ["shared_vs_bruteforce", "shared_composition"],
     "slice_scale_block": ["slice_requant_vs_torch", "slices_add_up"],
+    "a16_h_truncate": ["a16_activation_from_gu", "a16_vs_bruteforce"],
 }
 
 
