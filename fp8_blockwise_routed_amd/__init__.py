@@ -44,7 +44,7 @@ EXPORTED = (
     "moe_fp8_prefill_debug_gate_up",
     "moe_fp8_prefill_debug_unpack", "moe_fp8_prefill_debug_mfma", "moe_fp8_prefill_set_timing",
     "moe_fp8_prefill_set_timing_stages", "moe_fp8_prefill_read_timing", "moe_fp8_prefill_debug_inject_failure",
-    "moe_fp8_prefill_route", "moe_fp8_prefill_run_logits",
+    "moe_fp8_prefill_route", "moe_fp8_prefill_run_logits", "moe_fp8_prefill_run_decode",
     "moe_fp8_prefill_create_streamed", "moe_fp8_prefill_stage", "moe_fp8_prefill_select_slot",
 )
 
@@ -88,6 +88,7 @@ def load_library() -> ctypes.CDLL:
         "moe_fp8_prefill_weight_bytes": ([D], I64),
         "moe_fp8_prefill_create": ([D, ctypes.POINTER(P)], ctypes.c_int),
         "moe_fp8_prefill_run": ([P, P, P, P, I64, P, P], ctypes.c_int),
+        "moe_fp8_prefill_run_decode": ([P, P, P, P, I64, P, P], ctypes.c_int),
         "moe_fp8_prefill_status": ([P], ctypes.c_int),
         "moe_fp8_prefill_destroy": ([P], None),
         "moe_fp8_prefill_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -202,6 +203,12 @@ def moe_fp8_prefill_run(handle: int, x, ids, w, T: int, out, stream=None) -> int
     """Returns the MOE_* code (does not raise) so callers can test error paths."""
     return int(load_library().moe_fp8_prefill_run(ctypes.c_void_p(handle), _dev_ptr(x), _dev_ptr(ids),
                                                   _dev_ptr(w), T, _dev_ptr(out), _stream_ptr(stream)))
+
+
+def moe_fp8_prefill_run_decode(handle: int, x, ids, w, T: int, out, stream=None) -> int:
+    """The W8A16 decode path; returns the MOE_* code."""
+    return int(load_library().moe_fp8_prefill_run_decode(ctypes.c_void_p(handle), _dev_ptr(x), _dev_ptr(ids),
+                                                         _dev_ptr(w), T, _dev_ptr(out), _stream_ptr(stream)))
 
 
 def moe_fp8_prefill_route(handle: int, logits, router: int, T: int, ids, w, stream=None) -> int:
@@ -387,6 +394,16 @@ class MoeFp8Prefill:
             dt = torch.float32 if self.out_dtype == MOE_DTYPE_F32 else torch.bfloat16
             out = torch.empty((T, self.H), dtype=dt, device=x.device)
         _check(moe_fp8_prefill_run(self.handle, x, ids, w, T, out, stream), "moe_fp8_prefill_run")
+        return out
+
+    def run_decode(self, x, ids, w, out=None, stream=None):
+        """The W8A16 decode path (x and h stay 16-bit); arguments as run()."""
+        import torch
+        T = x.shape[0]
+        if out is None:
+            dt = torch.float32 if self.out_dtype == MOE_DTYPE_F32 else torch.bfloat16
+            out = torch.empty((T, self.H), dtype=dt, device=x.device)
+        _check(moe_fp8_prefill_run_decode(self.handle, x, ids, w, T, out, stream), "moe_fp8_prefill_run_decode")
         return out
 
     def route(self, logits, router: int, stream=None):

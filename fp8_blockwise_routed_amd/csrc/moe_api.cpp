@@ -74,14 +74,14 @@ int64_t align256(int64_t n) { return (n + 255) & ~int64_t(255); }
 // Workspace pieces, in allocation order.
 struct WsSizes {
   int64_t xq, sx, sxT, hq, sh, shT, y, counts, offsets, perm, inv, small_tiles, narrow_tiles, wide_tiles, n_tiles, chunk,
-      err, rids, rw;
+      err, rids, rw, hb;
   int64_t total() const {
     return align256(xq) + align256(sx) + align256(sxT) + align256(hq) + align256(sh) + align256(shT) +
            align256(y) +
            align256(counts) + align256(offsets) + align256(perm) + align256(inv) +
            align256(small_tiles) + align256(narrow_tiles) + align256(wide_tiles) + align256(n_tiles) + align256(chunk) +
            align256(err) +
-           align256(rids) + align256(rw);
+           align256(rids) + align256(rw) + align256(hb);
   }
 };
 
@@ -106,6 +106,8 @@ WsSizes ws_sizes(const Dims& m) {
   w.err = 4;
   w.rids = m.max_rows * m.kr * 4;  // one pass's routed ids and weights (run_logits)
   w.rw = m.max_rows * m.kr * 4;
+  // BF16 h of one W8A16 decode pass (at most kDecodeRows rows)
+  w.hb = std::min<int64_t>(m.max_rows, kDecodeRows) * m.k * m.Ip * 2;
   return w;
 }
 
@@ -142,6 +144,7 @@ struct moe_fp8_prefill {
   float* sx = nullptr;
   float* sxT = nullptr;
   uint8_t* hq = nullptr;
+  uint16_t* hb = nullptr;  // W8A16 decode: BF16 h
   float* sh = nullptr;
   float* shT = nullptr;
   float* y = nullptr;
@@ -426,8 +429,31 @@ int get_stage_events(moe_fp8_prefill* h, StageEvents* out) {
 
 // Checks and per-call stream handling shared by run() and run_logits(),
 // then the passes.  Exactly one of (ids, w) and logits is given.
+// The W8A16 gate_up and down of one pass over t rows / P slots (the plan is
+// in the workspace), with the events of the timed stages: gate_up and down
+// take the streaming slots, the other GEMM slots record empty intervals.
+hipError_t launch_a16(moe_fp8_prefill* h, const uint16_t* x, int64_t t, int64_t P, hipStream_t s, hipEvent_t* at) {
+  const Dims& m = h->m;
+  const int64_t max_tiles16 = P / 16 + m.E;  // tiles of <= 16 rows over all lists
+  GateUpA16Args ga{x, t * m.H * 2, h->perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip, h->w13, h->s13,
+                   {h->small_tiles, h->narrow_tiles, h->wide_tiles}, h->n_tiles, h->hb,
+                   h->desc.activation == MOE_ACT_SILU_CLAMPED ? h->desc.activation_limit : 0.0f};
+  const int64_t cap = h->num_cus * kDecodeWgPerCu;
+  hipError_t e = launch_gate_up_a16(ga, (int)std::max<int64_t>(1, std::min<int64_t>(max_tiles16 * (m.Ip / kBlock), cap)), s);
+  if (e != hipSuccess) return e;
+  for (int b = 3; b <= 5; ++b)
+    if (at[b] && (e = hipEventRecord(at[b], s)) != hipSuccess) return e;
+  DownA16Args da{h->hb, P * m.Ip * 2, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2,
+                 {h->small_tiles, h->narrow_tiles, h->wide_tiles}, h->n_tiles, h->y};
+  e = launch_down_a16(da, (int)std::max<int64_t>(1, std::min<int64_t>(max_tiles16 * (m.H / kBlock), cap)), s);
+  if (e != hipSuccess) return e;
+  for (int b = 6; b <= 8; ++b)
+    if (at[b] && (e = hipEventRecord(at[b], s)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
 int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const float* w,
-               const float* logits, int32_t router, int64_t T, void* out, void* stream_) {
+               const float* logits, int32_t router, int64_t T, void* out, void* stream_, bool a16 = false) {
   if (!h) return MOE_ERR_INVALID_ARG;
   if (h->failed) return MOE_ERR_FAILED_STATE;
   if (T < 0) return MOE_ERR_INVALID_ARG;
@@ -463,8 +489,9 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
   const Dims& m = h->m;
   const int64_t out_elem = h->desc.out_dtype == MOE_DTYPE_F32 ? 4 : 2;
 
-  for (int64_t r0 = 0; r0 < T; r0 += m.max_rows) {
-    const int64_t t = (T - r0) < m.max_rows ? (T - r0) : m.max_rows;
+  const int64_t pass_rows = a16 ? std::min<int64_t>(m.max_rows, kDecodeRows) : m.max_rows;
+  for (int64_t r0 = 0; r0 < T; r0 += pass_rows) {
+    const int64_t t = (T - r0) < pass_rows ? (T - r0) : pass_rows;
     const int64_t P = t * m.k;
     StageEvents ev{};
     hipEvent_t at[MOE_NUM_STAGES + 1] = {};  // the boundaries this pass records
@@ -487,12 +514,19 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
     if (launch_plan(pa, s) != hipSuccess) return fail(h);
     if (at[1] && hipEventRecord(at[1], s) != hipSuccess) return fail(h);
 
-    QuantArgs qa{(const uint16_t*)x + r0 * m.H, (int32_t)t, (int32_t)m.H, h->xq, h->sx, h->sxT};
-    if (launch_quant(qa, s) != hipSuccess) return fail(h);
-    if (at[2] && hipEventRecord(at[2], s) != hipSuccess) return fail(h);
+    if (a16) {
+      // W8A16: no activation quantisation; one gate_up and one down launch
+      // over all tiles (timed in the streaming slots)
+      if (at[2] && hipEventRecord(at[2], s) != hipSuccess) return fail(h);
+      if (launch_a16(h, (const uint16_t*)x + r0 * m.H, t, P, s, at) != hipSuccess) return fail(h);
+    } else {
+      QuantArgs qa{(const uint16_t*)x + r0 * m.H, (int32_t)t, (int32_t)m.H, h->xq, h->sx, h->sxT};
+      if (launch_quant(qa, s) != hipSuccess) return fail(h);
+      if (at[2] && hipEventRecord(at[2], s) != hipSuccess) return fail(h);
 
-    if (launch_gate_up_all(h, t, P, nullptr, s, &at[3]) != hipSuccess) return fail(h);
-    if (launch_down_all(h, P, s, &at[6]) != hipSuccess) return fail(h);
+      if (launch_gate_up_all(h, t, P, nullptr, s, &at[3]) != hipSuccess) return fail(h);
+      if (launch_down_all(h, P, s, &at[6]) != hipSuccess) return fail(h);
+    }
 
     CombineArgs ca{h->y, h->inv, w_p, (int32_t)t, (int32_t)m.k, (int32_t)m.H, (int32_t)m.kr,
                    h->desc.routed_scale, h->desc.out_dtype == MOE_DTYPE_F32 ? 1 : 0,
@@ -636,6 +670,7 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   h->err = (int32_t*)get(w.err);
   h->rids = (int32_t*)get(w.rids);
   h->rw = (float*)get(w.rw);
+  h->hb = (uint16_t*)get(w.hb);
   if (!ok) {
     free_all(h);
     delete h;
@@ -664,6 +699,11 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
 int moe_fp8_prefill_run(moe_fp8_prefill* h, const void* x, const int32_t* ids, const float* w,
                         int64_t T, void* out, void* stream) {
   return run_passes(h, x, ids, w, nullptr, 0, T, out, stream);
+}
+
+int moe_fp8_prefill_run_decode(moe_fp8_prefill* h, const void* x, const int32_t* ids, const float* w,
+                               int64_t T, void* out, void* stream) {
+  return run_passes(h, x, ids, w, nullptr, 0, T, out, stream, true);
 }
 
 int moe_fp8_prefill_run_logits(moe_fp8_prefill* h, const void* x, const float* logits,
@@ -970,6 +1010,7 @@ int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slo
   h->err = (int32_t*)get(w.err);
   h->rids = (int32_t*)get(w.rids);
   h->rw = (float*)get(w.rw);
+  h->hb = (uint16_t*)get(w.hb);
   if (!ok) {
     free_all(h);
     delete h;

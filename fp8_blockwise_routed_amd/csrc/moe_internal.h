@@ -155,6 +155,33 @@ struct SliceArgs {
 // GEMM variants (launch_gate_up / launch_down kind)
 constexpr int kGemmStream = 0, kGemmNarrow = 1, kGemmWide = 2;
 
+// The W8A16 decode path: activations stay BF16 (x as given, h rounded to
+// BF16); every tile of the three lists is taken 16 rows at a time.
+constexpr int kDecodeRows = 1024;  // rows per decode pass
+constexpr int kDecodeWgPerCu = 2;
+struct GateUpA16Args {
+  const uint16_t* x;     // bf16 [T][H]
+  int64_t x_bytes;
+  const int32_t* perm;
+  int32_t k, H, Ip;
+  const uint8_t* w13;    // swizzled
+  const float* s13;
+  const Tile* tiles[3];  // small, narrow, wide lists
+  const int32_t* n_tiles;
+  uint16_t* hb;          // bf16 [P][Ip]
+  float act_limit;
+};
+struct DownA16Args {
+  const uint16_t* hb;    // bf16 [P][Ip]
+  int64_t hb_bytes;
+  int32_t H, Ip;
+  const uint8_t* w2;     // swizzled
+  const float* s2;
+  const Tile* tiles[3];
+  const int32_t* n_tiles;
+  float* y;              // [P][H]
+};
+
 // Launchers (return the launch status).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
@@ -162,6 +189,8 @@ hipError_t launch_quant(const QuantArgs& a, hipStream_t s);
 hipError_t launch_gate_up(const GateUpArgs& a, int kind, int grid, hipStream_t s);
 hipError_t launch_down(const DownArgs& a, int kind, int grid, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_gate_up_a16(const GateUpA16Args& a, int grid, hipStream_t s);
+hipError_t launch_down_a16(const DownA16Args& a, int grid, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
 hipError_t launch_slice(const SliceArgs& a, hipStream_t s);
 hipError_t launch_mfma_probe(const uint8_t* a, const uint8_t* b, float* d, hipStream_t s);

@@ -1721,6 +1721,213 @@ hipError_t launch_down(const DownArgs& a, int kind, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------- W8A16 decode path --
+// The pages' path for decode and short continuations keeps the activations
+// 16-bit ("ktransformers #2244", Design): x enters gate_up as BF16 and h
+// enters down as BF16 (rounded to nearest even from FP32), against the same
+// E4M3 weights and 128x128 block scales.  The products run on the BF16
+// MFMA (16x16x32): a lane's 32-byte FP8 weight fragment (K 32g .. 32g + 31
+// of the 16x16x128 layout, g = lane / 16) is converted exactly to BF16 eight
+// codes at a time, and the four MFMAs of a 128-wide K block each take K
+// 32g + 8j .. + 7 from every lane (j = 0..3), so the activation fragment is
+// the matching 16 bytes of the row, read straight from memory and no weight
+// byte crosses lanes.  Per K block: p = sum over the four MFMAs, then
+// acc = fma(p, weight block scale, acc) in ascending K-block order.  Every
+// tile of the plan's three lists is taken 16 rows at a time by 4-wave
+// workgroups (weights streamed into registers D blocks deep, as in the
+// streaming W8A8 kernels), so a row's bits do not depend on its neighbours.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// FP8 bytes 0..7 of (lo, hi) as BF16 (exact: E4M3 values fit BF16)
+__device__ __forceinline__ bf16x8 fp8x8_bf16(int lo, int hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// One 128-wide K block of a 16x16 output tile: activation fragments A[j]
+// (8 BF16 each) against the lane's FP8 weight fragment.
+__device__ __forceinline__ f32x4 mfma_a16_block(const i32x4 (&A)[4], const i32x8& B) {
+  f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[j]), fp8x8_bf16(B[2 * j], B[2 * j + 1]),
+                                                p, 0, 0, 0);
+  return p;
+}
+
+// Tile ti of the three lists taken in order (small, narrow, wide).
+__device__ __forceinline__ const Tile* a16_tile(const Tile* const (&lists)[3], int n0, int n1, int ti) {
+  return ti < n0 ? lists[0] + ti : (ti < n0 + n1 ? lists[1] + (ti - n0) : lists[2] + (ti - n0 - n1));
+}
+
+// gate_up: item (tile, 128-column block nb); wave w owns n-tiles g0, g1, u0,
+// u1 of 32-column group w (as gate_up_stream_kernel).
+template <int D>
+__global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void gate_up_a16_kernel(GateUpA16Args a) {
+  __shared__ float ws_lds[2 * kMaxKBlocks];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int H = a.H, Ip = a.Ip, nH = H / kBlock, NB = Ip / kBlock;
+  const int n0 = a.n_tiles[0], n1 = a.n_tiles[1], n2 = a.n_tiles[2];
+  const int n_items = (n0 + n1 + n2) * NB;
+  const rsrc_t xr = make_rsrc(a.x, (uint32_t)a.x_bytes);
+  const uint32_t bvoff = (uint32_t)(wave * 8192 + lane * 16);
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int ti = item / NB, nb = item - ti * NB;
+    const Tile* tp = a16_tile(a.tiles, n0, n1, ti);
+    const int e = __builtin_amdgcn_readfirstlane(tp->e), p0 = __builtin_amdgcn_readfirstlane(tp->p0);
+    const int rows = __builtin_amdgcn_readfirstlane(tp->rows);
+    __syncthreads();  // the previous item's scales are no longer read
+    {
+      const float* ws = a.s13 + (size_t)(e * NB + nb) * nH * 2;
+      for (int i = tid; i < 2 * nH; i += kThreads) ws_lds[i] = ws[i];
+    }
+    __syncthreads();
+    const rsrc_t wr = make_rsrc(a.w13 + (size_t)(e * NB + nb) * nH * kGateUpChunk, (uint32_t)(nH * kGateUpChunk));
+
+    for (int c0 = 0; c0 < rows; c0 += 16) {
+      const int r = c0 + col;
+      const int tok = a.perm[p0 + (r < rows ? r : c0)] / a.k;
+      const uint32_t avo = (uint32_t)(tok * H * 2 + grp * 64);
+      f32x4 acc[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      i32x4 A[D][4];
+      i32x8 B[D][4];
+      // block kb's operands; kb >= nH reads out of range (zeros, no access)
+      auto load = [&](int kb, i32x4(&af)[4], i32x8(&bf)[4]) {
+        const bool in = kb < nH;
+        const uint32_t oob = in ? 0u : 0x80000000u;
+        const uint32_t sa = in ? (uint32_t)(kb * kBlock * 2) : 0u, so = in ? (uint32_t)(kb * kGateUpChunk) : 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) af[j] = bload16(xr, avo + oob, sa + j * 16);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          bf[t] = cat(wload16(wr, bvoff + oob, so + t * 2048), wload16(wr, bvoff + oob, so + t * 2048 + 1024));
+      };
+      auto compute = [&](int kb, const i32x4(&af)[4], const i32x8(&bf)[4]) {
+        const float wsg = ws_lds[2 * kb], wsu = ws_lds[2 * kb + 1];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const f32x4 p = mfma_a16_block(af, bf[t]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(p[i], t < 2 ? wsg : wsu, acc[t][i]);
+        }
+      };
+#pragma unroll
+      for (int s = 0; s < D - 1; ++s) load(s, A[s], B[s]);
+      for (int kb0 = 0; kb0 < nH; kb0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+          load(kb0 + s + D - 1, A[(s + D - 1) % D], B[(s + D - 1) % D]);
+          if (kb0 + s < nH) compute(kb0 + s, A[s], B[s]);
+        }
+      }
+      // h = silu(gate) * up in FP32, stored as BF16
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = c0 + grp * 4 + i;
+        if (row < rows) {
+          const float h0 = silu_mul_act(acc[0][i], acc[2][i], a.act_limit);
+          const float h1 = silu_mul_act(acc[1][i], acc[3][i], a.act_limit);
+          uint16_t* dst = a.hb + (size_t)(p0 + row) * Ip + nb * kBlock + wave * 32 + col;
+          dst[0] = (uint16_t)f32_to_bf16(h0);
+          dst[16] = (uint16_t)f32_to_bf16(h1);
+        }
+      }
+    }
+  }
+}
+
+// down: item (tile, 128-column block nb of H); wave w owns 32 columns (two
+// n-tiles), as down_stream_kernel.
+template <int D>
+__global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void down_a16_kernel(DownA16Args a) {
+  __shared__ float ws_lds[kMaxKBlocks];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int H = a.H, Ip = a.Ip, nI = Ip / kBlock, NB = H / kBlock;
+  const int n0 = a.n_tiles[0], n1 = a.n_tiles[1], n2 = a.n_tiles[2];
+  const int n_items = (n0 + n1 + n2) * NB;
+  const rsrc_t hr = make_rsrc(a.hb, (uint32_t)a.hb_bytes);
+  const uint32_t bvoff = (uint32_t)(wave * 4096 + lane * 16);
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int ti = item / NB, nb = item - ti * NB;
+    const Tile* tp = a16_tile(a.tiles, n0, n1, ti);
+    const int e = __builtin_amdgcn_readfirstlane(tp->e), p0 = __builtin_amdgcn_readfirstlane(tp->p0);
+    const int rows = __builtin_amdgcn_readfirstlane(tp->rows);
+    __syncthreads();
+    {
+      const float* ws = a.s2 + (size_t)(e * NB + nb) * nI;
+      for (int i = tid; i < nI; i += kThreads) ws_lds[i] = ws[i];
+    }
+    __syncthreads();
+    const rsrc_t wr = make_rsrc(a.w2 + (size_t)(e * NB + nb) * nI * kDownChunk, (uint32_t)(nI * kDownChunk));
+
+    for (int c0 = 0; c0 < rows; c0 += 16) {
+      const int r = c0 + col;
+      const uint32_t avo = (uint32_t)((p0 + (r < rows ? r : c0)) * Ip * 2 + grp * 64);
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      i32x4 A[D][4];
+      i32x8 B[D][2];
+      auto load = [&](int kb, i32x4(&af)[4], i32x8(&bf)[2]) {
+        const bool in = kb < nI;
+        const uint32_t oob = in ? 0u : 0x80000000u;
+        const uint32_t sa = in ? (uint32_t)(kb * kBlock * 2) : 0u, so = in ? (uint32_t)(kb * kDownChunk) : 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) af[j] = bload16(hr, avo + oob, sa + j * 16);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          bf[t] = cat(wload16(wr, bvoff + oob, so + t * 2048), wload16(wr, bvoff + oob, so + t * 2048 + 1024));
+      };
+      auto compute = [&](int kb, const i32x4(&af)[4], const i32x8(&bf)[2]) {
+        const float wsc = ws_lds[kb];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f32x4 p = mfma_a16_block(af, bf[t]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(p[i], wsc, acc[t][i]);
+        }
+      };
+#pragma unroll
+      for (int s = 0; s < D - 1; ++s) load(s, A[s], B[s]);
+      for (int kb0 = 0; kb0 < nI; kb0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+          load(kb0 + s + D - 1, A[(s + D - 1) % D], B[(s + D - 1) % D]);
+          if (kb0 + s < nI) compute(kb0 + s, A[s], B[s]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = c0 + grp * 4 + i;
+        if (row < rows) {
+          float* dst = a.y + (size_t)(p0 + row) * H + nb * kBlock + wave * 32 + col;
+          dst[0] = acc[0][i];
+          dst[16] = acc[1][i];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_gate_up_a16(const GateUpA16Args& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(gate_up_a16_kernel<3>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_a16(const DownA16Args& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(down_a16_kernel<4>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------------- combine --
 // A workgroup per token and 2048 columns; 8 consecutive columns per thread.
 // All of a token's y loads are issued before the sums (a skipped slot reads

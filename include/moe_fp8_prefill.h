@@ -158,6 +158,23 @@ int moe_fp8_prefill_run(moe_fp8_prefill* h, const void* x, const int32_t* ids,
                         const float* w, int64_t T, void* out, void* stream);
 
 /*
+ * The decode path: the same layer in its W8A16 form, which the pages use for
+ * decode and continuations shorter than 256 tokens ("ktransformers #2244",
+ * Design: prefill of >= 256 tokens runs W8A8 on the GPU, shorter
+ * continuations and decode W8A16).  The activations entering each GEMM stay
+ * 16-bit: x as given (BF16) and h = silu(g) * u rounded to BF16 (nearest
+ * even); each 128-wide K block is an FP32 dot of activations and decoded
+ * weight codes times the weight block scale, accumulated in FP32 in ascending
+ * block order; the combine is run()'s.  Arguments, ownership, stream rules
+ * and errors as run(); T > min(max_rows, 1024) rows run in passes of that
+ * size, and a row's output bits depend on neither its neighbours nor the
+ * pass split.  The result differs from run() (no activation quantisation):
+ * the two are different methods, each exact to its own definition.
+ */
+int moe_fp8_prefill_run_decode(moe_fp8_prefill* h, const void* x, const int32_t* ids,
+                               const float* w, int64_t T, void* out, void* stream);
+
+/*
  * The top-k router, on the device ("hpc-ops #80", gap table: the router's
  * top-k belongs to the fused MoE step; "TensorFold #2852": routed slots in
  * descending score).  For each token: the k experts with the largest logits,

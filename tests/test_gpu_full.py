@@ -4,7 +4,8 @@ Layer E=256, top-8, H=6144, I=2048 (9.002 GiB of FP8 codes and FP32 scales)
 at T=256 (sigmoid top-8, rho=2.5, 1% outlier rows), T=4096 (uniform routing
 logits) and T=8192 (Zipf(1.2) popularity with 8 experts never chosen), run
 exactly as the benchmark runs them (one handle, max_rows=8192, one call per
-batch); and the E=160, H=5120, I=192 slice at T=16/64/1024.
+batch); the W8A16 decode path on the same layer at T=16; and the E=160,
+H=5120, I=192 slice at T=16/64/1024.
 
 Integer work (plan, activation codes) is compared in full, bit for bit.  The
 output is compared on sampled rows (outlier rows included) that the oracle
@@ -105,6 +106,27 @@ def test_glm_t256(glm):
     # token permutation permutes rows bit for bit
     pi = np.random.default_rng(3).permutation(wl.T)
     assert np.array_equal(call(moe, x[pi], ids[pi], w[pi]), got[pi])
+
+
+def test_glm_decode_t16(glm):
+    """The W8A16 decode path on the full layer: a 16-token batch (the first
+    16 rows of the T=256 inputs, outlier rows among them) against the
+    oracle's W8A16 form, every row; and 256 rows through the decode path give
+    the same bits for those 16 rows."""
+    layer, moe = glm
+    wl = gen.GLM_T256
+    x, ids, w, outl = gen.make_inputs(wl)
+    S = np.arange(16)
+    note("glm decode T=16")
+    out = moe.run_decode(dev_bf16(x[S]), dev(ids[S]), dev(w[S]))
+    torch.cuda.synchronize()
+    got = out_to_np(out)
+    assert moe.status() == pkg.MOE_OK
+    ref = oracle.forward_a16(layer, x[S], ids[S], w[S], wl.rho, oracle.OUT_BF16)
+    assert_rows_close(got, ref, tol=TOL, what="glm decode T=16")
+    big = moe.run_decode(dev_bf16(x), dev(ids), dev(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(out_to_np(big)[S], got)
 
 
 def test_glm_t4096(glm):

@@ -86,6 +86,7 @@ def test_create_rejects_before_allocating():
 def test_null_handle_calls():
     lib = pkg.load_library()
     assert lib.moe_fp8_prefill_run(None, None, None, None, 1, None, None) == pkg.MOE_ERR_INVALID_ARG
+    assert lib.moe_fp8_prefill_run_decode(None, None, None, None, 1, None, None) == pkg.MOE_ERR_INVALID_ARG
     assert lib.moe_fp8_prefill_status(None) == pkg.MOE_ERR_INVALID_ARG
     assert lib.moe_fp8_prefill_set_timing(None, 1) == pkg.MOE_ERR_INVALID_ARG
     assert lib.moe_fp8_prefill_set_timing_stages(None, 1) == pkg.MOE_ERR_INVALID_ARG
