@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s (the W8A16 decode path)
 METRIC = "input tokens/sec per MoE layer (1 MI355X) + % FP8 MFMA peak / % HBM peak"
 PROFILES = os.path.join(ROOT, "profiles")
 COUNTERS_MD = os.path.join(PROFILES, "gate_up_stream_glm_e256_t256_counters.md")
@@ -31,7 +32,14 @@ GATE_UP_KERNELS = {
     "stream": "gate_up_stream_kernel (experts with 1..16 rows)",
     "narrow": "gate_up_narrow_kernel (experts with 17..128 rows)",
     "wide": "gate_up_wide_kernel (experts with more than 128 rows)",
+    "decode": "gate_up_a16_kernel (W8A16 decode, every expert hit)",
 }
+
+
+def gate_up_stage(kind):
+    """The library's timing stage of a gate_up launch group (the W8A16
+    decode path's single gate_up launch is timed in the streaming slot)."""
+    return "gate_up_stream" if kind == "decode" else "gate_up_" + kind
 STATS_MD = os.path.join(PROFILES, "kernel_stats_glm_e256_t256.md")
 KERNEL_SOURCE = os.path.join(ROOT, "fp8_blockwise_routed_amd", "csrc", "moe_kernels.hip")
 DOMINANT = "gate_up_stream_kernel"   # the 1-subtile gate_up launch (experts with 1..16 rows)
@@ -79,7 +87,7 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def algorithmic_work(wl, counts):
+def algorithmic_work(wl, counts, a16=False):
     """Algorithmic bytes / FLOPs from the plan's per-expert row counts.
 
     Per expert with n_e > 0 rows: weights 3*Ip*H code bytes + FP32 block
@@ -107,6 +115,13 @@ def algorithmic_work(wl, counts):
             experts=int(sel.sum()), rows=rows,
             bytes=int(sel.sum()) * (2 * Ip * H + 8 * nI * nH) + rows * (H + 4 * nH + Ip + 4 * nI),
             flops=4 * rows * Ip * H)
+    if a16:
+        # W8A16 decode: one gate_up launch over every tile; the activation row
+        # is read as BF16 (2H) and h written as BF16 (2Ip), no scales
+        rows = int(counts.sum())
+        groups = {"decode": dict(experts=int(hit.sum()), rows=rows,
+                                 bytes=int(hit.sum()) * (2 * Ip * H + 8 * nI * nH) + rows * (2 * H + 2 * Ip),
+                                 flops=4 * rows * Ip * H)}
     return dict(path_bytes=path_bytes, path_flops=path_flops, gate_up=groups,
                 experts_hit=int(hit.sum()), slots=P,
                 per_expert_gate_up_bytes=2 * Ip * H + 8 * nI * nH)
@@ -273,7 +288,7 @@ def streamed_bench(args, wl, layer, xd, idd, wd, out) -> int:
                   "host-link bound)",
         "value": wl.T / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": L, "warmup": 2,
         "ms_per_step": elapsed * 1e3 / L, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16 x fp8_e4m3 (fp32 accumulate)" if a16 else "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
         "config": {"workload": wl.name, "layers": L, "slots": 2, "slot_bytes": slot_bytes,
                    "host_memory": "page-locked, one layer staged L times"},
         "h2d_GBs": L * slot_bytes / elapsed / 1e9,
@@ -283,7 +298,7 @@ def streamed_bench(args, wl, layer, xd, idd, wd, out) -> int:
     return 0
 
 
-def cpu_baseline(layer, wl, x, ids, w, n_tokens, repeats):
+def cpu_baseline(layer, wl, x, ids, w, n_tokens, repeats, a16=False):
     """The oracle, as it stands, on the first n_tokens rows of the same batch:
     median wall clock of `repeats` runs."""
     import oracle
@@ -295,12 +310,13 @@ def cpu_baseline(layer, wl, x, ids, w, n_tokens, repeats):
     times = []
     for _ in range(repeats):
         t0 = time.perf_counter()
-        oracle.forward(layer, x[:n_tokens], ids, w, wl.rho, oracle.OUT_BF16, n_shared=wl.shared)
+        oracle.forward(layer, x[:n_tokens], ids, w, wl.rho, oracle.OUT_BF16, n_shared=wl.shared, a16=a16)
         times.append(time.perf_counter() - t0)
     dt = sorted(times)[len(times) // 2]
     return dict(value=n_tokens / dt, unit="tokens/s", cores=oracle.max_threads(), kind="oracle",
                 sample=f"first {n_tokens} of the {wl.T} rows of the timed batch with all their "
-                       f"routed experts; median of {repeats} runs, {dt:.2f} s each")
+                       f"routed experts{' (W8A16 form)' if a16 else ''}; median of {repeats} runs, "
+                       f"{dt:.2f} s each")
 
 
 def main() -> int:
@@ -318,6 +334,9 @@ def main() -> int:
                     help="instead of the resident-layer bench: whole-model prefill through L layers "
                          "whose weights are staged from pinned host memory into two device slots "
                          "(double-buffered H2D overlapped with compute)")
+    ap.add_argument("--decode", type=int, default=0, metavar="T",
+                    help="time the W8A16 decode path (run_decode) on the first T rows of the "
+                         "workload's batch instead of the W8A8 prefill path")
     ap.add_argument("--router", action="store_true",
                     help="start each step from FP32 router logits (run_logits: on-device top-k "
                          "router, then the path) instead of given ids and weights")
@@ -356,6 +375,12 @@ def main() -> int:
     t0 = time.perf_counter()
     layer = gen.make_layer(wl.E + wl.shared, wl.H, wl.I, seed=wl.seed)
     x, ids, w, _ = gen.make_inputs(wl)
+    a16 = args.decode > 0
+    if a16:  # the first T rows of the batch through the W8A16 decode path
+        import dataclasses
+        Td = min(args.decode, wl.T)
+        x, ids, w = x[:Td], ids[:Td], w[:Td]
+        wl = dataclasses.replace(wl, T=Td, name=f"{wl.name}_decode_t{Td}")
     log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; creating the handle")
     moe = pkg.MoeFp8Prefill(layer, wl.k, routed_scale=wl.rho, max_rows=8192,
                             out_dtype=pkg.MOE_DTYPE_BF16, shared_experts=wl.shared)
@@ -375,6 +400,8 @@ def main() -> int:
     def step():
         if args.router:
             rc = pkg.moe_fp8_prefill_run_logits(moe.handle, xd, ld, router, wl.T, out, stream)
+        elif a16:
+            rc = pkg.moe_fp8_prefill_run_decode(moe.handle, xd, idd, wd, wl.T, out, stream)
         else:
             rc = pkg.moe_fp8_prefill_run(moe.handle, xd, idd, wd, wl.T, out, stream)
         if rc != pkg.MOE_OK:
@@ -386,7 +413,7 @@ def main() -> int:
     torch.cuda.synchronize()
     counts, _, _, _ = pkg.moe_fp8_prefill_debug_plan(moe.handle, wl.E + wl.shared,
                                                      wl.T * (wl.k + wl.shared))
-    work = algorithmic_work(wl, counts)
+    work = algorithmic_work(wl, counts, a16=a16)
 
     # Stage breakdown from a few untimed steps with events at every launch
     # boundary; they also name the dominant gate_up launch.
@@ -400,8 +427,10 @@ def main() -> int:
         stages = pkg.moe_fp8_prefill_read_timing(moe.handle)
         mean = stages.mean(axis=0)
         kind = max(("stream", "narrow", "wide"), key=lambda k: float(mean[pkg.STAGES.index("gate_up_" + k)]))
+        if a16:
+            kind = "decode"  # the W8A16 gate_up is timed in the streaming slot
         # in the timed steps, events only around that launch (two per step)
-        pkg.moe_fp8_prefill_set_timing_stages(moe.handle, ["gate_up_" + kind])
+        pkg.moe_fp8_prefill_set_timing_stages(moe.handle, [gate_up_stage(kind)])
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -424,7 +453,7 @@ def main() -> int:
         "config": {"workload": wl.name, "experts": wl.E, "top_k": wl.k, "hidden": wl.H,
                    "intermediate": wl.I, "rows": wl.T, "routed_scale": wl.rho,
                    "outlier_rows": wl.outlier_frac, "seed": wl.seed,
-                   "shared_experts": wl.shared},
+                   "shared_experts": wl.shared, "path": "decode (W8A16)" if a16 else "prefill (W8A8)"},
     }
     res["path"] = {
         "algorithmic_bytes": work["path_bytes"], "algorithmic_flops": work["path_flops"],
@@ -440,12 +469,13 @@ def main() -> int:
         # the dominant gate_up launch, against the roof its algorithmic work
         # reaches first; its time from the events of the timed steps
         g = work["gate_up"][kind]
-        launch_ms = float(live[:, pkg.STAGES.index("gate_up_" + kind)].mean())
+        launch_ms = float(live[:, pkg.STAGES.index(gate_up_stage(kind))].mean())
+        mfma_peak = PEAK_BF16_TFLOPS if a16 else PEAK_FP8_TFLOPS
         t_hbm = g["bytes"] / (PEAK_HBM_GBS * 1e9)
-        t_mfma = g["flops"] / (PEAK_FP8_TFLOPS * 1e12)
+        t_mfma = g["flops"] / (mfma_peak * 1e12)
         if t_mfma >= t_hbm:
             achieved = g["flops"] / (launch_ms * 1e-3) / 1e12
-            bound, peak, unit = "mfma", PEAK_FP8_TFLOPS, "TFLOP/s"
+            bound, peak, unit = "mfma", mfma_peak, "TFLOP/s"
         else:
             achieved = g["bytes"] / (launch_ms * 1e-3) / 1e9
             bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
@@ -479,7 +509,7 @@ def main() -> int:
     if args.cpu_tokens > 0:
         log(f"[bench] CPU oracle on {args.cpu_tokens} rows")
         res["cpu_baseline"] = cpu_baseline(layer, wl, x, ids, w, min(args.cpu_tokens, wl.T),
-                                           max(1, args.cpu_repeats))
+                                           a16=a16, repeats=max(1, args.cpu_repeats))
     moe.close()
     print(json.dumps(res), flush=True)
     return 0
