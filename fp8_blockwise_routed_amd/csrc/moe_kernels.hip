@@ -711,10 +711,15 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds1[BM * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t w_lds0[kGateUpChunk];
   __shared__ __attribute__((aligned(1024))) uint8_t w_lds1[kGateUpChunk];
-  // row scales: rows in the first half, the other half takes waves 4-7's
-  // out-of-range loads
-  __shared__ __attribute__((aligned(256))) float sx_lds0[2 * BM];
-  __shared__ __attribute__((aligned(256))) float sx_lds1[2 * BM];
+  // Promotion factors of a K block, per stage: row scale x gate weight scale
+  // for rows 0-255, then row scale x up weight scale.  Waves 0-3 form them
+  // for their rows 64w .. + 63 at the end of the step before, so the matrix
+  // waves read two products per row instead of multiplying eight times per
+  // subtile.  sx0_lds takes block 0's row scales by DMA (the other half:
+  // waves 4-7's out-of-range loads).
+  __shared__ __attribute__((aligned(256))) float cs_lds0[2 * BM];
+  __shared__ __attribute__((aligned(256))) float cs_lds1[2 * BM];
+  __shared__ __attribute__((aligned(256))) float sx0_lds[2 * BM];
   // row list and weight scales of the current item and of the next one
   __shared__ float ws_lds[2][2 * kMaxKBlocks];
   __shared__ int tok_lds[2][BM];
@@ -796,9 +801,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
 #pragma unroll
       for (int j = 2 * (p - 2); j < 2 * (p - 2) + 2; ++j) dma16<0>(xr, al + (j * 8 + wave) * 1024, q.avo[j] | oob, sa);
     } else {
-      float* sl = st == 0 ? sx_lds0 : sx_lds1;
-      dma4(sr, sl + wave * 64, q.svo | oob, in ? (uint32_t)(kb * a.T * 4) : 0u);
+      static_assert(st == 0, "block 0's row scales only");
+      dma4(sr, sx0_lds + wave * 64, q.svo | oob, in ? (uint32_t)(kb * a.T * 4) : 0u);
     }
+  };
+  // block kb's row scale of row 64w + lane (waves 0-3; 0 past the last block)
+  auto row_scale = [&](int kb, const Src& q) __attribute__((always_inline)) {
+    const bool in = kb < nH;
+    return bloadf(sr, q.svo | (in ? 0u : 0x80000000u), in ? (uint32_t)(kb * a.T * 4) : 0u);
   };
   auto issue = [&](auto ST, int kb, const Src& q) __attribute__((always_inline)) {
     static_for<5>([&](auto PT) __attribute__((always_inline)) { issue_part(ST, PT, kb, q); });
@@ -830,6 +840,17 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
     // the next item's slots and weight scales into the other buffer (they
     // land with block 1)
     if (has_next) meta_dma(buf ^ 1, nit);
+    // block kb's promotion factors from row scale v into cs (waves 0-3, each
+    // its own 64 rows; the same FP32 products the promotion would form)
+    auto put_cs = [&](float* cs, int kb, float v) __attribute__((always_inline)) {
+      const int kc = kb < nH ? kb : nH - 1;
+      const int r = wave * 64 + lane;
+      cs[r] = v * ws_lds[buf][2 * kc];
+      cs[BM + r] = v * ws_lds[buf][2 * kc + 1];
+    };
+    if (wave < 4) put_cs(cs_lds0, 0, sx0_lds[wave * 64 + lane]);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    ring_barrier();
 
     // acc[m][t]: rows 128 mh + 16 m + 4 grp + i, n-tile t (gate 0-1, up 2-3)
     f32x4 acc[8][4];
@@ -839,64 +860,68 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
       for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // one K block over MT subtiles: issue block kb + 1 into the other stage
-    // (read last step), multiply block kb out of stage s, wait for kb + 1
+    // (read last step), multiply block kb out of stage s, wait for kb + 1,
+    // then (waves 0-3) form block kb + 1's promotion factors
     auto step = [&](auto S, auto MTC, int kb0) __attribute__((always_inline)) {
       constexpr int s = decltype(S)::value, MT = decltype(MTC)::value;
       const int kb = kb0 + s;
       constexpr auto NEXT = std::integral_constant<int, 1 - s>{};
+      float rs = 0.f;
       // without subtiles to interleave with, block kb + 1's loads go first
-      if constexpr (MT == 0) issue(NEXT, kb + 1, cur);
+      if constexpr (MT == 0) {
+        static_for<4>([&](auto PT) __attribute__((always_inline)) { issue_part(NEXT, PT, kb + 1, cur); });
+        if (wave < 4) rs = row_scale(kb + 1, cur);
+      }
       if (MT > 0 && kb < nH) {
-        const float wsg = ws_lds[buf][2 * kb], wsu = ws_lds[buf][2 * kb + 1];
         const uint8_t* wbuf = (s == 0 ? w_lds0 : w_lds1) + w_rd;
         const uint8_t* abuf = (s == 0 ? a_lds0 : a_lds1) + afr;
-        const float* srow = (s == 0 ? sx_lds0 : sx_lds1) + mh * 128 + grp * 4;
+        const float* crow = (s == 0 ? cs_lds0 : cs_lds1) + mh * 128 + grp * 4;
         i32x8 B[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) B[t] = cat(ld16(wbuf + t * 2048), ld16(wbuf + t * 2048 + 1024));
-        // Subtile m: the next subtile's fragment reads, its four MFMAs, a part
-        // of block kb + 1's loads under them, then the promotion of its own
-        // products (the other wave of the SIMD multiplies meanwhile).
+        // Subtile m: its factor reads and the next subtile's fragment reads,
+        // its four MFMAs, a part of block kb + 1's loads under them, then the
+        // promotion of its own products (the other wave of the SIMD
+        // multiplies meanwhile).
         i32x8 A2[2];
-        f32x4 R2[2], P[4];
+        f32x4 CG, CU, P[4];
         A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
-        R2[0] = ld16f(srow);
         static_for<MT>([&](auto M) __attribute__((always_inline)) {
           constexpr int m = decltype(M)::value;
           constexpr int per = MT >= 4 ? 1 : 4 / (MT > 0 ? MT : 1);  // load parts per subtile
-          if constexpr (m + 1 < MT) {
+          CG = ld16f(crow + m * 16);
+          CU = ld16f(crow + BM + m * 16);
+          if constexpr (m + 1 < MT)
             A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
-            R2[(m + 1) & 1] = ld16f(srow + (m + 1) * 16);
-          }
 #pragma unroll
           for (int t = 0; t < 4; ++t) P[t] = mfma_e4m3(A2[m & 1], B[t]);
           static_for<per>([&](auto J) __attribute__((always_inline)) {
             constexpr int q = m * per + decltype(J)::value;
             if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kb + 1, cur);
           });
-          if constexpr (m == 0) issue_part(NEXT, std::integral_constant<int, 4>{}, kb + 1, cur);
-          float cg[4], cu[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            cg[i] = R2[m & 1][i] * wsg;
-            cu[i] = R2[m & 1][i] * wsu;
+          if constexpr (m == 0) {
+            if (wave < 4) rs = row_scale(kb + 1, cur);
           }
 #pragma unroll
           for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[m][t][i] = __builtin_fmaf(P[t][i], t < 2 ? cg[i] : cu[i], acc[m][t][i]);
+            for (int i = 0; i < 4; ++i)
+              acc[m][t][i] = __builtin_fmaf(P[t][i], t < 2 ? CG[i] : CU[i], acc[m][t][i]);
           pin_in_place(acc[m]);
           constexpr int nl = (m * per < 4 ? 2 * per : 0) + (m == 0 ? 1 : 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS reads (next subtile)
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS reads (next subtile)
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // MFMA
           __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);  // VMEM reads
-          __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);  // VALU
+          __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // VALU
           __builtin_amdgcn_sched_barrier(0);
         });
       } else if constexpr (MT > 0) {
-        issue(NEXT, kb + 1, cur);
+        static_for<4>([&](auto PT) __attribute__((always_inline)) { issue_part(NEXT, PT, kb + 1, cur); });
+        if (wave < 4) rs = row_scale(kb + 1, cur);
       }
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block kb + 1 has landed
+      if (wave < 4) put_cs(s == 0 ? cs_lds1 : cs_lds0, kb + 1, rs);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the factors are in LDS
       ring_barrier();
     };
     auto kloop = [&](auto MTC) __attribute__((always_inline)) {
