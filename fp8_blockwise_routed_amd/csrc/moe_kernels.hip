@@ -1121,9 +1121,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
     int ltid = (int)threadIdx.x;
     asm volatile("" : "+v"(ltid));
     const int lane = ltid & 63;
+    // weights with the streaming kernels' cache policy (read once per pass;
+    // 10% faster on the E=160 I=192 T=1024 slice than the default policy)
 #pragma unroll
     for (int q = 0; q < 16; ++q)
-      dma16<0>(wr, wl + (2 * q + pw) * 1024, (uint32_t)((2 * q + pw) * 1024 + lane * 16) | oob, sw);
+      dma16<kWeightAux>(wr, wl + (2 * q + pw) * 1024, (uint32_t)((2 * q + pw) * 1024 + lane * 16) | oob, sw);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int row = (2 * q + pw) * 8 + (lane >> 3);
