@@ -391,13 +391,18 @@ hipError_t launch_down_all(moe_fp8_prefill* h, int64_t P, hipStream_t s, hipEven
   const Dims& m = h->m;
   const int64_t nb = m.H / kBlock, nb2 = (nb + 1) / 2;
   DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2,
-              h->small_tiles, h->n_tiles, h->y, h->shT, P * m.nI * 4, (int32_t)P};
+              h->small_tiles, h->n_tiles, h->y, h->shT, P * m.nI * 4, (int32_t)P, nullptr};
   Tile* lists[3] = {h->small_tiles, h->narrow_tiles, h->wide_tiles};
   for (int kind = kGemmStream; kind <= kGemmWide; ++kind) {
-    const int64_t items = max_tiles(m, P, kind) * (kind == kGemmStream ? nb : nb2);
+    // the 128-row and the 256-row tiles run in one launch of the same
+    // kernel (after[kGemmNarrow] is then recorded before it)
+    const int64_t items = kind == kGemmStream ? max_tiles(m, P, kind) * nb
+                          : kind == kGemmWide ? (max_tiles(m, P, kGemmNarrow) + max_tiles(m, P, kGemmWide)) * nb2
+                                              : 0;
     if (items > 0) {
-      da.tiles = lists[kind];
-      da.n_tiles = h->n_tiles + kind;
+      da.tiles = lists[kind == kGemmWide ? kGemmNarrow : kind];
+      da.n_tiles = h->n_tiles + (kind == kGemmWide ? kGemmNarrow : kind);
+      da.tiles2 = kind == kGemmWide ? h->wide_tiles : nullptr;
       hipError_t e = launch_down(da, kind, gemm_grid(h, items, kind, false), s);
       if (e != hipSuccess) return e;
     }

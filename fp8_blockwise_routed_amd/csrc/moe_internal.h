@@ -114,6 +114,9 @@ struct DownArgs {
   const float* shT;    // [Ip/128][P], K-block major
   int64_t shT_bytes;
   int32_t P;
+  // down_wide_kernel: a second tile list whose items follow the first list's
+  // (count n_tiles[1]), or null
+  const Tile* tiles2;
 };
 
 struct CombineArgs {

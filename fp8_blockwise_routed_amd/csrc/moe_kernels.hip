@@ -1534,7 +1534,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
   const int col = lane & 15, grp = lane >> 4;
   const int H = a.H, Ip = a.Ip, nI = Ip / kBlock, NB = H / kBlock;
   const int NB2 = (NB + 1) >> 1;
-  const int n_items = a.n_tiles[0] * NB2;
+  // items of the first list, then those of the second (one launch covers
+  // the 128-row and the 256-row tiles, so only one launch ends with a tail)
+  const int n_first = a.n_tiles[0] * NB2;
+  const int n_items = n_first + (a.tiles2 != nullptr ? a.n_tiles[1] * NB2 : 0);
+  auto item_at = [&](int i) __attribute__((always_inline)) {
+    return i < n_first ? item_of(i, NB2, a.tiles) : item_of(i - n_first, NB2, a.tiles2);
+  };
   const rsrc_t hr = make_rsrc(a.hq, (uint32_t)a.hq_bytes);
   const rsrc_t sr = make_rsrc(a.shT, (uint32_t)a.shT_bytes);
   // the wave's 8 KiB of the stage: block wn / 2, groups 2 (wn % 2), +1
@@ -1558,6 +1564,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
   struct Src {
     rsrc_t wr;
     uint32_t wvo[4], avo[4], svo;
+    int g8;  // 8-row groups of the tile that hold rows
   };
   auto src_of = [&](const Item& it) __attribute__((always_inline)) {
     Src q;
@@ -1566,6 +1573,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
     const int wblk = __builtin_amdgcn_readfirstlane(it.e * NB + nb2);
     const int wbytes = __builtin_amdgcn_readfirstlane((two ? 2 : 1) * nI * kDownChunk);
     q.wr = make_rsrc(a.w2 + (size_t)wblk * nI * kDownChunk, (uint32_t)wbytes);
+    q.g8 = (it.rows + 7) >> 3;
     // lane terms from an opaque thread id: not shared with (and kept live
     // from) the other call
     int ltid = (int)threadIdx.x;
@@ -1597,7 +1605,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
       uint8_t* al = st == 0 ? a_lds0 : a_lds1;
       const uint32_t sa = in ? (uint32_t)(kb * kBlock) : 0u;
 #pragma unroll
-      for (int j = 2 * (p - 2); j < 2 * (p - 2) + 2; ++j) dma16<0>(hr, al + (j * 8 + wave) * 1024, q.avo[j] | oob, sa);
+      // no DMA for 8-row groups past the tile's rows: those LDS rows keep
+      // stale bytes, which reach only output rows that are never stored (a
+      // row of the product depends on its own activation row alone); 2-5%
+      // faster where tiles are half full (T = 4096, E=160 T=1024)
+      for (int j = 2 * (p - 2); j < 2 * (p - 2) + 2; ++j)
+        if (j * 8 + wave < q.g8) dma16<0>(hr, al + (j * 8 + wave) * 1024, q.avo[j] | oob, sa);
     } else {
       float* sl = st == 0 ? s_lds0 : s_lds1;
       dma4(sr, sl + wave * 64, q.svo | oob, in ? (uint32_t)(kb * a.P * 4) : 0u);
@@ -1609,7 +1622,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
 
   int item = item_index(0);
   if (item >= n_items) return;
-  Item it = item_of(item, NB2, a.tiles);
+  Item it = item_at(item);
   ws_dma(0, it);
   issue(std::integral_constant<int, 0>{}, 0, src_of(it));
 
@@ -1617,7 +1630,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
     const int buf = r & 1;
     const int next = item_index(r + 1);
     const bool has_next = next < n_items;
-    const Item nit = item_of(has_next ? next : item, NB2, a.tiles);
+    const Item nit = item_at(has_next ? next : item);
     const int nb2 = it.nb * 2;
     const bool two = nb2 + 1 < NB;  // second weight block present
     const int p0 = it.p0, rows = it.rows;

@@ -288,7 +288,9 @@ int moe_fp8_prefill_debug_mfma(const uint8_t* a, const uint8_t* b, float* d);
  * quantise, gate_up of experts with 1-16 rows (streaming), 17-128 rows
  * (128-row tiles) and more rows (256-row tiles), down in the same three
  * groups, combine; then clears the record.  A group with no work in the
- * pass takes the time of an empty stream interval. */
+ * pass takes the time of an empty stream interval.  down's last two groups
+ * run as one launch: its time is reported under the 256-row group and the
+ * 128-row group takes an empty interval. */
 #define MOE_NUM_STAGES 9
 int moe_fp8_prefill_set_timing(moe_fp8_prefill* h, int32_t enable);
 /* Timing of some stages only: events are recorded just at the boundaries of
