@@ -1083,6 +1083,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
   __shared__ __attribute__((aligned(256))) float sx_lds2[BM];
   __shared__ float ws_lds[2 * kMaxKBlocks];
   __shared__ int tok_lds[BM];
+  // promotion factors per stage: row scale x gate weight scale (rows 0-127),
+  // then x up weight scale, formed by the producer pair that waited for the
+  // block (the matrix waves then read two factors per row)
+  __shared__ __attribute__((aligned(256))) float cs_lds0[2 * BM];
+  __shared__ __attribute__((aligned(256))) float cs_lds1[2 * BM];
+  __shared__ __attribute__((aligned(256))) float cs_lds2[2 * BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1138,6 +1144,21 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
     dma4(sr, sl + pw * 64, svo | oob, in ? (uint32_t)(kb * a.T * 4) : 0u);
   };
 
+  // block kb's factors of row 64 pw + lane into stage ST (producer pair that
+  // waited for the block; past the last block the last weight scales)
+  auto put_cs = [&](auto ST, int kb) __attribute__((always_inline)) {
+    constexpr int st = decltype(ST)::value;
+    const float* sl = st == 0 ? sx_lds0 : (st == 1 ? sx_lds1 : sx_lds2);
+    float* cs = st == 0 ? cs_lds0 : (st == 1 ? cs_lds1 : cs_lds2);
+    int ltid = (int)threadIdx.x;
+    asm volatile("" : "+v"(ltid));
+    const int row = pw * 64 + (ltid & 63);
+    const int kc = kb < nH ? kb : nH - 1;
+    const float v = sl[row];
+    cs[row] = v * ws_lds[2 * kc];
+    cs[BM + row] = v * ws_lds[2 * kc + 1];
+  };
+
   int item = item_index(0);
   if (item >= n_items) return;
   Item it = item_of(item, NB, a.tiles);
@@ -1170,10 +1191,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
           asm volatile("" : "+v"(ltid));
           const int ll = ltid & 63, lg = (ll >> 4) & 3;
           const int afc0 = ((2 * lg) ^ swz(ll)) << 4, afc1 = ((2 * lg + 1) ^ swz(ll)) << 4;
-          const float wsg = ws_lds[2 * kb], wsu = ws_lds[2 * kb + 1];
           const uint8_t* wbuf = (s == 0 ? w_lds0 : (s == 1 ? w_lds1 : w_lds2)) + wn * 8192 + ll * 16;
           const uint8_t* abuf = (s == 0 ? a_lds0 : (s == 1 ? a_lds1 : a_lds2)) + (ll & 15) * 128;
-          const float* srow = (s == 0 ? sx_lds0 : (s == 1 ? sx_lds1 : sx_lds2)) + lg * 4;
+          const float* crow = (s == 0 ? cs_lds0 : (s == 1 ? cs_lds1 : cs_lds2)) + lg * 4;
           i32x8 B[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) B[t] = cat(ld16(wbuf + t * 2048), ld16(wbuf + t * 2048 + 1024));
@@ -1181,15 +1201,16 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
           // the VALU promotes subtile m - 1 (the matrix wave is alone on its
           // SIMD, so nothing else would fill the MFMA pipe meanwhile)
           i32x8 A2[2];
-          f32x4 R3[3], P[2][4];
+          f32x4 P[2][4];
           A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
-          R3[0] = ld16f(srow);
+          f32x4 G3[3], U3[3];
+          G3[0] = ld16f(crow);
+          U3[0] = ld16f(crow + BM);
           auto promote = [&](auto J) __attribute__((always_inline)) {
             constexpr int j = decltype(J)::value;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float rs = R3[j % 3][i];
-              const float cg = rs * wsg, cu = rs * wsu;
+              const float cg = G3[j % 3][i], cu = U3[j % 3][i];
               acc[j][0][i] = __builtin_fmaf(P[j & 1][0][i], cg, acc[j][0][i]);
               acc[j][1][i] = __builtin_fmaf(P[j & 1][1][i], cg, acc[j][1][i]);
               acc[j][2][i] = __builtin_fmaf(P[j & 1][2][i], cu, acc[j][2][i]);
@@ -1201,7 +1222,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
             constexpr int m = decltype(M)::value;
             if constexpr (m + 1 < MT) {
               A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
-              R3[(m + 1) % 3] = ld16f(srow + (m + 1) * 16);
+              G3[(m + 1) % 3] = ld16f(crow + (m + 1) * 16);
+              U3[(m + 1) % 3] = ld16f(crow + BM + (m + 1) * 16);
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) P[m & 1][t] = mfma_e4m3(A2[m & 1], B[t]);
@@ -1330,16 +1352,22 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
       const rsrc_t wr = wrsrc(it);
       auto pstep = [&](auto S, int kb) __attribute__((always_inline)) {
         constexpr int s = decltype(S)::value;
-        if (pair == (kb & 1))
+        if (pair == (kb & 1)) {
           issue(std::integral_constant<int, (s + 2) % 3>{}, kb + 2, wr, rows);
-        else
+        } else {
           __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): block kb + 1 has landed
+          put_cs(std::integral_constant<int, (s + 1) % 3>{}, kb + 1);
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        }
         ring_barrier();
       };
-      if (pair == 1)
+      if (pair == 1) {
         issue(std::integral_constant<int, 1>{}, 1, wr, rows);
-      else
+      } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): block 0 has landed
+        put_cs(std::integral_constant<int, 0>{}, 0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      }
       ring_barrier();
       for (int kb0 = 0; kb0 < nH; kb0 += 3) {
         pstep(std::integral_constant<int, 0>{}, kb0);
