@@ -215,7 +215,7 @@ def summarize_profiles(out_dir: str) -> int:
     copy_kib = (1 << 30) / 1024
     f_scale, w_scale = copy_kib / cf_kib, copy_kib / cw_kib
     hbm = int(round((f_kib * f_scale + w_kib * w_scale) * 1024))
-    lines = [f"# HBM traffic of {DOMINANT}<3> (gate_up, experts with 1..16 rows), "
+    lines = [f"# HBM traffic of {DOMINANT}<5> (gate_up, experts with 1..16 rows), "
              "GLM-class layer E=256 T=256", "",
              "Commands (repository root, one MI355X), one counter per run:", ""]
     lines += [f"    {PROFILE_COMMANDS[k]}" for k in ("fetch", "write", "copy_fetch", "copy_write")]

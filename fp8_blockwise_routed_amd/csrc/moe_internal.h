@@ -14,7 +14,7 @@ constexpr int kSmallRows = 16;       // experts with <= this many rows use the 1
 constexpr int kNarrowRows = 128;     // experts with kSmallRows < rows <= kNarrowRows: one tile, 3-stage GEMMs
 constexpr int kWideRows = 256;       // rows per tile of the 8-wave GEMMs for experts with more rows
 #ifndef MOE_STREAM_DEPTH
-#define MOE_STREAM_DEPTH 3
+#define MOE_STREAM_DEPTH 5
 #endif
 #ifndef MOE_STREAM_DEPTH_DOWN
 #define MOE_STREAM_DEPTH_DOWN 6
@@ -23,7 +23,7 @@ constexpr int kWideRows = 256;       // rows per tile of the 8-wave GEMMs for ex
 #define MOE_WEIGHT_AUX 2
 #endif
 #ifndef MOE_GU_WG_PER_CU
-#define MOE_GU_WG_PER_CU 3
+#define MOE_GU_WG_PER_CU 2
 #endif
 #ifndef MOE_DN_WG_PER_CU
 #define MOE_DN_WG_PER_CU 2

@@ -555,7 +555,7 @@ __device__ __forceinline__ int item_index(int r) {
 // epilogue arithmetic as gate_up_kernel, so a row's bits do not depend on
 // which variant ran it.
 template <int D>
-__global__ __launch_bounds__(kThreads, D <= 2 ? 4 : 3) void gate_up_stream_kernel(GateUpArgs a) {
+__global__ __launch_bounds__(kThreads, kGateUpWgPerCu) void gate_up_stream_kernel(GateUpArgs a) {
   constexpr int BM = kSmallRows;
   __shared__ float sxt[BM][kMaxKBlocks];
   __shared__ float ws_lds[2 * kMaxKBlocks];
