@@ -2003,6 +2003,7 @@ hipError_t launch_down_a16(const DownA16Args& a, int grid, hipStream_t s) {
 // thread has its k rows in flight at once; the sums keep the slot order.
 
 constexpr int kCombineSlots = 8;  // routed slots loaded together (more: in groups of 8)
+constexpr int kCombineMaxSlots = 257;  // top_k <= 256, plus the shared slot
 
 __device__ __forceinline__ void acc_slot(f32x4 (&acc)[2], const f32x4 (&v)[2], float wj, bool on) {
 #pragma unroll
@@ -2017,8 +2018,9 @@ __device__ __forceinline__ void acc_slot(f32x4 (&acc)[2], const f32x4 (&v)[2], f
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x;
   const int k = a.k, H = a.H;
-  __shared__ int pos[256];
-  __shared__ float wt[256];
+  // a token's slots: up to 256 routed ones and the shared one
+  __shared__ int pos[kCombineMaxSlots];
+  __shared__ float wt[kCombineMaxSlots];
   const int kr = a.k_routed;
   for (int j = threadIdx.x; j < k; j += 256) {
     pos[j] = a.inv[(size_t)t * k + j];

@@ -23,6 +23,9 @@ CASES = [
     ("pad192", (6, 3, 512, 192, 50, 2.5, gen.ROUTE_SIGMOID_NORMAL)),
     ("many_rows", (4, 2, 256, 256, 600, 1.0, gen.ROUTE_SIGMOID_UNIFORM)),
     ("slice_t64", (160, 8, 5120, 192, 64, 1.0, gen.ROUTE_SIGMOID_NORMAL)),
+    # the most slots a token can have: every one of 256 experts plus the
+    # shared one (257 slots per token in the combine)
+    ("k256_all", (256, 256, 128, 128, 3, 1.0, gen.ROUTE_SIGMOID_NORMAL)),
 ]
 
 
@@ -30,7 +33,13 @@ def shared_case(spec, seed=0):
     E, k, H, I, T, rho, route = spec
     layer = gen.make_layer(E + 1, H, I, seed=seed)
     x, _ = gen.make_tokens(T, H, seed=seed, outlier_frac=0.02)
-    ids, w = gen.make_routing(T, E, k, route, seed=seed)
+    if k <= 64:
+        ids, w = gen.make_routing(T, E, k, route, seed=seed)
+    else:  # beyond the generator's router: every token takes k distinct experts
+        rng = np.random.default_rng(seed)
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        w = rng.uniform(0.5, 1.5, size=(T, k)).astype(np.float32)
+        w /= w.sum(axis=1, keepdims=True)
     return layer, x, ids, w, rho
 
 
