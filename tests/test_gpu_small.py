@@ -30,6 +30,10 @@ CASES = [
     # ~470 rows per expert: 256-row tiles with both halves full; odd K-block
     # counts (H/128 = 3, Ip/128 = 3) and an odd count of down column blocks
     ("wide_odd", (3, 2, 384, 320, 700, gen.ROUTE_SIGMOID_UNIFORM, 2.5, 0.01)),
+    # the largest K loops the library takes (H / 128 = 128 for gate_up,
+    # Ip / 128 = 128 for down), 150 rows per expert (256-row tiles)
+    ("max_h", (2, 2, 16384, 256, 150, gen.ROUTE_SIGMOID_NORMAL, 1.0, 0.01)),
+    ("max_i", (2, 2, 256, 16384, 150, gen.ROUTE_SIGMOID_NORMAL, 1.0, 0.01)),
 ]
 
 
