@@ -552,8 +552,8 @@ __device__ __forceinline__ int item_index(int r) {
 // fragment (L2 resident) and weight fragments straight into registers, D K
 // blocks deep, so the four waves stream independently.  Row scales for all K
 // blocks are staged in LDS once per tile.  Same MFMA, promotion order and
-// epilogue arithmetic as gate_up_kernel, so a row's bits do not depend on
-// which variant ran it.
+// epilogue arithmetic as the tile kernels, so a row's bits do not depend on
+// which kernel ran it.
 template <int D>
 __global__ __launch_bounds__(kThreads, kGateUpWgPerCu) void gate_up_stream_kernel(GateUpArgs a) {
   constexpr int BM = kSmallRows;
@@ -677,7 +677,7 @@ __global__ __launch_bounds__(kThreads, kGateUpWgPerCu) void gate_up_stream_kerne
   }
 }
 
-// gate_up for experts with more than kSmallRows rows: a 512-thread workgroup
+// gate_up for experts with more than kNarrowRows rows: a 512-thread workgroup
 // (two waves per SIMD, up to 256 registers each) computes a tile of up to 256
 // rows x (128 gate + 128 up) columns of one 128-row block nb, so the epilogue
 // sees whole 128-wide groups of h.  Both operands arrive in LDS by
@@ -1063,11 +1063,18 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
     it = nit;
   }
 }
-// waits for them at the end of the next step), so every wait is a plain
-// vmcnt(0) on the waiting wave's own loads, and the matrix waves never wait
-// on memory.  While the matrix waves quantise one item's h, the producers
-// already fetch the next item's row list, weight scales and first K block,
-// so the weight stream does not stop between items.
+// gate_up for experts with 17..128 rows: one 128-row tile per (expert,
+// 128-column block), bound by the weight stream.  Waves 0-3 multiply (one
+// per SIMD, 128 rows x 32 gate + 32 up columns each) out of three LDS
+// stages; waves 4-7 only move data.  Producer pair kb % 2 issues block
+// kb + 2 (weights, activation rows gathered through the plan, row scales)
+// into the stage read in step kb - 1, while the other pair waits for block
+// kb + 1 (which it issued the step before) and forms that block's promotion
+// factors in LDS, so every wait is a plain vmcnt(0) on the waiting wave's
+// own loads and the matrix waves never wait on memory.  While the matrix
+// waves quantise one item's h, the producers already fetch the next item's
+// row list, weight scales and first K block, so the weight stream does not
+// stop between items.
 template <bool kDbg>
 __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpArgs a) {
   constexpr int BM = kNarrowRows;
@@ -1539,8 +1546,9 @@ __global__ __launch_bounds__(kThreads, kDownWgPerCu) void down_stream_kernel(Dow
   }
 }
 
-// down for experts with more than kSmallRows rows: a 512-thread workgroup
-// computes up to 256 rows x 256 hidden columns (weight blocks nb2, nb2 + 1),
+// down for experts with more than kSmallRows rows (the 128-row and the
+// 256-row tile lists, in one launch): a 512-thread workgroup computes up to
+// 256 rows x 256 hidden columns (weight blocks nb2, nb2 + 1),
 // both operands double-buffered in LDS by buffer-load-to-LDS as in
 // gate_up_wide_kernel.  Wave w = 4 mh + wn owns rows 128 mh .. +127 and 64
 // columns: block nb2 + wn / 2, 32-column groups 2 (wn % 2) and 2 (wn % 2) + 1.
