@@ -83,8 +83,15 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source without comments and blank lines, so that a
+    comment edit does not retire counters taken on the same code."""
+    import re
+    with open(KERNEL_SOURCE, "r") as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    code = "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def algorithmic_work(wl, counts, a16=False):
