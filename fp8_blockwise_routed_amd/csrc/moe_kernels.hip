@@ -1994,13 +1994,129 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void down_a16_kernel(Down
   }
 }
 
+// down, one flat sequence per workgroup: its units (item, 16-row subtile of
+// the item's tile) in order, each Ip / 128 K steps, with the loads of the
+// next unit's first D - 1 blocks issued during the current unit's last
+// steps (D divides Ip / 128, so a block's ring slot is its index mod D in
+// every unit).  The weight scale of a step is a scalar load.  Same
+// arithmetic, in the same order, as down_a16_kernel.
+template <int D>
+__global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void down_a16_flat_kernel(DownA16Args a) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int H = a.H, Ip = a.Ip, nI = Ip / kBlock, NB = H / kBlock;
+  const int n0 = a.n_tiles[0], n1 = a.n_tiles[1], n2 = a.n_tiles[2];
+  const int n_items = (n0 + n1 + n2) * NB;
+  const int G = (int)gridDim.x;
+  if ((int)blockIdx.x >= n_items) return;
+  const rsrc_t hr = make_rsrc(a.hb, (uint32_t)a.hb_bytes);
+  const uint32_t bvoff = (uint32_t)(wave * 4096 + lane * 16);
+
+  struct Unit {
+    int item, wblk, p0, rows, c0;  // wblk = e * NB + nb; item >= n_items: past the end
+  };
+  auto first_unit = [&](int it) __attribute__((always_inline)) {
+    Unit u{it, 0, 0, 0, 0};
+    if (it < n_items) {
+      const int ti = it / NB, nb = it - ti * NB;
+      const Tile* tp = a16_tile(a.tiles, n0, n1, ti);
+      u.wblk = __builtin_amdgcn_readfirstlane(tp->e) * NB + nb;
+      u.p0 = __builtin_amdgcn_readfirstlane(tp->p0);
+      u.rows = __builtin_amdgcn_readfirstlane(tp->rows);
+    }
+    return u;
+  };
+  auto next_unit = [&](const Unit& u) __attribute__((always_inline)) {
+    if (u.c0 + 16 < u.rows) {
+      Unit v = u;
+      v.c0 += 16;
+      return v;
+    }
+    return first_unit(u.item + G);
+  };
+  auto load = [&](const Unit& u, int kb, i32x4(&af)[4], i32x8(&bf)[2]) __attribute__((always_inline)) {
+    const bool in = u.item < n_items;
+    const uint32_t oob = in ? 0u : 0x80000000u;
+    const uint32_t sa = in ? (uint32_t)(kb * kBlock * 2) : 0u, so = in ? (uint32_t)(kb * kDownChunk) : 0u;
+    const rsrc_t wr = make_rsrc(a.w2 + (size_t)u.wblk * nI * kDownChunk, (uint32_t)(nI * kDownChunk));
+    const int r = u.c0 + col;
+    const uint32_t avo = (uint32_t)((u.p0 + (r < u.rows ? r : u.c0)) * Ip * 2 + grp * 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) af[j] = bload16(hr, avo + oob, sa + j * 16);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      bf[t] = cat(wload16(wr, bvoff + oob, so + t * 2048), wload16(wr, bvoff + oob, so + t * 2048 + 1024));
+  };
+
+  // a unit's weight scales, lane l holding blocks l and l + 64; the next
+  // unit's are loaded at the start of the current one, so their wait does
+  // not hold up the blocks in flight
+  auto load_ws = [&](const Unit& u, float& w0, float& w1) __attribute__((always_inline)) {
+    const bool in = u.item < n_items;
+    const rsrc_t sr = make_rsrc(a.s2 + (size_t)u.wblk * nI, (uint32_t)(nI * 4));
+    w0 = bloadf(sr, (uint32_t)(lane * 4) | (in && lane < nI ? 0u : 0x80000000u), 0u);
+    w1 = bloadf(sr, (uint32_t)((lane + 64) * 4) | (in && lane + 64 < nI ? 0u : 0x80000000u), 0u);
+  };
+  Unit cu = first_unit((int)blockIdx.x);
+  Unit nu = next_unit(cu);
+  float ws0, ws1, wn0, wn1;
+  load_ws(cu, ws0, ws1);
+  i32x4 A[D][4];
+  i32x8 B[D][2];
+#pragma unroll
+  for (int s = 0; s < D - 1; ++s) load(cu, s, A[s], B[s]);
+  while (cu.item < n_items) {
+    load_ws(nu, wn0, wn1);
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int kb0 = 0; kb0 < nI; kb0 += D) {
+#pragma unroll
+      for (int s = 0; s < D; ++s) {
+        const int lk = kb0 + s + D - 1;
+        if (lk < nI)
+          load(cu, lk, A[(s + D - 1) % D], B[(s + D - 1) % D]);
+        else
+          load(nu, lk - nI, A[(s + D - 1) % D], B[(s + D - 1) % D]);
+        const int kb = kb0 + s;
+        const float wsc = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kb < 64 ? ws0 : ws1), kb & 63));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f32x4 p = mfma_a16_block(A[s], B[s][t]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(p[i], wsc, acc[t][i]);
+        }
+      }
+    }
+    const int nb = cu.wblk % NB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = cu.c0 + grp * 4 + i;
+      if (row < cu.rows) {
+        float* dst = a.y + (size_t)(cu.p0 + row) * H + nb * kBlock + wave * 32 + col;
+        dst[0] = acc[0][i];
+        dst[16] = acc[1][i];
+      }
+    }
+    cu = nu;
+    nu = next_unit(cu);
+    ws0 = wn0;
+    ws1 = wn1;
+  }
+}
+
 hipError_t launch_gate_up_a16(const GateUpA16Args& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL(gate_up_a16_kernel<3>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_a16(const DownA16Args& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(down_a16_kernel<4>, dim3(grid), dim3(kThreads), 0, s, a);
+  const int nI = a.Ip / kBlock;
+  if (nI % 4 == 0)
+    hipLaunchKernelGGL(down_a16_flat_kernel<4>, dim3(grid), dim3(kThreads), 0, s, a);
+  else if (nI % 2 == 0)
+    hipLaunchKernelGGL(down_a16_flat_kernel<2>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(down_a16_kernel<4>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
