@@ -350,6 +350,11 @@ SMALL_CASES = [
     (4, 3, 384, 192, 24, gen.ROUTE_SIGMOID_NORMAL, 2.5, 0.1),
     (3, 1, 256, 64, 16, gen.ROUTE_SIGMOID_NORMAL, 1.0, 0.1),
     (6, 6, 256, 256, 8, gen.ROUTE_SIGMOID_UNIFORM, 2.5, 0.2),
+    # top-8, as in the GLM-class layer
+    (10, 8, 256, 128, 12, gen.ROUTE_SIGMOID_NORMAL, 2.5, 0.1),
+    # the tensor-sliced share's shape (H=5120, I=192 padded to 256), few experts
+    (3, 2, 5120, 192, 6, gen.ROUTE_SIGMOID_NORMAL, 1.0, 0.2),
+    (12, 8, 5120, 192, 4, gen.ROUTE_SIGMOID_NORMAL, 1.0, 0.25),
 ]
 
 
@@ -379,6 +384,25 @@ def pin_ffn_vs_bruteforce(tol=2e-3):
             return _ok(False, f"non-finite output in case {case}")
         worst = max(worst, float(rel_l2_rows(out, ref).max()))
     return _ok(worst <= tol, f"worst per-row rel L2 {worst:.3g}")
+
+
+def pin_down_combine_reproduces_forward():
+    """The continuation used by the staged GPU comparisons: down_combine fed
+    with forward's own h codes and scales gives forward's y and output rows
+    bit for bit (routed layers in both output types, and with a shared slot)."""
+    ok, detail = True, ""
+    cases = [(small_case(c), 0) for c in SMALL_CASES]
+    layer, x, _, _, ids_x, w_x, _ = shared_case()
+    cases.append(((layer, x, ids_x, w_x, 2.5), 1))
+    for (layer, x, ids, w, rho), n_shared in cases:
+        for od in (oracle.OUT_F32, oracle.OUT_BF16):
+            out, d = oracle.forward(layer, x, ids, w, rho, od, debug=True, n_shared=n_shared)
+            out2, y2 = oracle.down_combine(layer, d["hq"], d["sh"], ids, w, rho, od, n_shared=n_shared)
+            same_y = np.array_equal(y2.view(np.uint32), d["y"].view(np.uint32))
+            same_o = np.array_equal(out2.view(np.uint8), out.view(np.uint8))
+            if not (same_y and same_o):
+                ok, detail = False, f"E={layer.E} H={layer.H} I={layer.I} od={od} y={same_y} out={same_o}"
+    return _ok(ok, detail)
 
 
 def _torch_qdq(v64: np.ndarray) -> np.ndarray:
@@ -794,6 +818,7 @@ ALL_PINS = {
     "dense_textbook": pin_dense_textbook,
     "integer_exact_gate_up": pin_integer_exact_gate_up,
     "down_vs_matmul": pin_down_vs_matmul,
+    "down_combine_reproduces_forward": pin_down_combine_reproduces_forward,
     "activation_from_gu": pin_activation_from_gu,
     "linearity": pin_linearity,
     "permutation_equivariance": pin_permutation_equivariance,
