@@ -113,6 +113,8 @@ def _load():
         lib.orc_set_activation_limit.restype = None
         lib.orc_route.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P]
         lib.orc_route.restype = ctypes.c_int32
+        lib.orc_silu_mul_array.argtypes = [P, P, ctypes.c_int64, P]
+        lib.orc_silu_mul_array.restype = None
         _lib = lib
     return _lib
 
@@ -163,6 +165,16 @@ def f32_to_bf16(f: np.ndarray) -> np.ndarray:
     v = np.ascontiguousarray(f, dtype=np.float32)
     out = np.empty(v.shape, np.uint16)
     _load().orc_f32_to_bf16_array(_p(v), v.size, _p(out))
+    return out
+
+
+def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """h = silu(g) * u elementwise in FP32, as the layer computes it (with
+    the activation limit currently set)."""
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    out = np.empty(g.shape, np.float32)
+    _load().orc_silu_mul_array(_p(g), _p(u), g.size, _p(out))
     return out
 
 

@@ -302,7 +302,16 @@ static float silu_mul(float g, float u) {
     if (u > L) u = L;
     if (u < -L) u = -L;
   }
-  return (g / (1.0f + expf(-g))) * u;
+  /* e^-g correctly rounded to FP32: evaluated in double and rounded once
+   * (the pages fix only "z / (1 + e^-z)" in FP32; a correctly rounded
+   * exponential makes that value independent of any libm's last bit). */
+  const float e = (float)exp(-(double)g);
+  return (g / (1.0f + e)) * u;
+}
+
+/* h = silu(g) * u elementwise, as the layer computes it (test access). */
+void orc_silu_mul_array(const float* g, const float* u, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = silu_mul(g[i], u[i]);
 }
 
 /* Down projection of the decoded h rows (sorted order) and the weighted

@@ -539,6 +539,41 @@ def pin_activation_from_gu():
     return _ok(err <= 1e-2, f"worst rel L2 {err:.3g}")
 
 
+def _f32_nearest(x):
+    """The FP32 value nearest to the mpmath number x (ties to even)."""
+    import mpmath
+    if abs(x) >= mpmath.mpf(2) ** 128 - mpmath.mpf(2) ** 103:  # rounds to infinity
+        return np.float32(np.inf) if x > 0 else np.float32(-np.inf)
+    f = np.float32(float(x))
+    best = f
+    for c in (np.nextafter(f, np.float32(-np.inf)), np.nextafter(f, np.float32(np.inf))):
+        dc, db = abs(mpmath.mpf(float(c)) - x), abs(mpmath.mpf(float(best)) - x)
+        if dc < db or (dc == db and (int(c.view(np.uint32)) & 1) == 0):
+            best = c
+    return best
+
+
+def pin_silu_exponential_correctly_rounded():
+    """silu(g) * u = (g / (1 + e)) * u in FP32 with e the correctly rounded
+    FP32 value of e^-g: checked against a 60-digit mpmath exponential rounded
+    to FP32 by comparison with both neighbours, then numpy's IEEE FP32 add,
+    divide and multiply."""
+    import mpmath
+    mpmath.mp.dps = 60
+    rng = np.random.default_rng(31)
+    g = np.concatenate([rng.standard_normal(1500) * 3, rng.uniform(-90, 90, 300),
+                        np.float32([0.0, -0.0, 1e-30, -1e-30, 88.0, -87.0, -103.0, 20.5])]).astype(np.float32)
+    u = rng.standard_normal(g.size).astype(np.float32)
+    got = oracle.silu_mul(g, u)
+    bad = 0
+    for gi, ui, hi in zip(g, u, got):
+        e = _f32_nearest(mpmath.exp(-mpmath.mpf(float(gi))))
+        ref = np.float32(np.float32(gi) / np.float32(np.float32(1.0) + e)) * ui
+        if ref.view(np.uint32) != np.float32(hi).view(np.uint32) and not (np.isnan(ref) and np.isnan(hi)):
+            bad += 1
+    return _ok(bad == 0, f"{bad} of {g.size} values differ")
+
+
 def pin_a16_vs_bruteforce(tol=4e-3):
     """The W8A16 form against the dense FP64 evaluation without activation
     quantisation.  tol = 2 x 2^-9: the BF16 rounding of h (relative error at
@@ -819,6 +854,7 @@ ALL_PINS = {
     "integer_exact_gate_up": pin_integer_exact_gate_up,
     "down_vs_matmul": pin_down_vs_matmul,
     "down_combine_reproduces_forward": pin_down_combine_reproduces_forward,
+    "silu_exponential_correctly_rounded": pin_silu_exponential_correctly_rounded,
     "activation_from_gu": pin_activation_from_gu,
     "linearity": pin_linearity,
     "permutation_equivariance": pin_permutation_equivariance,
