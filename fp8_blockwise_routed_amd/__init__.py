@@ -33,6 +33,8 @@ MOE_ACT_SILU_CLAMPED = 1
 MOE_ROUTER_SOFTMAX = 0
 MOE_ROUTER_SIGMOID = 1
 MOE_NUM_STAGES = 9
+MOE_CALIBRATE_MFMA = 0
+MOE_CALIBRATE_STREAM = 1
 STAGES = ("plan", "quant", "gate_up_stream", "gate_up_narrow", "gate_up_wide", "down_stream", "down_narrow",
           "down_wide", "combine")
 
@@ -46,6 +48,7 @@ EXPORTED = (
     "moe_fp8_prefill_set_timing_stages", "moe_fp8_prefill_read_timing", "moe_fp8_prefill_debug_inject_failure",
     "moe_fp8_prefill_route", "moe_fp8_prefill_run_logits", "moe_fp8_prefill_run_decode",
     "moe_fp8_prefill_create_streamed", "moe_fp8_prefill_stage", "moe_fp8_prefill_select_slot",
+    "moe_fp8_prefill_calibrate",
 )
 
 
@@ -107,6 +110,7 @@ def load_library() -> ctypes.CDLL:
         "moe_fp8_prefill_create_streamed": ([D, I32, ctypes.POINTER(P)], ctypes.c_int),
         "moe_fp8_prefill_stage": ([P, I32, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_fp8_prefill_select_slot": ([P, I32], ctypes.c_int),
+        "moe_fp8_prefill_calibrate": ([I32, I64, P, I64, P, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -327,6 +331,16 @@ def moe_fp8_prefill_debug_mfma(a: np.ndarray, b: np.ndarray, both: bool = False)
     _check(load_library().moe_fp8_prefill_debug_mfma(_np_ptr(a), _np_ptr(b), _np_ptr(d)),
            "moe_fp8_prefill_debug_mfma")
     return d[0] if not both else d
+
+
+def moe_fp8_prefill_calibrate(kind: int, n: int, buf, stream=None) -> float:
+    """Enqueue a calibration launch on `stream` over the device tensor buf;
+    returns its algorithmic work (FLOPs or bytes)."""
+    work = ctypes.c_double(0.0)
+    nbytes = int(buf.numel() * buf.element_size())
+    _check(load_library().moe_fp8_prefill_calibrate(int(kind), int(n), _dev_ptr(buf), nbytes,
+                                                   _stream_ptr(stream), ctypes.byref(work)), "calibrate")
+    return work.value
 
 
 def moe_fp8_prefill_set_timing(handle: int, enable: bool) -> None:

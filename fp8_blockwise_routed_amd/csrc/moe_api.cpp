@@ -25,6 +25,8 @@ struct Dims {
   int64_t E, k, H, I, Ip, nH, nI, max_rows, P;  // P = max_rows * k
   int64_t Er, kr, shared;
   int64_t I_full, I_off;  // checkpoint width and the share's start (I_full == I: no share)
+  // one 128-wide h group per row: h is quantised by the exact-tie quantiser
+  bool exact_ties() const { return nI == 1; }
 };
 
 // Description sizes of older callers: without shared_experts, and without
@@ -74,14 +76,14 @@ int64_t align256(int64_t n) { return (n + 255) & ~int64_t(255); }
 // Workspace pieces, in allocation order.
 struct WsSizes {
   int64_t xq, sx, sxT, hq, sh, shT, y, counts, offsets, perm, inv, small_tiles, narrow_tiles, wide_tiles, n_tiles, chunk,
-      err, rids, rw, hb;
+      err, rids, rw, hb, gu;
   int64_t total() const {
     return align256(xq) + align256(sx) + align256(sxT) + align256(hq) + align256(sh) + align256(shT) +
            align256(y) +
            align256(counts) + align256(offsets) + align256(perm) + align256(inv) +
            align256(small_tiles) + align256(narrow_tiles) + align256(wide_tiles) + align256(n_tiles) + align256(chunk) +
            align256(err) +
-           align256(rids) + align256(rw) + align256(hb);
+           align256(rids) + align256(rw) + align256(hb) + align256(gu);
   }
 };
 
@@ -108,13 +110,18 @@ WsSizes ws_sizes(const Dims& m) {
   w.rw = m.max_rows * m.kr * 4;
   // BF16 h of one W8A16 decode pass (at most kDecodeRows rows)
   w.hb = std::min<int64_t>(m.max_rows, kDecodeRows) * m.k * m.Ip * 2;
+  // FP32 gate|up of one pass for the exact-tie quantiser (Ip == 128 only)
+  w.gu = m.exact_ties() ? m.P * 2 * m.Ip * 4 : 0;
   return w;
 }
+
+// Gate|up row norms kept with the weights for the exact-tie quantiser.
+int64_t norm_bytes_of(const Dims& m) { return m.exact_ties() ? m.E * 2 * m.Ip * 4 : 0; }
 
 int64_t weight_bytes_of(const Dims& m) {
   const int64_t codes = m.E * (2 * m.Ip * m.H + m.H * m.Ip);
   const int64_t scales = m.E * (2 * m.nI * m.nH + m.nH * m.nI) * 4;
-  return align256(codes) + align256(scales);
+  return align256(codes) + align256(scales) + align256(norm_bytes_of(m));
 }
 
 struct StageEvents {
@@ -139,6 +146,7 @@ struct moe_fp8_prefill {
   float* s13 = nullptr;
   uint8_t* w2 = nullptr;
   float* s2 = nullptr;
+  float* n13 = nullptr;  // exact-tie layers: gate|up row norms
   // workspace
   uint8_t* xq = nullptr;
   float* sx = nullptr;
@@ -160,6 +168,7 @@ struct moe_fp8_prefill {
   int32_t* err = nullptr;
   int32_t* rids = nullptr;
   float* rw = nullptr;
+  float* gu = nullptr;  // exact-tie layers: FP32 gate|up of a pass
   std::vector<void*> allocations;
   // state
   std::atomic<int> busy{0};
@@ -172,6 +181,7 @@ struct moe_fp8_prefill {
     float* s13 = nullptr;
     uint8_t* w2 = nullptr;
     float* s2 = nullptr;
+    float* n13 = nullptr;
     hipEvent_t ready = nullptr;  // recorded when its staging has been enqueued
     hipEvent_t free = nullptr;   // recorded after the last pass that read it
     bool staged = false;
@@ -262,7 +272,7 @@ void staging_bytes(const Dims& m, bool src_on_device, int64_t out[4]) {
 // read it; no host synchronisation.
 int enqueue_upload(moe_fp8_prefill* h, const uint8_t* gate, const uint8_t* up, const uint8_t* down,
                    const float* gate_scale, const float* up_scale, const float* down_scale,
-                   bool src_on_device, uint8_t* w13, float* s13, uint8_t* w2, float* s2,
+                   bool src_on_device, uint8_t* w13, float* s13, uint8_t* w2, float* s2, float* n13,
                    const Staging& st, hipStream_t s) {
   const Dims& m = h->m;
   const int64_t wfull = m.I_full * m.H, sfull = (m.I_full + 127) / 128 * m.nH;
@@ -306,7 +316,7 @@ int enqueue_upload(moe_fp8_prefill* h, const uint8_t* gate, const uint8_t* up, c
       }
     }
     LayoutArgs a{dst[0], dst[1], dst[2], sdst[0], sdst[1], sdst[2], (int32_t)e0, (int32_t)n, (int32_t)m.H,
-                 (int32_t)m.I, (int32_t)m.Ip, w13, s13, w2, s2};
+                 (int32_t)m.I, (int32_t)m.Ip, w13, s13, w2, s2, n13};
     if (launch_layout(a, s) != hipSuccess) return MOE_ERR_DEVICE;
   }
   return MOE_OK;
@@ -336,7 +346,7 @@ int upload_weights(moe_fp8_prefill* h, hipStream_t s) {
   if (!(on_dev && !slicing(h->m))) rc = alloc_staging(h, on_dev, &st, &temp);
   if (rc == MOE_OK)
     rc = enqueue_upload(h, d->gate, d->up, d->down, d->gate_scale, d->up_scale, d->down_scale, on_dev,
-                        h->w13, h->s13, h->w2, h->s2, st, s);
+                        h->w13, h->s13, h->w2, h->s2, h->n13, st, s);
   if (hipStreamSynchronize(s) != hipSuccess && rc == MOE_OK) rc = MOE_ERR_DEVICE;
   for (void* p : temp) (void)hipFree(p);
   return rc;
@@ -365,6 +375,9 @@ hipError_t launch_gate_up_all(moe_fp8_prefill* h, int64_t t, int64_t P, float* g
                               hipEvent_t* after = nullptr) {
   const Dims& m = h->m;
   const int64_t nb = m.Ip / kBlock;
+  // layers with one h group per row: the GEMMs write FP32 gate|up, which the
+  // exact-tie quantiser turns into h codes and scales after the last launch
+  if (m.exact_ties() && !gu_dbg) gu_dbg = h->gu;
   GateUpArgs ga{h->xq, h->sx, t * m.H, t * m.nH * 4, h->perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip,
                 h->w13, h->s13, h->small_tiles, h->n_tiles, h->hq, h->sh, gu_dbg,
                 h->desc.activation == MOE_ACT_SILU_CLAMPED ? h->desc.activation_limit : 0.0f,
@@ -376,6 +389,14 @@ hipError_t launch_gate_up_all(moe_fp8_prefill* h, int64_t t, int64_t P, float* g
       ga.tiles = lists[kind];
       ga.n_tiles = h->n_tiles + kind;
       hipError_t e = launch_gate_up(ga, kind, gemm_grid(h, items, kind, true), s);
+      if (e != hipSuccess) return e;
+    }
+    if (kind == kGemmWide && m.exact_ties()) {
+      const float limit = h->desc.activation == MOE_ACT_SILU_CLAMPED ? h->desc.activation_limit : 0.0f;
+      TieArgs ta{gu_dbg, h->xq, h->sx, h->perm, h->offsets, (int32_t)m.E, (int32_t)m.k, (int32_t)m.H,
+                 h->w13, h->s13, h->n13, h->hq, h->sh, h->shT, limit,
+                 kTieMargin / sqrtf((float)m.nH)};
+      hipError_t e = launch_tie_exact(ta, P, s);
       if (e != hipSuccess) return e;
     }
     if (after && after[kind]) {
@@ -656,6 +677,7 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   h->s13 = (float*)get(m.E * m.nI * m.nH * 2 * 4);
   h->w2 = (uint8_t*)get(m.E * m.H * m.Ip);
   h->s2 = (float*)get(m.E * m.nH * m.nI * 4);
+  if (m.exact_ties()) h->n13 = (float*)get(norm_bytes_of(m));
   h->xq = (uint8_t*)get(w.xq);
   h->sx = (float*)get(w.sx);
   h->sxT = (float*)get(w.sxT);
@@ -676,6 +698,7 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   h->rids = (int32_t*)get(w.rids);
   h->rw = (float*)get(w.rw);
   h->hb = (uint16_t*)get(w.hb);
+  if (m.exact_ties()) h->gu = (float*)get(w.gu);
   if (!ok) {
     free_all(h);
     delete h;
@@ -892,6 +915,36 @@ int moe_fp8_prefill_debug_mfma(const uint8_t* a, const uint8_t* b, float* d) {
   return rc;
 }
 
+int moe_fp8_prefill_calibrate(int32_t kind, int64_t n, void* buf, int64_t buf_bytes, void* stream,
+                              double* work) {
+  constexpr int64_t kResultBytes = 64 * 1024;
+  if (!buf || !work || ((uintptr_t)buf & 15u) != 0 || buf_bytes < kResultBytes) return MOE_ERR_INVALID_ARG;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return MOE_ERR_DEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* result = (uint8_t*)buf + (buf_bytes - kResultBytes);
+  if (kind == MOE_CALIBRATE_MFMA) {
+    if (n < 1 || n > (int64_t(1) << 30)) return MOE_ERR_INVALID_ARG;
+    const int grid = 2 * cus;  // 8 waves per CU: two per SIMD
+    if (grid * 4 * 4 > kResultBytes) return MOE_ERR_UNSUPPORTED;
+    if (launch_peak_mfma((int32_t)n, grid, (float*)result, s) != hipSuccess) return MOE_ERR_DEVICE;
+    *work = (double)grid * 4 * (double)n * 8 * (2.0 * 16 * 16 * 128);
+    return MOE_OK;
+  }
+  if (kind == MOE_CALIBRATE_STREAM) {
+    const int64_t bytes = (buf_bytes - kResultBytes) & ~int64_t(15);
+    if (bytes <= 0) return MOE_ERR_INVALID_ARG;
+    const int grid = 4 * cus;
+    if (grid * 4 > kResultBytes) return MOE_ERR_UNSUPPORTED;
+    if (launch_peak_stream(buf, bytes, grid, (int32_t*)result, s) != hipSuccess) return MOE_ERR_DEVICE;
+    *work = (double)bytes;
+    return MOE_OK;
+  }
+  return MOE_ERR_INVALID_ARG;
+}
+
 int moe_fp8_prefill_set_timing(moe_fp8_prefill* h, int32_t enable) {
   if (!h) return MOE_ERR_INVALID_ARG;
   h->timing = enable != 0 ? (1u << MOE_NUM_STAGES) - 1u : 0u;
@@ -987,6 +1040,7 @@ int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slo
     h->slots[i].s13 = (float*)get(m.E * m.nI * m.nH * 2 * 4);
     h->slots[i].w2 = (uint8_t*)get(m.E * m.H * m.Ip);
     h->slots[i].s2 = (float*)get(m.E * m.nH * m.nI * 4);
+    if (m.exact_ties()) h->slots[i].n13 = (float*)get(norm_bytes_of(m));
   }
   if (ok) {
     Staging st;
@@ -1016,6 +1070,7 @@ int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slo
   h->rids = (int32_t*)get(w.rids);
   h->rw = (float*)get(w.rw);
   h->hb = (uint16_t*)get(w.hb);
+  if (m.exact_ties()) h->gu = (float*)get(w.gu);
   if (!ok) {
     free_all(h);
     delete h;
@@ -1036,6 +1091,7 @@ int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slo
   h->s13 = h->slots[0].s13;
   h->w2 = h->slots[0].w2;
   h->s2 = h->slots[0].s2;
+  h->n13 = h->slots[0].n13;
   *out = h;
   return MOE_OK;
 }
@@ -1072,7 +1128,7 @@ int moe_fp8_prefill_stage(moe_fp8_prefill* h, int32_t slot, const uint8_t* gate,
   st.full_codes = h->stage_full_codes;
   st.full_scales = h->stage_full_scales;
   const int rc = enqueue_upload(h, gate, up, down, gate_scale, up_scale, down_scale, false, sl.w13, sl.s13,
-                                sl.w2, sl.s2, st, s);
+                                sl.w2, sl.s2, sl.n13, st, s);
   if (rc != MOE_OK) return fail(h, rc);
   if (hipEventRecord(sl.ready, s) != hipSuccess || hipEventRecord(h->stage_done, s) != hipSuccess)
     return fail(h);
@@ -1092,6 +1148,7 @@ int moe_fp8_prefill_select_slot(moe_fp8_prefill* h, int32_t slot) {
   h->s13 = h->slots[slot].s13;
   h->w2 = h->slots[slot].w2;
   h->s2 = h->slots[slot].s2;
+  h->n13 = h->slots[slot].n13;
   h->busy.store(0);
   return MOE_OK;
 }

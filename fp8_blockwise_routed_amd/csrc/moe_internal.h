@@ -143,6 +143,26 @@ struct LayoutArgs {
   float* s13;
   uint8_t* w2;
   float* s2;
+  float* n13;  // [E][2*Ip] gate|up row norms for the exact-tie quantiser, or null
+};
+
+// The exact-tie quantiser of h for layers with Ip == 128 (tie_exact_kernel).
+constexpr float kTieMargin = 1.5e-4f;
+struct TieArgs {
+  const float* gu;         // [P][256] FP32 gate | up from the GEMM
+  const uint8_t* xq;       // [T][H]
+  const float* sx;         // [T][H/128]
+  const int32_t* perm;     // sorted position -> slot t*k+j
+  const int32_t* offsets;  // [E+1]
+  int32_t E, k, H;
+  const uint8_t* w13;      // swizzled
+  const float* s13;        // [E][1][H/128][2]
+  const float* n13;        // [E][256]
+  uint8_t* hq;             // [P][128]
+  float* sh;               // [P]
+  float* shT;              // [P]
+  float act_limit;
+  float margin;            // kTieMargin / sqrt(H / 128)
 };
 
 struct SliceArgs {
@@ -196,6 +216,10 @@ hipError_t launch_gate_up_a16(const GateUpA16Args& a, int grid, hipStream_t s);
 hipError_t launch_down_a16(const DownA16Args& a, int grid, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
 hipError_t launch_slice(const SliceArgs& a, hipStream_t s);
+hipError_t launch_tie_exact(const TieArgs& a, int64_t max_slots, hipStream_t s);
+hipError_t launch_wnorm(const LayoutArgs& a, hipStream_t s);
+hipError_t launch_peak_mfma(int32_t iters, int grid, float* out, hipStream_t s);
+hipError_t launch_peak_stream(const void* src, int64_t bytes, int grid, int32_t* out, hipStream_t s);
 hipError_t launch_mfma_probe(const uint8_t* a, const uint8_t* b, float* d, hipStream_t s);
 
 }  // namespace moe

@@ -2279,6 +2279,10 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(layout_w13_kernel, dim3((unsigned)((c13 + 255) / 256)), dim3(256), 0, s, a);
   hipLaunchKernelGGL(layout_w2_kernel, dim3((unsigned)((c2 + 255) / 256)), dim3(256), 0, s, a);
   hipLaunchKernelGGL(layout_scales_kernel, dim3((unsigned)((cs + 255) / 256)), dim3(256), 0, s, a);
+  if (a.n13) {
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_wnorm(a, s);
+  }
   return hipGetLastError();
 }
 
@@ -2358,6 +2362,276 @@ hipError_t launch_slice(const SliceArgs& a, hipStream_t s) {
   const int oR = a.axis == 0 ? a.len : a.R, oC = a.axis == 0 ? a.C : a.len;
   const int64_t blocks = (int64_t)a.n * ((oR + 127) / 128) * ((oC + 127) / 128);
   hipLaunchKernelGGL(slice_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- exact ties --
+// Layers whose intermediate width fits one 128-wide block (Ip = 128) have a
+// single E4M3 group of h per row, so one h code decided on the other side of
+// a rounding midpoint moves a row by about 1% (one of 128 values, changed by
+// up to 1/16 of its size).  The FP8 MFMA keeps only about 13 bits below the
+// largest product of a block dot, so its gate/up differ from the definition's
+// ascending FP32 sums by up to ~1e-5 of |x| |w| / sqrt(H / 128) (measured
+// over 2.3 M elements, H = 256 .. 6144), which decides ~0.2% of these codes
+// differently.  For such layers the GEMM stage writes FP32 gate/up and this
+// kernel quantises h, one 128-thread workgroup per slot row, thread n on
+// column n:
+//   1. h = silu(g) * u from the GEMM's gate/up, with the error bound
+//        dh = m |x| (|silu'(g) u| |w_g| + |silu(g)| |w_u|) + 2^-17 |h|,
+//      |x| the L2 norm of the dequantised activation row, |w_g|, |w_u| those
+//      of the dequantised weight rows (computed at load), m = kTieMargin /
+//      sqrt(H / 128), 14 times the largest measured ratio, and the last term
+//      for the fast SiLU;
+//   2. the elements that may hold the group's max |h| (|h| >= max|h| -
+//      2 max dh) are recomputed in the definition's order: per K block an
+//      FP32 sum of the exact products in ascending column order, then
+//      acc + p * (s_x * s_w), and SiLU with the correctly rounded FP32 e^-g;
+//      their largest |h| gives the scale s = max|h| / 448 of the definition;
+//   3. every other element whose |h| / s lies within dh / s of a midpoint
+//      between two E4M3 values, or whose |h| is within dh of zero (the sign
+//      of a zero code), is recomputed the same way;
+//   4. codes = E4M3(h / s) (IEEE division), from the recomputed h where
+//      there is one.
+// An element outside both sets is farther from every decision than its error
+// bound, so every code and the scale are those of the definition.  Rows with
+// a NaN or infinite h take s = max|h| / 448 and the codes of h / s directly.
+
+__device__ __forceinline__ float tie_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1];
+}
+
+__device__ __forceinline__ uint32_t tie_umax(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = umax(v, (uint32_t)__shfl_xor((int)v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return umax(red[0], red[1]);
+}
+
+__device__ __forceinline__ uint32_t byte_of(const i32x4& v, int i) {
+  return ((uint32_t)v[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+}
+
+// silu(g) * u of the definition: the clamp of the activation, then
+// (g / (1 + e)) * u with e the correctly rounded FP32 e^-g, IEEE operations.
+__device__ __forceinline__ float exact_silu_mul(float g, float u, float L) {
+  if (L > 0.0f) {
+    g = g > L ? L : g;
+    u = u > L ? L : (u < -L ? -L : u);
+  }
+  const float e = (float)exp(-(double)g);
+  return __fmul_rn(__fdiv_rn(g, __fadd_rn(1.0f, e)), u);
+}
+
+// Gate and up of column n (< 128) of expert e for the activation row in LDS,
+// in the definition's order, read from the MFMA-operand weight layout: row n
+// of the block lives in wave n / 32, tile (n / 16) & 1 (gate) or 2 + that
+// (up), lane n % 16 + 16 g, half h, for K bytes 32 g + 16 h .. + 15.
+__device__ __noinline__ float exact_h(const TieArgs& a, const uint8_t* xs, const float* sxs, int e, int n,
+                                      int nH) {
+  const uint8_t* wb = a.w13 + (size_t)e * nH * kGateUpChunk;
+  const float* ws = a.s13 + (size_t)e * nH * 2;
+  const int w = n >> 5, tt = (n >> 4) & 1, r16 = n & 15;
+  float ag = 0.0f, au = 0.0f;
+  for (int kb = 0; kb < nH; ++kb) {
+    const uint8_t* cb = wb + (size_t)kb * kGateUpChunk;
+    float pg = 0.0f, pu = 0.0f;
+    for (int g4 = 0; g4 < 4; ++g4) {
+      for (int half = 0; half < 2; ++half) {
+        const int lo = (g4 * 16 + r16) * 16;
+        const i32x4 G = ld16(cb + ((w * 4 + tt) * 2 + half) * 1024 + lo);
+        const i32x4 U = ld16(cb + ((w * 4 + 2 + tt) * 2 + half) * 1024 + lo);
+        const uint8_t* x = xs + kb * kBlock + g4 * 32 + half * 16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float xa = e4m3_dec(x[i]);
+          pg = __fadd_rn(pg, __fmul_rn(xa, e4m3_dec(byte_of(G, i))));
+          pu = __fadd_rn(pu, __fmul_rn(xa, e4m3_dec(byte_of(U, i))));
+        }
+      }
+    }
+    ag = __fadd_rn(ag, __fmul_rn(pg, __fmul_rn(sxs[kb], ws[2 * kb])));
+    au = __fadd_rn(au, __fmul_rn(pu, __fmul_rn(sxs[kb], ws[2 * kb + 1])));
+  }
+  return exact_silu_mul(ag, au, a.act_limit);
+}
+
+__global__ __launch_bounds__(128) void tie_exact_kernel(TieArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kMaxKBlocks * kBlock];
+  __shared__ float sxs[kMaxKBlocks];
+  __shared__ float redf[2];
+  __shared__ uint32_t redu[2];
+  const int p = blockIdx.x, n = threadIdx.x;
+  if (p >= a.offsets[a.E]) return;  // past the routed slots (whole workgroup)
+  // the expert of sorted slot p: the largest e with offsets[e] <= p (that
+  // expert is not empty, because offsets[e + 1] > p)
+  int lo = 0, hi = a.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.offsets[mid] <= p) lo = mid; else hi = mid;
+  }
+  const int e = lo, H = a.H, nH = H / kBlock;
+  const int64_t t = a.perm[p] / a.k;
+  for (int i = n * 16; i < H; i += 128 * 16) st16(&xs[i], ld16(a.xq + t * H + i));
+  for (int i = n; i < nH; i += 128) sxs[i] = a.sx[t * nH + i];
+  __syncthreads();
+  float ss = 0.0f;
+  for (int i = n; i < H; i += 128) {
+    const float v = e4m3_dec(xs[i]) * sxs[i >> 7];
+    ss = __builtin_fmaf(v, v, ss);
+  }
+  const float xnorm = sqrtf(tie_sum(ss, redf));
+
+  const float L = a.act_limit;
+  float g = a.gu[(size_t)p * 2 * kBlock + n], u = a.gu[(size_t)p * 2 * kBlock + kBlock + n];
+  if (L > 0.0f) {
+    g = g > L ? L : g;
+    u = u > L ? L : (u < -L ? -L : u);
+  }
+  const float hg = silu_mul(g, u);
+  const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
+  const float ds = sg * (1.0f + g * (1.0f - sg));
+  const float wg = a.n13[(size_t)e * 2 * kBlock + n], wu = a.n13[(size_t)e * 2 * kBlock + kBlock + n];
+  const float dh = a.margin * xnorm * (fabsf(ds * u) * wg + fabsf(g * sg) * wu) + fabsf(hg) * 0x1p-17f;
+  const float amax_g = __uint_as_float(tie_umax(abs_bits(hg), redu));
+  const float dh_max = __uint_as_float(tie_umax(abs_bits(dh), redu));
+
+  uint32_t code;
+  float s;
+  if (!(amax_g <= 3.4028234663852886e38f) || !(dh_max <= 3.4028234663852886e38f)) {
+    // NaN or infinity in the row: no decision is near a finite tie
+    s = __fdiv_rn(amax_g, 448.0f);
+    code = to_e4m3(__fdiv_rn(hg, s));
+  } else if (amax_g == 0.0f) {
+    // every h is zero (the MFMA keeps the largest product of a nonzero dot)
+    s = 0.0f;
+    code = 0u;
+  } else {
+    float hx = hg;
+    bool exact = false;
+    if (fabsf(hg) >= amax_g - 2.0f * dh_max) {
+      hx = exact_h(a, xs, sxs, e, n, nH);
+      exact = true;
+    }
+    const float amax = __uint_as_float(tie_umax(exact ? abs_bits(hx) : 0u, redu));
+    s = __fdiv_rn(amax, 448.0f);
+    if (amax == 0.0f) {
+      code = 0u;
+    } else {
+      if (!exact) {
+        const float v = __fdiv_rn(fabsf(hg), s), dv = __fdiv_rn(dh, s);
+        const uint32_t c = to_e4m3(v);
+        const float mc = e4m3_dec(c);
+        const bool near_lo = c > 0u && v - 0.5f * (e4m3_dec(c - 1u) + mc) <= dv;
+        const bool near_hi = c < 0x7Eu && 0.5f * (mc + e4m3_dec(c + 1u)) - v <= dv;
+        // |h| within its bound of 0: the sign, hence +0 / -0, is undecided
+        const bool near_zero = fabsf(hg) <= dh;
+        if (near_lo || near_hi || near_zero) {
+          hx = exact_h(a, xs, sxs, e, n, nH);
+          exact = true;
+        }
+      }
+      code = to_e4m3(__fdiv_rn(exact ? hx : hg, s));
+    }
+  }
+  a.hq[(size_t)p * kBlock + n] = (uint8_t)code;
+  if (n == 0) {
+    a.sh[p] = s;
+    a.shT[p] = s;
+  }
+}
+
+hipError_t launch_tie_exact(const TieArgs& a, int64_t max_slots, hipStream_t s) {
+  if (max_slots <= 0) return hipSuccess;
+  hipLaunchKernelGGL(tie_exact_kernel, dim3((unsigned)max_slots), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+// L2 norms of the dequantised gate and up rows of experts [e0, e0 + n) from
+// the canonical codes and scales: n13[e][r] for gate row r < Ip, up row r - Ip
+// otherwise; padding rows get 0.  Used only by the exact-tie quantiser.
+__global__ void wnorm_kernel(LayoutArgs a) {
+  const int Ip = a.Ip, nH = a.H / kBlock, nIc = (a.I + kBlock - 1) / kBlock;
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= (int64_t)a.n * 2 * Ip) return;
+  const int le = (int)(q / (2 * Ip)), r = (int)(q - (int64_t)le * 2 * Ip);
+  const int row = r < Ip ? r : r - Ip;
+  float ss = 0.0f;
+  if (row < a.I) {
+    const uint8_t* src = (r < Ip ? a.gate : a.up) + ((size_t)le * a.I + row) * a.H;
+    const float* sc = (r < Ip ? a.gate_scale : a.up_scale) + ((size_t)le * nIc + row / kBlock) * nH;
+    for (int kb = 0; kb < nH; ++kb) {
+      float bs = 0.0f;
+      for (int c = 0; c < kBlock; ++c) {
+        const float v = e4m3_dec(src[kb * kBlock + c]);
+        bs = __builtin_fmaf(v, v, bs);
+      }
+      ss = __builtin_fmaf(bs, sc[kb] * sc[kb], ss);
+    }
+  }
+  a.n13[(size_t)(a.e0 + le) * 2 * Ip + r] = sqrtf(ss);
+}
+
+hipError_t launch_wnorm(const LayoutArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.n * 2 * a.Ip;
+  hipLaunchKernelGGL(wnorm_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- calibration --
+// Measured ceilings for the rooflines: independent chains of the GEMMs' own
+// 16x16x128 FP8 MFMA (two waves per SIMD, eight chains per wave, nothing
+// else in the loop), and a streaming read of a device buffer with 16-byte
+// non-temporal loads, four in flight per thread.
+
+__global__ __launch_bounds__(256) void peak_mfma_kernel(int32_t iters, float* out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // E4M3 operands 1.0 (0x38) and 0.5 (0x30): the chains stay finite
+  const i32x8 a = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, lane};
+  const i32x8 b = {0x30303030, 0x30303030, 0x30303030, 0x30303030, 0x30303030, 0x30303030, 0x30303030, 0x30303030};
+  f32x4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int32_t i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[c], 0, 0, 0, 0, 0, 0);
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) sum += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  if (lane == 0) out[blockIdx.x * 4 + wave] = sum;
+}
+
+__global__ __launch_bounds__(256) void peak_stream_kernel(const i32x4* src, int64_t n16, int32_t* out) {
+  const int64_t step = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  i32x4 acc = {0, 0, 0, 0};
+  for (; i + 3 * step < n16; i += 4 * step) {
+    const i32x4 v0 = __builtin_nontemporal_load(src + i);
+    const i32x4 v1 = __builtin_nontemporal_load(src + i + step);
+    const i32x4 v2 = __builtin_nontemporal_load(src + i + 2 * step);
+    const i32x4 v3 = __builtin_nontemporal_load(src + i + 3 * step);
+    acc ^= v0 ^ v1 ^ v2 ^ v3;
+  }
+  for (; i < n16; i += step) acc ^= __builtin_nontemporal_load(src + i);
+  const int32_t r = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (r == 0x5EED1234) out[blockIdx.x] = r;  // depends on the data: the loads stay
+}
+
+hipError_t launch_peak_mfma(int32_t iters, int grid, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(peak_mfma_kernel, dim3(grid), dim3(256), 0, s, iters, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_peak_stream(const void* src, int64_t bytes, int grid, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(peak_stream_kernel, dim3(grid), dim3(256), 0, s, (const i32x4*)src, bytes / 16, out);
   return hipGetLastError();
 }
 

@@ -304,6 +304,22 @@ int moe_fp8_prefill_set_timing_stages(moe_fp8_prefill* h, uint32_t stage_mask);
 int moe_fp8_prefill_read_timing(moe_fp8_prefill* h, float* stage_ms, int32_t max_records,
                                 int32_t* n_records);
 
+/* ---- calibration (measurement only, not part of the method) ---------- */
+
+/* Measured ceilings for rooflines, on the current device, asynchronous on
+ * `stream`; *work (host) receives the launch's algorithmic work.
+ *   MOE_CALIBRATE_MFMA: a persistent launch (two waves per SIMD) of eight
+ *     independent chains of the 16x16x128 FP8 MFMA the GEMMs issue, n
+ *     iterations per wave (1 <= n <= 2^30); *work = FLOPs.
+ *   MOE_CALIBRATE_STREAM: a streaming read, with 16-byte non-temporal loads,
+ *     of the first buf_bytes - 64 KiB bytes of buf; *work = bytes read.
+ * buf: device memory owned by the caller, 16-byte aligned, at least 64 KiB;
+ * its last 64 KiB receive results.  Time the launch with events on
+ * `stream`.  Errors: MOE_ERR_INVALID_ARG (kind, n, buf), MOE_ERR_DEVICE. */
+enum { MOE_CALIBRATE_MFMA = 0, MOE_CALIBRATE_STREAM = 1 };
+int moe_fp8_prefill_calibrate(int32_t kind, int64_t n, void* buf, int64_t buf_bytes, void* stream,
+                              double* work);
+
 /* Test hook: force the next run to behave as if a HIP call failed (host-side
  * flag only; no GPU fault is produced). */
 int moe_fp8_prefill_debug_inject_failure(moe_fp8_prefill* h);

@@ -77,8 +77,10 @@ def assert_rows_close(got, ref, tol=TOL, what=""):
 # its largest product (the rest truncated), so gate/up differ from the
 # oracle's FP32 sums by ~1e-5 relative.  Where such an FP32 value decides an
 # E4M3 code of h near a rounding midpoint, the two sides can pick neighbouring
-# codes; with I=128 one such flip moves a row by ~1%.  That decision is taken
-# at the kernel's precision, so the comparison is staged:
+# codes.  Layers with one h group per row (Ip = 128), where one such flip
+# would move a row by ~1%, have those decisions recomputed exactly by the
+# library, so their codes and scales must equal the oracle's.  Elsewhere the
+# decision is taken at the kernel's precision and the comparison is staged:
 #   (1) gate/up (FP32, before the epilogue) vs the oracle: per-row rel L2;
 #   (2) the kernel's h codes and scales are exact E4M3 roundings of the
 #       kernel's own h = silu(g) * u (up to FP32 SiLU rounding at exact ties);
@@ -154,8 +156,23 @@ def compare_with_oracle(moe, layer, x, ids, w, rho, got, what="", n_shared=0, ac
     hq, sh, y = pkg.moe_fp8_prefill_debug_intermediates(moe.handle, n, layer.H, Ip)
     fin = np.isfinite(d["gu"]).all(axis=1)
     rel_gu = rel_l2_rows(gu[fin], d["gu"][fin])
-    ties = check_h_codes(hq[fin], sh[fin], gu[fin], Ip, act_limit)
     flips = int((hq[fin] != d["hq"][fin]).sum())
+    if Ip == 128:
+        # one h group per row: the library's exact-tie quantiser decides every
+        # code and scale as the definition does
+        ties = 0
+        if flips:
+            r, c = np.nonzero((hq != d["hq"]) & fin[:, None])
+            note(f"  {what}: h codes differ at (row, col) {list(zip(r[:4].tolist(), c[:4].tolist()))}: "
+                 f"kernel {hq[r[:4], c[:4]].tolist()} oracle {d['hq'][r[:4], c[:4]].tolist()} "
+                 f"gate {d['gu'][r[:4], c[:4]].tolist()} up {d['gu'][r[:4], Ip + c[:4]].tolist()} "
+                 f"kernel gate {gu[r[:4], c[:4]].tolist()} up {gu[r[:4], Ip + c[:4]].tolist()} "
+                 f"scale {sh[r[:4], 0].tolist()} vs {d['sh'][r[:4], 0].tolist()}")
+        assert flips == 0, f"{what}: {flips} h codes differ from the oracle's"
+        assert np.array_equal(sh[fin].view(np.uint32), d["sh"][fin].view(np.uint32)), \
+            f"{what}: h scales differ from the oracle's"
+    else:
+        ties = check_h_codes(hq[fin], sh[fin], gu[fin], Ip, act_limit)
     out2, y2 = oracle.down_combine(layer, hq, sh, ids, w, rho, od, n_shared=n_shared)
     rel_y = rel_l2_rows(y[fin], y2[fin])
     note(f"  {what}: gate/up rel L2 max {rel_gu.max() if rel_gu.size else 0:.2e}; h codes vs oracle's "
@@ -167,4 +184,5 @@ def compare_with_oracle(moe, layer, x, ids, w, rho, got, what="", n_shared=0, ac
     rows = np.isfinite(as_f64(ref)).all(1)
     worst_plain = float(rel_l2_rows(got[rows], ref[rows]).max()) if rows.any() else 0.0
     note(f"  {what}: plain end-to-end worst per-row rel L2 {worst_plain:.3e}")
+    assert worst_plain <= TOL, f"{what}: plain end-to-end worst per-row rel L2 {worst_plain} > {TOL}"
     return ref, d, worst_plain

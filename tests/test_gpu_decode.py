@@ -26,6 +26,11 @@ CASES = [
     ("pad192", (6, 3, 512, 192, 50, gen.ROUTE_SIGMOID_NORMAL, 2.5, 0.05)),
     ("many_rows", (4, 2, 256, 256, 600, gen.ROUTE_SIGMOID_UNIFORM, 2.5, 0.01)),
     ("odd_blocks", (3, 2, 384, 320, 90, gen.ROUTE_SIGMOID_UNIFORM, 2.5, 0.01)),
+    # the flat down variants over several K steps: Ip/128 = 4 (four blocks in
+    # flight) and Ip/128 = 6 (two in flight, three ring turns per unit), ~100
+    # rows per expert so workgroups run several 16-row units
+    ("flat4_i512", (6, 2, 256, 512, 300, gen.ROUTE_SIGMOID_UNIFORM, 2.5, 0.01)),
+    ("flat2_i768", (5, 2, 384, 768, 300, gen.ROUTE_SIGMOID_UNIFORM, 2.5, 0.01)),
 ]
 
 
@@ -78,6 +83,26 @@ def test_decode_rows_independent_and_pass_split():
         moe.close()
     assert np.array_equal(full.view(np.uint32), halves.view(np.uint32))
     assert np.array_equal(full[[0, 1, 1023, 1024, 1099]].view(np.uint32), singles.view(np.uint32))
+
+
+@pytest.mark.parametrize("name,spec", [c for c in CASES if c[0].startswith("flat")])
+def test_decode_flat_pass_split(name, spec):
+    """The flat down variants: a row's bits do not depend on the pass split
+    (300 rows in one call = 150 + 150 = passes of 64 rows)."""
+    layer, x, ids, w, rho = make_case(spec, seed=4)
+    note(f"decode pass split {name}")
+    moe = pkg.MoeFp8Prefill(layer, spec[1], routed_scale=rho, out_dtype=pkg.MOE_DTYPE_F32)
+    small = pkg.MoeFp8Prefill(layer, spec[1], routed_scale=rho, out_dtype=pkg.MOE_DTYPE_F32, max_rows=64)
+    try:
+        full = decode(moe, x, ids, w)
+        halves = np.concatenate([decode(moe, x[:150], ids[:150], w[:150]),
+                                 decode(moe, x[150:], ids[150:], w[150:])])
+        passes = decode(small, x, ids, w)
+    finally:
+        moe.close()
+        small.close()
+    assert np.array_equal(full.view(np.uint32), halves.view(np.uint32))
+    assert np.array_equal(full.view(np.uint32), passes.view(np.uint32))
 
 
 def test_decode_is_its_own_method():

@@ -8,8 +8,11 @@ batch); the W8A16 decode path on the same layer at T=16; and the E=160,
 H=5120, I=192 slice at T=16/64/1024.
 
 Integer work (plan, activation codes) is compared in full, bit for bit.  The
-output is compared on sampled rows (outlier rows included) that the oracle
-evaluates one token subset at a time, stage by stage as in gpu_util.  Row
+output is compared stage by stage as in gpu_util on every row at T=256 and
+on the slice, and at T=4096 and T=8192 on at least 64 rows that reach every
+GEMM tile kind (streaming, 128-row, 256-row, ragged last tiles, the largest
+expert) and the outlier rows; the oracle evaluates that token subset, whose
+rows equal the full call's (rows are independent).  Row
 invariance is checked bit for bit: 1x8192 vs 2x4096 vs 4102+4090 vs 1+8191,
 a row alone vs inside a 4096-row call, a token permutation, repeated calls.
 """
@@ -46,10 +49,34 @@ def call(moe, x, ids, w):
     return out_to_np(out)
 
 
-def sample_rows(T, is_outlier, n=6, seed=11):
+def tile_kind_rows(ids, E, outlier, n_min=64, seed=12):
+    """At least n_min token rows that together reach every GEMM tile kind of
+    the call: experts with 1..16 rows (streaming), 17..128 (one 128-row
+    tile) and more (256-row tiles), rows in the ragged last 256-row tile of
+    an expert, rows of the largest expert (first, middle, last), and the
+    outlier rows; the rest drawn at random."""
+    T, k = ids.shape
+    counts, offsets, perm, inv, _ = oracle.plan(ids, E)
     rng = np.random.default_rng(seed)
-    pick = set(rng.choice(T, size=min(n, T), replace=False).tolist())
-    pick.update(np.nonzero(is_outlier)[0][:2].tolist())
+    pick = []
+
+    def add(tokens, n):
+        tokens = [int(t) for t in tokens if int(t) not in pick]
+        pick.extend(tokens[:n])
+
+    for lo, hi in ((1, 16), (17, 128), (129, 1 << 30)):
+        experts = np.nonzero((counts >= lo) & (counts <= hi))[0]
+        if experts.size:
+            sel = rng.permutation(experts)[:16]
+            add([perm[offsets[e]] // k for e in sel], 12)
+    ragged = [e for e in np.nonzero(counts > 128)[0] if counts[e] % 256]
+    for e in ragged[:12]:
+        add([perm[offsets[e] + counts[e] - 1] // k], 1)
+    big = int(np.argmax(counts))
+    add([perm[offsets[big] + q] // k for q in (0, counts[big] // 2, counts[big] - 1)], 3)
+    add(np.nonzero(outlier)[0], 4)
+    rest = rng.permutation(T)
+    add(rest, max(0, n_min - len(pick)))
     return np.array(sorted(pick))
 
 
@@ -97,8 +124,8 @@ def test_glm_t256(glm):
     xq, sx = pkg.moe_fp8_prefill_debug_activations(moe.handle, wl.T, wl.H)
     q, s = oracle.quantize_rows(oracle.bf16_to_f32(x))
     assert np.array_equal(xq, q) and np.array_equal(sx.view(np.uint32), s.view(np.uint32))
-    S = sample_rows(wl.T, outl)
-    stagewise_on_sample(moe, layer, x, ids, w, wl.rho, got, S, wl.name)
+    # every row against the oracle
+    stagewise_on_sample(moe, layer, x, ids, w, wl.rho, got, np.arange(wl.T), wl.name)
     # repeated calls: identical hashes
     h0 = hashlib.sha256(got.tobytes()).hexdigest()
     for _ in range(2):
@@ -138,7 +165,7 @@ def test_glm_t4096(glm):
     counts, offsets, perm, inv = pkg.moe_fp8_prefill_debug_plan(moe.handle, wl.E, wl.T * wl.k)
     c, o, p, i, bad = oracle.plan(ids, wl.E)
     assert np.array_equal(counts, c) and np.array_equal(perm, p) and np.array_equal(inv, i)
-    S = sample_rows(wl.T, outl)
+    S = tile_kind_rows(ids, wl.E, outl)
     stagewise_on_sample(moe, layer, x, ids, w, wl.rho, got, S, wl.name)
     # a row alone gives the same bits as inside the 4096-row call
     for t in S[:4]:
@@ -156,7 +183,7 @@ def test_glm_t8192_zipf_chunking(glm):
     c, o, p, i, bad = oracle.plan(ids, wl.E)
     assert np.array_equal(counts, c) and np.array_equal(perm, p) and np.array_equal(inv, i)
     assert (counts == 0).sum() >= 8 and counts.max() > 4096
-    S = sample_rows(wl.T, outl)
+    S = tile_kind_rows(ids, wl.E, outl)
     stagewise_on_sample(moe, layer, x, ids, w, wl.rho, one, S, wl.name)
     for splits in ((4096, 8192), (4102, 8192), (1, 8192)):
         note(f"{wl.name}: calls split at {splits[0]}")
@@ -178,7 +205,7 @@ def test_slice_layer(wl):
         counts, offsets, perm, inv = pkg.moe_fp8_prefill_debug_plan(moe.handle, wl.E, wl.T * wl.k)
         c, o, p, i, bad = oracle.plan(ids, wl.E)
         assert np.array_equal(counts, c) and np.array_equal(perm, p) and np.array_equal(inv, i)
-        S = np.arange(wl.T) if wl.T <= 64 else sample_rows(wl.T, outl, n=12)
+        S = np.arange(wl.T)  # every row
         stagewise_on_sample(moe, layer, x, ids, w, wl.rho, got, S, wl.name)
     finally:
         moe.close()
