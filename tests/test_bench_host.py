@@ -57,3 +57,66 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "--gpus must be 1" in r.stdout + r.stderr
+
+
+def test_streamed_result_json():
+    import json
+
+    import bench
+    import gen
+    r = bench.streamed_result(gen.GLM_T4096, 6, 9_666_035_712, 1.2)
+    json.dumps(r)
+    assert r["steps"] == 6 and r["value"] == 4096 / 1.2 and r["dtype"].startswith("fp8_e4m3")
+    assert abs(r["h2d_GBs"] - 6 * 9.666035712 / 1.2) < 1e-9
+
+
+def test_two_call_step_work_is_the_sum_of_its_calls():
+    import bench
+    import gen
+    wl = gen.GLM_T256
+    rng = np.random.default_rng(0)
+    ids = rng.integers(0, wl.E, (wl.T, wl.k)).astype(np.int32)
+    one = bench.algorithmic_work(wl, bench.plan_counts(ids, wl.E))
+    half = SimpleNamespace(**{**wl.__dict__, "T": 128})
+    a = bench.algorithmic_work(half, bench.plan_counts(ids[:128], wl.E))
+    b = bench.algorithmic_work(half, bench.plan_counts(ids[128:], wl.E))
+    two = bench.add_work(a, b)
+    assert two["path_flops"] == one["path_flops"] and two["slots"] == one["slots"] == wl.T * wl.k
+    # two calls read the weights of the experts each hits
+    assert two["path_bytes"] >= one["path_bytes"]
+    g = bench.launch_work(two, "gate_up_stream", calls=2)
+    assert g["rows"] == (a["gate_up"]["stream"]["rows"] + b["gate_up"]["stream"]["rows"]) / 2
+    d = bench.launch_work(one, "down_wide")
+    assert d["flops"] == 2 * one["down"]["wide"]["rows"] * 2048 * 6144
+
+
+def test_profile_summaries_round_trip(tmp_path, monkeypatch):
+    """summarize_profiles turns rocprofv3-shaped CSVs into the committed
+    summaries, and read_traffic finds the scaled bytes of a kernel there."""
+    import bench
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    tag = "glm_e256_t256"
+    out = tmp_path / "prof"
+
+    def write_pmc(sub, counter, rows):
+        d = out / sub / "host"
+        d.mkdir(parents=True)
+        with open(d / "pmc_counter_collection.csv", "w") as f:
+            f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+            for i, (kern, val) in enumerate(rows):
+                f.write(f'{i},"{kern}",{counter},{val}\n')
+
+    write_pmc("copy_fetch", "FETCH_SIZE", [("void at::native::copyBuffer(char*)", 524288.0)])
+    write_pmc("copy_write", "WRITE_SIZE", [("void at::native::copyBuffer(char*)", 1048576.0)])
+    k = "void moe::gate_up_stream_kernel<5>(moe::GateUpArgs)"
+    write_pmc(f"fetch_{tag}", "FETCH_SIZE", [(k, 1000.0), (k, 1002.0)])
+    write_pmc(f"write_{tag}", "WRITE_SIZE", [(k, 10.0), (k, 10.0)])
+    d = out / f"kt_{tag}" / "host"
+    d.mkdir(parents=True)
+    with open(d / "kt_kernel_stats.csv", "w") as f:
+        f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs\n")
+        f.write(f'"{k}",10,9500000,950000,60.0,940000,960000\n')
+    assert bench.summarize_profiles(str(out)) == 0
+    # FETCH scaled by 2 (the copy reads half its bytes), WRITE by 1
+    assert bench.read_traffic("gate_up_stream_kernel", tag) == (1001.0 * 2 + 10.0) * 1024
+    assert (tmp_path / "profiles" / f"kernel_stats_{tag}.md").exists()
