@@ -918,6 +918,7 @@ int moe_fp8_prefill_debug_mfma(const uint8_t* a, const uint8_t* b, float* d) {
 int moe_fp8_prefill_calibrate(int32_t kind, int64_t n, void* buf, int64_t buf_bytes, void* stream,
                               double* work) {
   constexpr int64_t kResultBytes = 64 * 1024;
+  if (kind != MOE_CALIBRATE_MFMA && kind != MOE_CALIBRATE_STREAM) return MOE_ERR_INVALID_ARG;
   if (!buf || !work || ((uintptr_t)buf & 15u) != 0 || buf_bytes < kResultBytes) return MOE_ERR_INVALID_ARG;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -938,8 +939,9 @@ int moe_fp8_prefill_calibrate(int32_t kind, int64_t n, void* buf, int64_t buf_by
     if (bytes <= 0) return MOE_ERR_INVALID_ARG;
     const int grid = 4 * cus;
     if (grid * 4 > kResultBytes) return MOE_ERR_UNSUPPORTED;
-    if (launch_peak_stream(buf, bytes, grid, (int32_t*)result, s) != hipSuccess) return MOE_ERR_DEVICE;
-    *work = (double)bytes;
+    int64_t read = 0;
+    if (launch_peak_stream(buf, bytes, grid, (int32_t*)result, &read, s) != hipSuccess) return MOE_ERR_DEVICE;
+    *work = (double)read;
     return MOE_OK;
   }
   return MOE_ERR_INVALID_ARG;

@@ -219,7 +219,8 @@ hipError_t launch_slice(const SliceArgs& a, hipStream_t s);
 hipError_t launch_tie_exact(const TieArgs& a, int64_t max_slots, hipStream_t s);
 hipError_t launch_wnorm(const LayoutArgs& a, hipStream_t s);
 hipError_t launch_peak_mfma(int32_t iters, int grid, float* out, hipStream_t s);
-hipError_t launch_peak_stream(const void* src, int64_t bytes, int grid, int32_t* out, hipStream_t s);
+hipError_t launch_peak_stream(const void* src, int64_t max_bytes, int grid, int32_t* out, int64_t* bytes,
+                              hipStream_t s);
 hipError_t launch_mfma_probe(const uint8_t* a, const uint8_t* b, float* d, hipStream_t s);
 
 }  // namespace moe

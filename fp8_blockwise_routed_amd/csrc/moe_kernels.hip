@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -2609,20 +2610,35 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(int32_t iters, float* ou
   if (lane == 0) out[blockIdx.x * 4 + wave] = sum;
 }
 
-__global__ __launch_bounds__(256) void peak_stream_kernel(const i32x4* src, int64_t n16, int32_t* out) {
-  const int64_t step = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// Work group g streams 32 KiB chunks g, g + G, ...: eight 16-byte buffer
+// loads per thread (each wave instruction one contiguous KiB), with the next
+// chunk's eight loads issued before the current chunk is consumed.
+constexpr uint32_t kPeakChunk = 256 * 16 * 8;
+
+__global__ __launch_bounds__(256) void peak_stream_kernel(const uint8_t* src, uint32_t n_chunks, int32_t* out) {
+  const rsrc_t r = make_rsrc(src, n_chunks * kPeakChunk);
+  const uint32_t t16 = threadIdx.x * 16u;
   i32x4 acc = {0, 0, 0, 0};
-  for (; i + 3 * step < n16; i += 4 * step) {
-    const i32x4 v0 = __builtin_nontemporal_load(src + i);
-    const i32x4 v1 = __builtin_nontemporal_load(src + i + step);
-    const i32x4 v2 = __builtin_nontemporal_load(src + i + 2 * step);
-    const i32x4 v3 = __builtin_nontemporal_load(src + i + 3 * step);
-    acc ^= v0 ^ v1 ^ v2 ^ v3;
+  i32x4 a[8], b[8];
+  uint32_t c = blockIdx.x;
+  if (c < n_chunks) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = wload16(r, t16 + j * 4096u, c * kPeakChunk);
   }
-  for (; i < n16; i += step) acc ^= __builtin_nontemporal_load(src + i);
-  const int32_t r = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
-  if (r == 0x5EED1234) out[blockIdx.x] = r;  // depends on the data: the loads stay
+  for (; c < n_chunks; c += gridDim.x) {
+    const uint32_t nc = c + gridDim.x;
+    if (nc < n_chunks) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] = wload16(r, t16 + j * 4096u, nc * kPeakChunk);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc ^= a[j];
+      a[j] = b[j];
+    }
+  }
+  const int32_t v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (v == 0x5EED1234) out[blockIdx.x] = v;  // depends on the data: the loads stay
 }
 
 hipError_t launch_peak_mfma(int32_t iters, int grid, float* out, hipStream_t s) {
@@ -2630,8 +2646,14 @@ hipError_t launch_peak_mfma(int32_t iters, int grid, float* out, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_peak_stream(const void* src, int64_t bytes, int grid, int32_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(peak_stream_kernel, dim3(grid), dim3(256), 0, s, (const i32x4*)src, bytes / 16, out);
+// Streams the first n_chunks * 32 KiB bytes of src (under 4 GiB); returns
+// the bytes read in *bytes.
+hipError_t launch_peak_stream(const void* src, int64_t max_bytes, int grid, int32_t* out, int64_t* bytes,
+                              hipStream_t s) {
+  const int64_t cap = std::min<int64_t>(max_bytes, (int64_t(1) << 32) - kPeakChunk);
+  const uint32_t n_chunks = (uint32_t)(cap / kPeakChunk);
+  *bytes = (int64_t)n_chunks * kPeakChunk;
+  hipLaunchKernelGGL(peak_stream_kernel, dim3(grid), dim3(256), 0, s, (const uint8_t*)src, n_chunks, out);
   return hipGetLastError();
 }
 

@@ -311,8 +311,10 @@ int moe_fp8_prefill_read_timing(moe_fp8_prefill* h, float* stage_ms, int32_t max
  *   MOE_CALIBRATE_MFMA: a persistent launch (two waves per SIMD) of eight
  *     independent chains of the 16x16x128 FP8 MFMA the GEMMs issue, n
  *     iterations per wave (1 <= n <= 2^30); *work = FLOPs.
- *   MOE_CALIBRATE_STREAM: a streaming read, with 16-byte non-temporal loads,
- *     of the first buf_bytes - 64 KiB bytes of buf; *work = bytes read.
+ *   MOE_CALIBRATE_STREAM: a streaming read of buf (at most its first
+ *     buf_bytes - 64 KiB bytes, under 4 GiB, in whole 32 KiB chunks) with the
+ *     16-byte buffer loads and cache policy of the GEMMs' weight stream;
+ *     *work = bytes read.
  * buf: device memory owned by the caller, 16-byte aligned, at least 64 KiB;
  * its last 64 KiB receive results.  Time the launch with events on
  * `stream`.  Errors: MOE_ERR_INVALID_ARG (kind, n, buf), MOE_ERR_DEVICE. */
