@@ -48,7 +48,7 @@ EXPORTED = (
     "moe_fp8_prefill_set_timing_stages", "moe_fp8_prefill_read_timing", "moe_fp8_prefill_debug_inject_failure",
     "moe_fp8_prefill_route", "moe_fp8_prefill_run_logits", "moe_fp8_prefill_run_decode",
     "moe_fp8_prefill_create_streamed", "moe_fp8_prefill_stage", "moe_fp8_prefill_select_slot",
-    "moe_fp8_prefill_calibrate",
+    "moe_fp8_prefill_calibrate", "moe_fp8_prefill_run_static",
 )
 
 
@@ -92,6 +92,7 @@ def load_library() -> ctypes.CDLL:
         "moe_fp8_prefill_create": ([D, ctypes.POINTER(P)], ctypes.c_int),
         "moe_fp8_prefill_run": ([P, P, P, P, I64, P, P], ctypes.c_int),
         "moe_fp8_prefill_run_decode": ([P, P, P, P, I64, P, P], ctypes.c_int),
+        "moe_fp8_prefill_run_static": ([P, P, P, P, I64, P, P], ctypes.c_int),
         "moe_fp8_prefill_status": ([P], ctypes.c_int),
         "moe_fp8_prefill_destroy": ([P], None),
         "moe_fp8_prefill_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -212,6 +213,13 @@ def moe_fp8_prefill_run(handle: int, x, ids, w, T: int, out, stream=None) -> int
 def moe_fp8_prefill_run_decode(handle: int, x, ids, w, T: int, out, stream=None) -> int:
     """The W8A16 decode path; returns the MOE_* code."""
     return int(load_library().moe_fp8_prefill_run_decode(ctypes.c_void_p(handle), _dev_ptr(x), _dev_ptr(ids),
+                                                         _dev_ptr(w), T, _dev_ptr(out), _stream_ptr(stream)))
+
+
+def moe_fp8_prefill_run_static(handle: int, x, ids, w, T: int, out, stream=None) -> int:
+    """run() with its per-pass workspace in the library's static device array
+    (allocates nothing); returns the MOE_* code."""
+    return int(load_library().moe_fp8_prefill_run_static(ctypes.c_void_p(handle), _dev_ptr(x), _dev_ptr(ids),
                                                          _dev_ptr(w), T, _dev_ptr(out), _stream_ptr(stream)))
 
 

@@ -134,20 +134,8 @@ bool boundary_needed(uint32_t mask, int b) {
   return (b > 0 && ((mask >> (b - 1)) & 1u)) || (b < MOE_NUM_STAGES && ((mask >> b) & 1u));
 }
 
-}  // namespace
-
-struct moe_fp8_prefill {
-  moe_fp8_prefill_desc desc;
-  Dims m;
-  int device = 0;
-  int num_cus = 256;
-  // weights
-  uint8_t* w13 = nullptr;
-  float* s13 = nullptr;
-  uint8_t* w2 = nullptr;
-  float* s2 = nullptr;
-  float* n13 = nullptr;  // exact-tie layers: gate|up row norms
-  // workspace
+// Per-pass device buffers (pieces of WsSizes).
+struct Workspace {
   uint8_t* xq = nullptr;
   float* sx = nullptr;
   float* sxT = nullptr;
@@ -165,10 +153,84 @@ struct moe_fp8_prefill {
   Tile* wide_tiles = nullptr;
   int32_t* n_tiles = nullptr;
   int32_t* chunk = nullptr;
-  int32_t* err = nullptr;
   int32_t* rids = nullptr;
   float* rw = nullptr;
   float* gu = nullptr;  // exact-tie layers: FP32 gate|up of a pass
+};
+
+// The pieces of w laid out one after the other (256-byte aligned) from base.
+Workspace carve(const WsSizes& w, uint8_t* base) {
+  Workspace ws;
+  auto take = [&](int64_t bytes) -> void* {
+    void* p = bytes > 0 ? (void*)base : nullptr;
+    base += align256(bytes);
+    return p;
+  };
+  ws.xq = (uint8_t*)take(w.xq);
+  ws.sx = (float*)take(w.sx);
+  ws.sxT = (float*)take(w.sxT);
+  ws.hq = (uint8_t*)take(w.hq);
+  ws.sh = (float*)take(w.sh);
+  ws.shT = (float*)take(w.shT);
+  ws.y = (float*)take(w.y);
+  ws.counts = (int32_t*)take(w.counts);
+  ws.offsets = (int32_t*)take(w.offsets);
+  ws.perm = (int32_t*)take(w.perm);
+  ws.inv = (int32_t*)take(w.inv);
+  ws.small_tiles = (Tile*)take(w.small_tiles);
+  ws.narrow_tiles = (Tile*)take(w.narrow_tiles);
+  ws.wide_tiles = (Tile*)take(w.wide_tiles);
+  ws.n_tiles = (int32_t*)take(w.n_tiles);
+  ws.chunk = (int32_t*)take(w.chunk);
+  take(w.err);
+  ws.rids = (int32_t*)take(w.rids);
+  ws.rw = (float*)take(w.rw);
+  ws.hb = (uint16_t*)take(w.hb);
+  ws.gu = (float*)take(w.gu);
+  return ws;
+}
+
+// The workspace of run_static() for passes of `rows` rows: run()'s pieces
+// without those of run_logits() and the decode path.
+WsSizes static_sizes(const Dims& m, int64_t rows) {
+  Dims r = m;
+  r.max_rows = rows;
+  r.P = rows * m.k;
+  WsSizes w = ws_sizes(r);
+  w.rids = w.rw = w.hb = 0;
+  return w;
+}
+
+// The most rows (<= max_rows) whose static_sizes fit kStaticScratchBytes, or 0.
+int64_t static_rows_of(const Dims& m) {
+  int64_t lo = 0, hi = m.max_rows;  // fits(lo) (or lo == 0), find the largest
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (static_sizes(m, mid).total() <= kStaticScratchBytes) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace
+
+struct moe_fp8_prefill {
+  moe_fp8_prefill_desc desc;
+  Dims m;
+  int device = 0;
+  int num_cus = 256;
+  // weights
+  uint8_t* w13 = nullptr;
+  float* s13 = nullptr;
+  uint8_t* w2 = nullptr;
+  float* s2 = nullptr;
+  float* n13 = nullptr;  // exact-tie layers: gate|up row norms
+  // workspace for max_rows rows (allocated in create) and the bad-id flag
+  Workspace ws;
+  int32_t* err = nullptr;
+  // run_static(): this device's static scratch array and the rows per pass
+  // its workspace holds
+  uint8_t* scratch = nullptr;
+  int64_t static_rows = 0;
   std::vector<void*> allocations;
   // state
   std::atomic<int> busy{0};
@@ -371,30 +433,30 @@ int64_t max_tiles(const Dims& m, int64_t P, int kind) {
 // rows), 128-row tiles (17..128 rows), then tiles of up to 256 rows.
 // after[kind], if given and not null, is recorded after each of the three
 // (also when a launch is skipped for lack of work).
-hipError_t launch_gate_up_all(moe_fp8_prefill* h, int64_t t, int64_t P, float* gu_dbg, hipStream_t s,
+hipError_t launch_gate_up_all(moe_fp8_prefill* h, const Workspace& ws, int64_t t, int64_t P, float* gu_dbg, hipStream_t s,
                               hipEvent_t* after = nullptr) {
   const Dims& m = h->m;
   const int64_t nb = m.Ip / kBlock;
   // layers with one h group per row: the GEMMs write FP32 gate|up, which the
   // exact-tie quantiser turns into h codes and scales after the last launch
-  if (m.exact_ties() && !gu_dbg) gu_dbg = h->gu;
-  GateUpArgs ga{h->xq, h->sx, t * m.H, t * m.nH * 4, h->perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip,
-                h->w13, h->s13, h->small_tiles, h->n_tiles, h->hq, h->sh, gu_dbg,
+  if (m.exact_ties() && !gu_dbg) gu_dbg = ws.gu;
+  GateUpArgs ga{ws.xq, ws.sx, t * m.H, t * m.nH * 4, ws.perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip,
+                h->w13, h->s13, ws.small_tiles, ws.n_tiles, ws.hq, ws.sh, gu_dbg,
                 h->desc.activation == MOE_ACT_SILU_CLAMPED ? h->desc.activation_limit : 0.0f,
-                h->sxT, t * m.nH * 4, (int32_t)t, (int32_t)P, h->shT};
-  Tile* lists[3] = {h->small_tiles, h->narrow_tiles, h->wide_tiles};
+                ws.sxT, t * m.nH * 4, (int32_t)t, (int32_t)P, ws.shT};
+  Tile* lists[3] = {ws.small_tiles, ws.narrow_tiles, ws.wide_tiles};
   for (int kind = kGemmStream; kind <= kGemmWide; ++kind) {
     const int64_t items = max_tiles(m, P, kind) * nb;
     if (items > 0) {
       ga.tiles = lists[kind];
-      ga.n_tiles = h->n_tiles + kind;
+      ga.n_tiles = ws.n_tiles + kind;
       hipError_t e = launch_gate_up(ga, kind, gemm_grid(h, items, kind, true), s);
       if (e != hipSuccess) return e;
     }
     if (kind == kGemmWide && m.exact_ties()) {
       const float limit = h->desc.activation == MOE_ACT_SILU_CLAMPED ? h->desc.activation_limit : 0.0f;
-      TieArgs ta{gu_dbg, h->xq, h->sx, h->perm, h->offsets, (int32_t)m.E, (int32_t)m.k, (int32_t)m.H,
-                 h->w13, h->s13, h->n13, h->hq, h->sh, h->shT, limit,
+      TieArgs ta{gu_dbg, ws.xq, ws.sx, ws.perm, ws.offsets, (int32_t)m.E, (int32_t)m.k, (int32_t)m.H,
+                 h->w13, h->s13, h->n13, ws.hq, ws.sh, ws.shT, limit,
                  kTieMargin / sqrtf((float)m.nH)};
       hipError_t e = launch_tie_exact(ta, P, s);
       if (e != hipSuccess) return e;
@@ -408,12 +470,12 @@ hipError_t launch_gate_up_all(moe_fp8_prefill* h, int64_t t, int64_t P, float* g
 }
 
 // The down launches, in the same order.
-hipError_t launch_down_all(moe_fp8_prefill* h, int64_t P, hipStream_t s, hipEvent_t* after = nullptr) {
+hipError_t launch_down_all(moe_fp8_prefill* h, const Workspace& ws, int64_t P, hipStream_t s, hipEvent_t* after = nullptr) {
   const Dims& m = h->m;
   const int64_t nb = m.H / kBlock, nb2 = (nb + 1) / 2;
-  DownArgs da{h->hq, h->sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2,
-              h->small_tiles, h->n_tiles, h->y, h->shT, P * m.nI * 4, (int32_t)P, nullptr};
-  Tile* lists[3] = {h->small_tiles, h->narrow_tiles, h->wide_tiles};
+  DownArgs da{ws.hq, ws.sh, P * m.Ip, P * m.nI * 4, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2,
+              ws.small_tiles, ws.n_tiles, ws.y, ws.shT, P * m.nI * 4, (int32_t)P, nullptr};
+  Tile* lists[3] = {ws.small_tiles, ws.narrow_tiles, ws.wide_tiles};
   for (int kind = kGemmStream; kind <= kGemmWide; ++kind) {
     // the 128-row and the 256-row tiles run in one launch of the same
     // kernel (after[kGemmNarrow] is then recorded before it)
@@ -422,8 +484,8 @@ hipError_t launch_down_all(moe_fp8_prefill* h, int64_t P, hipStream_t s, hipEven
                                               : 0;
     if (items > 0) {
       da.tiles = lists[kind == kGemmWide ? kGemmNarrow : kind];
-      da.n_tiles = h->n_tiles + (kind == kGemmWide ? kGemmNarrow : kind);
-      da.tiles2 = kind == kGemmWide ? h->wide_tiles : nullptr;
+      da.n_tiles = ws.n_tiles + (kind == kGemmWide ? kGemmNarrow : kind);
+      da.tiles2 = kind == kGemmWide ? ws.wide_tiles : nullptr;
       hipError_t e = launch_down(da, kind, gemm_grid(h, items, kind, false), s);
       if (e != hipSuccess) return e;
     }
@@ -458,19 +520,19 @@ int get_stage_events(moe_fp8_prefill* h, StageEvents* out) {
 // The W8A16 gate_up and down of one pass over t rows / P slots (the plan is
 // in the workspace), with the events of the timed stages: gate_up and down
 // take the streaming slots, the other GEMM slots record empty intervals.
-hipError_t launch_a16(moe_fp8_prefill* h, const uint16_t* x, int64_t t, int64_t P, hipStream_t s, hipEvent_t* at) {
+hipError_t launch_a16(moe_fp8_prefill* h, const Workspace& ws, const uint16_t* x, int64_t t, int64_t P, hipStream_t s, hipEvent_t* at) {
   const Dims& m = h->m;
   const int64_t max_tiles16 = P / 16 + m.E;  // tiles of <= 16 rows over all lists
-  GateUpA16Args ga{x, t * m.H * 2, h->perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip, h->w13, h->s13,
-                   {h->small_tiles, h->narrow_tiles, h->wide_tiles}, h->n_tiles, h->hb,
+  GateUpA16Args ga{x, t * m.H * 2, ws.perm, (int32_t)m.k, (int32_t)m.H, (int32_t)m.Ip, h->w13, h->s13,
+                   {ws.small_tiles, ws.narrow_tiles, ws.wide_tiles}, ws.n_tiles, ws.hb,
                    h->desc.activation == MOE_ACT_SILU_CLAMPED ? h->desc.activation_limit : 0.0f};
   const int64_t cap = h->num_cus * kDecodeWgPerCu;
   hipError_t e = launch_gate_up_a16(ga, (int)std::max<int64_t>(1, std::min<int64_t>(max_tiles16 * (m.Ip / kBlock), cap)), s);
   if (e != hipSuccess) return e;
   for (int b = 3; b <= 5; ++b)
     if (at[b] && (e = hipEventRecord(at[b], s)) != hipSuccess) return e;
-  DownA16Args da{h->hb, P * m.Ip * 2, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2,
-                 {h->small_tiles, h->narrow_tiles, h->wide_tiles}, h->n_tiles, h->y};
+  DownA16Args da{ws.hb, P * m.Ip * 2, (int32_t)m.H, (int32_t)m.Ip, h->w2, h->s2,
+                 {ws.small_tiles, ws.narrow_tiles, ws.wide_tiles}, ws.n_tiles, ws.y};
   e = launch_down_a16(da, (int)std::max<int64_t>(1, std::min<int64_t>(max_tiles16 * (m.H / kBlock), cap)), s);
   if (e != hipSuccess) return e;
   for (int b = 6; b <= 8; ++b)
@@ -478,7 +540,7 @@ hipError_t launch_a16(moe_fp8_prefill* h, const uint16_t* x, int64_t t, int64_t 
   return hipSuccess;
 }
 
-int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const float* w,
+int run_passes(moe_fp8_prefill* h, const Workspace& ws, int64_t pass_limit, const void* x, const int32_t* ids, const float* w,
                const float* logits, int32_t router, int64_t T, void* out, void* stream_, bool a16 = false) {
   if (!h) return MOE_ERR_INVALID_ARG;
   if (h->failed) return MOE_ERR_FAILED_STATE;
@@ -515,7 +577,7 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
   const Dims& m = h->m;
   const int64_t out_elem = h->desc.out_dtype == MOE_DTYPE_F32 ? 4 : 2;
 
-  const int64_t pass_rows = a16 ? std::min<int64_t>(m.max_rows, kDecodeRows) : m.max_rows;
+  const int64_t pass_rows = std::min<int64_t>(pass_limit, a16 ? std::min<int64_t>(m.max_rows, kDecodeRows) : m.max_rows);
   for (int64_t r0 = 0; r0 < T; r0 += pass_rows) {
     const int64_t t = (T - r0) < pass_rows ? (T - r0) : pass_rows;
     const int64_t P = t * m.k;
@@ -528,15 +590,15 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
         if (boundary_needed(ev.mask, b)) at[b] = ev.ev[b];
       if (at[0] && hipEventRecord(at[0], s) != hipSuccess) return fail(h);
     }
-    const int32_t* ids_p = ids ? ids + r0 * m.kr : h->rids;
-    const float* w_p = w ? w + r0 * m.kr : h->rw;
+    const int32_t* ids_p = ids ? ids + r0 * m.kr : ws.rids;
+    const float* w_p = w ? w + r0 * m.kr : ws.rw;
     if (logits) {
-      RouteArgs ra{logits + r0 * m.Er, t, (int32_t)m.Er, (int32_t)m.kr, router, h->rids, h->rw};
+      RouteArgs ra{logits + r0 * m.Er, t, (int32_t)m.Er, (int32_t)m.kr, router, ws.rids, ws.rw};
       if (launch_route(ra, s) != hipSuccess) return fail(h);
     }
     PlanArgs pa{ids_p, (int32_t)t, (int32_t)m.k, (int32_t)m.E, (int32_t)m.kr, (int32_t)m.Er,
-                h->counts, h->offsets, h->perm, h->inv, h->small_tiles,
-                h->narrow_tiles, h->wide_tiles, h->n_tiles, h->err, h->chunk};
+                ws.counts, ws.offsets, ws.perm, ws.inv, ws.small_tiles,
+                ws.narrow_tiles, ws.wide_tiles, ws.n_tiles, h->err, ws.chunk};
     if (launch_plan(pa, s) != hipSuccess) return fail(h);
     if (at[1] && hipEventRecord(at[1], s) != hipSuccess) return fail(h);
 
@@ -544,17 +606,17 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
       // W8A16: no activation quantisation; one gate_up and one down launch
       // over all tiles (timed in the streaming slots)
       if (at[2] && hipEventRecord(at[2], s) != hipSuccess) return fail(h);
-      if (launch_a16(h, (const uint16_t*)x + r0 * m.H, t, P, s, at) != hipSuccess) return fail(h);
+      if (launch_a16(h, ws, (const uint16_t*)x + r0 * m.H, t, P, s, at) != hipSuccess) return fail(h);
     } else {
-      QuantArgs qa{(const uint16_t*)x + r0 * m.H, (int32_t)t, (int32_t)m.H, h->xq, h->sx, h->sxT};
+      QuantArgs qa{(const uint16_t*)x + r0 * m.H, (int32_t)t, (int32_t)m.H, ws.xq, ws.sx, ws.sxT};
       if (launch_quant(qa, s) != hipSuccess) return fail(h);
       if (at[2] && hipEventRecord(at[2], s) != hipSuccess) return fail(h);
 
-      if (launch_gate_up_all(h, t, P, nullptr, s, &at[3]) != hipSuccess) return fail(h);
-      if (launch_down_all(h, P, s, &at[6]) != hipSuccess) return fail(h);
+      if (launch_gate_up_all(h, ws, t, P, nullptr, s, &at[3]) != hipSuccess) return fail(h);
+      if (launch_down_all(h, ws, P, s, &at[6]) != hipSuccess) return fail(h);
     }
 
-    CombineArgs ca{h->y, h->inv, w_p, (int32_t)t, (int32_t)m.k, (int32_t)m.H, (int32_t)m.kr,
+    CombineArgs ca{ws.y, ws.inv, w_p, (int32_t)t, (int32_t)m.k, (int32_t)m.H, (int32_t)m.kr,
                    h->desc.routed_scale, h->desc.out_dtype == MOE_DTYPE_F32 ? 1 : 0,
                    (uint8_t*)out + r0 * m.H * out_elem};
     if (launch_combine(ca, s) != hipSuccess) return fail(h);
@@ -562,7 +624,7 @@ int run_passes(moe_fp8_prefill* h, const void* x, const int32_t* ids, const floa
       if (at[MOE_NUM_STAGES] && hipEventRecord(at[MOE_NUM_STAGES], s) != hipSuccess) return fail(h);
       h->pending.push_back(ev);
     }
-    h->last_T = t;
+    if (&ws == &h->ws) h->last_T = t;  // the inspection calls read the handle's workspace
   }
   if (hipEventRecord(h->done, s) != hipSuccess) return fail(h);
   if (slot) {
@@ -661,6 +723,8 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, h->device) == hipSuccess && prop.multiProcessorCount > 0)
     h->num_cus = prop.multiProcessorCount;
+  if (static_scratch(&h->scratch) != hipSuccess) h->scratch = nullptr;  // run_static() then refuses
+  h->static_rows = static_rows_of(m);
 
   const WsSizes w = ws_sizes(m);
   void* p;
@@ -678,27 +742,27 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
   h->w2 = (uint8_t*)get(m.E * m.H * m.Ip);
   h->s2 = (float*)get(m.E * m.nH * m.nI * 4);
   if (m.exact_ties()) h->n13 = (float*)get(norm_bytes_of(m));
-  h->xq = (uint8_t*)get(w.xq);
-  h->sx = (float*)get(w.sx);
-  h->sxT = (float*)get(w.sxT);
-  h->hq = (uint8_t*)get(w.hq);
-  h->sh = (float*)get(w.sh);
-  h->shT = (float*)get(w.shT);
-  h->y = (float*)get(w.y);
-  h->counts = (int32_t*)get(w.counts);
-  h->offsets = (int32_t*)get(w.offsets);
-  h->perm = (int32_t*)get(w.perm);
-  h->inv = (int32_t*)get(w.inv);
-  h->small_tiles = (Tile*)get(w.small_tiles);
-  h->narrow_tiles = (Tile*)get(w.narrow_tiles);
-  h->wide_tiles = (Tile*)get(w.wide_tiles);
-  h->n_tiles = (int32_t*)get(w.n_tiles);
-  h->chunk = (int32_t*)get(w.chunk);
+  h->ws.xq = (uint8_t*)get(w.xq);
+  h->ws.sx = (float*)get(w.sx);
+  h->ws.sxT = (float*)get(w.sxT);
+  h->ws.hq = (uint8_t*)get(w.hq);
+  h->ws.sh = (float*)get(w.sh);
+  h->ws.shT = (float*)get(w.shT);
+  h->ws.y = (float*)get(w.y);
+  h->ws.counts = (int32_t*)get(w.counts);
+  h->ws.offsets = (int32_t*)get(w.offsets);
+  h->ws.perm = (int32_t*)get(w.perm);
+  h->ws.inv = (int32_t*)get(w.inv);
+  h->ws.small_tiles = (Tile*)get(w.small_tiles);
+  h->ws.narrow_tiles = (Tile*)get(w.narrow_tiles);
+  h->ws.wide_tiles = (Tile*)get(w.wide_tiles);
+  h->ws.n_tiles = (int32_t*)get(w.n_tiles);
+  h->ws.chunk = (int32_t*)get(w.chunk);
   h->err = (int32_t*)get(w.err);
-  h->rids = (int32_t*)get(w.rids);
-  h->rw = (float*)get(w.rw);
-  h->hb = (uint16_t*)get(w.hb);
-  if (m.exact_ties()) h->gu = (float*)get(w.gu);
+  h->ws.rids = (int32_t*)get(w.rids);
+  h->ws.rw = (float*)get(w.rw);
+  h->ws.hb = (uint16_t*)get(w.hb);
+  if (m.exact_ties()) h->ws.gu = (float*)get(w.gu);
   if (!ok) {
     free_all(h);
     delete h;
@@ -726,18 +790,30 @@ int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out)
 
 int moe_fp8_prefill_run(moe_fp8_prefill* h, const void* x, const int32_t* ids, const float* w,
                         int64_t T, void* out, void* stream) {
-  return run_passes(h, x, ids, w, nullptr, 0, T, out, stream);
+  if (!h) return MOE_ERR_INVALID_ARG;
+  return run_passes(h, h->ws, h->m.max_rows, x, ids, w, nullptr, 0, T, out, stream);
+}
+
+int moe_fp8_prefill_run_static(moe_fp8_prefill* h, const void* x, const int32_t* ids, const float* w,
+                               int64_t T, void* out, void* stream) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  if (!h->scratch) return h->failed ? MOE_ERR_FAILED_STATE : MOE_ERR_DEVICE;  // its address was not found
+  if (h->static_rows < 1) return MOE_ERR_UNSUPPORTED;  // not one row's workspace fits the array
+  const Workspace ws = carve(static_sizes(h->m, h->static_rows), h->scratch);
+  return run_passes(h, ws, h->static_rows, x, ids, w, nullptr, 0, T, out, stream);
 }
 
 int moe_fp8_prefill_run_decode(moe_fp8_prefill* h, const void* x, const int32_t* ids, const float* w,
                                int64_t T, void* out, void* stream) {
-  return run_passes(h, x, ids, w, nullptr, 0, T, out, stream, true);
+  if (!h) return MOE_ERR_INVALID_ARG;
+  return run_passes(h, h->ws, h->m.max_rows, x, ids, w, nullptr, 0, T, out, stream, true);
 }
 
 int moe_fp8_prefill_run_logits(moe_fp8_prefill* h, const void* x, const float* logits,
                                int32_t router, int64_t T, void* out, void* stream) {
   if (!logits) return MOE_ERR_INVALID_ARG;
-  return run_passes(h, x, nullptr, nullptr, logits, router, T, out, stream);
+  if (!h) return MOE_ERR_INVALID_ARG;
+  return run_passes(h, h->ws, h->m.max_rows, x, nullptr, nullptr, logits, router, T, out, stream);
 }
 
 int moe_fp8_prefill_route(moe_fp8_prefill* h, const float* logits, int32_t router, int64_t T,
@@ -782,13 +858,13 @@ int moe_fp8_prefill_debug_plan(moe_fp8_prefill* h, int32_t* counts, int32_t* off
   if (cap < P) return MOE_ERR_INVALID_ARG;
   if (hipDeviceSynchronize() != hipSuccess) return fail(h);
   const int64_t E = h->m.E;
-  if (hipMemcpy(counts, h->counts, E * 4, hipMemcpyDeviceToHost) != hipSuccess ||
-      hipMemcpy(offsets, h->offsets, (E + 1) * 4, hipMemcpyDeviceToHost) != hipSuccess)
+  if (hipMemcpy(counts, h->ws.counts, E * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(offsets, h->ws.offsets, (E + 1) * 4, hipMemcpyDeviceToHost) != hipSuccess)
     return fail(h);
   const int64_t routed = offsets[E];
   if (routed > P) return fail(h);
-  if ((routed > 0 && hipMemcpy(perm, h->perm, routed * 4, hipMemcpyDeviceToHost) != hipSuccess) ||
-      (P > 0 && hipMemcpy(inv, h->inv, P * 4, hipMemcpyDeviceToHost) != hipSuccess))
+  if ((routed > 0 && hipMemcpy(perm, h->ws.perm, routed * 4, hipMemcpyDeviceToHost) != hipSuccess) ||
+      (P > 0 && hipMemcpy(inv, h->ws.inv, P * 4, hipMemcpyDeviceToHost) != hipSuccess))
     return fail(h);
   return MOE_OK;
 }
@@ -798,8 +874,8 @@ int moe_fp8_prefill_debug_activations(moe_fp8_prefill* h, uint8_t* xq, float* sx
   if (h->failed) return MOE_ERR_FAILED_STATE;
   if (hipDeviceSynchronize() != hipSuccess) return fail(h);
   if (rows == 0) return MOE_OK;
-  if (hipMemcpy(xq, h->xq, rows * h->m.H, hipMemcpyDeviceToHost) != hipSuccess ||
-      hipMemcpy(sx, h->sx, rows * h->m.nH * 4, hipMemcpyDeviceToHost) != hipSuccess)
+  if (hipMemcpy(xq, h->ws.xq, rows * h->m.H, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(sx, h->ws.sx, rows * h->m.nH * 4, hipMemcpyDeviceToHost) != hipSuccess)
     return fail(h);
   return MOE_OK;
 }
@@ -810,14 +886,14 @@ int moe_fp8_prefill_debug_intermediates(moe_fp8_prefill* h, uint8_t* hq, float* 
   if (h->failed) return MOE_ERR_FAILED_STATE;
   if (hipDeviceSynchronize() != hipSuccess) return fail(h);
   int32_t routed = 0;
-  if (hipMemcpy(&routed, h->offsets + h->m.E, 4, hipMemcpyDeviceToHost) != hipSuccess) return fail(h);
+  if (hipMemcpy(&routed, h->ws.offsets + h->m.E, 4, hipMemcpyDeviceToHost) != hipSuccess) return fail(h);
   *n_rows = routed;
   if (routed > cap_rows) return MOE_ERR_INVALID_ARG;
   if (routed == 0) return MOE_OK;
   const Dims& m = h->m;
-  if ((hq && hipMemcpy(hq, h->hq, routed * m.Ip, hipMemcpyDeviceToHost) != hipSuccess) ||
-      (sh && hipMemcpy(sh, h->sh, routed * m.nI * 4, hipMemcpyDeviceToHost) != hipSuccess) ||
-      (y && hipMemcpy(y, h->y, routed * m.H * 4, hipMemcpyDeviceToHost) != hipSuccess))
+  if ((hq && hipMemcpy(hq, h->ws.hq, routed * m.Ip, hipMemcpyDeviceToHost) != hipSuccess) ||
+      (sh && hipMemcpy(sh, h->ws.sh, routed * m.nI * 4, hipMemcpyDeviceToHost) != hipSuccess) ||
+      (y && hipMemcpy(y, h->ws.y, routed * m.H * 4, hipMemcpyDeviceToHost) != hipSuccess))
     return fail(h);
   return MOE_OK;
 }
@@ -827,7 +903,7 @@ int moe_fp8_prefill_debug_gate_up(moe_fp8_prefill* h, float* gu, int64_t cap_row
   if (h->failed) return MOE_ERR_FAILED_STATE;
   if (hipDeviceSynchronize() != hipSuccess) return fail(h);
   int32_t routed = 0;
-  if (hipMemcpy(&routed, h->offsets + h->m.E, 4, hipMemcpyDeviceToHost) != hipSuccess) return fail(h);
+  if (hipMemcpy(&routed, h->ws.offsets + h->m.E, 4, hipMemcpyDeviceToHost) != hipSuccess) return fail(h);
   *n_rows = routed;
   if (routed > cap_rows) return MOE_ERR_INVALID_ARG;
   if (routed == 0) return MOE_OK;
@@ -836,7 +912,7 @@ int moe_fp8_prefill_debug_gate_up(moe_fp8_prefill* h, float* gu, int64_t cap_row
   if (hipMalloc((void**)&dbg, (size_t)bytes) != hipSuccess) return MOE_ERR_OUT_OF_MEMORY;
   // re-run the last pass's gate_up (deterministic: rewrites identical h)
   int rc = MOE_OK;
-  if (launch_gate_up_all(h, h->last_T, h->last_T * h->m.k, dbg, nullptr) != hipSuccess ||
+  if (launch_gate_up_all(h, h->ws, h->last_T, h->last_T * h->m.k, dbg, nullptr) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess ||
       hipMemcpy(gu, dbg, (size_t)bytes, hipMemcpyDeviceToHost) != hipSuccess)
     rc = fail(h);
@@ -1025,6 +1101,8 @@ int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slo
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, h->device) == hipSuccess && prop.multiProcessorCount > 0)
     h->num_cus = prop.multiProcessorCount;
+  if (static_scratch(&h->scratch) != hipSuccess) h->scratch = nullptr;  // run_static() then refuses
+  h->static_rows = static_rows_of(m);
   const WsSizes w = ws_sizes(m);
   void* p;
   bool ok = true;
@@ -1052,27 +1130,27 @@ int moe_fp8_prefill_create_streamed(const moe_fp8_prefill_desc* d, int32_t n_slo
     h->stage_full_codes = st.full_codes;
     h->stage_full_scales = st.full_scales;
   }
-  h->xq = (uint8_t*)get(w.xq);
-  h->sx = (float*)get(w.sx);
-  h->sxT = (float*)get(w.sxT);
-  h->hq = (uint8_t*)get(w.hq);
-  h->sh = (float*)get(w.sh);
-  h->shT = (float*)get(w.shT);
-  h->y = (float*)get(w.y);
-  h->counts = (int32_t*)get(w.counts);
-  h->offsets = (int32_t*)get(w.offsets);
-  h->perm = (int32_t*)get(w.perm);
-  h->inv = (int32_t*)get(w.inv);
-  h->small_tiles = (Tile*)get(w.small_tiles);
-  h->narrow_tiles = (Tile*)get(w.narrow_tiles);
-  h->wide_tiles = (Tile*)get(w.wide_tiles);
-  h->n_tiles = (int32_t*)get(w.n_tiles);
-  h->chunk = (int32_t*)get(w.chunk);
+  h->ws.xq = (uint8_t*)get(w.xq);
+  h->ws.sx = (float*)get(w.sx);
+  h->ws.sxT = (float*)get(w.sxT);
+  h->ws.hq = (uint8_t*)get(w.hq);
+  h->ws.sh = (float*)get(w.sh);
+  h->ws.shT = (float*)get(w.shT);
+  h->ws.y = (float*)get(w.y);
+  h->ws.counts = (int32_t*)get(w.counts);
+  h->ws.offsets = (int32_t*)get(w.offsets);
+  h->ws.perm = (int32_t*)get(w.perm);
+  h->ws.inv = (int32_t*)get(w.inv);
+  h->ws.small_tiles = (Tile*)get(w.small_tiles);
+  h->ws.narrow_tiles = (Tile*)get(w.narrow_tiles);
+  h->ws.wide_tiles = (Tile*)get(w.wide_tiles);
+  h->ws.n_tiles = (int32_t*)get(w.n_tiles);
+  h->ws.chunk = (int32_t*)get(w.chunk);
   h->err = (int32_t*)get(w.err);
-  h->rids = (int32_t*)get(w.rids);
-  h->rw = (float*)get(w.rw);
-  h->hb = (uint16_t*)get(w.hb);
-  if (m.exact_ties()) h->gu = (float*)get(w.gu);
+  h->ws.rids = (int32_t*)get(w.rids);
+  h->ws.rw = (float*)get(w.rw);
+  h->ws.hb = (uint16_t*)get(w.hb);
+  if (m.exact_ties()) h->ws.gu = (float*)get(w.gu);
   if (!ok) {
     free_all(h);
     delete h;

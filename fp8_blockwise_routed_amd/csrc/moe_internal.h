@@ -218,6 +218,10 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
 hipError_t launch_slice(const SliceArgs& a, hipStream_t s);
 hipError_t launch_tie_exact(const TieArgs& a, int64_t max_slots, hipStream_t s);
 hipError_t launch_wnorm(const LayoutArgs& a, hipStream_t s);
+// run_static(): the static per-device workspace array and its address on the
+// current device (looked up once per device).
+constexpr int64_t kStaticScratchBytes = int64_t(64) << 20;
+hipError_t static_scratch(uint8_t** out);
 hipError_t launch_peak_mfma(int32_t iters, int grid, float* out, hipStream_t s);
 hipError_t launch_peak_stream(const void* src, int64_t max_bytes, int grid, int32_t* out, int64_t* bytes,
                               hipStream_t s);

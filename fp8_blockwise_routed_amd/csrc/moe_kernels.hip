@@ -20,6 +20,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -2583,6 +2584,34 @@ hipError_t launch_wnorm(const LayoutArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.n * 2 * a.Ip;
   hipLaunchKernelGGL(wnorm_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------- static scratch --
+// The per-pass workspace of moe_fp8_prefill_run_static, for callers that
+// cannot allocate: one array per device, held until the process ends and
+// shared by every handle and call on that device.  On the host the array's
+// name is a host-side stand-in, not a device address; host code uses only the
+// address hipGetSymbolAddress returns for the current device, looked up once
+// per device and kept.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(uint8_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static uint8_t* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = (uint8_t*)p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------- calibration --

@@ -158,6 +158,31 @@ int moe_fp8_prefill_run(moe_fp8_prefill* h, const void* x, const int32_t* ids,
                         const float* w, int64_t T, void* out, void* stream);
 
 /*
+ * run() for callers that cannot allocate device memory or whose workspace
+ * must not come from the handle: code that records work for later replay,
+ * tight serving loops, harnesses that forbid allocation.  Same computation,
+ * arguments, stream rules and errors as run(), and the same output bits.
+ * The per-pass workspace (activation codes and scales, plan, tile lists, h
+ * and y) lives in one static device array of MOE_STATIC_SCRATCH_BYTES that the
+ * library holds on every device it runs on until the process ends, instead
+ * of the handle's workspace; nothing is allocated and the host does not
+ * wait.  T rows run in passes of at most R rows, R the largest row count (at
+ * most max_rows) whose workspace fits the array (about 300 rows for E=256,
+ * top-8, H=6144, I=2048; every description validate() accepts fits at least
+ * three rows); a layer whose single row would not fit is refused with
+ * MOE_ERR_UNSUPPORTED.  MOE_ERR_DEVICE if the array's address could not be
+ * found when the handle was created.  The array is shared by every handle
+ * and call on a device and keeps the last call's contents (no part of it
+ * needs to start at zero): calls that overlap on one GPU, from other
+ * streams, threads or handles, race, and the caller must order them.  The
+ * inspection calls keep describing the last pass run in the handle's own
+ * workspace.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (64ll << 20)
+int moe_fp8_prefill_run_static(moe_fp8_prefill* h, const void* x, const int32_t* ids, const float* w,
+                               int64_t T, void* out, void* stream);
+
+/*
  * The decode path: the same layer in its W8A16 form, which the pages use for
  * decode and continuations shorter than 256 tokens ("ktransformers #2244",
  * Design: prefill of >= 256 tokens runs W8A8 on the GPU, shorter
