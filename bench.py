@@ -554,23 +554,26 @@ def summarize_profiles(out_dir: str) -> int:
             busy = _per_kernel(mrows, "SQ_VALU_MFMA_BUSY_CYCLES")
             mops = _per_kernel(mrows, "SQ_INSTS_VALU_MFMA_MOPS_F8")
             gui = _per_kernel(mrows, "GRBM_GUI_ACTIVE")
-            simds = 1024  # 256 CUs x 4 SIMDs
+            simds, xccs = 1024, 8  # 256 CUs x 4 SIMDs, in 8 XCDs
             lines = [f"# Matrix-core counters per launch, {TITLES[tag]}", "",
                      "Command (repository root, one MI355X):", "", f"    {cmds['mfma']}", "",
-                     "SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs: MFMA busy = that / (GRBM_GUI_ACTIVE x "
-                     f"{simds} SIMDs).  SQ_INSTS_VALU_MFMA_MOPS_F8 counts FP8 MFMA operations / 512.  The clock "
-                     "is GRBM_GUI_ACTIVE cycles over the kernel's average duration in the trace run of the same "
-                     "workload (kernel_stats file).", "",
+                     "rocprofv3 sums each counter over its dimensions: SQ_VALU_MFMA_BUSY_CYCLES over every SIMD, "
+                     f"GRBM_GUI_ACTIVE over the {xccs} XCDs, so one XCD's active cycles are GRBM_GUI_ACTIVE / "
+                     f"{xccs}.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xccs} x {simds} SIMDs).  "
+                     "SQ_INSTS_VALU_MFMA_MOPS_F8 counts FP8 MFMA operations / 512 (padded rows of a 16-row "
+                     "subtile included).  The clock is one XCD's active cycles over the kernel's average duration "
+                     "in the trace run of the same workload (kernel_stats file).", "",
                      f"- kernel_source_sha256_16: `{src}`", "",
-                     "| kernel | dispatches | MFMA busy | FP8 TFLOP per launch | GRBM_GUI_ACTIVE cycles | "
+                     "| kernel | dispatches | MFMA busy | FP8 TFLOP per launch | GRBM_GUI_ACTIVE cycles (sum) | "
                      "clock GHz | FP8 TFLOP/s |", "|---|---|---|---|---|---|---|"]
             for k in sorted(busy):
-                if k not in gui:
+                if k not in gui or not (k.startswith("gate_up") or k.startswith("down") or k.startswith("tie")):
                     continue
-                util = busy[k][0] / (gui[k][0] * simds) if gui[k][0] else float("nan")
+                cyc = gui[k][0] / xccs
+                util = busy[k][0] / (cyc * simds) if cyc else float("nan")
                 tflop = mops[k][0] * 512 / 1e12 if k in mops else float("nan")
                 dur = durations.get(k)
-                ghz = gui[k][0] / dur if dur else float("nan")
+                ghz = cyc / dur if dur else float("nan")
                 rate = tflop / (dur * 1e-9) if dur else float("nan")
                 lines.append(f"| `{k}` | {busy[k][1]} | {util:.3f} | {tflop:.4f} | {gui[k][0]:.0f} | "
                              f"{ghz:.2f} | {rate:.0f} |")

@@ -25,12 +25,16 @@ constexpr int kWideRows = 256;       // rows per tile of the 8-wave GEMMs for ex
 #ifndef MOE_GU_WG_PER_CU
 #define MOE_GU_WG_PER_CU 2
 #endif
+#ifndef MOE_MIX_LISTS
+#define MOE_MIX_LISTS 1  // interleave two tile lists of one launch by XCD runs
+#endif
 #ifndef MOE_DN_WG_PER_CU
 #define MOE_DN_WG_PER_CU 2
 #endif
 constexpr int kWeightAux = MOE_WEIGHT_AUX;          // cache-policy bits of the weight loads
 constexpr int kGateUpWgPerCu = MOE_GU_WG_PER_CU;  // persistent grid of the streaming gate_up
 constexpr int kDownWgPerCu = MOE_DN_WG_PER_CU;    // persistent grid of the streaming down
+constexpr bool kMixLists = MOE_MIX_LISTS != 0;
 constexpr int kStreamDepth = MOE_STREAM_DEPTH;           // K blocks in flight per wave, streaming gate_up
 constexpr int kStreamDepthDown = MOE_STREAM_DEPTH_DOWN;  // K blocks in flight per wave, streaming down
 constexpr int kMaxExperts = 1024;

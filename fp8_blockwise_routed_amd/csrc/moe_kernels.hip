@@ -548,6 +548,44 @@ __device__ __forceinline__ int item_index(int r) {
   return (r * kXcds + b % kXcds) * slots + b / kXcds;
 }
 
+// The items of a launch over two tile lists (n1 items of the first, then n2
+// of the second), dealt in the XCD runs of item_index, with the two lists'
+// runs interleaved in proportion to their counts: in every round some XCDs
+// stream the weight-bound items of one list while the others compute the
+// MFMA-bound items of the other, instead of one phase after the other.
+// next(q) returns the item at or after position q of this workgroup's
+// sequence and moves q past it: the first list's item i as i, the second's
+// as n1 + i, n1 + n2 past the end.  Positions beyond a list's last, partial
+// run are skipped.
+struct MixedItems {
+  int n1, n2, run, r1, r2, total;
+  __device__ __forceinline__ MixedItems(int n1_, int n2_) : n1(n1_), n2(n2_) {
+    const int G = (int)gridDim.x;
+    run = (G % kXcds) ? G : G / kXcds;
+    r1 = (n1 + run - 1) / run;
+    r2 = (n2 + run - 1) / run;
+    total = (r1 + r2) * run;
+  }
+  __device__ __forceinline__ int next(int& q) const {
+    if (!kMixLists) {  // the first list, then the second
+      const int g = item_index(q++);
+      return g < n1 + n2 ? g : n1 + n2;
+    }
+    for (;; ++q) {
+      const int g = item_index(q);
+      if (g >= total) return n1 + n2;
+      const int j = g / run, o = g - j * run;
+      const int c2 = (int)((long long)j * r2 / (r1 + r2));
+      const bool second = (int)((long long)(j + 1) * r2 / (r1 + r2)) > c2;
+      const int i = (second ? c2 : j - c2) * run + o;
+      if (i < (second ? n2 : n1)) {
+        ++q;
+        return second ? n1 + i : i;
+      }
+    }
+  }
+};
+
 // Streaming gate_up for experts with at most 16 rows (the HBM-bound regime):
 // one 16-row subtile, so every weight byte feeds one MFMA.  No LDS activation
 // tile and no barrier inside the K loop: each wave loads its own activation
@@ -1658,7 +1696,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
     static_for<5>([&](auto PT) __attribute__((always_inline)) { issue_part(ST, PT, kb, q); });
   };
 
-  int item = item_index(0);
+  const MixedItems mix(n_first, n_items - n_first);
+  int q = 0;
+  int item = mix.next(q);
   if (item >= n_items) return;
   Item it = item_at(item);
   ws_dma(0, it);
@@ -1666,7 +1706,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
 
   for (int r = 0;; ++r) {
     const int buf = r & 1;
-    const int next = item_index(r + 1);
+    const int next = mix.next(q);
     const bool has_next = next < n_items;
     const Item nit = item_at(has_next ? next : item);
     const int nb2 = it.nb * 2;
