@@ -75,7 +75,9 @@ DESCRIBE = {
 }
 
 # rocprofv3 runs whose CSV output --summarize-profiles reads (repository root)
-_BENCH1 = "python3 bench.py --steps 5 --warmup 2 --cpu-tokens 0 --protocol-calls 0 --no-peaks"
+# the bench's own warmup and timed steps, so the traced durations are those the
+# timed steps see (the first few launches of a fresh process run slower)
+_BENCH1 = "python3 bench.py --cpu-tokens 0 --protocol-calls 0 --no-peaks"
 PROFILED = {  # tag -> workload
     "glm_e256_t8192_zipf": HEADLINE,
     "glm_e256_t4096_uniform": "glm_e256_k8_h6144_i2048_t4096_uniform",
@@ -510,16 +512,25 @@ def summarize_profiles(out_dir: str) -> int:
     for tag in PROFILED:
         cmds = profile_commands(tag)
         stats = _csv_rows(os.path.join(out_dir, f"kt_{tag}", "**", "*kernel_stats.csv"))
+        trace = _csv_rows(os.path.join(out_dir, f"kt_{tag}", "**", "*kernel_trace.csv"))
+        per = {}
+        for r in trace:
+            per.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
         durations = {}
         if stats:
             lines = [f"# Kernel time, {TITLES[tag]}", "", "Command (repository root, one MI355X):", "",
                      f"    {cmds['trace']}", "", f"- kernel_source_sha256_16: `{src}`", "",
-                     "| kernel | calls | average us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+                     "Average, min and max are rocprofv3's --stats over every dispatch; the median is over the "
+                     "same dispatches in the kernel trace.", "",
+                     "| kernel | calls | average us | median us | min us | max us | % of GPU time |",
+                     "|---|---|---|---|---|---|---|"]
             for r in stats:
-                lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                d = sorted(per.get(r["Name"], []))
+                med = d[len(d) // 2] / 1e3 if d else float("nan")
+                lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {med:.1f} | "
                              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                              f"{float(r['Percentage']):.2f} |")
-                durations[_base_name(r["Name"])] = float(r["AverageNs"])
+                durations[_base_name(r["Name"])] = med * 1e3 if d else float(r["AverageNs"])
             lines += ["", "The layout kernels run once, inside create(), outside the timed steps."]
             with open(os.path.join(PROFILES, f"kernel_stats_{tag}.md"), "w") as f:
                 f.write("\n".join(lines) + "\n")
@@ -561,13 +572,16 @@ def summarize_profiles(out_dir: str) -> int:
                      f"GRBM_GUI_ACTIVE over the {xccs} XCDs, so one XCD's active cycles are GRBM_GUI_ACTIVE / "
                      f"{xccs}.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xccs} x {simds} SIMDs).  "
                      "SQ_INSTS_VALU_MFMA_MOPS_F8 counts FP8 MFMA operations / 512 (padded rows of a 16-row "
-                     "subtile included).  The clock is one XCD's active cycles over the kernel's average duration "
-                     "in the trace run of the same workload (kernel_stats file).", "",
+                     "subtile included).  The clock is one XCD's active cycles over the kernel's median duration "
+                     "in the trace run of the same workload (kernel_stats file).  Launches that find no work (an "
+                     "empty tile list) are left out.", "",
                      f"- kernel_source_sha256_16: `{src}`", "",
                      "| kernel | dispatches | MFMA busy | FP8 TFLOP per launch | GRBM_GUI_ACTIVE cycles (sum) | "
                      "clock GHz | FP8 TFLOP/s |", "|---|---|---|---|---|---|---|"]
             for k in sorted(busy):
                 if k not in gui or not (k.startswith("gate_up") or k.startswith("down") or k.startswith("tie")):
+                    continue
+                if mops.get(k, (0.0, 0))[0] == 0.0:
                     continue
                 cyc = gui[k][0] / xccs
                 util = busy[k][0] / (cyc * simds) if cyc else float("nan")

@@ -892,7 +892,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     ring_barrier();
 
-    // acc[m][t]: rows 128 mh + 16 m + 4 grp + i, n-tile t (gate 0-1, up 2-3)
+    // acc[m][t]: row 128 mh + 16 m + lane % 16, columns 4 (lane / 16) .. + 3
+    // of n-tile t (gate 0-1, up 2-3): the weights are the MFMA's A operand,
+    // so a lane's row needs one promotion factor per subtile, not four
     f32x4 acc[8][4];
 #pragma unroll
     for (int m = 0; m < 8; ++m)
@@ -915,7 +917,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
       if (MT > 0 && kb < nH) {
         const uint8_t* wbuf = (s == 0 ? w_lds0 : w_lds1) + w_rd;
         const uint8_t* abuf = (s == 0 ? a_lds0 : a_lds1) + afr;
-        const float* crow = (s == 0 ? cs_lds0 : cs_lds1) + mh * 128 + grp * 4;
+        const float* crow = (s == 0 ? cs_lds0 : cs_lds1) + mh * 128 + (lane & 15);
         i32x8 B[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) B[t] = cat(ld16(wbuf + t * 2048), ld16(wbuf + t * 2048 + 1024));
@@ -924,17 +926,18 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
         // promotion of its own products (the other wave of the SIMD
         // multiplies meanwhile).
         i32x8 A2[2];
-        f32x4 CG, CU, P[4];
+        float CG, CU;
+        f32x4 P[4];
         A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
         static_for<MT>([&](auto M) __attribute__((always_inline)) {
           constexpr int m = decltype(M)::value;
           constexpr int per = MT >= 4 ? 1 : 4 / (MT > 0 ? MT : 1);  // load parts per subtile
-          CG = ld16f(crow + m * 16);
-          CU = ld16f(crow + BM + m * 16);
+          CG = crow[m * 16];
+          CU = crow[BM + m * 16];
           if constexpr (m + 1 < MT)
             A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
 #pragma unroll
-          for (int t = 0; t < 4; ++t) P[t] = mfma_e4m3(A2[m & 1], B[t]);
+          for (int t = 0; t < 4; ++t) P[t] = mfma_e4m3(B[t], A2[m & 1]);
           static_for<per>([&](auto J) __attribute__((always_inline)) {
             constexpr int q = m * per + decltype(J)::value;
             if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kb + 1, cur);
@@ -946,7 +949,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
           for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              acc[m][t][i] = __builtin_fmaf(P[t][i], t < 2 ? CG[i] : CU[i], acc[m][t][i]);
+              acc[m][t][i] = __builtin_fmaf(P[t][i], t < 2 ? CG : CU, acc[m][t][i]);
           pin_in_place(acc[m]);
           constexpr int nl = (m * per < 4 ? 2 * per : 0) + (m == 0 ? 1 : 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS reads (next subtile)
@@ -988,25 +991,23 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
     const int ecol = etid & 15, egrp = (etid >> 4) & 3;
     if constexpr (kDbg) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = mh * 128 + m * 16 + egrp * 4 + i;
-          if (m < mtw && row < rows) {
-            float* g = a.gu_dbg + (size_t)(p0 + row) * 2 * Ip + nb * kBlock + wn * 32 + ecol;
-            g[0] = acc[m][0][i];
-            g[16] = acc[m][1][i];
-            g[Ip] = acc[m][2][i];
-            g[Ip + 16] = acc[m][3][i];
-          }
+      for (int m = 0; m < 8; ++m) {
+        const int row = mh * 128 + m * 16 + ecol;
+        if (m < mtw && row < rows) {
+          float* g = a.gu_dbg + (size_t)(p0 + row) * 2 * Ip + nb * kBlock + wn * 32 + egrp * 4;
+          *reinterpret_cast<f32x4*>(g) = acc[m][0];
+          *reinterpret_cast<f32x4*>(g + 16) = acc[m][1];
+          *reinterpret_cast<f32x4*>(g + Ip) = acc[m][2];
+          *reinterpret_cast<f32x4*>(g + Ip + 16) = acc[m][3];
         }
+      }
     }
     // h = silu(g) * u in FP32, one 128-row half at a time (the half's waves
     // write it to stage 1: a_lds1 rows 0-63, w_lds1 rows 64-127, 512 bytes
     // each), then four threads per row quantise it: thread t takes 16-byte
     // chunks 8 (t % 4) .. + 7 (32 columns) of row t / 4.  Chunk c of row r sits
-    // in slot c ^ (r % 32) ^ 8 (c / 16), so the stores of one instruction (4
-    // rows 4 apart, 16 columns) fill distinct banks.
+    // in slot c ^ (r % 32) ^ 8 (c / 16), so the 16-byte stores of one
+    // instruction (16 rows, one chunk each) fill distinct banks.
     auto hslot = [](int rr, int c) __attribute__((always_inline)) { return c ^ (rr & 31) ^ ((c >> 4) << 3); };
     // h of this wave's rows in registers first (the accumulators die here)
     float hv[8][4][2];
@@ -1039,12 +1040,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
         for (int m = 0; m < 8; ++m) {
           if (m < mtw) {
             uint8_t* hb = m < 4 ? a_lds1 : w_lds1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int rr = (m & 3) * 16 + egrp * 4 + i;
-              const int c0 = wn * 8 + (ecol >> 2), c1 = c0 + 4;
-              *reinterpret_cast<float*>(hb + rr * 512 + (hslot(rr, c0) << 4) + (ecol & 3) * 4) = hv[m][i][0];
-              *reinterpret_cast<float*>(hb + rr * 512 + (hslot(rr, c1) << 4) + (ecol & 3) * 4) = hv[m][i][1];
+            {
+              const int rr = (m & 3) * 16 + ecol;
+              const int c0 = wn * 8 + egrp, c1 = c0 + 4;
+              *reinterpret_cast<f32x4*>(hb + rr * 512 + (hslot(rr, c0) << 4)) =
+                  f32x4{hv[m][0][0], hv[m][1][0], hv[m][2][0], hv[m][3][0]};
+              *reinterpret_cast<f32x4*>(hb + rr * 512 + (hslot(rr, c1) << 4)) =
+                  f32x4{hv[m][0][1], hv[m][1][1], hv[m][2][1], hv[m][3][1]};
             }
           }
         }
@@ -1715,60 +1717,75 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
     const int rows_h = rows - mh * 128 < 0 ? 0 : (rows - mh * 128 > 128 ? 128 : rows - mh * 128);
     const int mtw = (half == 1 && !two) ? 0 : (rows_h + 15) >> 4;
 
-    // block 0 and the weight scales (issued before the previous item's
-    // stores) have landed everywhere, and the previous item's LDS is no
-    // longer read
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-    ring_barrier();
+    // The first item waits here for its block 0 and weight scales; a later
+    // item's block 0 landed in the previous item's last step, its weight
+    // scales in that item's first step, and every wave passed that last
+    // step's barrier after its final LDS read.  So the previous item's y
+    // stores are not waited for: they drain under step 0, whose closing
+    // vmcnt(0) covers them (stores and loads complete in issue order).
+    if (r == 0) {
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+      ring_barrier();
+    }
     const Src cur = src_of(it);
     // the next item's weight scales into the other buffer (they land with block 1)
     if (has_next) ws_dma(buf ^ 1, nit);
 
+    // acc[m][t]: row 128 mh + 16 m + lane % 16, columns 4 (lane / 16) .. + 3
+    // of n-tile t, so each lane stores 16 contiguous bytes of y per n-tile
     f32x4 acc[8][4];
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](auto S, auto MTC, int kb0) __attribute__((always_inline)) {
+    // LC: the last pair of steps.  Its second step (whose next stage is
+    // stage 0, read in the step before) loads the next item's block 0
+    // instead of the out-of-range block past this item's last one, so that
+    // block lands under this step's MFMAs rather than after the y stores.
+    auto step = [&](auto S, auto MTC, auto LC, int kb0) __attribute__((always_inline)) {
       constexpr int s = decltype(S)::value, MT = decltype(MTC)::value;
+      constexpr bool kNextItem = decltype(LC)::value && s == 1;
       const int kb = kb0 + s;
       constexpr auto NEXT = std::integral_constant<int, 1 - s>{};
-      if constexpr (MT == 0) issue(NEXT, kb + 1, cur);
+      const Src src = kNextItem ? src_of(nit) : cur;
+      const int kn = kNextItem ? (has_next ? 0 : nI) : kb + 1;
+      if constexpr (MT == 0) issue(NEXT, kn, src);
       if (MT > 0 && kb < nI) {
         const float wsc = ws_lds[buf][half][kb];
         const uint8_t* wbuf = (s == 0 ? w_lds0 : w_lds1) + w_rd;
         const uint8_t* abuf = (s == 0 ? a_lds0 : a_lds1) + afr;
-        const float* srw = (s == 0 ? s_lds0 : s_lds1) + mh * 128 + grp * 4;
+        const float* srw = (s == 0 ? s_lds0 : s_lds1) + mh * 128 + (lane & 15);
         i32x8 B[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) B[t] = cat(ld16(wbuf + t * 2048), ld16(wbuf + t * 2048 + 1024));
         // subtile by subtile as in gate_up_wide_kernel
         i32x8 A2[2];
-        f32x4 R2[2], Q[4];
+        float R2[2];
+        f32x4 Q[4];
         A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
-        R2[0] = ld16f(srw);
+        R2[0] = srw[0];
         static_for<MT>([&](auto M) __attribute__((always_inline)) {
           constexpr int m = decltype(M)::value;
           constexpr int per = MT >= 4 ? 1 : 4 / (MT > 0 ? MT : 1);
           if constexpr (m + 1 < MT) {
             A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
-            R2[(m + 1) & 1] = ld16f(srw + (m + 1) * 16);
+            R2[(m + 1) & 1] = srw[(m + 1) * 16];
           }
+          // weights as the A operand: lane l gets row l % 16 of the subtile
+          // and columns 4 (l / 16) .. + 3 of n-tile t
 #pragma unroll
-          for (int t = 0; t < 4; ++t) Q[t] = mfma_e4m3(A2[m & 1], B[t]);
+          for (int t = 0; t < 4; ++t) Q[t] = mfma_e4m3(B[t], A2[m & 1]);
           static_for<per>([&](auto J) __attribute__((always_inline)) {
-            constexpr int q = m * per + decltype(J)::value;
-            if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kb + 1, cur);
+            constexpr int qp = m * per + decltype(J)::value;
+            if constexpr (qp < 4) issue_part(NEXT, std::integral_constant<int, qp>{}, kn, src);
           });
-          if constexpr (m == 0) issue_part(NEXT, std::integral_constant<int, 4>{}, kb + 1, cur);
-          float sc[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sc[i] = R2[m & 1][i] * wsc;
+          if constexpr (m == 0) issue_part(NEXT, std::integral_constant<int, 4>{}, kn, src);
+          const float sc = R2[m & 1] * wsc;
 #pragma unroll
           for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[m][t][i] = __builtin_fmaf(Q[t][i], sc[i], acc[m][t][i]);
+            for (int i = 0; i < 4; ++i) acc[m][t][i] = __builtin_fmaf(Q[t][i], sc, acc[m][t][i]);
           pin_in_place(acc[m]);
           constexpr int nl = (m * per < 4 ? 2 * per : 0) + (m == 0 ? 1 : 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS reads (next subtile)
@@ -1778,17 +1795,20 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
           __builtin_amdgcn_sched_barrier(0);
         });
       } else if constexpr (MT > 0) {
-        issue(NEXT, kb + 1, cur);
+        issue(NEXT, kn, src);
       }
-      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block kb + 1 has landed
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block kn has landed
       ring_barrier();
     };
     auto kloop = [&](auto MTC) __attribute__((always_inline)) {
       static_assert(NS == 2, "the K loop is unrolled by the stage count");
-      for (int kb0 = 0; kb0 < nI; kb0 += NS) {
-        step(std::integral_constant<int, 0>{}, MTC, kb0);
-        step(std::integral_constant<int, 1>{}, MTC, kb0);
+      int kb0 = 0;
+      for (; kb0 + NS < nI; kb0 += NS) {
+        step(std::integral_constant<int, 0>{}, MTC, std::false_type{}, kb0);
+        step(std::integral_constant<int, 1>{}, MTC, std::false_type{}, kb0);
       }
+      step(std::integral_constant<int, 0>{}, MTC, std::true_type{}, kb0);
+      step(std::integral_constant<int, 1>{}, MTC, std::true_type{}, kb0);
     };
     if (mtw > 4)
       kloop(std::integral_constant<int, 8>{});
@@ -1797,25 +1817,34 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
     else
       kloop(std::integral_constant<int, 0>{});
 
-    // Both stages are free (the last step waited for its out-of-range loads
-    // and every wave has passed its barrier): the next item's first K block
-    // goes to stage 0 before this item's y rows are stored from registers.
-    if (has_next) issue(std::integral_constant<int, 0>{}, 0, src_of(nit));
-
     int etid = (int)threadIdx.x;
     asm volatile("" : "+v"(etid));
     const int ecol = etid & 15, egrp = (etid >> 4) & 3;
+    // y leaves through this wave's own four 1 KiB blocks of stage 1 (those
+    // its DMA fills next), 16 rows at a time: lane (r, g) writes chunks
+    // 4 t + g of row r, then reads back 4 rows x 16 chunks, so each store
+    // writes four whole 256-byte row segments (16-byte stores straight from
+    // the MFMA layout cover 16 rows x 64 bytes each and measured 4-6% slower
+    // for the whole kernel).  Chunk c of row r sits in slot c ^ r; row r is
+    // at (r / 4) x 8 KiB + (r % 4) x 256.  The stores are non-temporal: the
+    // combine that reads y runs 3-19% faster when no dirty y lines are left
+    // in the caches to be written back under it.
+    uint8_t* yst = a_lds1 + wave * 1024;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       if (m < mtw) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = mh * 128 + m * 16 + egrp * 4 + i;
-          if (row < rows) {
-            float* dst = a.y + (size_t)(p0 + row) * H + (nb2 + half) * kBlock + (wn & 1) * 64 + ecol;
+        for (int t = 0; t < 4; ++t)
+          *reinterpret_cast<f32x4*>(yst + (ecol >> 2) * 8192 + (ecol & 3) * 256 + (((4 * t + egrp) ^ ecol) << 4)) =
+              acc[m][t];
+        f32x4 v[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) dst[t * 16] = acc[m][t][i];
-          }
+        for (int j = 0; j < 4; ++j)
+          v[j] = *reinterpret_cast<const f32x4*>(yst + j * 8192 + egrp * 256 + ((ecol ^ (4 * j + egrp)) << 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = mh * 128 + m * 16 + 4 * j + egrp;
+          if (row < rows) __builtin_nontemporal_store(v[j], reinterpret_cast<f32x4*>(a.y + (size_t)(p0 + row) * H + (nb2 + half) * kBlock + (wn & 1) * 64 + ecol * 4));
         }
       }
     }

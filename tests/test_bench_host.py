@@ -116,7 +116,13 @@ def test_profile_summaries_round_trip(tmp_path, monkeypatch):
     with open(d / "kt_kernel_stats.csv", "w") as f:
         f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs\n")
         f.write(f'"{k}",10,9500000,950000,60.0,940000,960000\n')
+    with open(d / "kt_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for i, dur in enumerate((990000, 940000, 945000)):
+            f.write(f'"{k}",{i * 10**7},{i * 10**7 + dur}\n')
     assert bench.summarize_profiles(str(out)) == 0
+    stats = (tmp_path / "profiles" / f"kernel_stats_{tag}.md").read_text()
+    assert "| 950.0 | 945.0 | 940.0 | 960.0 |" in stats  # average, trace median, min, max
     # FETCH scaled by 2 (the copy reads half its bytes), WRITE by 1
     assert bench.read_traffic("gate_up_stream_kernel", tag) == (1001.0 * 2 + 10.0) * 1024
     assert (tmp_path / "profiles" / f"kernel_stats_{tag}.md").exists()
