@@ -1225,6 +1225,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
     // waves' accumulators are not live in the producers' code, which keeps
     // both within 256 registers.
     if (mma) {
+      // acc[m][t]: row 16 m + lane % 16, columns 4 (lane / 16) .. + 3 of
+      // n-tile t (weights as the MFMA's A operand, as in gate_up_wide_kernel)
       f32x4 acc[8][4];
 #pragma unroll
       for (int m = 0; m < 8; ++m)
@@ -1242,7 +1244,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
           const int afc0 = ((2 * lg) ^ swz(ll)) << 4, afc1 = ((2 * lg + 1) ^ swz(ll)) << 4;
           const uint8_t* wbuf = (s == 0 ? w_lds0 : (s == 1 ? w_lds1 : w_lds2)) + wn * 8192 + ll * 16;
           const uint8_t* abuf = (s == 0 ? a_lds0 : (s == 1 ? a_lds1 : a_lds2)) + (ll & 15) * 128;
-          const float* crow = (s == 0 ? cs_lds0 : (s == 1 ? cs_lds1 : cs_lds2)) + lg * 4;
+          const float* crow = (s == 0 ? cs_lds0 : (s == 1 ? cs_lds1 : cs_lds2)) + (ll & 15);
           i32x8 B[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) B[t] = cat(ld16(wbuf + t * 2048), ld16(wbuf + t * 2048 + 1024));
@@ -1252,14 +1254,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
           i32x8 A2[2];
           f32x4 P[2][4];
           A2[0] = cat(ld16(abuf + afc0), ld16(abuf + afc1));
-          f32x4 G3[3], U3[3];
-          G3[0] = ld16f(crow);
-          U3[0] = ld16f(crow + BM);
+          float G3[3], U3[3];
+          G3[0] = crow[0];
+          U3[0] = crow[BM];
           auto promote = [&](auto J) __attribute__((always_inline)) {
             constexpr int j = decltype(J)::value;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float cg = G3[j % 3][i], cu = U3[j % 3][i];
+              const float cg = G3[j % 3], cu = U3[j % 3];
               acc[j][0][i] = __builtin_fmaf(P[j & 1][0][i], cg, acc[j][0][i]);
               acc[j][1][i] = __builtin_fmaf(P[j & 1][1][i], cg, acc[j][1][i]);
               acc[j][2][i] = __builtin_fmaf(P[j & 1][2][i], cu, acc[j][2][i]);
@@ -1271,13 +1273,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
             constexpr int m = decltype(M)::value;
             if constexpr (m + 1 < MT) {
               A2[(m + 1) & 1] = cat(ld16(abuf + (m + 1) * 2048 + afc0), ld16(abuf + (m + 1) * 2048 + afc1));
-              G3[(m + 1) % 3] = ld16f(crow + (m + 1) * 16);
-              U3[(m + 1) % 3] = ld16f(crow + BM + (m + 1) * 16);
+              G3[(m + 1) % 3] = crow[(m + 1) * 16];
+              U3[(m + 1) % 3] = crow[BM + (m + 1) * 16];
             }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) P[m & 1][t] = mfma_e4m3(A2[m & 1], B[t]);
+            for (int t = 0; t < 4; ++t) P[m & 1][t] = mfma_e4m3(B[t], A2[m & 1]);
             if constexpr (m > 0) promote(std::integral_constant<int, m - 1>{});
-            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads (next subtile)
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads (next subtile)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -1312,39 +1314,39 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_narrow_kernel(GateUpA
       const int ecol = etid & 15, egrp = (etid >> 4) & 3;
       if constexpr (kDbg) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = m * 16 + egrp * 4 + i;
-            if (m < mt && row < rows) {
-              float* g = a.gu_dbg + (size_t)(p0 + row) * 2 * Ip + nb * kBlock + wn * 32 + ecol;
-              g[0] = acc[m][0][i];
-              g[16] = acc[m][1][i];
-              g[Ip] = acc[m][2][i];
-              g[Ip + 16] = acc[m][3][i];
-            }
+        for (int m = 0; m < 8; ++m) {
+          const int row = m * 16 + ecol;
+          if (m < mt && row < rows) {
+            float* g = a.gu_dbg + (size_t)(p0 + row) * 2 * Ip + nb * kBlock + wn * 32 + egrp * 4;
+            *reinterpret_cast<f32x4*>(g) = acc[m][0];
+            *reinterpret_cast<f32x4*>(g + 16) = acc[m][1];
+            *reinterpret_cast<f32x4*>(g + Ip) = acc[m][2];
+            *reinterpret_cast<f32x4*>(g + Ip + 16) = acc[m][3];
           }
+        }
       }
       auto act = [&](auto CL) __attribute__((always_inline)) {
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           if (m < mt) {
             uint8_t* hb = m < 4 ? w_lds1 : w_lds2;
+            f32x4 h0, h1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              float h0, h1;
               if constexpr (decltype(CL)::value) {
-                h0 = silu_mul_act(acc[m][0][i], acc[m][2][i], a.act_limit);
-                h1 = silu_mul_act(acc[m][1][i], acc[m][3][i], a.act_limit);
+                h0[i] = silu_mul_act(acc[m][0][i], acc[m][2][i], a.act_limit);
+                h1[i] = silu_mul_act(acc[m][1][i], acc[m][3][i], a.act_limit);
               } else {
-                h0 = silu_mul(acc[m][0][i], acc[m][2][i]);
-                h1 = silu_mul(acc[m][1][i], acc[m][3][i]);
+                h0[i] = silu_mul(acc[m][0][i], acc[m][2][i]);
+                h1[i] = silu_mul(acc[m][1][i], acc[m][3][i]);
               }
-              const int rr = (m & 3) * 16 + egrp * 4 + i;
-              const int c0 = wn * 8 + (ecol >> 2), c1 = c0 + 4;
-              *reinterpret_cast<float*>(hb + rr * 512 + (hslot(rr, c0) << 4) + (ecol & 3) * 4) = h0;
-              *reinterpret_cast<float*>(hb + rr * 512 + (hslot(rr, c1) << 4) + (ecol & 3) * 4) = h1;
             }
+            // row (m % 4) 16 + lane % 16, columns 32 wn + 4 (lane / 16) .. + 3
+            // (chunk c0) and 16 further (chunk c1)
+            const int rr = (m & 3) * 16 + ecol;
+            const int c0 = wn * 8 + egrp, c1 = c0 + 4;
+            *reinterpret_cast<f32x4*>(hb + rr * 512 + (hslot(rr, c0) << 4)) = h0;
+            *reinterpret_cast<f32x4*>(hb + rr * 512 + (hslot(rr, c1) << 4)) = h1;
           }
         }
       };
