@@ -205,7 +205,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_offsets_kernel(PlanArgs a) 
   const int n_chunks = (P + kPlanThreads - 1) / kPlanThreads;
   int n = 0;
   if (tid < E)
-    for (int c = 0; c < n_chunks; ++c) n += a.chunk[(size_t)c * E + tid];
+    for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+      int m[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m[j] = c0 + j < n_chunks ? a.chunk[(size_t)(c0 + j) * E + tid] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) n += m[j];
+    }
   int total;
   const int off = block_exclusive_scan(n, scan_scratch, &total);
   // each expert's rows go to one list: <= kSmallRows rows one streaming tile,
@@ -221,11 +227,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_offsets_kernel(PlanArgs a) 
   if (tid < E) {
     a.counts[tid] = n;
     a.offsets[tid] = off;
+    // eight chunk counts in flight per round (a store to a.chunk would
+    // otherwise keep the next load behind it)
     int run = off;
-    for (int c = 0; c < n_chunks; ++c) {
-      const int m = a.chunk[(size_t)c * E + tid];
-      a.chunk[(size_t)c * E + tid] = run;
-      run += m;
+    for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+      int m[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m[j] = c0 + j < n_chunks ? a.chunk[(size_t)(c0 + j) * E + tid] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c0 + j < n_chunks) {
+          a.chunk[(size_t)(c0 + j) * E + tid] = run;
+          run += m[j];
+        }
     }
     if (is_small) a.small_tiles[small_at] = Tile{tid, off, n, small_at, 1, 0, 0, 0};
     if (is_narrow) a.narrow_tiles[narrow_at] = Tile{tid, off, n, narrow_at, 1, 0, 0, 0};
@@ -377,13 +391,13 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
 // 16 lanes per 128-column group, 8 BF16 values (16 bytes) per lane.
 
 __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
+  // a block takes group kg of 16 consecutive rows, so the K-block-major
+  // scales (sxT) leave as one 64-byte run per block
   const int nH = a.H / kBlock;
-  const int64_t groups = (int64_t)a.T * nH;
-  const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int kg = (int)(blockIdx.x % (unsigned)nH);
+  const int64_t t = (int64_t)(blockIdx.x / (unsigned)nH) * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
-  if (g >= groups) return;  // whole 16-lane groups leave together
-  const int64_t t = g / nH;
-  const int kg = (int)(g - t * nH);
+  if (t >= a.T) return;  // whole 16-lane groups leave together
   const uint16_t* src = a.x + t * a.H + kg * kBlock + sub * 8;
   const i32x4 raw = ld16(src);
   float v[8];
@@ -399,7 +413,13 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
   const float amax = __uint_as_float(m);
   const float s = __fdiv_rn(amax, 448.0f);
   uint32_t lo = 0, hi = 0;
-  if (amax != 0.0f) {
+  if (amax >= kRowDivMin) {  // the group's quotients by one reciprocal (row_div)
+    const float y = __fdiv_rn(1.0f, s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= to_e4m3(row_div(v[i], s, y)) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= to_e4m3(row_div(v[4 + i], s, y)) << (8 * i);
+  } else if (amax != 0.0f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) lo |= to_e4m3(__fdiv_rn(v[i], s)) << (8 * i);
 #pragma unroll
@@ -409,14 +429,13 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
   dst[0] = lo;
   dst[1] = hi;
   if (sub == 0) {
-    a.sx[g] = s;
+    a.sx[t * nH + kg] = s;
     a.sxT[(int64_t)kg * a.T + t] = s;
   }
 }
 
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s) {
-  const int64_t groups = (int64_t)a.T * (a.H / kBlock);
-  const int64_t blocks = (groups + 15) / 16;
+  const int64_t blocks = (int64_t)(a.H / kBlock) * ((a.T + 15) / 16);
   hipLaunchKernelGGL(quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
