@@ -124,24 +124,32 @@ typedef struct moe_fp8_prefill_desc {
 
 typedef struct moe_fp8_prefill moe_fp8_prefill;
 
-/* Checks a description on the host: no GPU call, no allocation.
- * Returns MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED. */
+/* Checks a description on the host: no GPU call, no allocation ("ktransformers
+ * #2244", Design: unsupported dimensions, activation or quantisation are
+ * rejected up front).  Returns MOE_OK, MOE_ERR_INVALID_ARG or
+ * MOE_ERR_UNSUPPORTED. */
 int moe_fp8_prefill_validate(const moe_fp8_prefill_desc* d);
 
 /* Device bytes create() will allocate for workspace (all of it is reserved up
- * front; run() allocates nothing), and for the re-laid-out weights.  Negative
- * (minus an MOE_* code) for an invalid description. */
+ * front; run() allocates nothing: "ktransformers #2244", Design, one slot
+ * reserved before anything else claims the memory), and for the re-laid-out
+ * weights.  Negative (minus an MOE_* code) for an invalid description. */
 int64_t moe_fp8_prefill_workspace_bytes(const moe_fp8_prefill_desc* d);
 int64_t moe_fp8_prefill_weight_bytes(const moe_fp8_prefill_desc* d);
 
 /* Validates, allocates weights + workspace on the current device, uploads
- * and re-lays out the weights (NaN codes 0x7F/0xFF become 0x00/0x80, the I
- * edge is zero-padded), then synchronises.  *out stays NULL on error. */
+ * and re-lays out the weights (NaN codes 0x7F/0xFF become 0x00/0x80:
+ * "ktransformers #2245", Semantics and scope; the I edge is zero-padded:
+ * "hpc-ops #80", gap table row 6), then synchronises.  *out stays NULL on
+ * error. */
 int moe_fp8_prefill_create(const moe_fp8_prefill_desc* d, moe_fp8_prefill** out);
 
 /*
- * One prefill pass over T tokens, asynchronous on `stream` (hipStream_t; NULL
- * = null stream).  All pointers are device memory owned by the caller and must
+ * One prefill pass over T tokens ("TensorFold #2852", description: one call
+ * plans, runs the grouped gate+up with its epilogue, the grouped down and the
+ * combine for a whole prompt pass; "ktransformers #2244", Design: W8A8 with
+ * routed scaling), asynchronous on `stream` (hipStream_t; NULL = null
+ * stream).  All pointers are device memory owned by the caller and must
  * stay valid until the stream passes this call:
  *   x     : bf16 [T][H], 16-byte aligned
  *   ids   : i32 [T][k]; id < 0 is a skip slot (never loaded); id >= E is
@@ -255,10 +263,13 @@ int moe_fp8_prefill_stage(moe_fp8_prefill* h, int32_t slot, const uint8_t* gate,
 int moe_fp8_prefill_select_slot(moe_fp8_prefill* h, int32_t slot);
 
 /* Synchronises the handle's last stream; returns and clears device-detected
- * errors (MOE_ERR_BAD_EXPERT_ID), or MOE_ERR_FAILED_STATE, else MOE_OK. */
+ * errors (MOE_ERR_BAD_EXPERT_ID: "TensorFold #2852", an id outside the layer
+ * is never loaded), or MOE_ERR_FAILED_STATE ("ktransformers #2244", Design:
+ * fail closed), else MOE_OK. */
 int moe_fp8_prefill_status(moe_fp8_prefill* h);
 
-/* NULL-safe.  Synchronises, then frees everything. */
+/* NULL-safe.  Synchronises, then frees everything (library plumbing: no
+ * passage of the method). */
 void moe_fp8_prefill_destroy(moe_fp8_prefill* h);
 
 /* Static string for an MOE_* code. */
@@ -266,7 +277,8 @@ const char* moe_fp8_prefill_strerror(int code);
 
 /* ---- inspection (synchronous; for tests and tooling) ------------------ */
 
-/* The last pass's plan, copied to host buffers: counts i32[E], offsets
+/* The last pass's plan ("TensorFold #2852", description: the routing plan
+ * that groups a pass's slots by expert), copied to host buffers: counts i32[E], offsets
  * i32[E+1], perm i32[cap] (sorted position -> slot t*k+j), inv i32[cap]
  * (slot -> sorted position or -1).  cap must be >= that pass's T*k.  With a
  * shared expert, E and k here count it (E+1 experts, k+1 slots per token,
@@ -274,39 +286,45 @@ const char* moe_fp8_prefill_strerror(int code);
 int moe_fp8_prefill_debug_plan(moe_fp8_prefill* h, int32_t* counts, int32_t* offsets,
                                int32_t* perm, int32_t* inv, int64_t cap);
 
-/* The last pass's quantised activations: xq u8[rows][H], sx f32[rows][H/128]
- * (token order), rows = that pass's T. */
+/* The last pass's quantised activations (Q above: "ktransformers #2244",
+ * Design, FP8 activations; "hpc-ops #80", gap table row 6, 128-wide groups):
+ * xq u8[rows][H], sx f32[rows][H/128] (token order), rows = that pass's T. */
 int moe_fp8_prefill_debug_activations(moe_fp8_prefill* h, uint8_t* xq, float* sx,
                                       int64_t rows);
 
-/* The last pass's per-slot intermediates in sorted order: hq u8[n][Ip],
+/* The last pass's per-slot intermediates ("TensorFold #2852", description:
+ * the gate-up epilogue's quantised h and the grouped down's FP32 rows) in
+ * sorted order: hq u8[n][Ip],
  * sh f32[n][Ip/128], y f32[n][H]; n = number of routed slots (<= cap_rows).
  * Any pointer may be NULL. */
 int moe_fp8_prefill_debug_intermediates(moe_fp8_prefill* h, uint8_t* hq, float* sh,
                                         float* y, int64_t cap_rows, int64_t* n_rows);
 
-/* The last pass's FP32 gate and up outputs before the SiLU / quantisation
- * epilogue, gu f32[n][2*Ip] (gate columns then up columns, sorted order),
+/* The last pass's FP32 gate and up outputs ("TensorFold #2852", the grouped
+ * gate+up) before the SiLU / quantisation epilogue, gu f32[n][2*Ip] (gate columns then up columns, sorted order),
  * recomputed by re-running that pass's gate_up stage into a temporary device
  * buffer (this call allocates; it is an inspection tool). */
 int moe_fp8_prefill_debug_gate_up(moe_fp8_prefill* h, float* gu, int64_t cap_rows,
                                   int64_t* n_rows);
 
 /* Expert e's weights back in the canonical layout above (I rows / columns,
- * after NaN-code sanitising): gate, up u8[I][H]; down u8[H][I]; scales as in
+ * after NaN-code sanitising: "ktransformers #2245", Semantics and scope): gate, up u8[I][H]; down u8[H][I]; scales as in
  * the description.  Host buffers. */
 int moe_fp8_prefill_debug_unpack(moe_fp8_prefill* h, int32_t e, uint8_t* gate, uint8_t* up,
                                  uint8_t* down, float* gate_scale, float* up_scale,
                                  float* down_scale);
 
-/* One 16x16x128 FP8 MFMA through the library's operand convention, on the
- * current device: d[0][i][n] = sum_c dec(a[i][c]) * dec(b[n][c]); d[1] is the
+/* One 16x16x128 FP8 MFMA through the library's operand convention (a
+ * property of the hardware, checked by tests; no passage), on the current
+ * device: d[0][i][n] = sum_c dec(a[i][c]) * dec(b[n][c]); d[1] is the
  * same product as four 16x16x32 FP8 MFMAs chained through the accumulator,
  * d[2] as four independent 16x16x32 MFMAs summed in FP32.  Host buffers
  * a u8[16][128], b u8[16][128], d f32[3][16][16]. */
 int moe_fp8_prefill_debug_mfma(const uint8_t* a, const uint8_t* b, float* d);
 
-/* Per-launch GPU timing with HIP events on the run stream.  When enabled,
+/* Per-launch GPU timing with HIP events on the run stream (measurement
+ * plumbing; the per-call protocol of "ktransformers #2245", Real-checkpoint
+ * measurements, is the benchmark's).  When enabled,
  * every pass records events between its kernel launches; read_timing()
  * synchronises and returns up to max_records rows (one per pass) of
  * MOE_NUM_STAGES milliseconds: plan (with the router in run_logits),
@@ -347,8 +365,9 @@ enum { MOE_CALIBRATE_MFMA = 0, MOE_CALIBRATE_STREAM = 1 };
 int moe_fp8_prefill_calibrate(int32_t kind, int64_t n, void* buf, int64_t buf_bytes, void* stream,
                               double* work);
 
-/* Test hook: force the next run to behave as if a HIP call failed (host-side
- * flag only; no GPU fault is produced). */
+/* Test hook for the fail-closed rule ("ktransformers #2244", Design): force
+ * the next run to behave as if a HIP call failed (host-side flag only; no GPU
+ * fault is produced). */
 int moe_fp8_prefill_debug_inject_failure(moe_fp8_prefill* h);
 
 #ifdef __cplusplus
