@@ -891,10 +891,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
     const int rows_h = rows - mh * 128 < 0 ? 0 : (rows - mh * 128 > 128 ? 128 : rows - mh * 128);
     const int mtw = (rows_h + 15) >> 4;
 
-    // block 0 (issued before the previous epilogue) has landed everywhere,
-    // and the previous item's LDS is no longer read
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-    ring_barrier();
+    // The first item waits here for its block 0 and slot list.  A later
+    // item's block 0 (and its row scales) landed in the previous item's last
+    // K step, and the previous epilogue ended with a barrier after its last
+    // LDS read, so its h stores are not waited for.
+    if (r == 0) {
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+      ring_barrier();
+    }
     const Src cur = src_of(buf, it);
     // the next item's slots and weight scales into the other buffer (they
     // land with block 1)
@@ -923,14 +927,22 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
     // one K block over MT subtiles: issue block kb + 1 into the other stage
     // (read last step), multiply block kb out of stage s, wait for kb + 1,
     // then (waves 0-3) form block kb + 1's promotion factors
-    auto step = [&](auto S, auto MTC, int kb0) __attribute__((always_inline)) {
+    // LC: the last pair of steps, whose second step (next stage 0, read in
+    // the step before) loads the next item's block 0 and its row scales
+    // instead of the out-of-range block past this item's last one, so that
+    // block lands under this step's MFMAs rather than after the epilogue.
+    auto step = [&](auto S, auto MTC, auto LC, int kb0) __attribute__((always_inline)) {
       constexpr int s = decltype(S)::value, MT = decltype(MTC)::value;
+      constexpr bool kNextItem = decltype(LC)::value && s == 1;
       const int kb = kb0 + s;
       constexpr auto NEXT = std::integral_constant<int, 1 - s>{};
+      const Src src = kNextItem ? src_of(buf ^ 1, nit) : cur;
+      const int kn = kNextItem ? (has_next ? 0 : nH) : kb + 1;
+      if constexpr (kNextItem) issue_part(NEXT, std::integral_constant<int, 4>{}, kn, src);
       float rs = 0.f;
       // without subtiles to interleave with, block kb + 1's loads go first
       if constexpr (MT == 0) {
-        static_for<4>([&](auto PT) __attribute__((always_inline)) { issue_part(NEXT, PT, kb + 1, cur); });
+        static_for<4>([&](auto PT) __attribute__((always_inline)) { issue_part(NEXT, PT, kn, src); });
         if (wave < 4) rs = row_scale(kb + 1, cur);
       }
       if (MT > 0 && kb < nH) {
@@ -959,7 +971,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
           for (int t = 0; t < 4; ++t) P[t] = mfma_e4m3(B[t], A2[m & 1]);
           static_for<per>([&](auto J) __attribute__((always_inline)) {
             constexpr int q = m * per + decltype(J)::value;
-            if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kb + 1, cur);
+            if constexpr (q < 4) issue_part(NEXT, std::integral_constant<int, q>{}, kn, src);
           });
           if constexpr (m == 0) {
             if (wave < 4) rs = row_scale(kb + 1, cur);
@@ -978,7 +990,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
           __builtin_amdgcn_sched_barrier(0);
         });
       } else if constexpr (MT > 0) {
-        static_for<4>([&](auto PT) __attribute__((always_inline)) { issue_part(NEXT, PT, kb + 1, cur); });
+        static_for<4>([&](auto PT) __attribute__((always_inline)) { issue_part(NEXT, PT, kn, src); });
         if (wave < 4) rs = row_scale(kb + 1, cur);
       }
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block kb + 1 has landed
@@ -988,10 +1000,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
     };
     auto kloop = [&](auto MTC) __attribute__((always_inline)) {
       static_assert(NS == 2, "the K loop is unrolled by the stage count");
-      for (int kb0 = 0; kb0 < nH; kb0 += NS) {
-        step(std::integral_constant<int, 0>{}, MTC, kb0);
-        step(std::integral_constant<int, 1>{}, MTC, kb0);
+      int kb0 = 0;
+      for (; kb0 + NS < nH; kb0 += NS) {
+        step(std::integral_constant<int, 0>{}, MTC, std::false_type{}, kb0);
+        step(std::integral_constant<int, 1>{}, MTC, std::false_type{}, kb0);
       }
+      step(std::integral_constant<int, 0>{}, MTC, std::true_type{}, kb0);
+      step(std::integral_constant<int, 1>{}, MTC, std::true_type{}, kb0);
     };
     // every wave runs the same K loop and barriers; a half with few rows
     // multiplies fewer subtiles
@@ -1048,11 +1063,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void gate_up_wide_kernel(GateUpArg
       act(std::true_type{});
     else
       act(std::false_type{});
-    // Both stages are free (the last step waited for its out-of-range loads
-    // and every wave has passed its barrier): the next item's first K block
-    // goes to stage 0 now, under the rest of this epilogue, which stages h in
-    // stage 1.
-    if (has_next) issue(std::integral_constant<int, 0>{}, 0, src_of(buf ^ 1, nit));
+    // (the next item's first K block is in stage 0 already; this epilogue
+    // stages h in stage 1)
     for (int half = 0; half < 2 && half * 128 < rows; ++half) {
       if (mh == half) {
 #pragma unroll
