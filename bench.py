@@ -93,6 +93,16 @@ TITLES = {
     "slice_e160_t1024": "tensor-sliced share E=160 top-8 H=5120 I=192 (padded to 256), T=1024",
 }
 MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"
+# where the tile kernels' cycles go: three passes within rocprofv3's per-block
+# counter limits (8 SQ, 2 TA, 2 TD, 4 TCP, 2 GRBM)
+PIPE_COUNTERS = {
+    "pipe_a": "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS "
+              "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_VMEM GRBM_GUI_ACTIVE",
+    "pipe_b": "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES TA_TA_BUSY "
+              "TA_ADDR_STALLED_BY_TC_CYCLES TD_TD_BUSY TD_TC_STALL GRBM_GUI_ACTIVE",
+    "pipe_c": "TCP_TCC_READ_REQ_LATENCY TCP_TCC_READ_REQ TCP_PENDING_STALL_CYCLES SQ_INSTS_LDS SQ_INSTS_VALU "
+              "SQ_INSTS_MFMA SQ_INSTS_VMEM_RD GRBM_GUI_ACTIVE",
+}
 
 
 def profile_commands(tag):
@@ -102,6 +112,8 @@ def profile_commands(tag):
         "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof/fetch_{tag} -o pmc -- {b}",
         "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof/write_{tag} -o pmc -- {b}",
         "mfma": f"rocprofv3 --pmc {MFMA_COUNTERS} -f csv -d gpurun_out/prof/mfma_{tag} -o pmc -- {b}",
+        **{k: f"rocprofv3 --pmc {v} -f csv -d gpurun_out/prof/{k}_{tag} -o pmc -- {b}"
+           for k, v in PIPE_COUNTERS.items()},
     }
 
 
@@ -594,8 +606,59 @@ def summarize_profiles(out_dir: str) -> int:
             with open(os.path.join(PROFILES, f"mfma_{tag}.md"), "w") as f:
                 f.write("\n".join(lines) + "\n")
             wrote += 1
+        wrote += _pipe_summary(out_dir, tag, cmds, src)
     log(f"[bench] wrote {wrote} summaries")
     return 0 if wrote else 1
+
+
+def _pipe_summary(out_dir, tag, cmds, src):
+    """profiles/pipe_<tag>.md from the three pipe_* counter passes."""
+    vals = {}
+    for k in PIPE_COUNTERS:
+        rows = _csv_rows(os.path.join(out_dir, f"{k}_{tag}", "**", "*counter_collection.csv"))
+        if not rows:
+            return 0
+        names = {r["Counter_Name"] for r in rows}
+        for c in names:
+            for kern, (v, _n) in _per_kernel(rows, c).items():
+                vals.setdefault(kern, {})[c if c != "GRBM_GUI_ACTIVE" else f"GUI_{k}"] = v
+    cus, simds, xccs = 256, 1024, 8
+    lines = [f"# Where the cycles go, {TITLES[tag]}", "", "Commands (repository root, one MI355X), one pass each:", ""]
+    lines += [f"    {cmds[k]}" for k in PIPE_COUNTERS]
+    lines += ["", "Per launch, averaged over its dispatches.  C = one XCD's active cycles (GRBM_GUI_ACTIVE / "
+              f"{xccs}, from the same pass).  The SQ counts wave time in its own units, so the wave-time "
+              "fractions divide by SQ_WAVE_CYCLES: waiting = SQ_WAIT_INST_ANY (a wave stopped at a wait for "
+              "its own loads, LDS reads or stores), valu / lds / vmem = SQ_ACTIVE_INST_* (issuing that kind).  "
+              f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (C x {simds} SIMDs).  Per-CU unit busy = counter / "
+              f"(C x {cus} CUs): TA (address unit), TD (data return to VGPRs and LDS), LDS (SQ_LDS_IDX_ACTIVE); "
+              "TD stalled on TC = TD_TC_STALL / (C x 256).  L2 read latency = TCP_TCC_READ_REQ_LATENCY / "
+              "TCP_TCC_READ_REQ, in cycles.", "", f"- kernel_source_sha256_16: `{src}`", "",
+              "| kernel | MFMA busy | waiting | valu | lds | vmem | LDS busy | bank conflicts / LDS instr | "
+              "TA busy | TD busy | TD stalled on TC | L2 read latency | VALU instr / MFMA |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(vals):
+        v = vals[k]
+        if not (k.startswith("gate_up") or k.startswith("down") or k.startswith("combine")):
+            continue
+        if v.get("SQ_INSTS_VMEM_RD", 0.0) == 0.0:
+            continue  # a launch that found no work
+        ca = v["GUI_pipe_a"] / xccs
+        cb = v["GUI_pipe_b"] / xccs
+        wave = v["SQ_WAVE_CYCLES"] or float("nan")
+        lds_i = v.get("SQ_INSTS_LDS", 0.0)
+        mf = v.get("SQ_INSTS_MFMA", 0.0)
+        row = [v["SQ_VALU_MFMA_BUSY_CYCLES"] / (cb * simds), v["SQ_WAIT_INST_ANY"] / wave,
+               v["SQ_ACTIVE_INST_VALU"] / wave, v["SQ_ACTIVE_INST_LDS"] / wave, v["SQ_ACTIVE_INST_VMEM"] / wave,
+               v["SQ_LDS_IDX_ACTIVE"] / (cb * cus), (v["SQ_LDS_BANK_CONFLICT"] / lds_i) if lds_i else 0.0,
+               v["TA_TA_BUSY"] / (cb * cus), v["TD_TD_BUSY"] / (cb * cus), v["TD_TC_STALL"] / (cb * cus)]
+        lat = v["TCP_TCC_READ_REQ_LATENCY"] / v["TCP_TCC_READ_REQ"] if v.get("TCP_TCC_READ_REQ") else float("nan")
+        ratio = (v["SQ_INSTS_VALU"] - mf) / mf if mf else float("nan")
+        lines.append(f"| `{k}` | " + " | ".join(f"{x:.3f}" for x in row) + f" | {lat:.0f} | {ratio:.1f} |")
+    lines += ["", "Unit busy counters count a cycle in which the unit holds any work, waiting included, so "
+              "they bound the unit's share from above rather than measure its throughput."]
+    with open(os.path.join(PROFILES, f"pipe_{tag}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return 1
 
 
 # ------------------------------------------------------------------- main --

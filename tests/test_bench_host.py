@@ -126,3 +126,41 @@ def test_profile_summaries_round_trip(tmp_path, monkeypatch):
     # FETCH scaled by 2 (the copy reads half its bytes), WRITE by 1
     assert bench.read_traffic("gate_up_stream_kernel", tag) == (1001.0 * 2 + 10.0) * 1024
     assert (tmp_path / "profiles" / f"kernel_stats_{tag}.md").exists()
+
+
+def test_pipe_summary(tmp_path, monkeypatch):
+    """The memory-pipe summary turns the three counter passes into per-kernel
+    fractions (MFMA busy over C x 1024 SIMDs, waiting over wave time)."""
+    import bench
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    (tmp_path / "profiles").mkdir()
+    tag = "probe_e8_t4096"
+    k = "void moe::gate_up_wide_kernel<false>(moe::GateUpArgs)"
+    gui = 8 * 1000.0  # one XCD active for 1000 cycles
+    values = {
+        "pipe_a": {"SQ_WAVE_CYCLES": 2000.0, "SQ_WAIT_ANY": 500.0, "SQ_WAIT_INST_ANY": 800.0,
+                   "SQ_WAIT_INST_LDS": 100.0, "SQ_ACTIVE_INST_LDS": 150.0, "SQ_ACTIVE_INST_VALU": 900.0,
+                   "SQ_ACTIVE_INST_VMEM": 80.0, "GRBM_GUI_ACTIVE": gui},
+        "pipe_b": {"SQ_LDS_BANK_CONFLICT": 10.0, "SQ_LDS_IDX_ACTIVE": 76800.0,
+                   "SQ_VALU_MFMA_BUSY_CYCLES": 512000.0, "TA_TA_BUSY": 128000.0,
+                   "TA_ADDR_STALLED_BY_TC_CYCLES": 0.0, "TD_TD_BUSY": 192000.0, "TD_TC_STALL": 25600.0,
+                   "GRBM_GUI_ACTIVE": gui},
+        "pipe_c": {"TCP_TCC_READ_REQ_LATENCY": 30000.0, "TCP_TCC_READ_REQ": 100.0,
+                   "TCP_PENDING_STALL_CYCLES": 0.0, "SQ_INSTS_LDS": 100.0, "SQ_INSTS_VALU": 600.0,
+                   "SQ_INSTS_MFMA": 100.0, "SQ_INSTS_VMEM_RD": 50.0, "GRBM_GUI_ACTIVE": gui},
+    }
+    out = tmp_path / "prof"
+    for p, cs in values.items():
+        d = out / f"{p}_{tag}" / "host"
+        d.mkdir(parents=True)
+        with open(d / "pmc_counter_collection.csv", "w") as f:
+            f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+            for c, v in cs.items():
+                f.write(f'0,"{k}",{c},{v}\n')
+    cmds = bench.profile_commands(tag)
+    assert bench._pipe_summary(str(out), tag, cmds, "x") == 1
+    text = (tmp_path / "profiles" / f"pipe_{tag}.md").read_text()
+    # MFMA busy 0.5, waiting 0.4, valu 0.45, lds 0.075, vmem 0.04, LDS busy 0.3, conflicts 0.1,
+    # TA 0.5, TD 0.75, TD stalled 0.1, latency 300 cycles, 5 VALU per MFMA
+    assert ("| `gate_up_wide_kernel` | 0.500 | 0.400 | 0.450 | 0.075 | 0.040 | 0.300 | 0.100 | 0.500 | "
+            "0.750 | 0.100 | 300 | 5.0 |") in text
