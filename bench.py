@@ -298,17 +298,21 @@ def roofline(g, stage, launch_ms, peaks, a16=False):
     }
 
 
-def path_object(work, ms, peaks):
-    """The whole step against both peaks (algorithmic bytes and FLOPs)."""
+def path_object(work, ms, peaks, a16=False):
+    """The whole step against both peaks (algorithmic bytes and FLOPs); the
+    W8A16 decode path's products run on the BF16 MFMA, so its peak is BF16's."""
+    mfma_peak = PEAK_BF16_TFLOPS if a16 else PEAK_FP8_TFLOPS
     hbm = work["path_bytes"] / (ms * 1e-3) / 1e9
     mf = work["path_flops"] / (ms * 1e-3) / 1e12
-    roof_ms = max(work["path_bytes"] / (PEAK_HBM_GBS * 1e9), work["path_flops"] / (PEAK_FP8_TFLOPS * 1e12)) * 1e3
+    roof_ms = max(work["path_bytes"] / (PEAK_HBM_GBS * 1e9), work["path_flops"] / (mfma_peak * 1e12)) * 1e3
     o = {"algorithmic_bytes": work["path_bytes"], "algorithmic_flops": work["path_flops"],
-         "hbm_GBs": hbm, "hbm_frac": hbm / PEAK_HBM_GBS, "mfma_TFLOPs": mf, "mfma_frac": mf / PEAK_FP8_TFLOPS,
-         "roof_ms": roof_ms, "frac_of_roof": roof_ms / ms, "experts_hit": work["experts_hit"]}
+         "hbm_GBs": hbm, "hbm_frac": hbm / PEAK_HBM_GBS, "mfma_TFLOPs": mf, "mfma_frac": mf / mfma_peak,
+         "mfma_peak_TFLOPs": mfma_peak, "roof_ms": roof_ms, "frac_of_roof": roof_ms / ms,
+         "experts_hit": work["experts_hit"]}
     if peaks:
         o["hbm_frac_of_measured"] = hbm / peaks["hbm_read_GBs"]
-        o["mfma_frac_of_measured"] = mf / peaks["mfma_fp8_TFLOPs"]
+        if not a16:
+            o["mfma_frac_of_measured"] = mf / peaks["mfma_fp8_TFLOPs"]
     return o
 
 
@@ -419,7 +423,7 @@ def run_case(moe, case, args, peaks, stream, step_fn=None, a16=False):
     ms = elapsed * 1e3 / args.steps
     res["ms_per_step"] = ms
     res["tokens_per_s"] = wl.T * args.steps / elapsed
-    res["path"] = path_object(case.work, ms, peaks)
+    res["path"] = path_object(case.work, ms, peaks, a16=a16)
     if stage is not None and live is not None and len(live):
         launch_ms = float(live[:, pkg.STAGES.index(stage)].mean())
         passes = max(1, live.shape[0] // max(1, args.steps))

@@ -164,3 +164,15 @@ def test_pipe_summary(tmp_path, monkeypatch):
     # TA 0.5, TD 0.75, TD stalled 0.1, latency 300 cycles, 5 VALU per MFMA
     assert ("| `gate_up_wide_kernel` | 0.500 | 0.400 | 0.450 | 0.075 | 0.040 | 0.300 | 0.100 | 0.500 | "
             "0.750 | 0.100 | 300 | 5.0 |") in text
+
+
+def test_path_object_peaks():
+    """The path fraction takes the FP8 peak for W8A8 and the BF16 peak for
+    the W8A16 decode path."""
+    import bench
+    work = {"path_bytes": 8e9, "path_flops": 2.5e12, "experts_hit": 1}
+    w8 = bench.path_object(work, 1.0, None)
+    w16 = bench.path_object(work, 1.0, None, a16=True)
+    assert abs(w8["hbm_frac"] - 1.0) < 1e-12
+    assert abs(w8["mfma_frac"] - 0.5) < 1e-12 and abs(w16["mfma_frac"] - 1.0) < 1e-12
+    assert w16["mfma_peak_TFLOPs"] == bench.PEAK_BF16_TFLOPS
