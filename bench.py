@@ -84,13 +84,16 @@ PROFILED = {  # tag -> workload
     "glm_e256_t256": "glm_e256_k8_h6144_i2048_t256",
     "probe_e8_t4096": "probe_e8_k8_h6144_i2048_t4096",
     "slice_e160_t1024": "slice_e160_k8_h5120_i192_t1024",
+    "glm_e256_t4096_router": "glm_e256_k8_h6144_i2048_t4096_uniform",
 }
+PROFILE_ARGS = {"glm_e256_t4096_router": " --router"}  # extra bench arguments of a tag
 TITLES = {
     "glm_e256_t8192_zipf": "GLM-class layer E=256 top-8 H=6144 I=2048, T=8192 rows in one call, Zipf(1.2) routing",
     "glm_e256_t4096_uniform": "GLM-class layer E=256 top-8 H=6144 I=2048, T=4096 rows, uniform routing logits",
     "glm_e256_t256": "GLM-class layer E=256 top-8 H=6144 I=2048, T=256 rows",
     "probe_e8_t4096": "compute-bound probe: E=8, every token to all 8 experts, H=6144 I=2048, T=4096",
     "slice_e160_t1024": "tensor-sliced share E=160 top-8 H=5120 I=192 (padded to 256), T=1024",
+    "glm_e256_t4096_router": "GLM-class layer E=256 top-8 H=6144 I=2048, T=4096 rows from router logits",
 }
 MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"
 # where the tile kernels' cycles go: three passes within rocprofv3's per-block
@@ -106,7 +109,7 @@ PIPE_COUNTERS = {
 
 
 def profile_commands(tag):
-    b = f"{_BENCH1} --workload {PROFILED[tag]}"
+    b = f"{_BENCH1} --workload {PROFILED[tag]}{PROFILE_ARGS.get(tag, '')}"
     return {
         "trace": f"rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof/kt_{tag} -o kt -- {b}",
         "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof/fetch_{tag} -o pmc -- {b}",
