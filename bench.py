@@ -760,6 +760,9 @@ def main() -> int:
     ap.add_argument("--decode", type=int, default=0, metavar="T",
                     help="time the W8A16 decode path (run_decode) on the first T rows of the workload's "
                          "batch instead of the W8A8 prefill path")
+    ap.add_argument("--rows", type=int, default=0, metavar="T",
+                    help="the chosen workload's layer and routing recipe with T rows instead (one call "
+                         "up to 8192 rows, passes of 8192 above)")
     ap.add_argument("--router", action="store_true",
                     help="start each step from FP32 router logits (run_logits: on-device top-k router, then "
                          "the path) instead of given ids and weights")
@@ -810,6 +813,10 @@ def main() -> int:
         return 0
 
     wl = gen.WORKLOADS[args.workload or HEADLINE]
+    if args.rows > 0:
+        base = wl.name.rsplit("_t", 1)[0] if "_t" in wl.name else wl.name
+        suffix = wl.name.rsplit("_t", 1)[1].lstrip("0123456789") if "_t" in wl.name else ""
+        wl = dataclasses.replace(wl, T=args.rows, name=f"{base}_t{args.rows}{suffix}")
     log(f"[bench] generating {wl.name}")
     t0 = time.perf_counter()
     layer = gen.make_layer(wl.E + wl.shared, wl.H, wl.I, seed=wl.seed)
@@ -875,7 +882,7 @@ def main() -> int:
                          "avg_launch_us": r_us, "algorithmic_bytes": r_bytes, "GBs": r_bytes / (r_us * 1e-6) / 1e9,
                          "ids_equal_given": bool(torch.equal(ids_r, head.idd))}
 
-    if args.workload is None and not a16 and not args.router:
+    if args.workload is None and args.rows == 0 and not a16 and not args.router:
         subs = {}
         for key, name, rpc in SUBS:
             swl = gen.WORKLOADS[name]
