@@ -2264,8 +2264,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   auto load = [&](int j, f32x4 (&v)[2]) __attribute__((always_inline)) {
     const int p = pos[j];
     const f32x4* src = reinterpret_cast<const f32x4*>(a.y + (size_t)(p >= 0 ? p : 0) * H + c);
-    // plain loads: y was written just before, partly still in the caches
-    // (non-temporal loads measured 3% slower at T = 4096)
+    // plain loads (non-temporal ones measured 3-7% slower)
     v[0] = src[0];
     v[1] = src[1];
   };
