@@ -1854,18 +1854,24 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
     asm volatile("" : "+v"(etid));
     const int ecol = etid & 15, egrp = (etid >> 4) & 3;
     // y leaves through this wave's own four 1 KiB blocks of stage 1 (those
-    // its DMA fills next), 16 rows at a time: lane (r, g) writes chunks
-    // 4 t + g of row r, then reads back 4 rows x 16 chunks, so each store
-    // writes four whole 256-byte row segments (16-byte stores straight from
-    // the MFMA layout cover 16 rows x 64 bytes each and measured 4-6% slower
-    // for the whole kernel).  Chunk c of row r sits in slot c ^ r; row r is
-    // at (r / 4) x 8 KiB + (r % 4) x 256.  The stores are non-temporal: the
-    // combine that reads y runs 3-19% faster when no dirty y lines are left
-    // in the caches to be written back under it.
-    uint8_t* yst = a_lds1 + wave * 1024;
+    // its DMA fills next), 16 rows at a time, alternating between the a and
+    // the w blocks so one subtile's LDS writes need not wait for the previous
+    // one's reads: lane (r, g) writes chunks 4 t + g of row r, then reads back
+    // 4 rows x 16 chunks, so each store writes four whole 256-byte row
+    // segments (16-byte stores straight from the MFMA layout cover 16 rows x
+    // 64 bytes each and measured 4-6% slower for the whole kernel).  Chunk c
+    // of row r sits in slot c ^ r; row r is at (r / 4) x 8 KiB + (r % 4) x
+    // 256.  The stores go through a buffer descriptor of this item's rows, so
+    // stores to rows past the tile fall outside it and are dropped (no branch
+    // per store), with the non-temporal policy: the combine that reads y runs
+    // 3-19% faster when no dirty y lines are left in the caches to be written
+    // back under it.
+    const rsrc_t yr = make_rsrc(a.y + (size_t)p0 * H, (uint32_t)(rows * H * 4));
+    const uint32_t ycol = (uint32_t)((nb2 + half) * kBlock + (wn & 1) * 64 + ecol * 4) * 4u;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       if (m < mtw) {
+        uint8_t* yst = ((m & 1) ? w_lds1 : a_lds1) + wave * 1024;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           *reinterpret_cast<f32x4*>(yst + (ecol >> 2) * 8192 + (ecol & 3) * 256 + (((4 * t + egrp) ^ ecol) << 4)) =
@@ -1876,8 +1882,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void down_wide_kernel(DownArgs a) 
           v[j] = *reinterpret_cast<const f32x4*>(yst + j * 8192 + egrp * 256 + ((ecol ^ (4 * j + egrp)) << 4));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int row = mh * 128 + m * 16 + 4 * j + egrp;
-          if (row < rows) __builtin_nontemporal_store(v[j], reinterpret_cast<f32x4*>(a.y + (size_t)(p0 + row) * H + (nb2 + half) * kBlock + (wn & 1) * 64 + ecol * 4));
+          const uint32_t row = (uint32_t)(mh * 128 + m * 16 + 4 * j + egrp);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v[j]), yr, row * (uint32_t)H * 4u + ycol, 0,
+                                                 kWeightAux);
         }
       }
     }
