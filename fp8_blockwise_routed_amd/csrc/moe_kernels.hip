@@ -527,10 +527,17 @@ struct Item {
   int e, p0, rows, nb;
 };
 
+// The tile lists are written by the plan launch and only read afterwards, so
+// the GEMMs read them through the scalar cache (constant address space): a
+// vector load would count in vmcnt, and waiting for it would also wait for
+// every operand load the wave has in flight.
+typedef const __attribute__((address_space(4))) Tile* ctile_ptr;
+
 // All fields are workgroup-uniform; readfirstlane keeps them in SGPRs so the
 // buffer descriptors built from them stay scalar.
-__device__ __forceinline__ Item item_of(int i, int NB, const Tile* tiles) {
+__device__ __forceinline__ Item item_of(int i, int NB, const Tile* tiles_) {
   constexpr int IT = kItemTiles, IB = kItemBlocks;
+  const ctile_ptr tiles = (ctile_ptr)tiles_;
   const int tg = i / NB;
   const int first = __builtin_amdgcn_readfirstlane(tiles[tg].first);
   const int me = __builtin_amdgcn_readfirstlane(tiles[tg].count);
@@ -549,7 +556,7 @@ __device__ __forceinline__ Item item_of(int i, int NB, const Tile* tiles) {
   const int mb = rem / per_mb;
   const int r2 = rem - mb * per_mb;
   const int m_in = r2 / nbs;
-  const Tile* t = tiles + first + mb * IT + m_in;
+  const ctile_ptr t = tiles + first + mb * IT + m_in;
   Item it;
   it.e = __builtin_amdgcn_readfirstlane(t->e);
   it.p0 = __builtin_amdgcn_readfirstlane(t->p0);
@@ -632,8 +639,8 @@ __global__ __launch_bounds__(kThreads, kGateUpWgPerCu) void gate_up_stream_kerne
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int tile = item / NB, nb = item - tile * NB;
-    const Tile td = a.tiles[tile];
-    const int e = td.e, p0 = td.p0, rows = td.rows;
+    const ctile_ptr td = (ctile_ptr)a.tiles + tile;
+    const int e = td->e, p0 = td->p0, rows = td->rows;
 
     __syncthreads();  // LDS of the previous item is no longer read
     if (tid < BM) tok_lds[tid] = a.perm[p0 + (tid < rows ? tid : 0)] / a.k;
