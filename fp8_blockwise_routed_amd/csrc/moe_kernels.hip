@@ -756,9 +756,11 @@ __global__ __launch_bounds__(kThreads, kGateUpWgPerCu) void gate_up_stream_kerne
 // MFMAs and promotion order as the streaming kernel.
 //
 // Per K block the tile moves 64 KiB through the vector memory pipe for
-// 256 x 256 x 128 MACs, about two thirds of the MFMA time at peak; a 128-row
-// tile would move 48 KiB for half the MACs.  Block kb + 1 is loaded while
-// block kb is multiplied, and each K step ends with vmcnt(0) and a barrier.
+// 256 x 256 x 128 MACs: half the MFMA time at peak, at the ~64 bytes per
+// cycle a CU's loads reach from L2 when enough are in flight; a 128-row tile
+// would move 48 KiB for half the MACs.  Two 64 KiB stages are all the LDS
+// holds, so block kb + 1 is loaded while block kb is multiplied and each K
+// step ends with vmcnt(0) and a barrier: the loads drain at every step's end.
 // A half with few rows multiplies fewer 16-row subtiles (8, 4 or none) but
 // runs the same loads and barriers.
 constexpr int kWideThreads = 512;
