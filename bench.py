@@ -108,22 +108,26 @@ PIPE_COUNTERS = {
 }
 
 
+# raw rocprofv3 output of the profile runs (read back by --summarize-profiles)
+PROF_RAW = "rocprof_raw"
+
+
 def profile_commands(tag):
     b = f"{_BENCH1} --workload {PROFILED[tag]}{PROFILE_ARGS.get(tag, '')}"
     return {
-        "trace": f"rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof/kt_{tag} -o kt -- {b}",
-        "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof/fetch_{tag} -o pmc -- {b}",
-        "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof/write_{tag} -o pmc -- {b}",
-        "mfma": f"rocprofv3 --pmc {MFMA_COUNTERS} -f csv -d gpurun_out/prof/mfma_{tag} -o pmc -- {b}",
-        **{k: f"rocprofv3 --pmc {v} -f csv -d gpurun_out/prof/{k}_{tag} -o pmc -- {b}"
+        "trace": f"rocprofv3 --kernel-trace --stats -f csv -d {PROF_RAW}/kt_{tag} -o kt -- {b}",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {PROF_RAW}/fetch_{tag} -o pmc -- {b}",
+        "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {PROF_RAW}/write_{tag} -o pmc -- {b}",
+        "mfma": f"rocprofv3 --pmc {MFMA_COUNTERS} -f csv -d {PROF_RAW}/mfma_{tag} -o pmc -- {b}",
+        **{k: f"rocprofv3 --pmc {v} -f csv -d {PROF_RAW}/{k}_{tag} -o pmc -- {b}"
            for k, v in PIPE_COUNTERS.items()},
     }
 
 
 COPY_COMMANDS = {
-    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof/copy_fetch -o pmc -- "
+    "copy_fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {PROF_RAW}/copy_fetch -o pmc -- "
                   "python3 bench.py --copy-calibration",
-    "copy_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof/copy_write -o pmc -- "
+    "copy_write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {PROF_RAW}/copy_write -o pmc -- "
                   "python3 bench.py --copy-calibration",
 }
 
